@@ -47,6 +47,13 @@ def lib() -> ctypes.CDLL:
         L.or_gated_rmsnorm.argtypes = [_p, _p, _p, _i, _p]
         L.or_layer_step.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]
         L.or_layer_step.restype = _i
+        L.or_quant_forced.argtypes = [_p, _i, _p, ctypes.c_double, _p, _p]
+        L.or_quant_forced.restype = _i
+        L.or_layer_step_forced.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_double,
+                                           _p]
+        L.or_layer_step_forced.restype = _i
+        L.or_lm_head_forced.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_double, _p]
+        L.or_lm_head_forced.restype = _i
         L.or_lm_head.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p]
         L.or_lm_head.restype = _i
         L.or_embed.argtypes = [_p, _p, _p, _i, _p]
@@ -89,6 +96,28 @@ def quant(u) -> Tuple[np.ndarray, np.float32]:
     s = np.zeros(1, dtype=np.float32)
     lib().or_quant(_ptr(u), u.size, _ptr(q), _ptr(s))
     return q, s[0]
+
+
+# Half-width, in units of the int8 step, of the band around a rounding tie in
+# which a code one away from the oracle's own is still a correct result.  An
+# fp32 implementation's scaled value u * 127 / amax differs from the oracle's
+# by its accumulated rounding error: a few ulp of u after the residual stream
+# has gone through the stack (relative 1e-6 at most), times |u * 127/amax|
+# <= 127, i.e. below 1.3e-4; the band keeps a margin of about 8x over that.
+TIE_BAND = 1e-3
+
+
+def quant_forced(u, force, delta: float = TIE_BAND) -> Tuple[np.ndarray, np.float32, int]:
+    """Quantise u (fp64) taking the proposed codes where they are valid roundings.
+
+    Returns (q, s, number of rejected proposals)."""
+    u = _c(u, np.float64)
+    force = _c(force, np.int8)
+    assert force.size == u.size
+    q = np.empty(u.size, dtype=np.int8)
+    s = np.zeros(1, dtype=np.float32)
+    bad = lib().or_quant_forced(_ptr(u), u.size, _ptr(force), float(delta), _ptr(q), _ptr(s))
+    return q, s[0], bad
 
 
 def rmsnorm(x, w) -> np.ndarray:
@@ -204,10 +233,16 @@ class State:
         return c
 
 
+class ForcedCodeError(AssertionError):
+    """A proposed int8 code is not a correct rounding of the oracle's value."""
+
+
 def layer_step(s: Shape, layer: Dict[str, np.ndarray], h_in, conv_state: np.ndarray, ssm_state: np.ndarray,
-               want_dbg: bool = False):
+               want_dbg: bool = False, q1_force=None, q2_force=None, delta: float = TIE_BAND):
     """One layer, one token. conv_state [conv_dim][K-1] and ssm_state [H][P][N] (fp64) update in place.
 
+    q1_force / q2_force (optional int8 codes) are taken where they are correct
+    roundings (see quant_forced); any other proposal raises ForcedCodeError.
     Returns h_out, or (h_out, dbg dict) with the intermediate vectors and the
     int8 activations (q1, s1, q2, s2) when want_dbg is set.
     """
@@ -226,10 +261,20 @@ def layer_step(s: Shape, layer: Dict[str, np.ndarray], h_in, conv_state: np.ndar
     s1 = np.zeros(1, dtype=np.float32)
     s2 = np.zeros(1, dtype=np.float32)
     sh = _shape_arr(s)
-    rc = lib().or_layer_step(_ptr(sh), lw, _ptr(h_in), _ptr(conv_state), _ptr(ssm_state), _ptr(h_out),
-                             _ptr(dbg), _ptr(q1), _ptr(s1), _ptr(q2), _ptr(s2))
+    f1 = None if q1_force is None else _c(q1_force, np.int8)
+    f2 = None if q2_force is None else _c(q2_force, np.int8)
+    if f1 is not None:
+        assert f1.size == s.d_model
+    if f2 is not None:
+        assert f2.size == s.d_inner
+    rej = np.zeros(1, dtype=np.int32)
+    rc = lib().or_layer_step_forced(_ptr(sh), lw, _ptr(h_in), _ptr(conv_state), _ptr(ssm_state), _ptr(h_out),
+                                    _ptr(dbg), _ptr(q1), _ptr(s1), _ptr(q2), _ptr(s2), _ptr(f1), _ptr(f2),
+                                    float(delta), _ptr(rej))
     if rc != 0:
         raise OverflowError("integer accumulator overflow")
+    if rej[0]:
+        raise ForcedCodeError(f"{int(rej[0])} proposed int8 codes are not correct roundings")
     if not want_dbg:
         return h_out
     d = {k: dbg[a:b].copy() for k, (a, b) in lay.items() if k != "_total"}
@@ -282,7 +327,8 @@ class Model:
             raise ValueError("token out of range or accumulator overflow")
         return nxt, logits
 
-    def lm_head(self, h):
+    def lm_head(self, h, qf_force=None, delta: float = TIE_BAND):
+        """Final norm + tied int8 LM head. Returns (argmax, logits, qf, sf)."""
         s = self.s
         h = _c(h, np.float64)
         logits = np.empty(s.vocab, dtype=np.float64)
@@ -291,8 +337,13 @@ class Model:
         E = self.weights["E"]
         sE = self.weights["sE"]
         fn = self.weights["final_norm"]
-        best = lib().or_lm_head(_ptr(self._sh), _ptr(np.ascontiguousarray(E)), _ptr(np.ascontiguousarray(sE)),
-                                _ptr(np.ascontiguousarray(fn)), _ptr(h), _ptr(logits), _ptr(qf), _ptr(sf))
+        ff = None if qf_force is None else _c(qf_force, np.int8)
+        rej = np.zeros(1, dtype=np.int32)
+        best = lib().or_lm_head_forced(_ptr(self._sh), _ptr(np.ascontiguousarray(E)), _ptr(np.ascontiguousarray(sE)),
+                                       _ptr(np.ascontiguousarray(fn)), _ptr(h), _ptr(logits), _ptr(qf), _ptr(sf),
+                                       _ptr(ff), float(delta), _ptr(rej))
+        if rej[0]:
+            raise ForcedCodeError(f"{int(rej[0])} proposed int8 codes are not correct roundings")
         return best, logits, qf, sf[0]
 
     def embed(self, tok: int) -> np.ndarray:

@@ -89,6 +89,39 @@ void or_quant(const double* u, int n, int8_t* q, float* s_out) {
   free(uf);
 }
 
+/* Several roundings are correct near a tie.  An implementation that computes
+ * u in fp32 may land on the other side of a rounding tie than this oracle
+ * when u * 127/amax lies within its own rounding error of k + 1/2.  Such a
+ * code is accepted here: `force` (nullable) proposes codes; a proposed code
+ * is taken only if it equals the oracle's own code, or differs from it by
+ * one with the oracle's scaled value within `delta` of the tie between the
+ * two.  Returns the number of proposed codes that were rejected (then q holds
+ * the oracle's own codes).                                                   */
+int or_quant_forced(const double* u, int n, const int8_t* force, double delta, int8_t* q, float* s_out) {
+  float* uf = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+  for (int i = 0; i < n; ++i) uf[i] = (float)u[i];
+  or_quant_f32(uf, n, q, s_out);
+  int bad = 0;
+  if (force && *s_out > 0.0f) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) if (fabsf(uf[i]) > amax) amax = fabsf(uf[i]);
+    const float inv = 127.0f / amax;
+    for (int i = 0; i < n; ++i) {
+      if (force[i] == q[i]) continue;
+      const int d = (int)force[i] - (int)q[i];
+      const double x = (double)(uf[i] * inv);
+      const double tie = (double)q[i] + 0.5 * d;
+      if ((d == 1 || d == -1) && fabs(x - tie) <= delta) q[i] = force[i];
+      else ++bad;
+    }
+    if (bad) or_quant_f32(uf, n, q, s_out);
+  } else if (force) {
+    for (int i = 0; i < n; ++i) bad += force[i] != 0;
+  }
+  free(uf);
+  return bad;
+}
+
 /* ------------------------------------------------------------------------ */
 /* RMSNorm: u = x / sqrt(mean(x^2) + eps) * w. */
 void or_rmsnorm(const double* x, const float* w, int n, double* u) {
@@ -221,9 +254,10 @@ void or_gated_rmsnorm(const double* y, const double* z, const float* w, int n, d
  *   | u2[d_inner] | out[d_model].
  * q1/s1, q2/s2 (nullable): the int8 activations and scales fed to in_proj and
  * out_proj.                                                                   */
-int or_layer_step(const int* sh, const void* const* lw, const double* h_in,
-                  double* conv_state, double* ssm_state, double* h_out, double* dbg,
-                  int8_t* q1_out, float* s1_out, int8_t* q2_out, float* s2_out) {
+int or_layer_step_forced(const int* sh, const void* const* lw, const double* h_in,
+                         double* conv_state, double* ssm_state, double* h_out, double* dbg,
+                         int8_t* q1_out, float* s1_out, int8_t* q2_out, float* s2_out,
+                         const int8_t* q1_force, const int8_t* q2_force, double delta, int* rejected) {
   const int dm = sh[SH_DM], di = sh[SH_DI], ds = sh[SH_DS], hd = sh[SH_HD], K = sh[SH_K], r = sh[SH_R];
   const int H = di / hd, cdim = di + 2 * ds, dproj = 2 * di + 2 * ds + H;
   double* u = (double*)malloc(sizeof(double) * (size_t)dm);
@@ -238,8 +272,9 @@ int or_layer_step(const int* sh, const void* const* lw, const double* h_in,
   float s1, s2;
   int rc = 0;
 
+  int rej = 0;
   or_rmsnorm(h_in, (const float*)lw[T_NORM_W], dm, u);
-  or_quant(u, dm, q1, &s1);
+  rej += or_quant_forced(u, dm, q1_force, delta, q1, &s1);
   rc |= or_proj((const uint32_t*)lw[T_IN_BITS], (const float*)lw[T_IN_SW], (const int8_t*)lw[T_IN_A],
                 (const float*)lw[T_IN_SA], (const int8_t*)lw[T_IN_B], (const float*)lw[T_IN_SB],
                 dm, dproj, r, q1, s1, zx, NULL, NULL);
@@ -250,7 +285,8 @@ int or_layer_step(const int* sh, const void* const* lw, const double* h_in,
   or_ssm_step(xc, xc + di, xc + di + ds, dt_raw, (const float*)lw[T_A_LOG], (const float*)lw[T_DT_BIAS],
               (const float*)lw[T_D], H, hd, ds, ssm_state, y, dt);
   or_gated_rmsnorm(y, z, (const float*)lw[T_GNORM_W], di, u2);
-  or_quant(u2, di, q2, &s2);
+  rej += or_quant_forced(u2, di, q2_force, delta, q2, &s2);
+  if (rejected) *rejected = rej;
   rc |= or_proj((const uint32_t*)lw[T_OUT_BITS], (const float*)lw[T_OUT_SW], (const int8_t*)lw[T_OUT_A],
                 (const float*)lw[T_OUT_SA], (const int8_t*)lw[T_OUT_B], (const float*)lw[T_OUT_SB],
                 di, dm, r, q2, s2, out, NULL, NULL);
@@ -273,20 +309,29 @@ int or_layer_step(const int* sh, const void* const* lw, const double* h_in,
   return rc;
 }
 
+int or_layer_step(const int* sh, const void* const* lw, const double* h_in,
+                  double* conv_state, double* ssm_state, double* h_out, double* dbg,
+                  int8_t* q1_out, float* s1_out, int8_t* q2_out, float* s2_out) {
+  return or_layer_step_forced(sh, lw, h_in, conv_state, ssm_state, h_out, dbg, q1_out, s1_out, q2_out, s2_out,
+                              NULL, NULL, 0.0, NULL);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Tied int8 LM head (gist.science summary §2.B: embedding / LM head int8 with
  * per-row scales; §3 size composition: one int8 copy):
  *   logits[v] = (sum_i E[v][i] qf_i) * sE[v] * sf.  Returns argmax, lowest
  *   index on ties.                                                          */
-int or_lm_head(const int* sh, const int8_t* E, const float* sE, const float* fnorm,
-               const double* h, double* logits, int8_t* qf_out, float* sf_out) {
+int or_lm_head_forced(const int* sh, const int8_t* E, const float* sE, const float* fnorm,
+                      const double* h, double* logits, int8_t* qf_out, float* sf_out,
+                      const int8_t* qf_force, double delta, int* rejected) {
   const int dm = sh[SH_DM], V = sh[SH_V];
   double* u = (double*)malloc(sizeof(double) * (size_t)dm);
   int8_t* qf = (int8_t*)malloc((size_t)dm);
   int64_t* acc = (int64_t*)malloc(sizeof(int64_t) * (size_t)V);
   float sf;
   or_rmsnorm(h, fnorm, dm, u);
-  or_quant(u, dm, qf, &sf);
+  int rej = or_quant_forced(u, dm, qf_force, delta, qf, &sf);
+  if (rejected) *rejected = rej;
   int8_matvec(E, V, dm, qf, acc);
   int best = 0;
   for (int v = 0; v < V; ++v) {
@@ -297,6 +342,11 @@ int or_lm_head(const int* sh, const int8_t* E, const float* sE, const float* fno
   if (sf_out) *sf_out = sf;
   free(u); free(qf); free(acc);
   return best;
+}
+
+int or_lm_head(const int* sh, const int8_t* E, const float* sE, const float* fnorm,
+               const double* h, double* logits, int8_t* qf_out, float* sf_out) {
+  return or_lm_head_forced(sh, E, sE, fnorm, h, logits, qf_out, sf_out, NULL, 0.0, NULL);
 }
 
 /* Embedding lookup with the tied table: h[i] = E[tok][i] * sE[tok]. */

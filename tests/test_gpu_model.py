@@ -1,0 +1,237 @@
+"""Whole-layer and whole-model parity of the GPU path against the CPU oracle,
+plus the invariants the path must keep (prefill == decode loop, batch
+independence, determinism, state round trip, graph replay == eager)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._common import assert_close, engine, rel_err, token_ok
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+# ---------------------------------------------------------------------------
+# one layer, state carried over steps (tiny and 1.3B-shaped)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape,steps", [(synth.TINY, 50), (synth.LAYER_1P3B, 12)])
+def test_layer_steps_match_oracle(shape, steps):
+    seed = synth.SEED_BASE + 1
+    eng = engine(shape)
+    eng.load_synthetic(seed)
+    lay = synth.gen_layer(shape, seed, 0)
+    cs = np.zeros((shape.conv_dim, shape.d_conv - 1))
+    ss = np.zeros((shape.n_heads, shape.headdim, shape.d_state))
+    worst = 0.0
+    for t in range(steps):
+        h16 = synth.gen_fp16_normal(seed, 1, shape.d_model, start=t * shape.d_model)
+        h = h16.astype(np.float32)
+        hg = eng.layer_step(0, torch.from_numpy(h[None]).cuda()).cpu().numpy()[0]
+        ho = oracle.layer_step(shape, lay, h.astype(np.float64), cs, ss)
+        # compare the mixer output (h_out - h_in) and the residual stream
+        worst = max(worst, rel_err(hg - h, ho - h))
+        assert_close(hg, ho, what=f"h_out step {t}")
+    conv_g, ssm_g = eng.get_state(0)
+    assert_close(conv_g[0], cs, what="conv state")
+    assert_close(ssm_g[0], ss, what="ssm state")
+    assert worst <= 5e-3, worst
+    eng.close()
+
+
+# ---------------------------------------------------------------------------
+# tiny model: 64 greedy decode steps, teacher-forced on the GPU's tokens
+# ---------------------------------------------------------------------------
+
+def test_tiny_decode_64_steps():
+    s = synth.TINY
+    seed = synth.SEED_BASE
+    eng = engine(s)
+    eng.load_synthetic(seed)
+    om = oracle.Model(s, synth.gen_model(s, seed))
+    st = oracle.State(s)
+    tok = int(synth.gen_tokens(seed, 0, 1, s.vocab)[0])
+    tt = _i32([tok])
+    for step in range(64):
+        logits, nxt = eng.decode_step(tt)
+        lg = logits.cpu().numpy()[0]
+        gtok = int(nxt.cpu().numpy()[0])
+        otok, ol, _ = om.decode_step(st, tok)
+        assert_close(lg, ol, what=f"logits step {step}")
+        assert gtok == int(np.argmax(lg))
+        assert token_ok(gtok, ol), (step, gtok, otok)
+        tok = gtok
+        tt = _i32([tok])
+    conv_g, ssm_g = eng.get_state(0)
+    assert_close(conv_g, st.conv, what="conv state")
+    assert_close(ssm_g, st.ssm, what="ssm state")
+    eng.check()
+    eng.close()
+
+
+# ---------------------------------------------------------------------------
+# full 48-layer model, batch 1: per-layer teacher forcing through the trace
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def full_model():
+    s = synth.FULL_1P3B
+    seed = synth.SEED_BASE + 2
+    w = synth.gen_model(s, seed)
+    return s, seed, w, oracle.Model(s, w)
+
+
+def test_full_model_layerwise_teacher_forced(full_model):
+    s, seed, w, om = full_model
+    eng = engine(s)
+    eng.load_synthetic(seed)
+    toks = synth.gen_tokens(seed, 0, 3, s.vocab)
+    st = oracle.State(s)
+    for step, tok in enumerate(toks):
+        trace, logits = eng.trace_step(_i32([tok]))
+        tr = trace.cpu().numpy()[:, 0, :].astype(np.float64)
+        assert np.array_equal(tr[0], om.embed(int(tok)).astype(np.float32).astype(np.float64))
+        for l in range(s.n_layer):
+            ho = oracle.layer_step(s, w["layers"][l], tr[l], st.conv[l], st.ssm[l])
+            assert_close(tr[l + 1] - tr[l], ho - tr[l], tol=5e-3, what=f"mixer out step {step} layer {l}")
+            assert_close(tr[l + 1], ho, what=f"h step {step} layer {l}")
+        best, ol, _, _ = om.lm_head(tr[-1])
+        assert_close(logits.cpu().numpy()[0], ol, what=f"logits step {step}")
+    eng.close()
+
+
+def test_full_model_free_running_logits(full_model):
+    # no teacher forcing inside the stack: 4 decode steps, logits within tolerance
+    s, seed, w, om = full_model
+    eng = engine(s)
+    eng.load_synthetic(seed)
+    st = oracle.State(s)
+    tok = int(synth.gen_tokens(seed, 0, 1, s.vocab)[0])
+    errs = []
+    for step in range(4):
+        logits, nxt = eng.decode_step(_i32([tok]))
+        otok, ol, _ = om.decode_step(st, tok)
+        errs.append(rel_err(logits.cpu().numpy()[0], ol))
+        gtok = int(nxt.cpu().numpy()[0])
+        assert token_ok(gtok, ol, tol=1e-2), (step, gtok, otok)
+        tok = gtok
+    print("free-running logit errors", errs)
+    assert max(errs) <= 1e-2, errs
+    eng.close()
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+def test_prefill_then_decode_equals_decode_loop():
+    s = synth.TINY
+    eng = engine(s, max_batch=2)
+    eng.load_synthetic(synth.SEED_BASE)
+    toks = synth.gen_tokens(synth.SEED_BASE, 3, 2 * 9, s.vocab).reshape(2, 9)
+    eng.reset_state(2)
+    lg_p, nx_p = eng.prefill(_i32(toks[:, :8]))
+    st_p = [eng.get_state(b) for b in range(2)]
+    eng.reset_state(2)
+    for t in range(8):
+        lg_d, nx_d = eng.decode_step(_i32(toks[:, t]))
+    st_d = [eng.get_state(b) for b in range(2)]
+    assert torch.equal(lg_p, lg_d) and torch.equal(nx_p, nx_d)
+    for b in range(2):
+        assert np.array_equal(st_p[b][0], st_d[b][0]) and np.array_equal(st_p[b][1], st_d[b][1])
+    eng.close()
+
+
+def test_batch_independence():
+    s = synth.TINY
+    B = 5
+    toks = synth.gen_tokens(synth.SEED_BASE, 4, B * 6, s.vocab).reshape(B, 6)
+    eng = engine(s, max_batch=B)
+    eng.load_synthetic(synth.SEED_BASE)
+    eng.reset_state(B)
+    lg_b, _ = eng.prefill(_i32(toks))
+    one = engine(s, max_batch=1)
+    one.load_synthetic(synth.SEED_BASE)
+    for b in range(B):
+        one.reset_state(1)
+        lg_1, _ = one.prefill(_i32(toks[b:b + 1]))
+        assert torch.equal(lg_b[b], lg_1[0]), b
+        assert np.array_equal(eng.get_state(b)[1], one.get_state(0)[1]), b
+    eng.close()
+    one.close()
+
+
+def test_run_to_run_determinism():
+    s = synth.TINY
+    outs = []
+    for _ in range(2):
+        eng = engine(s)
+        eng.load_synthetic(synth.SEED_BASE)
+        tok = _i32([7])
+        out = eng.generate(tok, 20, use_graph=False)
+        outs.append(out.cpu().numpy())
+        eng.close()
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_graph_replay_equals_eager():
+    s = synth.TINY
+    eng = engine(s, max_batch=3)
+    eng.load_synthetic(synth.SEED_BASE)
+    start = synth.gen_tokens(synth.SEED_BASE, 5, 3, s.vocab)
+    eng.reset_state(3)
+    a = eng.generate(_i32(start), 16, use_graph=False).cpu().numpy()
+    sa = eng.get_state(2)
+    eng.reset_state(3)
+    b = eng.generate(_i32(start), 16, use_graph=True).cpu().numpy()
+    sb = eng.get_state(2)
+    assert np.array_equal(a, b)
+    assert np.array_equal(sa[1], sb[1])
+    # replay the cached graph again after eager work in between
+    eng.reset_state(3)
+    eng.decode_step(_i32(start))
+    eng.reset_state(3)
+    c = eng.generate(_i32(start), 16, use_graph=True).cpu().numpy()
+    assert np.array_equal(a, c)
+    eng.close()
+
+
+def test_state_round_trip_resume():
+    s = synth.TINY
+    toks = synth.gen_tokens(synth.SEED_BASE, 6, 12, s.vocab)
+    eng = engine(s)
+    eng.load_synthetic(synth.SEED_BASE)
+    eng.prefill(_i32(toks[None, :6]))
+    conv, ssm = eng.get_state(0)
+    lg_a, _ = eng.prefill(_i32(toks[None, 6:]))
+    eng.close()
+    eng2 = engine(s)
+    eng2.load_synthetic(synth.SEED_BASE)
+    eng2.set_state(0, conv, ssm)
+    lg_b, _ = eng2.prefill(_i32(toks[None, 6:]))
+    assert torch.equal(lg_a, lg_b)
+    eng2.close()
+
+
+def test_errors_are_reported_without_work():
+    from bit_quantized_mamba_amd import DfssmError
+    s = synth.TINY
+    eng = engine(s, max_batch=2)
+    with pytest.raises(DfssmError):  # weights not loaded
+        eng.decode_step(_i32([1]))
+    eng.load_synthetic(synth.SEED_BASE)
+    with pytest.raises(DfssmError):  # batch above max_batch
+        eng.decode_step(_i32([1, 2, 3]))
+    with pytest.raises(ValueError):
+        eng.set_tensor(0, "in_sw", np.zeros(5, np.float32))
+    eng.decode_step(_i32([s.vocab + 5]))  # flagged on the device, read as token 0
+    with pytest.raises(DfssmError):
+        eng.check()
+    eng.check()  # flag cleared
+    eng.close()

@@ -566,3 +566,38 @@ def test_model_size_matches_pages():
     assert b["embedding"] == synth.FULL_1P3B.vocab * synth.FULL_1P3B.d_model
     # 9.7x smaller than the 2.7 GB fp16 teacher (1.3B parameters at 2 bytes)
     assert abs(2.7e9 / total - 9.7) < 0.15
+
+
+# ---------------------------------------------------------------------------
+# several correct roundings near a tie
+# ---------------------------------------------------------------------------
+
+def test_quant_forced_accepts_only_tie_neighbours():
+    # amax 127 -> scale 1: values 2.5 + tiny sit on a tie; 3.2 does not
+    u = np.array([127.0, 2.5 + 1e-5, 3.2, -4.5 - 2e-5, 0.1])
+    q, s = oracle.quant(u)
+    assert q.tolist() == [127, 3, 3, -5, 0]
+    # proposing the other side of each near-tie is accepted
+    qf, sf, bad = oracle.quant_forced(u, np.array([127, 2, 3, -4, 0], dtype=np.int8))
+    assert bad == 0 and qf.tolist() == [127, 2, 3, -4, 0] and sf == s
+    # a code off by one away from any tie, or off by two, is rejected
+    for prop in ([127, 3, 2, -5, 0], [127, 3, 3, -5, 1], [127, 1, 3, -5, 0]):
+        qf, _, bad = oracle.quant_forced(u, np.array(prop, dtype=np.int8))
+        assert bad == 1 and np.array_equal(qf, q)
+    # outside the band the tie neighbour is rejected as well
+    qf, _, bad = oracle.quant_forced(np.array([127.0, 2.5 + 5e-3]), np.array([127, 2], dtype=np.int8))
+    assert bad == 1
+
+
+def test_layer_forced_codes_equal_to_own_codes_change_nothing():
+    lay = _tiny_layer()
+    h = _h0(S_T)
+    cs1, ss1 = _zero_state(S_T)
+    cs2, ss2 = _zero_state(S_T)
+    o1, d = oracle.layer_step(S_T, lay, h, cs1, ss1, want_dbg=True)
+    o2 = oracle.layer_step(S_T, lay, h, cs2, ss2, q1_force=d["q1"], q2_force=d["q2"])
+    assert np.array_equal(o1, o2) and np.array_equal(ss1, ss2)
+    bad = d["q1"].copy()
+    bad[0] = np.clip(int(bad[0]) + 2, -127, 127) if abs(int(bad[0])) < 120 else int(bad[0]) - 2
+    with pytest.raises(oracle.ForcedCodeError):
+        oracle.layer_step(S_T, lay, h, *_zero_state(S_T), q1_force=bad)
