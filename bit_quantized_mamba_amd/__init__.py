@@ -1,0 +1,236 @@
+"""DF-SSM 1-bit-scaffold Mamba-2 decode on AMD Instinct MI355X (gfx950).
+
+A thin Python face of the C-ABI library libdfssm.so (include/dfssm.h).  PyTorch
+supplies device memory and streams; every step of the model runs in the
+library's HIP kernels.  If the library is missing, importing the binding
+raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import _lib
+from ._lib import DfssmConfig, DfssmError, call
+
+LAYER_KINDS = ["in_bits", "in_sw", "in_A", "in_sA", "in_B", "in_sB", "out_bits", "out_sw", "out_A", "out_sA",
+               "out_B", "out_sB", "conv_w", "conv_b", "A_log", "dt_bias", "D", "norm_w", "gnorm_w"]
+GLOBAL_KINDS = ["E", "sE", "final_norm"]
+
+__all__ = ["Engine", "DfssmError", "k_quant", "k_proj", "version", "LAYER_KINDS", "GLOBAL_KINDS"]
+
+
+def version() -> str:
+    return _lib.load().dfssm_version().decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dp(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class Engine:
+    """A DF-SSM model held on one GPU: weights, the recurrent state of
+    `max_batch` sequence slots and the workspace, owned by the library."""
+
+    def __init__(self, n_layer: int, d_model: int, d_inner: int, d_state: int, headdim: int, vocab: int,
+                 d_conv: int = 4, rank: int = 16, max_batch: int = 1, device: int = 0, norm_eps: float = 1e-5):
+        self.cfg = DfssmConfig(n_layer, d_model, d_inner, d_state, headdim, vocab, d_conv, rank, max_batch, norm_eps)
+        self.n_layer, self.d_model, self.d_inner, self.d_state = n_layer, d_model, d_inner, d_state
+        self.headdim, self.vocab, self.d_conv, self.rank, self.max_batch = headdim, vocab, d_conv, rank, max_batch
+        self.n_heads = d_inner // headdim
+        self.conv_dim = d_inner + 2 * d_state
+        self.d_in_proj = 2 * d_inner + 2 * d_state + self.n_heads
+        self.device = device
+        h = ctypes.c_void_p()
+        call("dfssm_create", ctypes.byref(self.cfg), device, ctypes.byref(h))
+        self._h = h
+
+    @classmethod
+    def from_shape(cls, s, max_batch: int = 1, device: int = 0) -> "Engine":
+        return cls(s.n_layer, s.d_model, s.d_inner, s.d_state, s.headdim, s.vocab, s.d_conv, s.rank,
+                   max_batch=max_batch, device=device)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _lib.load().dfssm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- weights -----------------------------------------------------------
+    def load_synthetic(self, seed: int, stream=None) -> None:
+        call("dfssm_load_synthetic", self._h, ctypes.c_uint64(seed), _stream(stream))
+
+    def _tensor_shape(self, layer: int, kind: str):
+        r = self.rank
+        if layer < 0:
+            return {"E": ((self.vocab, self.d_model), np.int8), "sE": ((self.vocab,), np.float32),
+                    "final_norm": ((self.d_model,), np.float32)}[kind]
+        dp, dm, di, cd, H = self.d_in_proj, self.d_model, self.d_inner, self.conv_dim, self.n_heads
+        return {"in_bits": ((dp, dm // 32), np.uint32), "in_sw": ((dp,), np.float32), "in_A": ((r, dm), np.int8),
+                "in_sA": ((r,), np.float32), "in_B": ((dp, r), np.int8), "in_sB": ((dp,), np.float32),
+                "out_bits": ((dm, di // 32), np.uint32), "out_sw": ((dm,), np.float32),
+                "out_A": ((r, di), np.int8), "out_sA": ((r,), np.float32), "out_B": ((dm, r), np.int8),
+                "out_sB": ((dm,), np.float32), "conv_w": ((cd, self.d_conv), np.float32),
+                "conv_b": ((cd,), np.float32), "A_log": ((H,), np.float32), "dt_bias": ((H,), np.float32),
+                "D": ((H,), np.float32), "norm_w": ((dm,), np.float32), "gnorm_w": ((di,), np.float32)}[kind]
+
+    def _kind_id(self, layer: int, kind: str) -> int:
+        return GLOBAL_KINDS.index(kind) if layer < 0 else LAYER_KINDS.index(kind)
+
+    def set_tensor(self, layer: int, kind: str, value: np.ndarray) -> None:
+        shp, dt = self._tensor_shape(layer, kind)
+        a = np.ascontiguousarray(value, dtype=dt)
+        if a.shape != shp:
+            raise ValueError(f"{kind}: shape {a.shape}, expected {shp}")
+        call("dfssm_set_tensor", self._h, layer, self._kind_id(layer, kind), a.ctypes.data, a.nbytes)
+
+    def get_tensor(self, layer: int, kind: str) -> np.ndarray:
+        shp, dt = self._tensor_shape(layer, kind)
+        a = np.empty(shp, dtype=dt)
+        call("dfssm_get_tensor", self._h, layer, self._kind_id(layer, kind), a.ctypes.data, a.nbytes)
+        return a
+
+    def set_weights(self, weights) -> None:
+        """Upload a whole model given as {"layers": [dict per layer], "E", "sE", "final_norm"}."""
+        for l, lay in enumerate(weights["layers"]):
+            for k in LAYER_KINDS:
+                self.set_tensor(l, k, lay[k])
+        for k in GLOBAL_KINDS:
+            if k in weights:
+                self.set_tensor(-1, k, weights[k])
+
+    # -- state -------------------------------------------------------------
+    def reset_state(self, batch: Optional[int] = None, stream=None) -> None:
+        call("dfssm_reset_state", self._h, batch or self.max_batch, _stream(stream))
+
+    def get_state(self, seq: int) -> Tuple[np.ndarray, np.ndarray]:
+        conv = np.empty((self.n_layer, self.conv_dim, self.d_conv - 1), dtype=np.float32)
+        ssm = np.empty((self.n_layer, self.n_heads, self.headdim, self.d_state), dtype=np.float32)
+        call("dfssm_get_state", self._h, seq, conv.ctypes.data, ssm.ctypes.data)
+        return conv, ssm
+
+    def set_state(self, seq: int, conv: Optional[np.ndarray], ssm: Optional[np.ndarray]) -> None:
+        c = None if conv is None else np.ascontiguousarray(conv, dtype=np.float32)
+        s = None if ssm is None else np.ascontiguousarray(ssm, dtype=np.float32)
+        if c is not None and c.shape != (self.n_layer, self.conv_dim, self.d_conv - 1):
+            raise ValueError("conv state shape")
+        if s is not None and s.shape != (self.n_layer, self.n_heads, self.headdim, self.d_state):
+            raise ValueError("ssm state shape")
+        call("dfssm_set_state", self._h, seq, None if c is None else c.ctypes.data,
+             None if s is None else s.ctypes.data)
+
+    # -- compute -----------------------------------------------------------
+    def _check_tok(self, tok, ndim: int):
+        torch = _torch()
+        if tok.dtype != torch.int32 or not tok.is_cuda or not tok.is_contiguous() or tok.dim() != ndim:
+            raise ValueError(f"tokens must be a contiguous {ndim}-D int32 CUDA tensor")
+
+    def decode_step(self, tok, logits=None, next_tok=None, stream=None):
+        torch = _torch()
+        self._check_tok(tok, 1)
+        B = tok.shape[0]
+        if logits is None:
+            logits = torch.empty((B, self.vocab), dtype=torch.float32, device=tok.device)
+        if next_tok is None:
+            next_tok = torch.empty((B,), dtype=torch.int32, device=tok.device)
+        call("dfssm_decode_step", self._h, _dp(tok), B, _dp(logits), _dp(next_tok), _stream(stream))
+        return logits, next_tok
+
+    def generate(self, tok, n_steps: int, out=None, use_graph: bool = True, stream=None):
+        """Greedy decode n_steps from tok ([B] int32, updated in place to the last token)."""
+        torch = _torch()
+        self._check_tok(tok, 1)
+        B = tok.shape[0]
+        if out is None:
+            out = torch.empty((n_steps, B), dtype=torch.int32, device=tok.device)
+        call("dfssm_generate", self._h, _dp(tok), B, n_steps, _dp(out), int(use_graph), _stream(stream))
+        return out
+
+    def prefill(self, tok, want_logits: bool = True, stream=None):
+        torch = _torch()
+        self._check_tok(tok, 2)
+        B, T = tok.shape
+        logits = torch.empty((B, self.vocab), dtype=torch.float32, device=tok.device) if want_logits else None
+        nxt = torch.empty((B,), dtype=torch.int32, device=tok.device)
+        call("dfssm_prefill", self._h, _dp(tok), B, T, _dp(logits), _dp(nxt), _stream(stream))
+        return logits, nxt
+
+    def layer_step(self, layer: int, h_in, h_out=None, want_codes: bool = False, stream=None):
+        """One layer on h_in ([B][d_model] fp32). Returns h_out, or (h_out, q1, q2) with want_codes."""
+        torch = _torch()
+        if h_in.dtype != torch.float32 or not h_in.is_cuda or not h_in.is_contiguous():
+            raise ValueError("h_in must be a contiguous fp32 CUDA tensor [B][d_model]")
+        B = h_in.shape[0]
+        if h_out is None:
+            h_out = torch.empty_like(h_in)
+        q1 = torch.empty((B, self.d_model), dtype=torch.int8, device=h_in.device) if want_codes else None
+        q2 = torch.empty((B, self.d_inner), dtype=torch.int8, device=h_in.device) if want_codes else None
+        call("dfssm_layer_step", self._h, layer, _dp(h_in), _dp(h_out), B, _dp(q1), _dp(q2), _stream(stream))
+        return (h_out, q1, q2) if want_codes else h_out
+
+    def trace_step(self, tok, stream=None):
+        """Decode step recording the residual stream per layer and every int8 activation code.
+
+        Returns dict(h=[L+1][B][d_model], q1=[L][B][d_model], q2=[L][B][d_inner], qf=[B][d_model], logits)."""
+        torch = _torch()
+        self._check_tok(tok, 1)
+        B = tok.shape[0]
+        dev = tok.device
+        t = {"h": torch.empty((self.n_layer + 1, B, self.d_model), dtype=torch.float32, device=dev),
+             "q1": torch.empty((self.n_layer, B, self.d_model), dtype=torch.int8, device=dev),
+             "q2": torch.empty((self.n_layer, B, self.d_inner), dtype=torch.int8, device=dev),
+             "qf": torch.empty((B, self.d_model), dtype=torch.int8, device=dev),
+             "logits": torch.empty((B, self.vocab), dtype=torch.float32, device=dev)}
+        call("dfssm_trace_step", self._h, _dp(tok), B, _dp(t["h"]), _dp(t["q1"]), _dp(t["q2"]), _dp(t["qf"]),
+             _dp(t["logits"]), _stream(stream))
+        return t
+
+    def check(self, stream=None) -> None:
+        call("dfssm_check_device", self._h, _stream(stream))
+
+    def device_bytes(self) -> int:
+        n = ctypes.c_size_t()
+        call("dfssm_device_bytes", self._h, ctypes.byref(n))
+        return n.value
+
+
+def k_quant(u, stream=None):
+    """Per-row int8 quantiser on the GPU: u fp32 [rows][n] -> (q int8, s fp32 [rows])."""
+    torch = _torch()
+    rows, n = u.shape
+    q = torch.empty((rows, n), dtype=torch.int8, device=u.device)
+    s = torch.empty((rows,), dtype=torch.float32, device=u.device)
+    call("dfssm_k_quant", _dp(u), rows, n, _dp(q), _dp(s), _stream(stream))
+    return q, s
+
+
+def k_proj(bits, sw, A, sA, Bm, sB, q, s, stream=None):
+    """Scaffold + LoRA projection of int8 rows q [B][d_in] -> (acc int32, y fp32) [B][d_out]."""
+    torch = _torch()
+    d_out = bits.shape[0]
+    d_in = bits.shape[1] * 32
+    r = A.shape[0]
+    B = q.shape[0]
+    acc = torch.empty((B, d_out), dtype=torch.int32, device=q.device)
+    y = torch.empty((B, d_out), dtype=torch.float32, device=q.device)
+    call("dfssm_k_proj", _dp(bits), _dp(sw), _dp(A), _dp(sA), _dp(Bm), _dp(sB), d_in, d_out, r, _dp(q), _dp(s), B,
+         _dp(acc), _dp(y), _stream(stream))
+    return acc, y

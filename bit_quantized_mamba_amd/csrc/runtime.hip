@@ -1,0 +1,697 @@
+// Host runtime behind include/dfssm.h: context, device memory, synthetic
+// load, state I/O, the decode / prefill / layer step orchestration and the
+// graph cache.  Every step of the model runs in the kernels of kernels.hip.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/dfssm.h"
+#include "common.h"
+
+using namespace dfssm;
+
+namespace {
+
+thread_local std::string g_err;
+
+dfssm_status fail(dfssm_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                          \
+  do {                                                                                         \
+    hipError_t _e = (expr);                                                                    \
+    if (_e != hipSuccess)                                                                      \
+      return fail(DFSSM_E_HIP, std::string(#expr) + ": " + hipGetErrorString(_e));             \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct TensorInfo {
+  size_t offset = 0;  // into the weight block
+  size_t bytes = 0;
+  size_t count = 0;
+  int elem = 4;
+};
+
+}  // namespace
+
+struct dfssm_ctx {
+  dfssm_config cfg{};
+  int device = 0;
+  int H = 0, P = 0, N = 0, dm = 0, di = 0, cdim = 0, dproj = 0, K = 0, r = 0, V = 0, L = 0, maxB = 0;
+  float eps = 1e-5f;
+
+  // weights
+  std::vector<TensorInfo> layer_t;  // L * 19
+  std::vector<TensorInfo> global_t; // 3
+  char* wbuf = nullptr;
+  size_t wbytes = 0;
+  bool loaded = false;
+
+  // state
+  float* conv = nullptr;  // [maxB][L][K-1][cdim]
+  float* ssm = nullptr;   // [maxB][L][H][P/16][N][16]
+  size_t conv_bstride = 0, ssm_bstride = 0;
+
+  // workspace (all [maxB][...])
+  float *h = nullptr, *zx = nullptr, *xc = nullptr, *g = nullptr, *logits = nullptr;
+  int8_t *q1 = nullptr, *q2 = nullptr;
+  uint32_t *pl1 = nullptr, *pl2 = nullptr;
+  int32_t *qs1 = nullptr, *qs2 = nullptr;
+  float *s1 = nullptr, *s2 = nullptr, *t1 = nullptr, *t2 = nullptr;
+  int32_t* next = nullptr;
+  int32_t* counter = nullptr;
+  int* err = nullptr;
+  char* ws = nullptr;
+  size_t wsbytes = 0, sbytes = 0;
+  char* sbuf = nullptr;
+
+  // graphs keyed by (B, d_tok, d_out)
+  std::map<std::tuple<int, const void*, const void*>, hipGraphExec_t> graphs;
+
+  void* tensor_ptr(int layer, int kind) const {
+    const TensorInfo& t = layer >= 0 ? layer_t[(size_t)layer * DFSSM_T_PER_LAYER + kind] : global_t[kind];
+    return wbuf + t.offset;
+  }
+  template <typename T>
+  T* lt(int layer, int kind) const { return (T*)tensor_ptr(layer, kind); }
+};
+
+namespace {
+
+dfssm_status validate(const dfssm_config* c) {
+  if (!c) return fail(DFSSM_E_INVALID, "null config");
+  if (c->n_layer < 1 || c->d_model < 1 || c->d_inner < 1 || c->d_state < 1 || c->headdim < 1 || c->vocab < 1 ||
+      c->lora_rank < 1 || c->max_batch < 1)
+    return fail(DFSSM_E_INVALID, "config dimensions must be positive");
+  auto pow2le64 = [](int x) { return x >= 1 && x <= 64 && (x & (x - 1)) == 0; };
+  if (c->d_model % 128 || !pow2le64(c->d_model / 128))
+    return fail(DFSSM_E_UNSUPPORTED, "d_model must be 128 * 2^k <= 8192");
+  if (c->d_inner % 128 || !pow2le64(c->d_inner / 128))
+    return fail(DFSSM_E_UNSUPPORTED, "d_inner must be 128 * 2^k <= 8192");
+  if (c->headdim % 16 || c->d_inner % c->headdim) return fail(DFSSM_E_UNSUPPORTED, "headdim must be a multiple of 16 dividing d_inner");
+  if (c->d_state % 2) return fail(DFSSM_E_UNSUPPORTED, "d_state must be even");
+  if (c->d_conv != 4) return fail(DFSSM_E_UNSUPPORTED, "d_conv must be 4");
+  if (c->lora_rank > 32) return fail(DFSSM_E_UNSUPPORTED, "lora_rank must be <= 32");
+  if (c->max_batch > 1024) return fail(DFSSM_E_UNSUPPORTED, "max_batch must be <= 1024");
+  if (!(c->norm_eps >= 0.0f)) return fail(DFSSM_E_INVALID, "norm_eps must be >= 0");
+  return DFSSM_OK;
+}
+
+struct Spec {
+  size_t count;
+  int elem;
+};
+
+Spec layer_spec(const dfssm_ctx* c, int kind) {
+  const size_t dm = c->dm, di = c->di, dp = c->dproj, r = c->r, cd = c->cdim, H = c->H;
+  switch (kind) {
+    case DFSSM_T_IN_BITS: return {dp * (dm / 32), 4};
+    case DFSSM_T_IN_SW: return {dp, 4};
+    case DFSSM_T_IN_A: return {r * dm, 1};
+    case DFSSM_T_IN_SA: return {r, 4};
+    case DFSSM_T_IN_B: return {dp * r, 1};
+    case DFSSM_T_IN_SB: return {dp, 4};
+    case DFSSM_T_OUT_BITS: return {dm * (di / 32), 4};
+    case DFSSM_T_OUT_SW: return {dm, 4};
+    case DFSSM_T_OUT_A: return {r * di, 1};
+    case DFSSM_T_OUT_SA: return {r, 4};
+    case DFSSM_T_OUT_B: return {dm * r, 1};
+    case DFSSM_T_OUT_SB: return {dm, 4};
+    case DFSSM_T_CONV_W: return {cd * (size_t)c->K, 4};
+    case DFSSM_T_CONV_B: return {cd, 4};
+    case DFSSM_T_A_LOG: case DFSSM_T_DT_BIAS: case DFSSM_T_D: return {H, 4};
+    case DFSSM_T_NORM_W: return {dm, 4};
+    default: return {di, 4};  // GNORM_W
+  }
+}
+
+Spec global_spec(const dfssm_ctx* c, int kind) {
+  if (kind == DFSSM_G_EMBED) return {(size_t)c->V * c->dm, 1};
+  if (kind == DFSSM_G_EMBED_SCALE) return {(size_t)c->V, 4};
+  return {(size_t)c->dm, 4};
+}
+
+// synthetic generator parameters per kind
+struct GenParam {
+  int mode;
+  double a, b;
+  float cval;
+};
+
+GenParam layer_gen(int kind) {
+  switch (kind) {
+    case DFSSM_T_IN_BITS: case DFSSM_T_OUT_BITS: return {GEN_WORDS, 0, 0, 0};
+    case DFSSM_T_IN_SW: case DFSSM_T_OUT_SW: return {GEN_UNIFORM, 0.01, 0.05, 0};
+    case DFSSM_T_IN_A: case DFSSM_T_IN_B: case DFSSM_T_OUT_A: case DFSSM_T_OUT_B: return {GEN_INT8, 0, 0, 0};
+    case DFSSM_T_IN_SA: case DFSSM_T_IN_SB: case DFSSM_T_OUT_SA: case DFSSM_T_OUT_SB:
+      return {GEN_CONST, 0, 0, (float)1e-3};
+    case DFSSM_T_CONV_W: case DFSSM_T_CONV_B: return {GEN_UNIFORM, -0.5, 0.5, 0};
+    case DFSSM_T_A_LOG: return {GEN_UNIFORM, 0.0, 2.772588722239781, 0};
+    case DFSSM_T_DT_BIAS: return {GEN_UNIFORM, -4.0, -1.0, 0};
+    case DFSSM_T_D: return {GEN_NORMAL, 0, 0, 0};
+    default: return {GEN_UNIFORM, 0.5, 1.5, 0};  // norm weights
+  }
+}
+
+GenParam global_gen(int kind) {
+  if (kind == DFSSM_G_EMBED) return {GEN_INT8, 0, 0, 0};
+  if (kind == DFSSM_G_EMBED_SCALE) return {GEN_UNIFORM, 0.01, 0.02, 0};
+  return {GEN_UNIFORM, 0.5, 1.5, 0};
+}
+
+hipStream_t S(void* s) { return (hipStream_t)s; }
+
+// ---------------------------------------------------------------------------
+// one layer on the context's workspace h[0..B)
+// ---------------------------------------------------------------------------
+dfssm_status enqueue_layer(dfssm_ctx* c, int l, int B, hipStream_t st, int8_t* q1_out = nullptr,
+                           int8_t* q2_out = nullptr) {
+  HIP_TRY(launch_norm_quant(c->h, c->lt<float>(l, DFSSM_T_NORM_W), c->dm, B, c->eps, c->lt<int8_t>(l, DFSSM_T_IN_A),
+                            c->lt<float>(l, DFSSM_T_IN_SA), c->r, c->q1, c->pl1, c->qs1, c->s1, c->t1, st));
+  if (q1_out) HIP_TRY(hipMemcpyAsync(q1_out, c->q1, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st));
+  ProjArgs a{};
+  a.bits = c->lt<uint32_t>(l, DFSSM_T_IN_BITS);
+  a.sw = c->lt<float>(l, DFSSM_T_IN_SW);
+  a.Bm = c->lt<int8_t>(l, DFSSM_T_IN_B);
+  a.sB = c->lt<float>(l, DFSSM_T_IN_SB);
+  a.in = QPrep{c->q1, c->pl1, c->qs1, c->s1, c->t1};
+  a.d_in = c->dm;
+  a.d_out = c->dproj;
+  a.r = c->r;
+  a.B = B;
+  a.zx = c->zx;
+  a.xc = c->xc;
+  a.conv_state = c->conv + (size_t)l * (c->K - 1) * c->cdim;
+  a.conv_bstride = c->conv_bstride;
+  a.conv_w = c->lt<float>(l, DFSSM_T_CONV_W);
+  a.conv_b = c->lt<float>(l, DFSSM_T_CONV_B);
+  a.d_inner = c->di;
+  a.conv_dim = c->cdim;
+  a.K = c->K;
+  HIP_TRY(launch_proj(a, EPI_IN_PROJ, st));
+  HIP_TRY(launch_ssm(c->xc, c->zx, c->dproj, c->lt<float>(l, DFSSM_T_A_LOG), c->lt<float>(l, DFSSM_T_DT_BIAS),
+                     c->lt<float>(l, DFSSM_T_D), c->ssm + (size_t)l * c->H * c->P * c->N, c->ssm_bstride, c->g, B,
+                     c->H, c->P, c->N, c->di, c->cdim, st));
+  HIP_TRY(launch_norm_quant(c->g, c->lt<float>(l, DFSSM_T_GNORM_W), c->di, B, c->eps, c->lt<int8_t>(l, DFSSM_T_OUT_A),
+                            c->lt<float>(l, DFSSM_T_OUT_SA), c->r, c->q2, c->pl2, c->qs2, c->s2, c->t2, st));
+  if (q2_out) HIP_TRY(hipMemcpyAsync(q2_out, c->q2, (size_t)B * c->di, hipMemcpyDeviceToDevice, st));
+  ProjArgs o{};
+  o.bits = c->lt<uint32_t>(l, DFSSM_T_OUT_BITS);
+  o.sw = c->lt<float>(l, DFSSM_T_OUT_SW);
+  o.Bm = c->lt<int8_t>(l, DFSSM_T_OUT_B);
+  o.sB = c->lt<float>(l, DFSSM_T_OUT_SB);
+  o.in = QPrep{c->q2, c->pl2, c->qs2, c->s2, c->t2};
+  o.d_in = c->di;
+  o.d_out = c->dm;
+  o.r = c->r;
+  o.B = B;
+  o.h = c->h;
+  HIP_TRY(launch_proj(o, EPI_OUT_PROJ, st));
+  return DFSSM_OK;
+}
+
+// full step: embed -> layers -> (final norm, LM head, argmax)
+struct Trace {
+  float* h = nullptr;
+  int8_t* q1 = nullptr;
+  int8_t* q2 = nullptr;
+  int8_t* qf = nullptr;
+};
+
+dfssm_status enqueue_step(dfssm_ctx* c, const int32_t* tok, int tok_stride, int B, float* logits, int32_t* next,
+                          int32_t* out, const Trace* tr, bool head, hipStream_t st) {
+  float* trace = tr ? tr->h : nullptr;
+  HIP_TRY(launch_embed(tok, tok_stride, c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), c->dm,
+                       c->V, B, c->h, c->err, st));
+  for (int l = 0; l < c->L; ++l) {
+    if (trace)
+      HIP_TRY(hipMemcpyAsync(trace + (size_t)l * B * c->dm, c->h, sizeof(float) * B * c->dm,
+                             hipMemcpyDeviceToDevice, st));
+    dfssm_status r = enqueue_layer(c, l, B, st, tr && tr->q1 ? tr->q1 + (size_t)l * B * c->dm : nullptr,
+                                   tr && tr->q2 ? tr->q2 + (size_t)l * B * c->di : nullptr);
+    if (r != DFSSM_OK) return r;
+  }
+  if (trace)
+    HIP_TRY(hipMemcpyAsync(trace + (size_t)c->L * B * c->dm, c->h, sizeof(float) * B * c->dm,
+                           hipMemcpyDeviceToDevice, st));
+  if (!head) return DFSSM_OK;
+  HIP_TRY(launch_norm_quant(c->h, c->lt<float>(-1, DFSSM_G_FINAL_NORM), c->dm, B, c->eps, nullptr, nullptr, 0, c->q1,
+                            c->pl1, c->qs1, c->s1, c->t1, st));
+  if (tr && tr->qf) HIP_TRY(hipMemcpyAsync(tr->qf, c->q1, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st));
+  float* lg = logits ? logits : c->logits;
+  HIP_TRY(launch_lm_head(c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), c->q1, c->s1, c->V,
+                         c->dm, B, lg, st));
+  if (next || out) HIP_TRY(launch_argmax(lg, c->V, B, next ? next : c->next, out, c->counter, st));
+  return DFSSM_OK;
+}
+
+dfssm_status check_ctx(const dfssm_ctx* c, bool need_loaded = true) {
+  if (!c) return fail(DFSSM_E_INVALID, "null context");
+  if (need_loaded && !c->loaded) return fail(DFSSM_E_STATE, "weights not loaded");
+  return DFSSM_OK;
+}
+
+dfssm_status check_B(const dfssm_ctx* c, int B) {
+  if (B < 1 || B > c->maxB)
+    return fail(DFSSM_E_INVALID, "batch " + std::to_string(B) + " outside [1, " + std::to_string(c->maxB) + "]");
+  return DFSSM_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+
+extern "C" {
+
+const char* dfssm_version(void) { return "dfssm-mi355x 0.1 (gfx950)"; }
+
+const char* dfssm_last_error(const dfssm_ctx*) { return g_err.c_str(); }
+
+dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** out) {
+  if (!out) return fail(DFSSM_E_INVALID, "null output pointer");
+  *out = nullptr;
+  dfssm_status v = validate(cfg);
+  if (v != DFSSM_OK) return v;
+  int ndev = 0;
+  HIP_TRY(hipGetDeviceCount(&ndev));
+  if (device < 0 || device >= ndev) return fail(DFSSM_E_INVALID, "device index out of range");
+  HIP_TRY(hipSetDevice(device));
+
+  dfssm_ctx* c = new dfssm_ctx();
+  c->cfg = *cfg;
+  c->device = device;
+  c->L = cfg->n_layer;
+  c->dm = cfg->d_model;
+  c->di = cfg->d_inner;
+  c->N = cfg->d_state;
+  c->P = cfg->headdim;
+  c->H = cfg->d_inner / cfg->headdim;
+  c->V = cfg->vocab;
+  c->K = cfg->d_conv;
+  c->r = cfg->lora_rank;
+  c->maxB = cfg->max_batch;
+  c->cdim = c->di + 2 * c->N;
+  c->dproj = 2 * c->di + 2 * c->N + c->H;
+  c->eps = cfg->norm_eps > 0.0f ? cfg->norm_eps : 1e-5f;
+
+  // weights
+  size_t off = 0;
+  c->layer_t.resize((size_t)c->L * DFSSM_T_PER_LAYER);
+  for (int l = 0; l < c->L; ++l)
+    for (int k = 0; k < DFSSM_T_PER_LAYER; ++k) {
+      Spec sp = layer_spec(c, k);
+      TensorInfo& t = c->layer_t[(size_t)l * DFSSM_T_PER_LAYER + k];
+      t.offset = off;
+      t.count = sp.count;
+      t.elem = sp.elem;
+      t.bytes = sp.count * sp.elem;
+      off += align_up(t.bytes);
+    }
+  c->global_t.resize(3);
+  for (int k = 0; k < 3; ++k) {
+    Spec sp = global_spec(c, k);
+    TensorInfo& t = c->global_t[k];
+    t.offset = off;
+    t.count = sp.count;
+    t.elem = sp.elem;
+    t.bytes = sp.count * sp.elem;
+    off += align_up(t.bytes);
+  }
+  c->wbytes = off;
+
+  // state
+  c->conv_bstride = (size_t)c->L * (c->K - 1) * c->cdim;
+  c->ssm_bstride = (size_t)c->L * c->H * c->P * c->N;
+  const size_t conv_bytes = align_up(sizeof(float) * c->conv_bstride * c->maxB);
+  const size_t ssm_bytes = align_up(sizeof(float) * c->ssm_bstride * c->maxB);
+  c->sbytes = conv_bytes + ssm_bytes;
+
+  // workspace
+  const size_t B = c->maxB;
+  size_t wo = 0;
+  auto take = [&](size_t bytes) { size_t o = wo; wo += align_up(bytes); return o; };
+  const size_t o_h = take(sizeof(float) * B * c->dm), o_zx = take(sizeof(float) * B * c->dproj),
+               o_xc = take(sizeof(float) * B * c->cdim), o_g = take(sizeof(float) * B * c->di),
+               o_lg = take(sizeof(float) * B * c->V), o_q1 = take(B * c->dm), o_q2 = take(B * c->di),
+               o_p1 = take(sizeof(uint32_t) * B * (c->dm / 32) * 8),
+               o_p2 = take(sizeof(uint32_t) * B * (c->di / 32) * 8), o_qs1 = take(4 * B), o_qs2 = take(4 * B),
+               o_s1 = take(4 * B), o_s2 = take(4 * B), o_t1 = take(4 * B * c->r), o_t2 = take(4 * B * c->r),
+               o_nx = take(4 * B), o_ct = take(4), o_er = take(4);
+  c->wsbytes = wo;
+
+  if (hipMalloc(&c->wbuf, c->wbytes) != hipSuccess || hipMalloc(&c->sbuf, c->sbytes) != hipSuccess ||
+      hipMalloc(&c->ws, c->wsbytes) != hipSuccess) {
+    (void)hipGetLastError();
+    dfssm_destroy(c);
+    return fail(DFSSM_E_OOM, "device allocation failed");
+  }
+  c->conv = (float*)c->sbuf;
+  c->ssm = (float*)(c->sbuf + conv_bytes);
+  char* w = c->ws;
+  c->h = (float*)(w + o_h);
+  c->zx = (float*)(w + o_zx);
+  c->xc = (float*)(w + o_xc);
+  c->g = (float*)(w + o_g);
+  c->logits = (float*)(w + o_lg);
+  c->q1 = (int8_t*)(w + o_q1);
+  c->q2 = (int8_t*)(w + o_q2);
+  c->pl1 = (uint32_t*)(w + o_p1);
+  c->pl2 = (uint32_t*)(w + o_p2);
+  c->qs1 = (int32_t*)(w + o_qs1);
+  c->qs2 = (int32_t*)(w + o_qs2);
+  c->s1 = (float*)(w + o_s1);
+  c->s2 = (float*)(w + o_s2);
+  c->t1 = (float*)(w + o_t1);
+  c->t2 = (float*)(w + o_t2);
+  c->next = (int32_t*)(w + o_nx);
+  c->counter = (int32_t*)(w + o_ct);
+  c->err = (int*)(w + o_er);
+  if (launch_zero(c->sbuf, c->sbytes, nullptr) != hipSuccess || launch_zero(c->ws, c->wsbytes, nullptr) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    dfssm_destroy(c);
+    return fail(DFSSM_E_HIP, "initial clear failed");
+  }
+  *out = c;
+  return DFSSM_OK;
+}
+
+void dfssm_destroy(dfssm_ctx* c) {
+  if (!c) return;
+  (void)hipSetDevice(c->device);
+  (void)hipDeviceSynchronize();
+  for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (c->wbuf) (void)hipFree(c->wbuf);
+  if (c->sbuf) (void)hipFree(c->sbuf);
+  if (c->ws) (void)hipFree(c->ws);
+  delete c;
+}
+
+dfssm_status dfssm_device_bytes(const dfssm_ctx* c, size_t* bytes) {
+  if (!c || !bytes) return fail(DFSSM_E_INVALID, "null argument");
+  *bytes = c->wbytes + c->sbytes + c->wsbytes;
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_load_synthetic(dfssm_ctx* c, uint64_t seed, void* stream) {
+  dfssm_status v = check_ctx(c, false);
+  if (v != DFSSM_OK) return v;
+  HIP_TRY(hipSetDevice(c->device));
+  for (int l = 0; l < c->L; ++l)
+    for (int k = 0; k < DFSSM_T_PER_LAYER; ++k) {
+      const TensorInfo& t = c->layer_t[(size_t)l * DFSSM_T_PER_LAYER + k];
+      const GenParam gp = layer_gen(k);
+      const uint64_t tid = (uint64_t)(64 * l + k);
+      const uint64_t key = host_mix64(seed ^ (tid << 32));
+      HIP_TRY(launch_gen(c->wbuf + t.offset, t.count, gp.mode, key, gp.a, gp.b - gp.a, gp.cval, S(stream)));
+    }
+  for (int k = 0; k < 3; ++k) {
+    const TensorInfo& t = c->global_t[k];
+    const GenParam gp = global_gen(k);
+    const uint64_t tid = (uint64_t)(4096 + k);
+    const uint64_t key = host_mix64(seed ^ (tid << 32));
+    HIP_TRY(launch_gen(c->wbuf + t.offset, t.count, gp.mode, key, gp.a, gp.b - gp.a, gp.cval, S(stream)));
+  }
+  HIP_TRY(launch_zero(c->sbuf, c->sbytes, S(stream)));
+  c->loaded = true;
+  return DFSSM_OK;
+}
+
+static dfssm_status tensor_lookup(dfssm_ctx* c, int32_t layer, int32_t kind, size_t bytes, const TensorInfo** ti) {
+  if (!c) return fail(DFSSM_E_INVALID, "null context");
+  if (layer >= c->L || layer < -1) return fail(DFSSM_E_INVALID, "layer out of range");
+  if (layer >= 0 && (kind < 0 || kind >= DFSSM_T_PER_LAYER)) return fail(DFSSM_E_INVALID, "tensor kind out of range");
+  if (layer < 0 && (kind < 0 || kind > 2)) return fail(DFSSM_E_INVALID, "global tensor kind out of range");
+  const TensorInfo& t = layer >= 0 ? c->layer_t[(size_t)layer * DFSSM_T_PER_LAYER + kind] : c->global_t[kind];
+  if (bytes != t.bytes)
+    return fail(DFSSM_E_INVALID, "tensor size mismatch: got " + std::to_string(bytes) + ", need " + std::to_string(t.bytes));
+  *ti = &t;
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_set_tensor(dfssm_ctx* c, int32_t layer, int32_t kind, const void* host, size_t bytes) {
+  const TensorInfo* t = nullptr;
+  dfssm_status v = tensor_lookup(c, layer, kind, bytes, &t);
+  if (v != DFSSM_OK) return v;
+  if (!host) return fail(DFSSM_E_INVALID, "null host pointer");
+  HIP_TRY(hipSetDevice(c->device));
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(c->wbuf + t->offset, host, bytes, hipMemcpyHostToDevice));
+  c->loaded = true;
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_get_tensor(dfssm_ctx* c, int32_t layer, int32_t kind, void* host, size_t bytes) {
+  const TensorInfo* t = nullptr;
+  dfssm_status v = tensor_lookup(c, layer, kind, bytes, &t);
+  if (v != DFSSM_OK) return v;
+  if (!host) return fail(DFSSM_E_INVALID, "null host pointer");
+  HIP_TRY(hipSetDevice(c->device));
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(host, c->wbuf + t->offset, bytes, hipMemcpyDeviceToHost));
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_reset_state(dfssm_ctx* c, int32_t batch, void* stream) {
+  dfssm_status v = check_ctx(c, false);
+  if (v != DFSSM_OK) return v;
+  if ((v = check_B(c, batch)) != DFSSM_OK) return v;
+  HIP_TRY(launch_zero(c->conv, sizeof(float) * c->conv_bstride * batch, S(stream)));
+  HIP_TRY(launch_zero(c->ssm, sizeof(float) * c->ssm_bstride * batch, S(stream)));
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_get_state(dfssm_ctx* c, int32_t seq, float* host_conv, float* host_ssm) {
+  dfssm_status v = check_ctx(c, false);
+  if (v != DFSSM_OK) return v;
+  if (seq < 0 || seq >= c->maxB) return fail(DFSSM_E_INVALID, "sequence slot out of range");
+  HIP_TRY(hipSetDevice(c->device));
+  HIP_TRY(hipDeviceSynchronize());
+  const int K1 = c->K - 1;
+  if (host_conv) {
+    std::vector<float> tmp(c->conv_bstride);
+    HIP_TRY(hipMemcpy(tmp.data(), c->conv + (size_t)seq * c->conv_bstride, sizeof(float) * tmp.size(),
+                      hipMemcpyDeviceToHost));
+    for (int l = 0; l < c->L; ++l)
+      for (int k = 0; k < K1; ++k)
+        for (int ch = 0; ch < c->cdim; ++ch)
+          host_conv[((size_t)l * c->cdim + ch) * K1 + k] = tmp[((size_t)l * K1 + k) * c->cdim + ch];
+  }
+  if (host_ssm) {
+    std::vector<float> tmp(c->ssm_bstride);
+    HIP_TRY(hipMemcpy(tmp.data(), c->ssm + (size_t)seq * c->ssm_bstride, sizeof(float) * tmp.size(),
+                      hipMemcpyDeviceToHost));
+    const int G = c->P / 16;
+    for (int l = 0; l < c->L; ++l)
+      for (int h = 0; h < c->H; ++h)
+        for (int p = 0; p < c->P; ++p)
+          for (int n = 0; n < c->N; ++n) {
+            const size_t src = ((((size_t)l * c->H + h) * G + p / 16) * c->N + n) * 16 + (p % 16);
+            host_ssm[(((size_t)l * c->H + h) * c->P + p) * c->N + n] = tmp[src];
+          }
+  }
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_set_state(dfssm_ctx* c, int32_t seq, const float* host_conv, const float* host_ssm) {
+  dfssm_status v = check_ctx(c, false);
+  if (v != DFSSM_OK) return v;
+  if (seq < 0 || seq >= c->maxB) return fail(DFSSM_E_INVALID, "sequence slot out of range");
+  HIP_TRY(hipSetDevice(c->device));
+  HIP_TRY(hipDeviceSynchronize());
+  const int K1 = c->K - 1;
+  if (host_conv) {
+    std::vector<float> tmp(c->conv_bstride);
+    for (int l = 0; l < c->L; ++l)
+      for (int k = 0; k < K1; ++k)
+        for (int ch = 0; ch < c->cdim; ++ch)
+          tmp[((size_t)l * K1 + k) * c->cdim + ch] = host_conv[((size_t)l * c->cdim + ch) * K1 + k];
+    HIP_TRY(hipMemcpy(c->conv + (size_t)seq * c->conv_bstride, tmp.data(), sizeof(float) * tmp.size(),
+                      hipMemcpyHostToDevice));
+  }
+  if (host_ssm) {
+    std::vector<float> tmp(c->ssm_bstride);
+    const int G = c->P / 16;
+    for (int l = 0; l < c->L; ++l)
+      for (int h = 0; h < c->H; ++h)
+        for (int p = 0; p < c->P; ++p)
+          for (int n = 0; n < c->N; ++n) {
+            const size_t dst = ((((size_t)l * c->H + h) * G + p / 16) * c->N + n) * 16 + (p % 16);
+            tmp[dst] = host_ssm[(((size_t)l * c->H + h) * c->P + p) * c->N + n];
+          }
+    HIP_TRY(hipMemcpy(c->ssm + (size_t)seq * c->ssm_bstride, tmp.data(), sizeof(float) * tmp.size(),
+                      hipMemcpyHostToDevice));
+  }
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_decode_step(dfssm_ctx* c, const int32_t* d_tok, int32_t B, float* d_logits, int32_t* d_next,
+                               void* stream) {
+  dfssm_status v = check_ctx(c);
+  if (v != DFSSM_OK) return v;
+  if ((v = check_B(c, B)) != DFSSM_OK) return v;
+  if (!d_tok) return fail(DFSSM_E_INVALID, "null token pointer");
+  return enqueue_step(c, d_tok, 1, B, d_logits, d_next, nullptr, nullptr, true, S(stream));
+}
+
+dfssm_status dfssm_generate(dfssm_ctx* c, int32_t* d_tok, int32_t B, int32_t n_steps, int32_t* d_out,
+                            int32_t use_graph, void* stream) {
+  dfssm_status v = check_ctx(c);
+  if (v != DFSSM_OK) return v;
+  if ((v = check_B(c, B)) != DFSSM_OK) return v;
+  if (!d_tok) return fail(DFSSM_E_INVALID, "null token pointer");
+  if (n_steps < 0) return fail(DFSSM_E_INVALID, "negative step count");
+  if (n_steps == 0) return DFSSM_OK;
+  hipStream_t st = S(stream);
+  if (d_out) HIP_TRY(launch_zero(c->counter, 4, st));
+  if (!use_graph) {
+    for (int i = 0; i < n_steps; ++i) {
+      v = enqueue_step(c, d_tok, 1, B, nullptr, d_tok, d_out, nullptr, true, st);
+      if (v != DFSSM_OK) return v;
+    }
+    return DFSSM_OK;
+  }
+  auto key = std::make_tuple((int)B, (const void*)d_tok, (const void*)d_out);
+  auto it = c->graphs.find(key);
+  hipGraphExec_t exec = nullptr;
+  if (it == c->graphs.end()) {
+    hipStream_t cap = nullptr;
+    HIP_TRY(hipStreamCreateWithFlags(&cap, hipStreamNonBlocking));
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      v = enqueue_step(c, d_tok, 1, B, nullptr, d_tok, d_out, nullptr, true, cap);
+      hipError_t e2 = hipStreamEndCapture(cap, &graph);
+      if (v == DFSSM_OK && e2 != hipSuccess) v = fail(DFSSM_E_HIP, std::string("graph capture: ") + hipGetErrorString(e2));
+    } else {
+      v = fail(DFSSM_E_HIP, std::string("begin capture: ") + hipGetErrorString(e));
+    }
+    if (v == DFSSM_OK) {
+      e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      if (e != hipSuccess) v = fail(DFSSM_E_HIP, std::string("graph instantiate: ") + hipGetErrorString(e));
+    }
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(cap);
+    if (v != DFSSM_OK) return v;
+    c->graphs[key] = exec;
+  } else {
+    exec = it->second;
+  }
+  for (int i = 0; i < n_steps; ++i) HIP_TRY(hipGraphLaunch(exec, st));
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_prefill(dfssm_ctx* c, const int32_t* d_tok, int32_t B, int32_t T, float* d_last_logits,
+                           int32_t* d_next, void* stream) {
+  dfssm_status v = check_ctx(c);
+  if (v != DFSSM_OK) return v;
+  if ((v = check_B(c, B)) != DFSSM_OK) return v;
+  if (!d_tok) return fail(DFSSM_E_INVALID, "null token pointer");
+  if (T < 1) return fail(DFSSM_E_INVALID, "prompt length must be >= 1");
+  for (int t = 0; t < T; ++t) {
+    const bool last = t == T - 1;
+    v = enqueue_step(c, d_tok + t, T, B, last ? d_last_logits : nullptr, last ? d_next : nullptr, nullptr, nullptr,
+                     last && (d_last_logits || d_next), S(stream));
+    if (v != DFSSM_OK) return v;
+  }
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_layer_step(dfssm_ctx* c, int32_t layer, const float* d_h_in, float* d_h_out, int32_t B,
+                              int8_t* d_q1, int8_t* d_q2, void* stream) {
+  dfssm_status v = check_ctx(c);
+  if (v != DFSSM_OK) return v;
+  if ((v = check_B(c, B)) != DFSSM_OK) return v;
+  if (layer < 0 || layer >= c->L) return fail(DFSSM_E_INVALID, "layer out of range");
+  if (!d_h_in || !d_h_out) return fail(DFSSM_E_INVALID, "null activation pointer");
+  hipStream_t st = S(stream);
+  HIP_TRY(hipMemcpyAsync(c->h, d_h_in, sizeof(float) * B * c->dm, hipMemcpyDeviceToDevice, st));
+  v = enqueue_layer(c, layer, B, st, d_q1, d_q2);
+  if (v != DFSSM_OK) return v;
+  HIP_TRY(hipMemcpyAsync(d_h_out, c->h, sizeof(float) * B * c->dm, hipMemcpyDeviceToDevice, st));
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_trace_step(dfssm_ctx* c, const int32_t* d_tok, int32_t B, float* d_h_trace, int8_t* d_q1_trace,
+                              int8_t* d_q2_trace, int8_t* d_qf, float* d_logits, void* stream) {
+  dfssm_status v = check_ctx(c);
+  if (v != DFSSM_OK) return v;
+  if ((v = check_B(c, B)) != DFSSM_OK) return v;
+  if (!d_tok || !d_h_trace) return fail(DFSSM_E_INVALID, "null pointer");
+  Trace tr;
+  tr.h = d_h_trace;
+  tr.q1 = d_q1_trace;
+  tr.q2 = d_q2_trace;
+  tr.qf = d_qf;
+  return enqueue_step(c, d_tok, 1, B, d_logits, nullptr, nullptr, &tr, true, S(stream));
+}
+
+dfssm_status dfssm_check_device(dfssm_ctx* c, void* stream) {
+  dfssm_status v = check_ctx(c, false);
+  if (v != DFSSM_OK) return v;
+  HIP_TRY(hipStreamSynchronize(S(stream)));
+  int flag = 0;
+  HIP_TRY(hipMemcpy(&flag, c->err, sizeof(int), hipMemcpyDeviceToHost));
+  if (flag) {
+    HIP_TRY(launch_zero(c->err, 4, nullptr));
+    HIP_TRY(hipDeviceSynchronize());
+    return fail(DFSSM_E_DEVICE, "a kernel flagged an out-of-range token id");
+  }
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_k_quant(const float* d_u, int32_t rows, int32_t n, int8_t* d_q, float* d_s, void* stream) {
+  if (!d_u || !d_q || !d_s) return fail(DFSSM_E_INVALID, "null pointer");
+  if (rows < 1 || n < 1 || n > 65536) return fail(DFSSM_E_INVALID, "rows must be >= 1 and 1 <= n <= 65536");
+  HIP_TRY(launch_quant_rows(d_u, rows, n, d_q, d_s, S(stream)));
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_k_proj(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
+                          const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out, int32_t r,
+                          const int8_t* d_q, const float* d_s, int32_t B, int32_t* d_acc, float* d_y, void* stream) {
+  if (!d_bits || !d_sw || !d_A || !d_sA || !d_B || !d_sB || !d_q || !d_s || !d_y)
+    return fail(DFSSM_E_INVALID, "null pointer");
+  if (d_in < 128 || d_in % 128 || (d_in / 128) > 64 || ((d_in / 128) & (d_in / 128 - 1)))
+    return fail(DFSSM_E_UNSUPPORTED, "d_in must be 128 * 2^k <= 8192");
+  if (d_out < 1 || r < 1 || r > 32 || B < 1 || B > 65535) return fail(DFSSM_E_INVALID, "bad d_out / r / B");
+  hipStream_t st = S(stream);
+  const size_t pl_bytes = sizeof(uint32_t) * (size_t)B * (d_in / 32) * 8;
+  char* tmp = nullptr;
+  const size_t tbytes = align_up(pl_bytes) + align_up(4 * (size_t)B) + align_up(4 * (size_t)B * r);
+  HIP_TRY(hipMallocAsync((void**)&tmp, tbytes, st));
+  uint32_t* planes = (uint32_t*)tmp;
+  int32_t* qsum = (int32_t*)(tmp + align_up(pl_bytes));
+  float* t = (float*)(tmp + align_up(pl_bytes) + align_up(4 * (size_t)B));
+  hipError_t e = launch_qprep(d_q, d_s, d_in, B, d_A, d_sA, r, planes, qsum, t, st);
+  if (e == hipSuccess) {
+    ProjArgs a{};
+    a.bits = d_bits;
+    a.sw = d_sw;
+    a.Bm = d_B;
+    a.sB = d_sB;
+    a.in = QPrep{d_q, planes, qsum, d_s, t};
+    a.d_in = d_in;
+    a.d_out = d_out;
+    a.r = r;
+    a.B = B;
+    a.acc = d_acc;
+    a.y = d_y;
+    e = launch_proj(a, EPI_STORE, st);
+  }
+  hipError_t e2 = hipFreeAsync(tmp, st);
+  if (e != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_proj: ") + hipGetErrorString(e));
+  if (e2 != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_proj free: ") + hipGetErrorString(e2));
+  return DFSSM_OK;
+}
+
+}  // extern "C"

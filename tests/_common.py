@@ -39,3 +39,26 @@ def engine(shape, max_batch=1):
 
 def ssm_canonical_to_oracle(ssm_l):
     return np.ascontiguousarray(ssm_l, dtype=np.float64)
+
+
+def trace_to_numpy(tr):
+    return {k: v.cpu().numpy() for k, v in tr.items()}
+
+
+def oracle_follow_step(om, st, tok, tr, b=0):
+    """One oracle decode step of sequence b that takes the GPU's int8 codes
+    (recorded in trace `tr`) wherever they are correct roundings of the
+    oracle's own values -- several codes are correct near a rounding tie --
+    and otherwise raises.  The oracle runs on its own residual stream.
+
+    Returns (h per layer [L+1][d_model], logits, argmax)."""
+    import oracle
+    s = om.s
+    h = om.embed(int(tok))
+    hs = [h]
+    for l in range(s.n_layer):
+        h = oracle.layer_step(s, om.weights["layers"][l], h, st.conv[l], st.ssm[l],
+                              q1_force=tr["q1"][l, b], q2_force=tr["q2"][l, b])
+        hs.append(h)
+    best, logits, _, _ = om.lm_head(h, qf_force=tr["qf"][b])
+    return np.array(hs), logits, best

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from tests._common import assert_close, engine, rel_err, token_ok
+from tests._common import assert_close, engine, oracle_follow_step, rel_err, token_ok, trace_to_numpy
 
 pytestmark = pytest.mark.gpu
 
@@ -21,7 +21,7 @@ def _i32(a):
 # one layer, state carried over steps (tiny and 1.3B-shaped)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shape,steps", [(synth.TINY, 50), (synth.LAYER_1P3B, 12)])
+@pytest.mark.parametrize("shape,steps", [(synth.TINY, 64), (synth.LAYER_1P3B, 1000)])
 def test_layer_steps_match_oracle(shape, steps):
     seed = synth.SEED_BASE + 1
     eng = engine(shape)
@@ -33,15 +33,17 @@ def test_layer_steps_match_oracle(shape, steps):
     for t in range(steps):
         h16 = synth.gen_fp16_normal(seed, 1, shape.d_model, start=t * shape.d_model)
         h = h16.astype(np.float32)
-        hg = eng.layer_step(0, torch.from_numpy(h[None]).cuda()).cpu().numpy()[0]
-        ho = oracle.layer_step(shape, lay, h.astype(np.float64), cs, ss)
-        # compare the mixer output (h_out - h_in) and the residual stream
+        hg, q1, q2 = eng.layer_step(0, torch.from_numpy(h[None]).cuda(), want_codes=True)
+        hg = hg.cpu().numpy()[0]
+        ho = oracle.layer_step(shape, lay, h.astype(np.float64), cs, ss,
+                               q1_force=q1.cpu().numpy()[0], q2_force=q2.cpu().numpy()[0])
+        # the mixer output (h_out - h_in) and the residual stream
         worst = max(worst, rel_err(hg - h, ho - h))
         assert_close(hg, ho, what=f"h_out step {t}")
     conv_g, ssm_g = eng.get_state(0)
     assert_close(conv_g[0], cs, what="conv state")
     assert_close(ssm_g[0], ss, what="ssm state")
-    assert worst <= 5e-3, worst
+    assert worst <= 1e-3, worst
     eng.close()
 
 
@@ -59,12 +61,13 @@ def test_tiny_decode_64_steps():
     tok = int(synth.gen_tokens(seed, 0, 1, s.vocab)[0])
     tt = _i32([tok])
     for step in range(64):
-        logits, nxt = eng.decode_step(tt)
-        lg = logits.cpu().numpy()[0]
-        gtok = int(nxt.cpu().numpy()[0])
-        otok, ol, _ = om.decode_step(st, tok)
+        tr = trace_to_numpy(eng.trace_step(tt))
+        lg = tr["logits"][0]
+        gtok = int(np.argmax(lg))
+        hs, ol, otok = oracle_follow_step(om, st, tok, tr)
+        for l in range(s.n_layer + 1):
+            assert_close(tr["h"][l, 0], hs[l], what=f"h step {step} layer {l}")
         assert_close(lg, ol, what=f"logits step {step}")
-        assert gtok == int(np.argmax(lg))
         assert token_ok(gtok, ol), (step, gtok, otok)
         tok = gtok
         tt = _i32([tok])
@@ -87,42 +90,29 @@ def full_model():
     return s, seed, w, oracle.Model(s, w)
 
 
-def test_full_model_layerwise_teacher_forced(full_model):
-    s, seed, w, om = full_model
-    eng = engine(s)
-    eng.load_synthetic(seed)
-    toks = synth.gen_tokens(seed, 0, 3, s.vocab)
-    st = oracle.State(s)
-    for step, tok in enumerate(toks):
-        trace, logits = eng.trace_step(_i32([tok]))
-        tr = trace.cpu().numpy()[:, 0, :].astype(np.float64)
-        assert np.array_equal(tr[0], om.embed(int(tok)).astype(np.float32).astype(np.float64))
-        for l in range(s.n_layer):
-            ho = oracle.layer_step(s, w["layers"][l], tr[l], st.conv[l], st.ssm[l])
-            assert_close(tr[l + 1] - tr[l], ho - tr[l], tol=5e-3, what=f"mixer out step {step} layer {l}")
-            assert_close(tr[l + 1], ho, what=f"h step {step} layer {l}")
-        best, ol, _, _ = om.lm_head(tr[-1])
-        assert_close(logits.cpu().numpy()[0], ol, what=f"logits step {step}")
-    eng.close()
-
-
-def test_full_model_free_running_logits(full_model):
-    # no teacher forcing inside the stack: 4 decode steps, logits within tolerance
+def test_full_model_greedy_decode(full_model):
+    # 48 layers, batch 1: prefill 16 seeded tokens, then greedy steps; the oracle
+    # follows the GPU's int8 decisions where they are correct roundings and its
+    # greedy token where it is a near-tie
     s, seed, w, om = full_model
     eng = engine(s)
     eng.load_synthetic(seed)
     st = oracle.State(s)
-    tok = int(synth.gen_tokens(seed, 0, 1, s.vocab)[0])
-    errs = []
-    for step in range(4):
-        logits, nxt = eng.decode_step(_i32([tok]))
-        otok, ol, _ = om.decode_step(st, tok)
-        errs.append(rel_err(logits.cpu().numpy()[0], ol))
-        gtok = int(nxt.cpu().numpy()[0])
-        assert token_ok(gtok, ol, tol=1e-2), (step, gtok, otok)
-        tok = gtok
-    print("free-running logit errors", errs)
-    assert max(errs) <= 1e-2, errs
+    prompt = synth.gen_tokens(seed, 0, 16, s.vocab)
+    for step, tok in enumerate(list(prompt) + [None] * 4):
+        if tok is None:
+            tok = gtok
+        tr = trace_to_numpy(eng.trace_step(_i32([tok])))
+        hs, ol, otok = oracle_follow_step(om, st, tok, tr)
+        if step in (0, 15, 19):
+            for l in range(s.n_layer + 1):
+                assert_close(tr["h"][l, 0], hs[l], what=f"h step {step} layer {l}")
+        assert_close(tr["logits"][0], ol, what=f"logits step {step}")
+        gtok = int(np.argmax(tr["logits"][0]))
+        assert token_ok(gtok, ol), (step, gtok, otok)
+    conv_g, ssm_g = eng.get_state(0)
+    assert_close(ssm_g, st.ssm, what="ssm state after 20 steps")
+    assert_close(conv_g, st.conv, what="conv state after 20 steps")
     eng.close()
 
 
