@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Decode throughput of the 48-layer DF-SSM model (Mamba-2 1.3B shape) at batch 1
+on one MI355X.
+
+Workload: seeded synthetic weights (1-bit scaffold + int8 LoRA r=16, int8 tied
+embedding / LM head, vocab 50288), a 16-token seeded prompt prefilled, then
+greedy decoding where every step is one replay of the captured HIP graph of
+the whole step and the argmax is fed back on the device.  A step is one token
+through all 48 layers, the LM head and the argmax.
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (HIP-event
+timing of that kernel, algorithmic bytes per launch), the whole-step HBM
+roofline, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def algorithmic_bytes(s):
+    """Bytes each decode-step kernel must move at batch 1 (reads + writes)."""
+    dm, di, N, H, P, V, r = s.d_model, s.d_inner, s.d_state, s.n_heads, s.headdim, s.vocab, s.rank
+    dp, cd, K = s.d_in_proj, s.conv_dim, s.d_conv
+    f = 4
+    k = {}
+    k["in_proj"] = (dp * dm // 8 + dp * f + dp * r + dp * f      # bits, row scale, LoRA up + scale
+                    + (dm // 32) * 8 * 4 + 3 * f + r * f          # bit planes, qsum/s, t
+                    + cd * K * f + cd * f                          # conv weight, bias
+                    + 2 * (K - 1) * cd * f                         # conv state read + write
+                    + (di + H) * f + cd * f)                       # z, dt_raw, conv output
+    k["ssm"] = (2 * H * P * N * f                                 # state read + write
+                + cd * f + (di + H) * f + 3 * H * f + di * f)      # x,B,C; z, dt; A_log,dt_bias,D; gated y
+    k["out_proj"] = (dm * di // 8 + dm * f + dm * r + dm * f + (di // 32) * 8 * 4 + 3 * f + r * f
+                     + 2 * dm * f)                                 # residual read + write
+    k["lm_head"] = V * dm + V * f + V * f + dm                    # E, sE, logits, qf
+    k["norm_quant"] = dm * f + dm * f + r * dm + dm + (dm // 32) * 8 * 4 + (r + 3) * f
+    return k
+
+
+def step_bytes(s):
+    """Algorithmic HBM bytes of one batch-1 decode step of the whole model."""
+    dm, di, N, H, P, V, r = s.d_model, s.d_inner, s.d_state, s.n_heads, s.headdim, s.vocab, s.rank
+    dp, cd, K = s.d_in_proj, s.conv_dim, s.d_conv
+    f = 4
+    per_layer = (dp * dm // 8 + dm * di // 8                      # scaffold bits
+                 + (dp + dm) * f                                   # scaffold row scales
+                 + r * (dm + dp + di + dm)                         # LoRA int8
+                 + (2 * r + dp + dm) * f                           # LoRA scales
+                 + cd * (K + 1) * f                                # conv weight + bias
+                 + K * cd * f                                      # conv state: read K-1 columns, write 1
+                 + 2 * H * P * N * f                               # SSM state read + write
+                 + (3 * H + dm + di) * f)                          # A_log, dt_bias, D, norm weights
+    once = V * dm + V * f + dm * f + dm + V * f                    # LM head + scales, final norm, embed row, logits
+    return s.n_layer * per_layer + once
+
+
+def cpu_baseline(shape, seed, prompt, budget_s):
+    """The CPU oracle decoding the same model, timed on a bounded number of steps."""
+    import numpy as np
+    import oracle
+    import synth
+    t0 = time.perf_counter()
+    om = oracle.Model(shape, synth.gen_model(shape, seed))
+    st = oracle.State(shape)
+    setup = time.perf_counter() - t0
+    tok = int(prompt[0])
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        tok, _, _ = om.decode_step(st, tok)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 1000:
+            break
+    return {"value": round(steps / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{steps} greedy decode steps of the 48-layer model at batch 1 from a zero state "
+                      f"({el:.1f} s; weight generation {setup:.1f} s not timed); plain C, fp64, OpenMP over rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256, help="timed greedy decode steps")
+    ap.add_argument("--warmup", type=int, default=16, help="untimed decode steps before the timed region")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (the decode path is per-sequence data-parallel; "
+              f"see the sharding notes); --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from bit_quantized_mamba_amd import Engine
+
+    s = synth.FULL_1P3B
+    seed = synth.SEED_BASE + 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    eng = Engine.from_shape(s, max_batch=1, device=0)
+    eng.load_synthetic(seed)
+    prompt = synth.gen_tokens(seed, 0, 16, s.vocab)
+    _, nxt = eng.prefill(torch.from_numpy(prompt[None].astype("int32")).to(dev))
+    tok = nxt.clone()
+    out = torch.empty((max(args.steps, args.warmup, 1), 1), dtype=torch.int32, device=dev)
+    if args.warmup:
+        eng.generate(tok, args.warmup, out=out, use_graph=True)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    eng.generate(tok, args.steps, out=out, use_graph=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eng.check()
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / args.steps
+    value = args.steps / (ms / 1e3)
+    sb = step_bytes(s)
+    step_gbs = sb / (ms_per_step / 1e3) / 1e9
+
+    kernels = {}
+    roofline = None
+    if not args.no_kernel_timing:
+        ab = algorithmic_bytes(s)
+        per_step = {"in_proj": s.n_layer, "ssm": s.n_layer, "out_proj": s.n_layer, "lm_head": 1,
+                    "norm_quant": 2 * s.n_layer + 1}
+        for name in ("in_proj", "ssm", "out_proj", "lm_head", "norm_quant"):
+            iters = 960 if name != "lm_head" else 64
+            us = eng.time_kernel(name, 1, iters)
+            gbs = ab[name] / (us * 1e-6) / 1e9
+            kernels[name] = {"us_per_launch": round(us, 3), "launches_per_step": per_step[name],
+                             "us_per_step": round(us * per_step[name], 2), "bytes_per_launch": ab[name],
+                             "GB/s": round(gbs, 1)}
+        dom = max(kernels, key=lambda k: kernels[k]["us_per_step"])
+        kd = kernels[dom]
+        achieved = kd["bytes_per_launch"] / (kd["us_per_launch"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom}
+        eng.reset_state(1)
+
+    result = {
+        "metric": "decode tokens/s, batch=1, 48-layer 1.3B shape; % of HBM roofline",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8/1-bit weights, int32 accumulation, f32 state",
+        "data": "synthetic (seeded weights and tokens)",
+        "config": {"workload": "DF-SSM 48-layer Mamba-2 1.3B shape (d_model 2048, d_inner 4096, d_state 128, "
+                               "64 heads, vocab 50288), batch 1, 16-token prefill then greedy decode, one "
+                               "hipGraph replay per token",
+                   "batch": 1, "prefill": 16},
+        "roofline": roofline,
+        "step_roofline": {"bound": "hbm", "bytes_per_step": sb, "achieved": round(step_gbs, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(s, seed, prompt, args.cpu_seconds)
+    eng.close()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -203,6 +203,14 @@ class Engine:
              _dp(t["logits"]), _stream(stream))
         return t
 
+    KERNELS = {"in_proj": 0, "ssm": 1, "out_proj": 2, "lm_head": 3, "norm_quant": 4}
+
+    def time_kernel(self, kernel: str, batch: int = 1, iters: int = 480, stream=None) -> float:
+        """Mean microseconds per launch of one decode-step kernel (leaves the state undefined)."""
+        avg = ctypes.c_float()
+        call("dfssm_time_kernel", self._h, self.KERNELS[kernel], batch, iters, ctypes.byref(avg), _stream(stream))
+        return avg.value
+
     def check(self, stream=None) -> None:
         call("dfssm_check_device", self._h, _stream(stream))
 

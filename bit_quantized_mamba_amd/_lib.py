@@ -38,6 +38,7 @@ EXPORTS = {
     "dfssm_layer_step": [_p, _i32, _p, _p, _i32, _p, _p, _p],
     "dfssm_trace_step": [_p, _p, _i32, _p, _p, _p, _p, _p, _p],
     "dfssm_check_device": [_p, _p],
+    "dfssm_time_kernel": [_p, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_float), _p],
     "dfssm_k_quant": [_p, _i32, _i32, _p, _p, _p],
     "dfssm_k_proj": [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p],
 }

@@ -172,11 +172,12 @@ hipStream_t S(void* s) { return (hipStream_t)s; }
 // ---------------------------------------------------------------------------
 // one layer on the context's workspace h[0..B)
 // ---------------------------------------------------------------------------
-dfssm_status enqueue_layer(dfssm_ctx* c, int l, int B, hipStream_t st, int8_t* q1_out = nullptr,
-                           int8_t* q2_out = nullptr) {
-  HIP_TRY(launch_norm_quant(c->h, c->lt<float>(l, DFSSM_T_NORM_W), c->dm, B, c->eps, c->lt<int8_t>(l, DFSSM_T_IN_A),
-                            c->lt<float>(l, DFSSM_T_IN_SA), c->r, c->q1, c->pl1, c->qs1, c->s1, c->t1, st));
-  if (q1_out) HIP_TRY(hipMemcpyAsync(q1_out, c->q1, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st));
+hipError_t norm_quant_in(dfssm_ctx* c, int l, int B, hipStream_t st) {
+  return launch_norm_quant(c->h, c->lt<float>(l, DFSSM_T_NORM_W), c->dm, B, c->eps, c->lt<int8_t>(l, DFSSM_T_IN_A),
+                           c->lt<float>(l, DFSSM_T_IN_SA), c->r, c->q1, c->pl1, c->qs1, c->s1, c->t1, st);
+}
+
+hipError_t in_proj(dfssm_ctx* c, int l, int B, hipStream_t st) {
   ProjArgs a{};
   a.bits = c->lt<uint32_t>(l, DFSSM_T_IN_BITS);
   a.sw = c->lt<float>(l, DFSSM_T_IN_SW);
@@ -196,13 +197,21 @@ dfssm_status enqueue_layer(dfssm_ctx* c, int l, int B, hipStream_t st, int8_t* q
   a.d_inner = c->di;
   a.conv_dim = c->cdim;
   a.K = c->K;
-  HIP_TRY(launch_proj(a, EPI_IN_PROJ, st));
-  HIP_TRY(launch_ssm(c->xc, c->zx, c->dproj, c->lt<float>(l, DFSSM_T_A_LOG), c->lt<float>(l, DFSSM_T_DT_BIAS),
-                     c->lt<float>(l, DFSSM_T_D), c->ssm + (size_t)l * c->H * c->P * c->N, c->ssm_bstride, c->g, B,
-                     c->H, c->P, c->N, c->di, c->cdim, st));
-  HIP_TRY(launch_norm_quant(c->g, c->lt<float>(l, DFSSM_T_GNORM_W), c->di, B, c->eps, c->lt<int8_t>(l, DFSSM_T_OUT_A),
-                            c->lt<float>(l, DFSSM_T_OUT_SA), c->r, c->q2, c->pl2, c->qs2, c->s2, c->t2, st));
-  if (q2_out) HIP_TRY(hipMemcpyAsync(q2_out, c->q2, (size_t)B * c->di, hipMemcpyDeviceToDevice, st));
+  return launch_proj(a, EPI_IN_PROJ, st);
+}
+
+hipError_t ssm_step(dfssm_ctx* c, int l, int B, hipStream_t st) {
+  return launch_ssm(c->xc, c->zx, c->dproj, c->lt<float>(l, DFSSM_T_A_LOG), c->lt<float>(l, DFSSM_T_DT_BIAS),
+                    c->lt<float>(l, DFSSM_T_D), c->ssm + (size_t)l * c->H * c->P * c->N, c->ssm_bstride, c->g, B,
+                    c->H, c->P, c->N, c->di, c->cdim, st);
+}
+
+hipError_t norm_quant_out(dfssm_ctx* c, int l, int B, hipStream_t st) {
+  return launch_norm_quant(c->g, c->lt<float>(l, DFSSM_T_GNORM_W), c->di, B, c->eps, c->lt<int8_t>(l, DFSSM_T_OUT_A),
+                           c->lt<float>(l, DFSSM_T_OUT_SA), c->r, c->q2, c->pl2, c->qs2, c->s2, c->t2, st);
+}
+
+hipError_t out_proj(dfssm_ctx* c, int l, int B, hipStream_t st) {
   ProjArgs o{};
   o.bits = c->lt<uint32_t>(l, DFSSM_T_OUT_BITS);
   o.sw = c->lt<float>(l, DFSSM_T_OUT_SW);
@@ -214,7 +223,23 @@ dfssm_status enqueue_layer(dfssm_ctx* c, int l, int B, hipStream_t st, int8_t* q
   o.r = c->r;
   o.B = B;
   o.h = c->h;
-  HIP_TRY(launch_proj(o, EPI_OUT_PROJ, st));
+  return launch_proj(o, EPI_OUT_PROJ, st);
+}
+
+hipError_t lm_head(dfssm_ctx* c, int B, float* logits, hipStream_t st) {
+  return launch_lm_head(c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), c->q1, c->s1, c->V,
+                        c->dm, B, logits, st);
+}
+
+dfssm_status enqueue_layer(dfssm_ctx* c, int l, int B, hipStream_t st, int8_t* q1_out = nullptr,
+                           int8_t* q2_out = nullptr) {
+  HIP_TRY(norm_quant_in(c, l, B, st));
+  if (q1_out) HIP_TRY(hipMemcpyAsync(q1_out, c->q1, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(in_proj(c, l, B, st));
+  HIP_TRY(ssm_step(c, l, B, st));
+  HIP_TRY(norm_quant_out(c, l, B, st));
+  if (q2_out) HIP_TRY(hipMemcpyAsync(q2_out, c->q2, (size_t)B * c->di, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(out_proj(c, l, B, st));
   return DFSSM_OK;
 }
 
@@ -247,8 +272,7 @@ dfssm_status enqueue_step(dfssm_ctx* c, const int32_t* tok, int tok_stride, int 
                             c->pl1, c->qs1, c->s1, c->t1, st));
   if (tr && tr->qf) HIP_TRY(hipMemcpyAsync(tr->qf, c->q1, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st));
   float* lg = logits ? logits : c->logits;
-  HIP_TRY(launch_lm_head(c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), c->q1, c->s1, c->V,
-                         c->dm, B, lg, st));
+  HIP_TRY(lm_head(c, B, lg, st));
   if (next || out) HIP_TRY(launch_argmax(lg, c->V, B, next ? next : c->next, out, c->counter, st));
   return DFSSM_OK;
 }
@@ -633,6 +657,42 @@ dfssm_status dfssm_trace_step(dfssm_ctx* c, const int32_t* d_tok, int32_t B, flo
   tr.q2 = d_q2_trace;
   tr.qf = d_qf;
   return enqueue_step(c, d_tok, 1, B, d_logits, nullptr, nullptr, &tr, true, S(stream));
+}
+
+dfssm_status dfssm_time_kernel(dfssm_ctx* c, int32_t kernel, int32_t B, int32_t iters, float* avg_us, void* stream) {
+  dfssm_status v = check_ctx(c);
+  if (v != DFSSM_OK) return v;
+  if ((v = check_B(c, B)) != DFSSM_OK) return v;
+  if (iters < 1 || !avg_us) return fail(DFSSM_E_INVALID, "iters must be >= 1 and avg_us non-null");
+  if (kernel < DFSSM_K_IN_PROJ || kernel > DFSSM_K_NORM_QUANT) return fail(DFSSM_E_INVALID, "unknown kernel id");
+  hipStream_t st = S(stream);
+  auto launch = [&](int i) -> hipError_t {
+    const int l = i % c->L;
+    switch (kernel) {
+      case DFSSM_K_IN_PROJ: return in_proj(c, l, B, st);
+      case DFSSM_K_SSM: return ssm_step(c, l, B, st);
+      case DFSSM_K_OUT_PROJ: return out_proj(c, l, B, st);
+      case DFSSM_K_LM_HEAD: return lm_head(c, B, c->logits, st);
+      default: return norm_quant_in(c, l, B, st);
+    }
+  };
+  // operands of the in_proj / LM head kernels come from the norm kernel
+  HIP_TRY(norm_quant_in(c, 0, B, st));
+  for (int i = 0; i < 3; ++i) HIP_TRY(launch(i));
+  hipEvent_t e0, e1;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  hipError_t e = hipEventRecord(e0, st);
+  for (int i = 0; i < iters && e == hipSuccess; ++i) e = launch(i);
+  if (e == hipSuccess) e = hipEventRecord(e1, st);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return fail(DFSSM_E_HIP, std::string("time_kernel: ") + hipGetErrorString(e));
+  *avg_us = ms * 1000.0f / (float)iters;
+  return DFSSM_OK;
 }
 
 dfssm_status dfssm_check_device(dfssm_ctx* c, void* stream) {

@@ -181,6 +181,22 @@ dfssm_status dfssm_trace_step(dfssm_ctx* ctx, const int32_t* d_tok, int32_t B, f
                               int8_t* d_q1_trace, int8_t* d_q2_trace, int8_t* d_qf, float* d_logits,
                               void* stream);
 
+/* Kernel timing for roofline reports.  Launches one kernel of the batch-B
+ * decode step `iters` times back to back on `stream` (layer i % n_layer on
+ * launch i, same arguments as inside the step) between two HIP events and
+ * writes the mean time per launch in microseconds to *avg_us.  Synchronous.
+ * Leaves the recurrent state and the workspace undefined: reset the state
+ * before decoding again.                                                   */
+enum {
+  DFSSM_K_IN_PROJ = 0,    /* norm-quantised input -> 1-bit GEMV + LoRA + conv epilogue */
+  DFSSM_K_SSM = 1,        /* SSM state update + gate                                  */
+  DFSSM_K_OUT_PROJ = 2,   /* 1-bit GEMV + LoRA + residual                             */
+  DFSSM_K_LM_HEAD = 3,    /* tied int8 LM head GEMV                                   */
+  DFSSM_K_NORM_QUANT = 4  /* RMSNorm + quantise + operand prep of the in_proj input    */
+};
+dfssm_status dfssm_time_kernel(dfssm_ctx* ctx, int32_t kernel, int32_t B, int32_t iters, float* avg_us,
+                               void* stream);
+
 /* Wait for `stream` and report (then clear) any error flagged by a kernel. */
 dfssm_status dfssm_check_device(dfssm_ctx* ctx, void* stream);
 

@@ -61,8 +61,14 @@ def lib() -> ctypes.CDLL:
         L.or_decode_step.restype = _i
         L.or_prefill.argtypes = [_p, _p, _p, _p, _p, _i, _p]
         L.or_prefill.restype = _i
+        L.or_num_threads.restype = _i
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(lib().or_num_threads())
 
 
 def _ptr(a: Optional[np.ndarray]):

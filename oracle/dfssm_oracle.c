@@ -400,3 +400,11 @@ int or_prefill(const int* sh, const void* const* w, double* conv, double* ssm, c
   }
   return next;
 }
+
+/* Threads the OpenMP loops above use (1 when built without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int or_num_threads(void) { return omp_get_max_threads(); }
+#else
+int or_num_threads(void) { return 1; }
+#endif
