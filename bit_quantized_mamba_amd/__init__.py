@@ -203,6 +203,12 @@ class Engine:
              _dp(t["logits"]), _stream(stream))
         return t
 
+    PATHS = {"auto": 0, "kernels": 1, "persistent": 2}
+
+    def set_path(self, path: str) -> None:
+        """Batch-1 execution path: "auto", "kernels" (per-layer kernels) or "persistent"."""
+        call("dfssm_set_path", self._h, self.PATHS[path])
+
     KERNELS = {"in_proj": 0, "ssm": 1, "out_proj": 2, "lm_head": 3, "norm_quant": 4}
 
     def time_kernel(self, kernel: str, batch: int = 1, iters: int = 480, stream=None) -> float:
@@ -210,6 +216,15 @@ class Engine:
         avg = ctypes.c_float()
         call("dfssm_time_kernel", self._h, self.KERNELS[kernel], batch, iters, ctypes.byref(avg), _stream(stream))
         return avg.value
+
+    def profile_persistent(self, tok, n_tokens: int, prof_tokens: int, stream=None):
+        """Phase timestamps of the persistent kernel: uint64 [prof_tokens][n_layer+1][grid][10] (100 MHz)."""
+        torch = _torch()
+        self._check_tok(tok, 1)
+        grid = self.n_heads * (self.headdim // 16)
+        prof = torch.zeros((prof_tokens, self.n_layer + 1, grid, 10), dtype=torch.int64, device=tok.device)
+        call("dfssm_profile_persistent", self._h, _dp(tok), n_tokens, _dp(prof), prof_tokens, _stream(stream))
+        return prof
 
     def check(self, stream=None) -> None:
         call("dfssm_check_device", self._h, _stream(stream))

@@ -26,6 +26,7 @@ EXPORTS = {
     "dfssm_create": [ctypes.POINTER(DfssmConfig), _i32, ctypes.POINTER(_p)],
     "dfssm_destroy": [_p],
     "dfssm_device_bytes": [_p, ctypes.POINTER(_sz)],
+    "dfssm_set_path": [_p, _i32],
     "dfssm_load_synthetic": [_p, ctypes.c_uint64, _p],
     "dfssm_set_tensor": [_p, _i32, _i32, _p, _sz],
     "dfssm_get_tensor": [_p, _i32, _i32, _p, _sz],
@@ -38,6 +39,7 @@ EXPORTS = {
     "dfssm_layer_step": [_p, _i32, _p, _p, _i32, _p, _p, _p],
     "dfssm_trace_step": [_p, _p, _i32, _p, _p, _p, _p, _p, _p],
     "dfssm_check_device": [_p, _p],
+    "dfssm_profile_persistent": [_p, _p, _i32, _p, _i32, _p],
     "dfssm_time_kernel": [_p, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_float), _p],
     "dfssm_k_quant": [_p, _i32, _i32, _p, _p, _p],
     "dfssm_k_proj": [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p],

@@ -15,20 +15,72 @@ __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)
 // softplus with the usual linear branch above 20 (log1p(e^a) - a < 2.1e-9 there)
 __device__ __forceinline__ float softplus_f(float a) { return a > 20.0f ? a : log1pf(__expf(a)); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// ---------------------------------------------------------------------------
+// cross-lane reductions on DPP (data movement inside the VALU; no LDS round
+// trip).  Lanes form rows of 16.  quad_perm swaps within 4 lanes, the row
+// half-mirror pairs the two quads of each half row, the row mirror pairs the
+// two halves of a row, and row_bcast:15 / :31 carry a row's last lane into
+// the next row(s).  All lanes must be active.
+// ---------------------------------------------------------------------------
+enum : int {
+  kDppQuadSwap1 = 0xB1,  // quad_perm [1,0,3,2]
+  kDppQuadSwap2 = 0x4E,  // quad_perm [2,3,0,1]
+  kDppRowHalfMirror = 0x141,
+  kDppRowMirror = 0x140,
+  kDppRowBcast15 = 0x142,
+  kDppRowBcast31 = 0x143
+};
+
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
+}
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xF, false));
+}
+
+// Sum over aligned groups of U lanes (U a power of two, 1..64).  For U <= 16
+// every lane of a group ends with the group sum; for U = 32 the sum is valid
+// in lanes 16..31 and 48..63 (rows 1 and 3); for U = 64 in lanes 48..63.
+__device__ __forceinline__ int group_sum_i(int v, int U) {
+  if (U >= 2) v += dpp_i<kDppQuadSwap1>(v);
+  if (U >= 4) v += dpp_i<kDppQuadSwap2>(v);
+  if (U >= 8) v += dpp_i<kDppRowHalfMirror>(v);
+  if (U >= 16) v += dpp_i<kDppRowMirror>(v);
+  if (U >= 32) v += dpp_i<kDppRowBcast15, 0xA>(v);
+  if (U >= 64) v += dpp_i<kDppRowBcast31, 0x8>(v);
   return v;
+}
+// lane holding the sum of the group that starts at lane g0 (see group_sum_i)
+__device__ __forceinline__ int group_sum_lane(int g0, int U) {
+  return U <= 16 ? g0 : (U == 32 ? g0 + 16 : 48);
+}
+
+// row (16-lane) all-reduce, then the four rows combined through readlane:
+// the result is uniform across the wave.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<kDppQuadSwap1>(v);
+  v += dpp_f<kDppQuadSwap2>(v);
+  v += dpp_f<kDppRowHalfMirror>(v);
+  v += dpp_f<kDppRowMirror>(v);
+  const int b = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<kDppQuadSwap1>(v));
+  v = fmaxf(v, dpp_f<kDppQuadSwap2>(v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  const int b = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = group_sum_i(v, 16);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
 // ---------------------------------------------------------------------------

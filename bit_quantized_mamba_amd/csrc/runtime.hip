@@ -11,6 +11,7 @@
 
 #include "../../include/dfssm.h"
 #include "common.h"
+#include "persistent.h"
 
 using namespace dfssm;
 
@@ -75,6 +76,16 @@ struct dfssm_ctx {
 
   // graphs keyed by (B, d_tok, d_out)
   std::map<std::tuple<int, const void*, const void*>, hipGraphExec_t> graphs;
+
+  // persistent batch-1 path
+  int path = DFSSM_PATH_AUTO;
+  bool persist_ok = false;
+  std::string persist_why;
+  int persist_grid = 0;
+  uint64_t* boxes = nullptr;
+  size_t box_words = 0;
+  int* abort_flag = nullptr;
+  unsigned host_epoch = 1;
 
   void* tensor_ptr(int layer, int kind) const {
     const TensorInfo& t = layer >= 0 ? layer_t[(size_t)layer * DFSSM_T_PER_LAYER + kind] : global_t[kind];
@@ -277,6 +288,70 @@ dfssm_status enqueue_step(dfssm_ctx* c, const int32_t* tok, int tok_stride, int 
   return DFSSM_OK;
 }
 
+// Whether batch-B work runs on the persistent kernel; fails when it is required but cannot run.
+dfssm_status use_persistent(const dfssm_ctx* c, int B, bool* yes) {
+  *yes = false;
+  if (B != 1 || c->path == DFSSM_PATH_KERNELS) return DFSSM_OK;
+  if (!c->persist_ok) {
+    if (c->path == DFSSM_PATH_PERSISTENT)
+      return fail(DFSSM_E_UNSUPPORTED, "persistent decode unavailable: " + c->persist_why);
+    return DFSSM_OK;
+  }
+  *yes = true;
+  return DFSSM_OK;
+}
+
+dfssm_status run_persistent(dfssm_ctx* c, const int32_t* tok_in, int32_t* tok_last, int32_t* tok_out, int n_tokens,
+                            float* logits, const Trace* tr, hipStream_t st, unsigned long long* prof = nullptr,
+                            int prof_tokens = 0) {
+  const unsigned need = (unsigned)n_tokens * persistent_exchanges_per_token(c->L) + 1;
+  if ((unsigned long long)c->host_epoch + need >= 0x7fffffffull) {
+    // epochs are never reused: clear the boxes and start over
+    HIP_TRY(launch_zero(c->boxes, sizeof(uint64_t) * c->box_words, st));
+    c->host_epoch = 1;
+  }
+  PersistArgs a{};
+  a.wbase = c->wbuf;
+  a.n_layer = c->L;
+  a.d_model = c->dm;
+  a.d_inner = c->di;
+  a.d_state = c->N;
+  a.headdim = c->P;
+  a.n_heads = c->H;
+  a.vocab = c->V;
+  a.d_conv = c->K;
+  a.rank = c->r;
+  a.eps = c->eps;
+  a.E = c->lt<int8_t>(-1, DFSSM_G_EMBED);
+  a.sE = c->lt<float>(-1, DFSSM_G_EMBED_SCALE);
+  a.final_norm = c->lt<float>(-1, DFSSM_G_FINAL_NORM);
+  a.conv = c->conv;
+  a.ssm = c->ssm;
+  a.hbox = c->boxes;
+  a.bcbox = a.hbox + (size_t)8 * c->dm;
+  a.gbox = a.bcbox + (size_t)8 * 2 * c->N;
+  a.abox = a.gbox + (size_t)8 * c->di;
+  a.epoch0 = c->host_epoch;
+  a.abort_flag = c->abort_flag;
+  a.err = c->err;
+  a.tok_in = tok_in;
+  a.tok_last = tok_last;
+  a.tok_out = tok_out;
+  a.n_tokens = n_tokens;
+  a.logits = logits ? logits : c->logits;
+  if (tr) {
+    a.trace_h = tr->h;
+    a.trace_q1 = tr->q1;
+    a.trace_q2 = tr->q2;
+    a.trace_qf = tr->qf;
+  }
+  a.prof = prof;
+  a.prof_tokens = prof_tokens;
+  c->host_epoch += need;
+  HIP_TRY(launch_decode_persistent(a, c->persist_grid, st));
+  return DFSSM_OK;
+}
+
 dfssm_status check_ctx(const dfssm_ctx* c, bool need_loaded = true) {
   if (!c) return fail(DFSSM_E_INVALID, "null context");
   if (need_loaded && !c->loaded) return fail(DFSSM_E_STATE, "weights not loaded");
@@ -405,6 +480,37 @@ dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** o
     dfssm_destroy(c);
     return fail(DFSSM_E_HIP, "initial clear failed");
   }
+  // persistent batch-1 path: layer pointer table, exchange boxes, abort flag
+  c->persist_grid = c->H * (c->P / 16);
+  const char* why = "";
+  c->persist_ok = persistent_supported(c->dm, c->di, c->N, c->P, c->H, c->r, c->persist_grid, &why);
+  c->persist_why = why;
+  if (c->persist_ok) {
+    // the kernel addresses layer l, kind k as base + l * stride + offset(k): check that this is our layout
+    size_t stride = 0, offs[DFSSM_T_PER_LAYER];
+    bool same = persistent_layout(c->dm, c->di, c->N, c->P, &stride, offs);
+    for (int l = 0; same && l < c->L; ++l)
+      for (int k = 0; same && k < DFSSM_T_PER_LAYER; ++k)
+        same = c->layer_t[(size_t)l * DFSSM_T_PER_LAYER + k].offset == (size_t)l * stride + offs[k];
+    if (!same) {
+      c->persist_ok = false;
+      c->persist_why = "weight layout differs from the persistent kernel's";
+    }
+  }
+  if (c->persist_ok) {
+    c->box_words = persistent_box_words(c->dm, c->di, c->N, c->persist_grid);
+    if (hipMalloc(&c->boxes, sizeof(uint64_t) * c->box_words) != hipSuccess ||
+        hipMalloc(&c->abort_flag, 256) != hipSuccess) {
+      (void)hipGetLastError();
+      dfssm_destroy(c);
+      return fail(DFSSM_E_OOM, "device allocation failed");
+    }
+    if (launch_zero(c->boxes, sizeof(uint64_t) * c->box_words, nullptr) != hipSuccess ||
+        launch_zero(c->abort_flag, 256, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      dfssm_destroy(c);
+      return fail(DFSSM_E_HIP, "persistent path setup failed");
+    }
+  }
   *out = c;
   return DFSSM_OK;
 }
@@ -417,6 +523,8 @@ void dfssm_destroy(dfssm_ctx* c) {
   if (c->wbuf) (void)hipFree(c->wbuf);
   if (c->sbuf) (void)hipFree(c->sbuf);
   if (c->ws) (void)hipFree(c->ws);
+  if (c->boxes) (void)hipFree(c->boxes);
+  if (c->abort_flag) (void)hipFree(c->abort_flag);
   delete c;
 }
 
@@ -564,6 +672,9 @@ dfssm_status dfssm_decode_step(dfssm_ctx* c, const int32_t* d_tok, int32_t B, fl
   if (v != DFSSM_OK) return v;
   if ((v = check_B(c, B)) != DFSSM_OK) return v;
   if (!d_tok) return fail(DFSSM_E_INVALID, "null token pointer");
+  bool pers = false;
+  if ((v = use_persistent(c, B, &pers)) != DFSSM_OK) return v;
+  if (pers) return run_persistent(c, d_tok, nullptr, d_next, 1, d_logits, nullptr, S(stream));
   return enqueue_step(c, d_tok, 1, B, d_logits, d_next, nullptr, nullptr, true, S(stream));
 }
 
@@ -576,6 +687,9 @@ dfssm_status dfssm_generate(dfssm_ctx* c, int32_t* d_tok, int32_t B, int32_t n_s
   if (n_steps < 0) return fail(DFSSM_E_INVALID, "negative step count");
   if (n_steps == 0) return DFSSM_OK;
   hipStream_t st = S(stream);
+  bool pers = false;
+  if ((v = use_persistent(c, B, &pers)) != DFSSM_OK) return v;
+  if (pers) return run_persistent(c, d_tok, d_tok, d_out, n_steps, nullptr, nullptr, st);
   if (d_out) HIP_TRY(launch_zero(c->counter, 4, st));
   if (!use_graph) {
     for (int i = 0; i < n_steps; ++i) {
@@ -656,6 +770,9 @@ dfssm_status dfssm_trace_step(dfssm_ctx* c, const int32_t* d_tok, int32_t B, flo
   tr.q1 = d_q1_trace;
   tr.q2 = d_q2_trace;
   tr.qf = d_qf;
+  bool pers = false;
+  if ((v = use_persistent(c, B, &pers)) != DFSSM_OK) return v;
+  if (pers) return run_persistent(c, d_tok, nullptr, nullptr, 1, d_logits, &tr, S(stream));
   return enqueue_step(c, d_tok, 1, B, d_logits, nullptr, nullptr, &tr, true, S(stream));
 }
 
@@ -703,9 +820,33 @@ dfssm_status dfssm_check_device(dfssm_ctx* c, void* stream) {
   HIP_TRY(hipMemcpy(&flag, c->err, sizeof(int), hipMemcpyDeviceToHost));
   if (flag) {
     HIP_TRY(launch_zero(c->err, 4, nullptr));
+    if (c->abort_flag) HIP_TRY(launch_zero(c->abort_flag, 4, nullptr));
     HIP_TRY(hipDeviceSynchronize());
-    return fail(DFSSM_E_DEVICE, "a kernel flagged an out-of-range token id");
+    std::string msg;
+    if (flag & 1) msg += "a kernel flagged an out-of-range token id; ";
+    if (flag & 2) msg += "the persistent decode kernel gave up waiting on another workgroup and aborted; ";
+    return fail(DFSSM_E_DEVICE, msg);
   }
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_profile_persistent(dfssm_ctx* c, int32_t* d_tok, int32_t n_tokens, uint64_t* d_prof,
+                                      int32_t prof_tokens, void* stream) {
+  dfssm_status v = check_ctx(c);
+  if (v != DFSSM_OK) return v;
+  if (!c->persist_ok) return fail(DFSSM_E_UNSUPPORTED, "persistent decode unavailable: " + c->persist_why);
+  if (!d_tok || !d_prof || n_tokens < 1 || prof_tokens < 1 || prof_tokens > n_tokens)
+    return fail(DFSSM_E_INVALID, "bad profile arguments");
+  return run_persistent(c, d_tok, d_tok, nullptr, n_tokens, nullptr, nullptr, S(stream),
+                        (unsigned long long*)d_prof, prof_tokens);
+}
+
+dfssm_status dfssm_set_path(dfssm_ctx* c, int32_t path) {
+  if (!c) return fail(DFSSM_E_INVALID, "null context");
+  if (path < DFSSM_PATH_AUTO || path > DFSSM_PATH_PERSISTENT) return fail(DFSSM_E_INVALID, "unknown path");
+  if (path == DFSSM_PATH_PERSISTENT && !c->persist_ok)
+    return fail(DFSSM_E_UNSUPPORTED, "persistent decode unavailable: " + c->persist_why);
+  c->path = path;
   return DFSSM_OK;
 }
 

@@ -110,6 +110,16 @@ const char* dfssm_last_error(const dfssm_ctx* ctx);
 dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** out);
 void dfssm_destroy(dfssm_ctx* ctx);
 
+/* Execution path of batch-1 decode.  DFSSM_PATH_AUTO (default) runs batch-1
+ * decode_step / generate / trace_step as one persistent kernel (every
+ * workgroup resident across all layers and tokens, hops between workgroups
+ * through device memory) when the shape and device allow it, and every
+ * other call as a sequence of per-layer kernels; DFSSM_PATH_KERNELS forces
+ * the per-layer kernels; DFSSM_PATH_PERSISTENT requires the persistent
+ * kernel for batch 1 and fails with DFSSM_E_UNSUPPORTED where it cannot run. */
+enum { DFSSM_PATH_AUTO = 0, DFSSM_PATH_KERNELS = 1, DFSSM_PATH_PERSISTENT = 2 };
+dfssm_status dfssm_set_path(dfssm_ctx* ctx, int32_t path);
+
 /* Device bytes the context holds (weights + state + workspace). */
 dfssm_status dfssm_device_bytes(const dfssm_ctx* ctx, size_t* bytes);
 
@@ -196,6 +206,21 @@ enum {
 };
 dfssm_status dfssm_time_kernel(dfssm_ctx* ctx, int32_t kernel, int32_t B, int32_t iters, float* avg_us,
                                void* stream);
+
+/* Phase timestamps of the persistent batch-1 decode kernel, for performance
+ * analysis: greedy-decodes n_tokens from d_tok[0] (updated in place like
+ * dfssm_generate) and writes, for the first prof_tokens tokens, the device
+ * clock (100 MHz counter, uint64) at 10 points of every layer (index n_layer
+ * covers the LM head) of every workgroup into d_prof: uint64
+ * [prof_tokens][n_layer + 1][n_heads * headdim / 16][10].  Points per layer:
+ * 0 start, 1 residual stream received, 2 normalised and quantised, 3 LoRA
+ * down done, 4 in_proj rows done, 5 conv done and B/C published, 6 B/C
+ * received, 7 SSM done and output published, 8 SSM outputs received,
+ * 9 out_proj rows done and published.  LM head: 0 start, 1 residual
+ * received, 2 quantised, 3 logits and local argmax done, 4 token chosen.
+ * Requires the persistent path.  Enqueued.                                 */
+dfssm_status dfssm_profile_persistent(dfssm_ctx* ctx, int32_t* d_tok, int32_t n_tokens, uint64_t* d_prof,
+                                      int32_t prof_tokens, void* stream);
 
 /* Wait for `stream` and report (then clear) any error flagged by a kernel. */
 dfssm_status dfssm_check_device(dfssm_ctx* ctx, void* stream);

@@ -51,10 +51,12 @@ def test_layer_steps_match_oracle(shape, steps):
 # tiny model: 64 greedy decode steps, teacher-forced on the GPU's tokens
 # ---------------------------------------------------------------------------
 
-def test_tiny_decode_64_steps():
+@pytest.mark.parametrize("path", ["kernels", "persistent"])
+def test_tiny_decode_64_steps(path):
     s = synth.TINY
     seed = synth.SEED_BASE
     eng = engine(s)
+    eng.set_path(path)
     eng.load_synthetic(seed)
     om = oracle.Model(s, synth.gen_model(s, seed))
     st = oracle.State(s)
@@ -90,12 +92,14 @@ def full_model():
     return s, seed, w, oracle.Model(s, w)
 
 
-def test_full_model_greedy_decode(full_model):
+@pytest.mark.parametrize("path", ["kernels", "persistent"])
+def test_full_model_greedy_decode(full_model, path):
     # 48 layers, batch 1: prefill 16 seeded tokens, then greedy steps; the oracle
     # follows the GPU's int8 decisions where they are correct roundings and its
     # greedy token where it is a near-tie
     s, seed, w, om = full_model
     eng = engine(s)
+    eng.set_path(path)
     eng.load_synthetic(seed)
     st = oracle.State(s)
     prompt = synth.gen_tokens(seed, 0, 16, s.vocab)
@@ -189,6 +193,33 @@ def test_graph_replay_equals_eager():
     eng.reset_state(3)
     c = eng.generate(_i32(start), 16, use_graph=True).cpu().numpy()
     assert np.array_equal(a, c)
+    eng.close()
+
+
+@pytest.mark.parametrize("shape", [synth.TINY, synth.FULL_1P3B])
+def test_persistent_generate_equals_step_loop(shape):
+    # one launch decoding n tokens == n single-token launches (same kernel, same arithmetic)
+    seed = synth.SEED_BASE
+    n = 12
+    eng = engine(shape)
+    eng.set_path("persistent")
+    eng.load_synthetic(seed)
+    start = int(synth.gen_tokens(seed, 7, 1, shape.vocab)[0])
+    tok = _i32([start])
+    out = eng.generate(tok, n).cpu().numpy()[:, 0]
+    last = int(tok.cpu().numpy()[0])
+    st_a = eng.get_state(0)
+    eng.reset_state(1)
+    t = _i32([start])
+    seq = []
+    for _ in range(n):
+        _, nxt = eng.decode_step(t)
+        t = nxt.clone()
+        seq.append(int(nxt.cpu().numpy()[0]))
+    st_b = eng.get_state(0)
+    assert out.tolist() == seq and last == seq[-1]
+    assert np.array_equal(st_a[0], st_b[0]) and np.array_equal(st_a[1], st_b[1])
+    eng.check()
     eng.close()
 
 
