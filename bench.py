@@ -94,6 +94,9 @@ def main():
     ap.add_argument("--kernel-breakdown", action="store_true",
                     help="also time each kernel of the per-layer (multi-kernel) path")
     ap.add_argument("--path", choices=["auto", "kernels", "persistent"], default="auto")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy (read + write) of this many MiB, "
+                         "a known-size reference for the HBM byte counters of a profiler run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (the decode path is per-sequence data-parallel; "
@@ -126,6 +129,13 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     eng.check()
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # elementwise: reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        del src, dst
     ms = e0.elapsed_time(e1)
     ms_per_step = ms / args.steps
     value = args.steps / (ms / 1e3)

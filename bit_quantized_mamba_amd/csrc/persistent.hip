@@ -36,6 +36,7 @@ constexpr int kPT = 256;  // threads per workgroup: one wave per SIMD, so each w
 constexpr int kPW = kPT / 64;
 constexpr int kR = 8;     // replicas of each published word
 constexpr long kSpinLimit = 1 << 21;
+constexpr int kLutCopies = 16;
 
 __device__ __forceinline__ uint64_t ld64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -44,6 +45,18 @@ __device__ __forceinline__ void st64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t pack(float v, unsigned e) { return ((uint64_t)e << 32) | __float_as_uint(v); }
+
+// The launch's arguments re-read from the kernel-argument segment at the point
+// of use.  The pointer passes through an empty asm so the compiler cannot keep
+// the loaded values live in scalar registers across the token loop: fields used
+// once per token (LM head, token I/O, tracing) cost a scalar load there instead
+// of occupying registers that the layer loop needs.
+typedef __attribute__((address_space(4))) const PersistArgs* KArgs;
+__device__ __forceinline__ KArgs kargs() {
+  uint64_t v = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(v));
+  return (KArgs)v;
+}
 
 __device__ __forceinline__ bool aborted(const int* flag) {
   return __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
@@ -56,32 +69,14 @@ __device__ __forceinline__ void publish(uint64_t* box, int n, int i, float v, un
   for (int r = 0; r < kR; ++r) st64(box + (size_t)r * n + i, w);
 }
 
-// Read words [0, n) of this workgroup's replica into LDS.  All loads of a
-// thread are issued before any is checked; in the common case every word is
-// already current and the check is a handful of compares.  Stale words are
-// re-polled one by one in a compact loop (kept rolled: the layer loop must fit
-// the instruction cache).  Returns false (for every thread of the workgroup)
-// on abort.
-__device__ __noinline__ bool gather_slow(const uint64_t* src, int n, unsigned e, float* dst, int* abort_flag,
-                                         int maxw) {
-  for (int m = 0; m < maxw; ++m) {
-    const int i = threadIdx.x + m * kPT;
-    if (i >= n) break;
-    uint64_t v = ld64(src + i);
-    long spins = 0;
-    while ((unsigned)(v >> 32) != e) {
-      if (++spins > kSpinLimit) {
-        __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return false;
-      }
-      if ((spins & 63) == 0 && aborted(abort_flag)) return false;
-      v = ld64(src + i);
-    }
-    dst[i] = __uint_as_float((unsigned)v);
-  }
-  return true;
-}
-
+// Read words [0, n) of this workgroup's replica into LDS.  A thread issues
+// all of its loads before checking any.  While some are stale it waits on the
+// first stale one alone (a single poll in flight per thread keeps the polling
+// traffic low while the publishers are still working), then re-issues every
+// word that is still stale at once: publishers finish at nearly the same
+// time, so the words missing when the first one lands arrive together and one
+// parallel round picks them up.  Returns false (for every thread of the
+// workgroup) on abort.
 template <int MAXW>
 __device__ bool gather(const uint64_t* box, int n, unsigned e, float* dst, int* abort_flag, int* s_stop) {
   const uint64_t* src = box + (size_t)(blockIdx.x % kR) * n;
@@ -91,20 +86,44 @@ __device__ bool gather(const uint64_t* box, int n, unsigned e, float* dst, int* 
     const int i = threadIdx.x + m * kPT;
     w[m] = i < n ? ld64(src + i) : pack(0.0f, e);
   }
-  bool fresh = true;
-#pragma unroll
-  for (int m = 0; m < MAXW; ++m) fresh &= (unsigned)(w[m] >> 32) == e;
   bool ok = true;
-  if (fresh) {
+  long spins = 0;
+  for (;;) {
+    int first = -1;
+#pragma unroll
+    for (int m = MAXW - 1; m >= 0; --m)
+      if ((unsigned)(w[m] >> 32) != e) first = m;
+    if (first < 0) break;
+    // wait on the first stale word
+    const uint64_t* p = src + threadIdx.x + first * kPT;
+    uint64_t v = ld64(p);
+    while ((unsigned)(v >> 32) != e) {
+      if (++spins > kSpinLimit) {
+        __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = false;
+        break;
+      }
+      if ((spins & 63) == 0 && aborted(abort_flag)) {
+        ok = false;
+        break;
+      }
+      v = ld64(p);
+    }
+    if (!ok) break;
+    // then one parallel round over every word still stale (including that one)
+#pragma unroll
+    for (int m = 0; m < MAXW; ++m)
+      if ((unsigned)(w[m] >> 32) != e) w[m] = ld64(src + threadIdx.x + m * kPT);
+  }
+  if (ok) {
 #pragma unroll
     for (int m = 0; m < MAXW; ++m) {
       const int i = threadIdx.x + m * kPT;
       if (i < n) dst[i] = __uint_as_float((unsigned)w[m]);
     }
   } else {
-    ok = gather_slow(src, n, e, dst, abort_flag, MAXW);
+    *s_stop = 1;
   }
-  if (!ok) *s_stop = 1;
   __syncthreads();
   const bool stop = *s_stop != 0;
   return !stop;
@@ -133,33 +152,12 @@ __device__ __forceinline__ void lds_prefetch(const uint4* src, uint4* lds, int n
 // LDS when its phase starts.
 // ---------------------------------------------------------------------------
 
-// v_writelane (put the wave-uniform v into lane L of r) through the compiler's
-// intrinsic rather than inline asm, so that the wait states gfx950 needs
-// between a VALU write of an SGPR (the ballot's compare) and a VALU read of
-// it are inserted by the compiler
-extern "C" __device__ int dfssm_writelane_i32(int v, int lane_sel, int old) __asm("llvm.amdgcn.writelane.i32");
-template <int L>
-__device__ __forceinline__ void write_lane(uint32_t& r, uint32_t v) {
-  r = (uint32_t)dfssm_writelane_i32((int)v, L, (int)r);
-}
-
-// plane words b of the two 32-input halves covered by one wave-wide ballot,
-// placed in lanes b and 8 + b of pw
-template <int B>
-__device__ __forceinline__ void put_plane_pair(uint32_t& pw, int qi) {
-  const uint64_t mk = __ballot((qi >> B) & 1);
-  write_lane<B>(pw, (uint32_t)mk);
-  write_lane<8 + B>(pw, (uint32_t)(mk >> 32));
-}
-
-// RMSNorm of x[0..n) (LDS) with the norm weight in registers (thread t holds
-// w[t + kPT*m]), then per-token int8 quantisation: q to qs (LDS bytes) and its
-// 8 two's-complement bit planes to planes (LDS, [n/32][8] words).  With
-// p = x*w and u = rstd*p, max|u| = rstd*max|p| exactly (rounding is monotone),
-// so the sum of squares and max|p| share one cross-wave round.  Returns s.
+// RMSNorm with weight w fused with the per-token int8 quantiser: thread t holds
+// inputs t + 256 m.  Sum of squares and max |x w| cross the waves in one LDS
+// round; since rstd > 0 scales every |u| = rstd |x w| alike, the absmax of u
+// is rstd * max |x w|.  Codes go to qs (LDS); returns the scale amax / 127.
 template <int MW>
-__device__ float p_norm_quant(const float* xs, const float (&wr)[MW], int n, float eps, int8_t* qs,
-                              uint32_t* planes, float* red) {
+__device__ float p_norm_quant(const float* xs, const float (&wr)[MW], int n, float eps, int8_t* qs, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float p[MW];
   float ss = 0.0f, pm = 0.0f;
@@ -189,25 +187,12 @@ __device__ float p_norm_quant(const float* xs, const float (&wr)[MW], int n, flo
   const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
 #pragma unroll
   for (int m = 0; m < MW; ++m) {
-    const int i0 = m * kPT + wave * 64;  // this wave's 64 consecutive inputs for this m
-    if (i0 < n) {                        // uniform per wave
+    const int i = threadIdx.x + m * kPT;
+    if (i < n) {
       const float u = rstd * p[m];
       float rq = rintf(u * inv);
       rq = fminf(fmaxf(rq, -127.0f), 127.0f);
-      const int qi = (int)rq;
-      qs[i0 + lane] = (int8_t)qi;
-      // the 16 plane words of these 64 inputs (word i0/32 planes 0..7, word i0/32 + 1 planes 0..7)
-      // collected into lanes 0..15 of one register, then stored by those lanes at once
-      uint32_t pw = 0;
-      put_plane_pair<0>(pw, qi);
-      put_plane_pair<1>(pw, qi);
-      put_plane_pair<2>(pw, qi);
-      put_plane_pair<3>(pw, qi);
-      put_plane_pair<4>(pw, qi);
-      put_plane_pair<5>(pw, qi);
-      put_plane_pair<6>(pw, qi);
-      put_plane_pair<7>(pw, qi);
-      if (lane < 16) planes[(i0 >> 5) * 8 + lane] = pw;
+      qs[i] = (int8_t)(int)rq;
     }
   }
   __syncthreads();
@@ -241,45 +226,58 @@ __device__ void p_lora_down(const uint4* alds, int n, const int8_t* qs, float sA
   __syncthreads();
 }
 
-// sum of q over the +1 weights of four packed words (w), from the 32 plane
-// words of those inputs (pl: [4 words][8 planes])
-__device__ __forceinline__ int p_plane_dot(const uint4 w, const uint32_t (&pl)[32]) {
-  int pos = 0;
+
+// Sign table: entry v (one byte of scaffold bits, input k at bit k) holds the
+// eight signs +1 / -1 of those inputs as int8, inputs 0..3 in .x and 4..7 in
+// .y, so that the 1-bit x int8 dot product runs on the packed int8 dot unit
+// with no bit-plane transpose of the activations.  The table is stored
+// kLutCopies times interleaved (entry v of copy c at [v][c]) and lane l reads
+// copy l % kLutCopies: the 16 lanes an LDS cycle serves for 8-byte reads then
+// hit 16 distinct bank pairs whatever bytes they look up.
+__device__ __forceinline__ uint2 sign_entry(uint32_t v) {
+  uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    uint32_t v = __builtin_popcount(w.x & pl[b]);
-    v += __builtin_popcount(w.y & pl[8 + b]);
-    v += __builtin_popcount(w.z & pl[16 + b]);
-    v += __builtin_popcount(w.w & pl[24 + b]);
-    pos += b < 7 ? (int)(v << b) : -(int)(v << 7);
+  for (int k = 0; k < 4; ++k) {
+    lo |= (((v >> k) & 1u) ? 0x01u : 0xFFu) << (8 * k);
+    hi |= (((v >> (k + 4)) & 1u) ? 0x01u : 0xFFu) << (8 * k);
   }
-  return pos;
+  return make_uint2(lo, hi);
 }
 
-// sum of q over the 128 inputs whose planes are pl
-__device__ __forceinline__ int p_plane_sum(const uint32_t (&pl)[32]) {
-  int q = 0;
+// sum_i s_i q_i over the 128 inputs of one 16-byte chunk of scaffold bits w
+// (word x = inputs 0..31, bit i of a word = input i), s_i = +1 where the bit is
+// set and -1 where it is clear; qd holds the 128 int8 codes as 32 words.
+// lut: this lane's copy of the sign table (table + lane % kLutCopies).
+__device__ __forceinline__ int p_sign_dot(const uint4 w, const uint32_t (&qd)[32], const uint2* lut) {
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+  uint2 sg[16];  // all 16 lookups in flight before the first is used
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const uint32_t v = __builtin_popcount(pl[b]) + __builtin_popcount(pl[8 + b]) + __builtin_popcount(pl[16 + b]) +
-                       __builtin_popcount(pl[24 + b]);
-    q += b < 7 ? (int)(v << b) : -(int)(v << 7);
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) sg[4 * c + b] = lut[((wv[c] >> (8 * b)) & 0xFFu) * kLutCopies];
+  int acc = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      acc = __builtin_amdgcn_sdot4((int)sg[4 * c + b].x, (int)qd[8 * c + 2 * b], acc, false);
+      acc = __builtin_amdgcn_sdot4((int)sg[4 * c + b].y, (int)qd[8 * c + 2 * b + 1], acc, false);
+    }
   }
-  return q;
+  return acc;
 }
-
-__device__ __forceinline__ void load_planes(const uint32_t* planes, int j, uint32_t (&pl)[32]) {
-  const uint4* p4 = (const uint4*)(planes + j * 32);
+// the int8 codes of inputs [128 j, 128 j + 128) as 32 words
+__device__ __forceinline__ void load_codes(const int8_t* qs, int j, uint32_t (&qd)[32]) {
+  const uint4* q4 = (const uint4*)(qs + 128 * j);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const uint4 v = p4[k];
-    pl[4 * k + 0] = v.x;
-    pl[4 * k + 1] = v.y;
-    pl[4 * k + 2] = v.z;
-    pl[4 * k + 3] = v.w;
+    const uint4 v = q4[k];
+    qd[4 * k + 0] = v.x;
+    qd[4 * k + 1] = v.y;
+    qd[4 * k + 2] = v.z;
+    qd[4 * k + 3] = v.w;
   }
 }
-
 __device__ __forceinline__ float lora_up(const uint4 b, const float* t) {
   // sum_k B[k] t[k] over the 16 int8 of one LoRA up row, k in order
   const uint32_t wv[4] = {b.x, b.y, b.z, b.w};
@@ -360,7 +358,9 @@ struct PShape {
 constexpr int kHeadDepth = 8;  // LM-head rows in flight per wave
 static_assert(kPT == 256 && kPW == 4, "one wave per 4 state channels and 16 lanes per LoRA rank row");
 
-template <class S>
+// TR: the variant that also writes traces and phase timestamps (tests and
+// profiling); the plain variant has none of that code.
+template <class S, bool TR>
 __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a) {
   extern __shared__ unsigned char smem[];
   constexpr int DM = S::DM, DI = S::DI, NS = S::NS, HP = S::HP, G = S::G, CDIM = S::CDIM;
@@ -372,8 +372,8 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
   float* hs = (float*)smem;                     // [DM] residual stream
   float* gs = hs + DM;                          // [DI] gated SSM output (all heads); also argmax candidates
   int8_t* qs = (int8_t*)(gs + DI);              // [MX] int8 codes
-  uint32_t* pl = (uint32_t*)(qs + MX);          // [MX/32][8] bit planes
-  float* bcs = (float*)(pl + (MX / 32) * 8);    // [2NS] B, C
+  uint2* lut = (uint2*)(qs + MX);               // [256][kLutCopies] sign table
+  float* bcs = (float*)(lut + 256 * kLutCopies);  // [2NS] B, C
   float* tls = bcs + 2 * NS;                    // [16] LoRA down vector
   float* rowv = tls + 16;                       // [kMaxInRows] outputs of own in_proj rows
   float* red = rowv + kMaxInRows;               // [2*kPW]
@@ -383,12 +383,18 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
   uint4* ains = (uint4*)(((uintptr_t)(s_arg + 2 * kPW) + 15) & ~(uintptr_t)15);  // [16 * DM/16] LoRA-down A, in_proj
   uint4* aouts = ains + 16 * (DM / 16);         // [16 * DI/16] LoRA-down A, out_proj
   if (threadIdx.x == 0) *s_stop = 0;
+  for (int f = threadIdx.x; f < 256 * kLutCopies; f += kPT) lut[f] = sign_entry((uint32_t)(f / kLutCopies));
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint2* lut_l = lut + (lane % kLutCopies);
   unsigned e = a.epoch0;  // same value in every workgroup
-  int tok = a.tok_in[0];
+  int tok = kargs()->tok_in[0];
   const char* wb = a.wbase;
+  uint64_t* const hbox = a.boxes;
+  uint64_t* const bcbox = hbox + kR * DM;
+  uint64_t* const gbox = bcbox + kR * 2 * NS;
+  uint64_t* const abox = gbox + kR * DI;
 
   auto in_row = [&](int k) -> int {
     if (k < 16) return hd * HP + j * 16 + k;                 // z
@@ -488,8 +494,11 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
 
   // phase timestamps (100 MHz device clock) for performance analysis
   auto prof = [&](int t, int l, int ev) {
-    if (a.prof && t < a.prof_tokens && threadIdx.x == 0)
-      a.prof[(((size_t)t * (a.n_layer + 1) + l) * G + w) * kProfEvents + ev] = wall_clock64();
+    if constexpr (TR) {
+      const KArgs k = kargs();
+      if (k->prof && t < k->prof_tokens && threadIdx.x == 0)
+        k->prof[(((size_t)t * (k->n_layer + 1) + l) * G + w) * kProfEvents + ev] = wall_clock64();
+    }
   };
 
   load_A(0);
@@ -500,45 +509,52 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
   for (int t = 0; t < T && ok; ++t) {
     // ---- embedding (every workgroup, no hop)
     {
+      const KArgs k = kargs();
       int tk = tok;
-      if (tk < 0 || tk >= a.vocab) {
-        if (threadIdx.x == 0 && w == 0) atomicOr(a.err, 1);
+      if (tk < 0 || tk >= k->vocab) {
+        if (threadIdx.x == 0 && w == 0) atomicOr(k->err, 1);
         tk = 0;
       }
-      const float sc = a.sE[tk];
+      const float sc = k->sE[tk];
+      const int8_t* er = k->E + (size_t)tk * DM;
 #pragma unroll
       for (int m = 0; m < S::MW1; ++m) {
         const int i = threadIdx.x + m * kPT;
-        hs[i] = (float)a.E[(size_t)tk * DM + i] * sc;
+        hs[i] = (float)er[i] * sc;
       }
       __syncthreads();
     }
     for (int l = 0; l < Lm && ok; ++l) {
       prof(t, l, 0);
       if (l > 0) {
-        ok = gather<S::MW1>(a.hbox, DM, e, hs, a.abort_flag, s_stop);
+        ok = gather<S::MW1>(hbox, DM, e, hs, a.abort_flag, s_stop);
         ++e;
         if (!ok) break;
       }
       prof(t, l, 1);
-      if (a.trace_h && w == 0)
-        for (int i = threadIdx.x; i < DM; i += kPT) a.trace_h[(size_t)l * DM + i] = hs[i];
+      if constexpr (TR) {
+        float* th = kargs()->trace_h;
+        if (th && w == 0)
+          for (int i = threadIdx.x; i < DM; i += kPT) th[(size_t)l * DM + i] = hs[i];
+      }
       // ---- phase A: norm, quantise, LoRA down, 1-bit GEMV of own rows, conv
-      const float s1 = p_norm_quant<S::MW1>(hs, nw, DM, a.eps, qs, pl, red);
+      const float s1 = p_norm_quant<S::MW1>(hs, nw, DM, a.eps, qs, red);
       prof(t, l, 2);
-      if (a.trace_q1 && w == 0)
-        for (int i = threadIdx.x; i < DM; i += kPT) a.trace_q1[(size_t)l * DM + i] = qs[i];
+      if constexpr (TR) {
+        int8_t* tq = kargs()->trace_q1;
+        if (tq && w == 0)
+          for (int i = threadIdx.x; i < DM; i += kPT) tq[(size_t)l * DM + i] = qs[i];
+      }
       p_lora_down<S::MC1>(ains, DM, qs, sAi, s1, tls);
       prof(t, l, 3);
       {
-        uint32_t plw[32];
-        load_planes(pl, ji, plw);
-        const int qpart = p_plane_sum(plw);
+        uint32_t qd[32];
+        load_codes(qs, ji, qd);
 #pragma unroll
         for (int m = 0; m < S::NGI; ++m) {
           const int g = wave + m * kPW;
           if (g < S::NGI_T) {  // uniform per wave
-            const int acc = group_sum_i(2 * p_plane_dot(win[m], plw) - qpart, S::UI);
+            const int acc = group_sum_i(p_sign_dot(win[m], qd, lut_l), S::UI);
             const int k = g * S::RPPI + subi;
             if (lead_i && k < S::NROWS) rowv[k] = (float)acc * isw[m] * s1 + isb[m] * lora_up(ib[m], tls);
           }
@@ -551,7 +567,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         const float v = cb + cw[0] * cst[0] + cw[1] * cst[1] + cw[2] * cst[2] + cw[3] * y;
         const float xv = silu_f(v);
         rowv[conv_k] = xv;
-        if (conv_k >= 33) publish(a.bcbox, 2 * NS, conv_c - DI, xv, e);
+        if (conv_k >= 33) publish(bcbox, 2 * NS, conv_c - DI, xv, e);
         cst[0] = cst[1];  // shifted window, written back after the next hop
         cst[1] = cst[2];
         cst[2] = y;
@@ -562,7 +578,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       // the next layer's phase-A operands stream in during the two hops below
       // (after the last layer: layer 0 of the next token)
       load_A(l + 1 < Lm ? l + 1 : 0);
-      ok = gather<(2 * NS + kPT - 1) / kPT>(a.bcbox, 2 * NS, e, bcs, a.abort_flag, s_stop);
+      ok = gather<(2 * NS + kPT - 1) / kPT>(bcbox, 2 * NS, e, bcs, a.abort_flag, s_stop);
       ++e;
       if (!ok) break;
       prof(t, l, 6);
@@ -606,11 +622,11 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
           const int c = wave * 4 + lane;  // channel within the slice
           const float y = (lane == 0 ? y0 : lane == 1 ? y1 : lane == 2 ? y2 : y3) + dval * rowv[16 + c];
           const float g = y * silu_f(rowv[c]);
-          publish(a.gbox, DI, hd * HP + j * 16 + c, g, e);
+          publish(gbox, DI, hd * HP + j * 16 + c, g, e);
         }
       }
       prof(t, l, 7);
-      ok = gather<S::MW2>(a.gbox, DI, e, gs, a.abort_flag, s_stop);
+      ok = gather<S::MW2>(gbox, DI, e, gs, a.abort_flag, s_stop);
       ++e;
       if (!ok) break;
       prof(t, l, 8);
@@ -624,23 +640,25 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       }
       // ---- phase B: gated norm, quantise, LoRA down, 1-bit GEMV of own rows, residual
       {
-        const float s2 = p_norm_quant<S::MW2>(gs, gw, DI, a.eps, qs, pl, red);
-        if (a.trace_q2 && w == 0)
-          for (int i = threadIdx.x; i < DI; i += kPT) a.trace_q2[(size_t)l * DI + i] = qs[i];
+        const float s2 = p_norm_quant<S::MW2>(gs, gw, DI, a.eps, qs, red);
+        if constexpr (TR) {
+          int8_t* tq = kargs()->trace_q2;
+          if (tq && w == 0)
+            for (int i = threadIdx.x; i < DI; i += kPT) tq[(size_t)l * DI + i] = qs[i];
+        }
         p_lora_down<S::MC2>(aouts, DI, qs, sAo, s2, tls);
-        uint32_t plw[32];
-        load_planes(pl, jo, plw);
-        const int qpart = p_plane_sum(plw);
+        uint32_t qd[32];
+        load_codes(qs, jo, qd);
 #pragma unroll
         for (int m = 0; m < S::NGO; ++m) {
           const int g = wave + m * kPW;
           if (g < S::NGO_T) {
-            const int acc = group_sum_i(2 * p_plane_dot(wout[m], plw) - qpart, S::UO);
+            const int acc = group_sum_i(p_sign_dot(wout[m], qd, lut_l), S::UO);
             const int k = g * S::RPPO + subo;
             if (lead_o && k < S::OUT_PER) {
               const int row = w * S::OUT_PER + k;
               const float y = (float)acc * osw[m] * s2 + osb[m] * lora_up(ob[m], tls);
-              publish(a.hbox, DM, row, hs[row] + y, e);
+              publish(hbox, DM, row, hs[row] + y, e);
             }
           }
         }
@@ -653,34 +671,52 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     // ---- final norm + LM head + argmax
     prof(t, Lm, 0);
     constexpr int LH = S::LH, MH = S::MH, RPPH = S::RPPH, STEPH = S::STEPH;
-    const int rows_per = (a.vocab + G - 1) / G;
+    const int8_t* const E = kargs()->E;
+    const float* const sE = kargs()->sE;
+    const int vocab = kargs()->vocab;
+    // logits are an output for the last token of the launch only
+    float* const logits = t == T - 1 ? kargs()->logits : nullptr;
+    const int rows_per = (vocab + G - 1) / G;
     const int r0 = w * rows_per;
-    const int r1 = min(a.vocab, r0 + rows_per);
+    const int r1 = min(vocab, r0 + rows_per);
     const int jh = lane & (LH - 1), subh = lane / LH;
     const bool lead_h = lane == group_sum_lane(subh * LH, LH);
     float fn[S::MW1];
+    {
+      const float* fnp = kargs()->final_norm;
 #pragma unroll
-    for (int m = 0; m < S::MW1; ++m) fn[m] = a.final_norm[threadIdx.x + m * kPT];
+      for (int m = 0; m < S::MW1; ++m) fn[m] = fnp[threadIdx.x + m * kPT];
+    }
+    // kHeadDepth rows per wave in flight: their bytes and their scales
     uint4 eb[kHeadDepth][MH];
+    float es[kHeadDepth];
     int erow[kHeadDepth];
 #pragma unroll
     for (int d = 0; d < kHeadDepth; ++d) {
       const int row = r0 + wave * RPPH + d * STEPH + subh;
       erow[d] = row;
-      const uint4* e4 = (const uint4*)(a.E + (size_t)(row < r1 ? row : 0) * DM);
+      const bool live = row < r1;
+      const uint4* e4 = (const uint4*)(E + (size_t)(live ? row : 0) * DM);
 #pragma unroll
-      for (int c = 0; c < MH; ++c) eb[d][c] = row < r1 ? e4[jh + c * LH] : make_uint4(0, 0, 0, 0);
+      for (int c = 0; c < MH; ++c) eb[d][c] = live ? e4[jh + c * LH] : make_uint4(0, 0, 0, 0);
+      es[d] = live ? sE[row] : 0.0f;
     }
-    ok = gather<S::MW1>(a.hbox, DM, e, hs, a.abort_flag, s_stop);
+    ok = gather<S::MW1>(hbox, DM, e, hs, a.abort_flag, s_stop);
     ++e;
     if (!ok) break;
     prof(t, Lm, 1);
-    if (a.trace_h && w == 0)
-      for (int i = threadIdx.x; i < DM; i += kPT) a.trace_h[(size_t)Lm * DM + i] = hs[i];
-    const float sf = p_norm_quant<S::MW1>(hs, fn, DM, a.eps, qs, pl, red);
+    if constexpr (TR) {
+      float* th = kargs()->trace_h;
+      if (th && w == 0)
+        for (int i = threadIdx.x; i < DM; i += kPT) th[(size_t)Lm * DM + i] = hs[i];
+    }
+    const float sf = p_norm_quant<S::MW1>(hs, fn, DM, a.eps, qs, red);
     prof(t, Lm, 2);
-    if (a.trace_qf && w == 0)
-      for (int i = threadIdx.x; i < DM; i += kPT) a.trace_qf[i] = qs[i];
+    if constexpr (TR) {
+      int8_t* tq = kargs()->trace_qf;
+      if (tq && w == 0)
+        for (int i = threadIdx.x; i < DM; i += kPT) tq[i] = qs[i];
+    }
     {
       const uint4* q4 = (const uint4*)qs;
       uint4 qv[MH];
@@ -702,16 +738,18 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
           }
           acc = group_sum_i(acc, LH);
           if (lead_h && row < r1) {
-            const float lg = (float)acc * a.sE[row] * sf;
-            a.logits[row] = lg;
+            const float lg = (float)acc * es[d] * sf;
+            if (logits) logits[row] = lg;
             argmax_step(best, bidx, lg, row);
           }
           // refill this slot with the row kHeadDepth iterations ahead
           const int nrow = row + kHeadDepth * STEPH;
           erow[d] = nrow;
-          const uint4* e4 = (const uint4*)(a.E + (size_t)(nrow < r1 ? nrow : 0) * DM);
+          const bool live = nrow < r1;
+          const uint4* e4 = (const uint4*)(E + (size_t)(live ? nrow : 0) * DM);
 #pragma unroll
-          for (int c = 0; c < MH; ++c) eb[d][c] = nrow < r1 ? e4[jh + c * LH] : make_uint4(0, 0, 0, 0);
+          for (int c = 0; c < MH; ++c) eb[d][c] = live ? e4[jh + c * LH] : make_uint4(0, 0, 0, 0);
+          es[d] = live ? sE[nrow] : 0.0f;
         }
       }
       wave_argmax(best, bidx);
@@ -723,15 +761,15 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       if (threadIdx.x == 0) {
         for (int wv = 1; wv < kPW; ++wv) argmax_step(best, bidx, s_arg[wv], ((int*)s_arg)[kPW + wv]);
         // argmax candidates: value word and index word per workgroup
-        publish(a.abox, 2 * G, w, best, e);
-        publish(a.abox, 2 * G, G + w, __int_as_float(bidx), e);
+        publish(abox, 2 * G, w, best, e);
+        publish(abox, 2 * G, G + w, __int_as_float(bidx), e);
       }
     }
     prof(t, Lm, 3);
     // every workgroup reduces the G candidates itself
     {
       float* cand = gs;
-      ok = gather<(2 * G + kPT - 1) / kPT>(a.abox, 2 * G, e, cand, a.abort_flag, s_stop);
+      ok = gather<(2 * G + kPT - 1) / kPT>(abox, 2 * G, e, cand, a.abort_flag, s_stop);
       ++e;
       if (!ok) break;
       if (wave == 0) {
@@ -742,7 +780,8 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         if (lane == 0) {
           if (bidx == 0x7fffffff) bidx = 0;
           *s_tok = bidx;
-          if (w == 0 && a.tok_out) a.tok_out[t] = bidx;
+          int32_t* to = kargs()->tok_out;
+          if (w == 0 && to) to[t] = bidx;
         }
       }
       __syncthreads();
@@ -751,10 +790,11 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     }
   }
   if (w == 0 && threadIdx.x == 0) {
+    const KArgs k = kargs();
     if (ok) {
-      if (a.tok_last) a.tok_last[0] = tok;
+      if (k->tok_last) k->tok_last[0] = tok;
     } else {
-      atomicOr(a.err, 2);
+      atomicOr(k->err, 2);
     }
   }
 }
@@ -765,21 +805,23 @@ using Shape1p3b = PShape<2048, 4096, 128, 64>;
 
 static size_t lds_bytes(int dm, int di, int ns) {
   const int mx = dm > di ? dm : di;
-  return (size_t)dm * 4 + (size_t)di * 4 + (size_t)mx + (size_t)(mx / 32) * 8 * 4 + (size_t)2 * ns * 4 + 16 * 4 +
+  return (size_t)dm * 4 + (size_t)di * 4 + (size_t)mx + 256 * kLutCopies * 8 + (size_t)2 * ns * 4 + 16 * 4 +
          kMaxInRows * 4 + 2 * kPW * 4 + 16 + 2 * kPW * 4 + 16 + (size_t)16 * (dm + di);
 }
 
 template <class S>
-static const void* kernel_of() { return (const void*)decode_persistent_kernel<S>; }
+static const void* kernel_of(bool tr) {
+  return tr ? (const void*)decode_persistent_kernel<S, true> : (const void*)decode_persistent_kernel<S, false>;
+}
 
 template <class S>
 static bool shape_is(int dm, int di, int ns, int hp) {
   return dm == S::DM && di == S::DI && ns == S::NS && hp == S::HP;
 }
 
-static const void* select_kernel(int dm, int di, int ns, int hp, size_t* stride, const size_t** /*unused*/) {
-  if (shape_is<Shape1p3b>(dm, di, ns, hp)) { *stride = Shape1p3b::LSTRIDE; return kernel_of<Shape1p3b>(); }
-  if (shape_is<ShapeTiny>(dm, di, ns, hp)) { *stride = ShapeTiny::LSTRIDE; return kernel_of<ShapeTiny>(); }
+static const void* select_kernel(int dm, int di, int ns, int hp, size_t* stride, bool tr = false) {
+  if (shape_is<Shape1p3b>(dm, di, ns, hp)) { *stride = Shape1p3b::LSTRIDE; return kernel_of<Shape1p3b>(tr); }
+  if (shape_is<ShapeTiny>(dm, di, ns, hp)) { *stride = ShapeTiny::LSTRIDE; return kernel_of<ShapeTiny>(tr); }
   return nullptr;
 }
 
@@ -788,7 +830,7 @@ static size_t off_of(int k) { return S::OFF(k); }
 
 bool persistent_layout(int d_model, int d_inner, int d_state, int headdim, size_t* stride, size_t* offsets) {
   size_t st = 0;
-  if (!select_kernel(d_model, d_inner, d_state, headdim, &st, nullptr)) return false;
+  if (!select_kernel(d_model, d_inner, d_state, headdim, &st)) return false;
   *stride = st;
   for (int k = 0; k < 19; ++k)
     offsets[k] = shape_is<Shape1p3b>(d_model, d_inner, d_state, headdim) ? off_of<Shape1p3b>(k) : off_of<ShapeTiny>(k);
@@ -797,7 +839,8 @@ bool persistent_layout(int d_model, int d_inner, int d_state, int headdim, size_
 
 hipError_t launch_decode_persistent(const PersistArgs& a, int grid, hipStream_t st) {
   size_t stride = 0;
-  const void* k = select_kernel(a.d_model, a.d_inner, a.d_state, a.headdim, &stride, nullptr);
+  const bool tr = a.prof || a.trace_h || a.trace_q1 || a.trace_q2 || a.trace_qf;
+  const void* k = select_kernel(a.d_model, a.d_inner, a.d_state, a.headdim, &stride, tr);
   if (!k) return hipErrorInvalidValue;
   PersistArgs args = a;
   void* params[] = {&args};
@@ -811,16 +854,20 @@ bool persistent_supported(int d_model, int d_inner, int d_state, int headdim, in
                           const char** why) {
   auto no = [&](const char* m) { *why = m; return false; };
   size_t stride = 0;
-  const void* k = select_kernel(d_model, d_inner, d_state, headdim, &stride, nullptr);
+  const void* k = select_kernel(d_model, d_inner, d_state, headdim, &stride);
   if (!k) return no("the persistent kernel is compiled for d_model/d_inner/d_state/headdim 2048/4096/128/64 and 256/512/16/32");
   if (grid != n_heads * (headdim / 16)) return no("grid mismatch");
   if (rank != 16) return no("the persistent path needs LoRA rank 16");
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return no("no device");
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return no("no CU count");
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kPT, lds_bytes(d_model, d_inner, d_state)) != hipSuccess)
-    return no("occupancy query failed");
-  if ((long)per_cu * cus < grid) return no("grid does not fit co-resident on this device");
+  for (int tr = 0; tr < 2; ++tr) {  // both variants (plain, tracing) must fit
+    k = select_kernel(d_model, d_inner, d_state, headdim, &stride, tr != 0);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kPT, lds_bytes(d_model, d_inner, d_state)) !=
+        hipSuccess)
+      return no("occupancy query failed");
+    if ((long)per_cu * cus < grid) return no("grid does not fit co-resident on this device");
+  }
   return true;
 }
 

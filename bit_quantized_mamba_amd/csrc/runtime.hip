@@ -327,10 +327,7 @@ dfssm_status run_persistent(dfssm_ctx* c, const int32_t* tok_in, int32_t* tok_la
   a.final_norm = c->lt<float>(-1, DFSSM_G_FINAL_NORM);
   a.conv = c->conv;
   a.ssm = c->ssm;
-  a.hbox = c->boxes;
-  a.bcbox = a.hbox + (size_t)8 * c->dm;
-  a.gbox = a.bcbox + (size_t)8 * 2 * c->N;
-  a.abox = a.gbox + (size_t)8 * c->di;
+  a.boxes = c->boxes;
   a.epoch0 = c->host_epoch;
   a.abort_flag = c->abort_flag;
   a.err = c->err;
