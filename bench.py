@@ -23,6 +23,28 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 
+# HBM bytes per decoded token of the persistent kernel, from rocprofv3 counter
+# passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over a 64-token launch,
+# each scaled by what the same counter reads for a plain 1 GiB device copy
+# (FETCH_SIZE reads 0.5 GiB for it: factor 2.0; WRITE_SIZE reads 1 GiB: 1.0).
+# Valid only for the kernel sources they were taken from (hash below).
+COUNTED_TRAFFIC = {
+    "sources_sha256": "d2eadf0bf46cdcabe0983c3e24bf6f77a543649de0fa140807305b5210a10c61",
+    "fetch_bytes_per_token": 464800613,
+    "write_bytes_per_token": 132648174,
+}
+KERNEL_SOURCES = ("bit_quantized_mamba_amd/csrc/persistent.hip", "bit_quantized_mamba_amd/csrc/persistent.h",
+                  "bit_quantized_mamba_amd/csrc/common.h")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
 
 def algorithmic_bytes(s):
     """Bytes each decode-step kernel must move at batch 1 (reads + writes)."""
@@ -149,8 +171,12 @@ def main():
     roofline = None
     if persistent:
         achieved = sb * args.steps / (ms / 1e3) / 1e9
+        traffic = None
+        if kernel_sources_sha256() == COUNTED_TRAFFIC["sources_sha256"]:
+            traffic = int((COUNTED_TRAFFIC["fetch_bytes_per_token"] + COUNTED_TRAFFIC["write_bytes_per_token"])
+                          * args.steps)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "kernel": "decode_persistent_kernel", "bytes_per_launch": sb * args.steps,
                     "us_per_launch": round(ms * 1e3, 1)}
     kernels = {}
