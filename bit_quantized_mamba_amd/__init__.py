@@ -19,7 +19,7 @@ LAYER_KINDS = ["in_bits", "in_sw", "in_A", "in_sA", "in_B", "in_sB", "out_bits",
                "out_B", "out_sB", "conv_w", "conv_b", "A_log", "dt_bias", "D", "norm_w", "gnorm_w"]
 GLOBAL_KINDS = ["E", "sE", "final_norm"]
 
-__all__ = ["Engine", "DfssmError", "k_quant", "k_proj", "version", "LAYER_KINDS", "GLOBAL_KINDS"]
+__all__ = ["Engine", "DfssmError", "k_quant", "k_proj", "k_gemm", "version", "LAYER_KINDS", "GLOBAL_KINDS"]
 
 
 def version() -> str:
@@ -203,10 +203,31 @@ class Engine:
              _dp(t["logits"]), _stream(stream))
         return t
 
-    PATHS = {"auto": 0, "kernels": 1, "persistent": 2}
+    def trace_prefill(self, tok, stream=None):
+        """Prefill of tok ([B][T] int32, one chunk) on the batched path, recording, per token row
+        m = b * T + t, the residual stream per layer and every int8 activation code.
+
+        Returns dict(h=[L+1][B*T][d_model], q1=[L][B*T][d_model], q2=[L][B*T][d_inner],
+        qf=[B][d_model], logits=[B][vocab]) (the last two for the last position)."""
+        torch = _torch()
+        self._check_tok(tok, 2)
+        B, T = tok.shape
+        M = B * T
+        dev = tok.device
+        t = {"h": torch.empty((self.n_layer + 1, M, self.d_model), dtype=torch.float32, device=dev),
+             "q1": torch.empty((self.n_layer, M, self.d_model), dtype=torch.int8, device=dev),
+             "q2": torch.empty((self.n_layer, M, self.d_inner), dtype=torch.int8, device=dev),
+             "qf": torch.empty((B, self.d_model), dtype=torch.int8, device=dev),
+             "logits": torch.empty((B, self.vocab), dtype=torch.float32, device=dev)}
+        call("dfssm_trace_prefill", self._h, _dp(tok), B, T, _dp(t["h"]), _dp(t["q1"]), _dp(t["q2"]),
+             _dp(t["qf"]), _dp(t["logits"]), _stream(stream))
+        return t
+
+    PATHS = {"auto": 0, "kernels": 1, "persistent": 2, "gemm": 3}
 
     def set_path(self, path: str) -> None:
-        """Batch-1 execution path: "auto", "kernels" (per-layer kernels) or "persistent"."""
+        """Execution path: "auto", "kernels" (per-layer GEMV kernels), "persistent" (batch 1 required
+        on the persistent kernel) or "gemm" (every decode and prefill on the batched GEMM path)."""
         call("dfssm_set_path", self._h, self.PATHS[path])
 
     KERNELS = {"in_proj": 0, "ssm": 1, "out_proj": 2, "lm_head": 3, "norm_quant": 4}
@@ -243,6 +264,19 @@ def k_quant(u, stream=None):
     s = torch.empty((rows,), dtype=torch.float32, device=u.device)
     call("dfssm_k_quant", _dp(u), rows, n, _dp(q), _dp(s), _stream(stream))
     return q, s
+
+
+def k_gemm(bits, sw, A, sA, Bm, sB, q, s, stream=None):
+    """The same projection on the batched path's int8 matrix-core GEMM (rank 16)."""
+    torch = _torch()
+    d_out = bits.shape[0]
+    d_in = bits.shape[1] * 32
+    M = q.shape[0]
+    acc = torch.empty((M, d_out), dtype=torch.int32, device=q.device)
+    y = torch.empty((M, d_out), dtype=torch.float32, device=q.device)
+    call("dfssm_k_gemm", _dp(bits), _dp(sw), _dp(A), _dp(sA), _dp(Bm), _dp(sB), d_in, d_out, _dp(q), _dp(s), M,
+         _dp(acc), _dp(y), _stream(stream))
+    return acc, y
 
 
 def k_proj(bits, sw, A, sA, Bm, sB, q, s, stream=None):

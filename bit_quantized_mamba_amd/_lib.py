@@ -38,11 +38,13 @@ EXPORTS = {
     "dfssm_prefill": [_p, _p, _i32, _i32, _p, _p, _p],
     "dfssm_layer_step": [_p, _i32, _p, _p, _i32, _p, _p, _p],
     "dfssm_trace_step": [_p, _p, _i32, _p, _p, _p, _p, _p, _p],
+    "dfssm_trace_prefill": [_p, _p, _i32, _i32, _p, _p, _p, _p, _p, _p],
     "dfssm_check_device": [_p, _p],
     "dfssm_profile_persistent": [_p, _p, _i32, _p, _i32, _p],
     "dfssm_time_kernel": [_p, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_float), _p],
     "dfssm_k_quant": [_p, _i32, _i32, _p, _p, _p],
     "dfssm_k_proj": [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p],
+    "dfssm_k_gemm": [_p, _p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _p, _p, _p],
 }
 _RESTYPE = {"dfssm_version": ctypes.c_char_p, "dfssm_last_error": ctypes.c_char_p, "dfssm_destroy": None}
 

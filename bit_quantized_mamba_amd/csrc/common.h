@@ -127,6 +127,78 @@ struct ProjArgs {
 };
 
 // ---------------------------------------------------------------------------
+// batched path (gemm.hip)
+// ---------------------------------------------------------------------------
+
+// rows x [M][ldx] (fp32) -> codes q [M][K], scale s [M], code sum qsum [M]
+// (may be null) and, when A is non-null, the LoRA-down vectors t [M][16].
+struct RowsArgs {
+  const float* x;
+  int ldx;
+  const float* w;   // norm weight [K]
+  int M;
+  float eps;
+  const int8_t* A;  // [16][K] or null
+  const float* sA;  // [16]
+  int8_t* q;
+  float* s;
+  int32_t* qsum;
+  float* t;
+};
+
+enum GemmEpilogue : int { GEMM_EPI_STORE = 0, GEMM_EPI_RESIDUAL = 1 };
+
+// y[m][n] (=, or += for the residual) float(sum_k q[m][k] sign(n, k)) * sw[n] * s[m]
+//                                      + sB[n] * sum_j B[n][j] t[m][j]
+struct GemmArgs {
+  const int8_t* q;      // [M][K]
+  const float* s;       // [M]
+  const int32_t* qsum;  // [M]
+  const float* t;       // [M][16]
+  const uint32_t* bits; // [N][K/32]
+  const float* sw;      // [N]
+  const int8_t* Bm;     // [N][16]
+  const float* sB;      // [N]
+  int M, N, K;
+  float* y;             // [M][ldy]
+  int ldy;
+  int32_t* acc;         // [M][N] signed scaffold sums, or null
+};
+
+// causal depthwise conv over T tokens of B sequences (rows b * T + t)
+struct ConvSeqArgs {
+  const float* zx;  // in_proj output rows [B*T][ldzx]; conv inputs at columns x_off + c
+  int ldzx, x_off;
+  float* xc;        // [B*T][cdim]
+  float* state;     // sequence 0's window [3][cdim] (oldest first); sequence b at + b * state_bstride
+  size_t state_bstride;
+  const float* w;   // [cdim][4]
+  const float* bias;
+  int B, T, cdim;
+};
+
+struct ScanArgs {
+  const float* xc;  // [B*T][cdim]: x at [0, d_inner), B at d_inner, C at d_inner + N
+  const float* zx;  // [B*T][ldzx]: z at [0, d_inner), dt_raw at dt_off
+  int ldzx, dt_off;
+  const float* A_log;
+  const float* dt_bias;
+  const float* D;
+  float* ssm;       // this layer, sequence 0: [H][P/16][N][16]; sequence b at + b * ssm_bstride
+  size_t ssm_bstride;
+  float* g;         // [B*T][d_inner]
+  int B, T, H, d_inner, cdim;
+};
+
+hipError_t launch_rows_quant(const RowsArgs& a, int K, hipStream_t st);
+hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st);
+hipError_t launch_conv_seq(const ConvSeqArgs& a, hipStream_t st);
+hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st);
+bool scan_supported(int P, int N);
+hipError_t launch_embed_rows(const int32_t* tok, int tok_stride, int t0, int B, int T, const int8_t* E,
+                             const float* sE, int dm, int V, float* h, int* err, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // launchers (kernels.hip, gen.hip)
 // ---------------------------------------------------------------------------
 

@@ -1,0 +1,475 @@
+// Kernels of the batched path: many token rows per layer (batched decode, one
+// row per sequence; prefill, B x T rows), gfx950.
+//
+//  * rows_quant: RMSNorm + per-token int8 quantisation of one row per wave,
+//    plus the row sum of the codes and the LoRA down-projection
+//    t = float(A q) * sA * s.
+//  * bitgemm: the 1-bit scaffold GEMM on the int8 matrix cores.  The 0/1
+//    bytes of the scaffold bits (bit 1 -> 1) multiply the int8 codes on
+//    v_mfma_i32_32x32x32_i8, giving pos[m][n] = sum of q over the +1 weights;
+//    the signed product is 2 pos - sum(q).  Each k-tile of scaffold bits is
+//    expanded once per workgroup into LDS.  The LoRA up-projection is a
+//    rank-16 fp32 product on v_mfma_f32_32x32x2f32 in the epilogue, then row
+//    scales and either a plain store (in_proj) or the residual add (out_proj).
+//  * conv_seq / conv_state_update: the depthwise causal conv over T tokens of
+//    each sequence, with the stored window as the history before t = 0.
+//  * scan: the SSM recurrence over T tokens, one workgroup per (sequence,
+//    head), state in registers, B and C staged through LDS; gated output.
+#include "common.h"
+
+namespace dfssm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// rows_quant: one wave per row, four rows per workgroup.  Lane L holds the
+// float4 groups i = 4 L + 256 m (m < K / 256), so every load and store of the
+// row is one coalesced 1 KB access per m.
+// ---------------------------------------------------------------------------
+template <int K>
+__global__ __launch_bounds__(256) void rows_quant_kernel(RowsArgs a) {
+  constexpr int MQ = K / 256;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.M) return;  // whole wave leaves together
+  const float4* x4 = (const float4*)(a.x + (size_t)row * a.ldx);
+  const float4* w4 = (const float4*)a.w;
+  float4 p[MQ];
+  float ss = 0.0f, pm = 0.0f;
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) {
+    const float4 xv = x4[lane + 64 * m];
+    const float4 wv = w4[lane + 64 * m];
+    ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+    p[m] = make_float4(xv.x * wv.x, xv.y * wv.y, xv.z * wv.z, xv.w * wv.w);
+    pm = fmaxf(pm, fmaxf(fmaxf(fabsf(p[m].x), fabsf(p[m].y)), fmaxf(fabsf(p[m].z), fabsf(p[m].w))));
+  }
+  ss = wave_sum(ss);
+  pm = wave_max(pm);
+  const float rstd = 1.0f / sqrtf(ss / (float)K + a.eps);
+  const float amax = rstd * pm;
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  const float s = amax > 0.0f ? amax / 127.0f : 0.0f;
+  auto qz = [&](float v) -> uint32_t {
+    float r = rintf(rstd * v * inv);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (uint32_t)(uint8_t)(int8_t)(int)r;
+  };
+  uint32_t qd[MQ];
+  int qsum = 0;
+  uint32_t* qrow = (uint32_t*)(a.q + (size_t)row * K);
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) {
+    const uint32_t b0 = qz(p[m].x), b1 = qz(p[m].y), b2 = qz(p[m].z), b3 = qz(p[m].w);
+    qd[m] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    qsum += (int)(int8_t)b0 + (int)(int8_t)b1 + (int)(int8_t)b2 + (int)(int8_t)b3;
+    qrow[lane + 64 * m] = qd[m];
+  }
+  qsum = wave_sum_i(qsum);
+  if (lane == 0) {
+    a.s[row] = s;
+    if (a.qsum) a.qsum[row] = qsum;
+  }
+  if (!a.A) return;
+  // LoRA down: t[k] = float(sum_i A[k][i] q_i) * sA[k] * s, all 16 sums in flight
+  int acc[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t* ar = (const uint32_t*)(a.A + (size_t)k * K);
+    int v = 0;
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) v = __builtin_amdgcn_sdot4((int)ar[lane + 64 * m], (int)qd[m], v, false);
+    acc[k] = v;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = wave_sum_i(acc[k]);
+  if (lane < 16) {
+    int v = acc[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) v = lane == k ? acc[k] : v;
+    a.t[(size_t)row * 16 + lane] = (float)v * a.sA[lane] * s;
+  }
+}
+
+hipError_t launch_rows_quant(const RowsArgs& a, int K, hipStream_t st) {
+  if (a.M <= 0) return hipSuccess;
+  const dim3 grid((a.M + 3) / 4), block(256);
+  switch (K) {
+    case 256: hipLaunchKernelGGL(rows_quant_kernel<256>, grid, block, 0, st, a); break;
+    case 512: hipLaunchKernelGGL(rows_quant_kernel<512>, grid, block, 0, st, a); break;
+    case 1024: hipLaunchKernelGGL(rows_quant_kernel<1024>, grid, block, 0, st, a); break;
+    case 2048: hipLaunchKernelGGL(rows_quant_kernel<2048>, grid, block, 0, st, a); break;
+    case 4096: hipLaunchKernelGGL(rows_quant_kernel<4096>, grid, block, 0, st, a); break;
+    case 8192: hipLaunchKernelGGL(rows_quant_kernel<8192>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bitgemm
+// ---------------------------------------------------------------------------
+
+// 0/1 bytes of nibble x (bits 0..3): byte j = bit j.  The shifted copies of
+// the four bits land on distinct positions (bit j at 8 j and at 7 i + j for
+// the others), so the 24-bit multiply makes no carries.
+__device__ __forceinline__ uint32_t spread_nibble(uint32_t x) { return __umul24(x & 15u, 0x00204081u) & 0x01010101u; }
+
+constexpr int kGemmKB = 64;       // k per LDS stage
+constexpr int kGemmLdsRow = 80;   // bytes per LDS tile row (64 + 16 padding)
+
+template <int TM, int TN>
+struct GemmTile {
+  static constexpr int WAVES_M = TM >= 128 ? 2 : 1, WAVES_N = 4 / WAVES_M;
+  static constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N;  // wave tile
+  static constexpr int BM = WM / 32, BN = WN / 32;            // 32x32 blocks per wave
+  static constexpr int A_BYTES = TM * kGemmLdsRow, B_BYTES = TN * kGemmLdsRow;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_CHUNKS = TM * kGemmKB / 16;  // 16-byte chunks of an A k-tile
+  static constexpr int B_WORDS = TN * kGemmKB / 32;   // scaffold words of a B k-tile
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
+};
+
+template <int TM, int TN, int EPI>
+__global__ __launch_bounds__(256) void bitgemm_kernel(GemmArgs a) {
+  using T = GemmTile<TM, TN>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
+  const int wm0 = (wave / T::WAVES_N) * T::WM, wn0 = (wave % T::WAVES_N) * T::WN;
+  const int K = a.K, KW = K / 32;
+  const int nk = K / kGemmKB;
+
+  // global -> registers for one k-tile
+  constexpr int AC = (T::A_CHUNKS + 255) / 256, BW = (T::B_WORDS + 255) / 256;
+  uint4 ar[AC];
+  uint32_t br[BW];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int r = c >> 2, ch = c & 3;
+      const int m = m0 + r;
+      ar[i] = (c < T::A_CHUNKS && m < a.M)
+                  ? *(const uint4*)(a.q + (size_t)m * K + (size_t)kt * kGemmKB + ch * 16)
+                  : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < BW; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int r = c >> 1, hw = c & 1;
+      const int n = n0 + r;
+      br[i] = (c < T::B_WORDS && n < a.N) ? a.bits[(size_t)n * KW + kt * 2 + hw] : 0u;
+    }
+  };
+  // registers -> LDS stage (scaffold words expanded to 0/1 bytes)
+  auto store_tile = [&](int stg) {
+    unsigned char* As = gsm + stg * T::STAGE;
+    unsigned char* Bs = As + T::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      if (c < T::A_CHUNKS) *(uint4*)(As + (c >> 2) * kGemmLdsRow + (c & 3) * 16) = ar[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BW; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      if (c < T::B_WORDS) {
+        const uint32_t wv = br[i];
+        uint4 lo, hi;
+        lo.x = spread_nibble(wv);
+        lo.y = spread_nibble(wv >> 4);
+        lo.z = spread_nibble(wv >> 8);
+        lo.w = spread_nibble(wv >> 12);
+        hi.x = spread_nibble(wv >> 16);
+        hi.y = spread_nibble(wv >> 20);
+        hi.z = spread_nibble(wv >> 24);
+        hi.w = spread_nibble(wv >> 28);
+        unsigned char* dst = Bs + (c >> 1) * kGemmLdsRow + (c & 1) * 32;
+        *(uint4*)dst = lo;
+        *(uint4*)(dst + 16) = hi;
+      }
+    }
+  };
+
+  v16i acc[T::BM][T::BN];
+#pragma unroll
+  for (int i = 0; i < T::BM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::BN; ++j) acc[i][j] = (v16i){};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int stg = kt & 1;
+    if (kt + 1 < nk) load_tile(kt + 1);
+    const unsigned char* As = gsm + stg * T::STAGE;
+    const unsigned char* Bs = As + T::A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < kGemmKB / 32; ++kk) {
+      const int koff = kk * 32 + 16 * (lane >> 5);
+      v4i af[T::BM], bf[T::BN];
+#pragma unroll
+      for (int i = 0; i < T::BM; ++i) af[i] = *(const v4i*)(As + (wm0 + 32 * i + (lane & 31)) * kGemmLdsRow + koff);
+#pragma unroll
+      for (int j = 0; j < T::BN; ++j) bf[j] = *(const v4i*)(Bs + (wn0 + 32 * j + (lane & 31)) * kGemmLdsRow + koff);
+#pragma unroll
+      for (int i = 0; i < T::BM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::BN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      store_tile(stg ^ 1);  // the other stage: last read before the previous barrier
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue.  Row data of the tile into LDS (stage 0 is free after a barrier).
+  __syncthreads();
+  float* s_s = (float*)gsm;              // [TM]
+  int* s_qs = (int*)(s_s + TM);          // [TM]
+  float* s_t = (float*)(s_qs + TM);      // [TM][16]
+  for (int i = threadIdx.x; i < TM; i += 256) {
+    const int m = m0 + i;
+    s_s[i] = m < a.M ? a.s[m] : 0.0f;
+    s_qs[i] = m < a.M ? a.qsum[m] : 0;
+  }
+  for (int i = threadIdx.x; i < TM * 16; i += 256) {
+    const int m = m0 + i / 16;
+    s_t[i] = m < a.M ? a.t[(size_t)m * 16 + (i & 15)] : 0.0f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < T::BN; ++j) {
+    const int n = n0 + wn0 + 32 * j + (lane & 31);
+    const bool nok = n < a.N;
+    const float sw = nok ? a.sw[n] : 0.0f, sb = nok ? a.sB[n] : 0.0f;
+    // LoRA up operands of this column: B[n][2p + lane/32], p = 0..7
+    const uint4 bq = nok ? *(const uint4*)(a.Bm + (size_t)n * 16) : make_uint4(0, 0, 0, 0);
+    const uint32_t bw[4] = {bq.x, bq.y, bq.z, bq.w};
+    float bcol[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int k = 2 * p + (lane >> 5);
+      bcol[p] = (float)(int8_t)(bw[k >> 2] >> (8 * (k & 3)));
+    }
+#pragma unroll
+    for (int i = 0; i < T::BM; ++i) {
+      const int rb = wm0 + 32 * i;  // tile-local first row of the block
+      v16f lo = (v16f){};
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        lo = __builtin_amdgcn_mfma_f32_32x32x2f32(s_t[(rb + (lane & 31)) * 16 + 2 * p + (lane >> 5)], bcol[p], lo, 0,
+                                                   0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ml = rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int m = m0 + ml;
+        if (m < a.M && nok) {
+          const int sacc = 2 * acc[i][j][r] - s_qs[ml];
+          const float y = (float)sacc * sw * s_s[ml] + sb * lo[r];
+          float* yp = a.y + (size_t)m * a.ldy + n;
+          if (EPI == GEMM_EPI_RESIDUAL)
+            *yp += y;
+          else
+            *yp = y;
+          if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
+        }
+      }
+    }
+  }
+}
+
+template <int TM, int TN>
+static hipError_t launch_bitgemm_t(const GemmArgs& a, int epi, hipStream_t st) {
+  using T = GemmTile<TM, TN>;
+  const dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM), block(256);
+  size_t lds = 2 * (size_t)T::STAGE;
+  const size_t epi_lds = (size_t)TM * (4 + 4 + 64);
+  if (epi_lds > lds) lds = epi_lds;
+  if (epi == GEMM_EPI_RESIDUAL)
+    hipLaunchKernelGGL((bitgemm_kernel<TM, TN, GEMM_EPI_RESIDUAL>), grid, block, lds, st, a);
+  else
+    hipLaunchKernelGGL((bitgemm_kernel<TM, TN, GEMM_EPI_STORE>), grid, block, lds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.K % kGemmKB) return hipErrorInvalidValue;
+  if (a.M <= 32) return launch_bitgemm_t<32, 128>(a, epi, st);
+  return launch_bitgemm_t<128, 256>(a, epi, st);
+}
+
+// ---------------------------------------------------------------------------
+// causal conv over T (depthwise, width 4) + SiLU
+// ---------------------------------------------------------------------------
+constexpr int kConvChunk = 32;  // tokens per thread
+
+__global__ __launch_bounds__(256) void conv_seq_kernel(ConvSeqArgs a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.z;
+  if (c >= a.cdim) return;
+  const int t0 = blockIdx.y * kConvChunk;
+  const int t1 = min(a.T, t0 + kConvChunk);
+  const float* st = a.state + (size_t)b * a.state_bstride;  // [3][cdim], oldest first
+  const float* xin = a.zx + a.x_off + c;
+  auto raw = [&](int t) -> float {
+    return t >= 0 ? xin[(size_t)((size_t)b * a.T + t) * a.ldzx] : st[(size_t)(t + 3) * a.cdim + c];
+  };
+  const float w0 = a.w[(size_t)c * 4 + 0], w1 = a.w[(size_t)c * 4 + 1], w2 = a.w[(size_t)c * 4 + 2],
+              w3 = a.w[(size_t)c * 4 + 3], bias = a.bias[c];
+  float x0 = raw(t0 - 3), x1 = raw(t0 - 2), x2 = raw(t0 - 1);
+  for (int t = t0; t < t1; ++t) {
+    const float x3 = raw(t);
+    const float v = bias + w0 * x0 + w1 * x1 + w2 * x2 + w3 * x3;
+    a.xc[(size_t)((size_t)b * a.T + t) * a.cdim + c] = silu_f(v);
+    x0 = x1;
+    x1 = x2;
+    x2 = x3;
+  }
+}
+
+// window after the T tokens: the last three raw inputs (older ones from the
+// previous window when T < 3)
+__global__ __launch_bounds__(256) void conv_state_update_kernel(ConvSeqArgs a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (c >= a.cdim) return;
+  float* st = a.state + (size_t)b * a.state_bstride;
+  const float* xin = a.zx + a.x_off + c;
+  float nv[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int t = a.T - 3 + j;
+    nv[j] = t >= 0 ? xin[(size_t)((size_t)b * a.T + t) * a.ldzx] : st[(size_t)(j + a.T) * a.cdim + c];
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) st[(size_t)j * a.cdim + c] = nv[j];
+}
+
+hipError_t launch_conv_seq(const ConvSeqArgs& a, hipStream_t st) {
+  if (a.B <= 0 || a.T <= 0) return hipSuccess;
+  const dim3 g1((a.cdim + 255) / 256, (a.T + kConvChunk - 1) / kConvChunk, a.B);
+  hipLaunchKernelGGL(conv_seq_kernel, g1, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g2((a.cdim + 255) / 256, a.B);
+  hipLaunchKernelGGL(conv_state_update_kernel, g2, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// SSM scan over T tokens.  Workgroup (head h, sequence b) of 4 P threads:
+// thread (p = tid / 4, seg = tid % 4) holds S[p][seg N/4 .. +N/4) in
+// registers.  B, C, x, z and dt of kScanChunk tokens are staged in LDS; y[p]
+// is the sum over the four threads of a quad (DPP).
+// ---------------------------------------------------------------------------
+constexpr int kScanChunk = 16;
+
+template <int P, int N>
+__global__ __launch_bounds__(4 * P) void scan_kernel(ScanArgs a) {
+  constexpr int NPT = N / 4;
+  constexpr int NT = 4 * P;
+  __shared__ float sB[kScanChunk][N], sC[kScanChunk][N], sx[kScanChunk][P], sz[kScanChunk][P], sdt[kScanChunk];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int p = tid >> 2, seg = tid & 3;
+  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;  // [P/16][N][16]
+  float S[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int n = seg * NPT + j;
+    S[j] = stb[((size_t)(p >> 4) * N + n) * 16 + (p & 15)];
+  }
+  const float dtb = a.dt_bias[h], ea = __expf(a.A_log[h]), Dh = a.D[h];
+  const size_t row0 = (size_t)b * a.T;
+  for (int t0 = 0; t0 < a.T; t0 += kScanChunk) {
+    const int tc = min(kScanChunk, a.T - t0);
+    __syncthreads();  // previous chunk fully consumed
+    for (int i = tid; i < tc * N; i += NT) {
+      const int tt = i / N, n = i % N;
+      const float* xr = a.xc + (row0 + t0 + tt) * a.cdim;
+      sB[tt][n] = xr[a.d_inner + n];
+      sC[tt][n] = xr[a.d_inner + N + n];
+    }
+    for (int i = tid; i < tc * P; i += NT) {
+      const int tt = i / P, pp = i % P;
+      sx[tt][pp] = a.xc[(row0 + t0 + tt) * a.cdim + (size_t)h * P + pp];
+      sz[tt][pp] = a.zx[(row0 + t0 + tt) * a.ldzx + (size_t)h * P + pp];
+    }
+    for (int i = tid; i < tc; i += NT) sdt[i] = a.zx[(row0 + t0 + i) * a.ldzx + a.dt_off + h];
+    __syncthreads();
+    for (int tt = 0; tt < tc; ++tt) {
+      const float dt = softplus_f(sdt[tt] + dtb);
+      const float dA = __expf(-dt * ea);
+      const float x = sx[tt][p];
+      const float dtx = dt * x;
+      float y = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        const int n = seg * NPT + j;
+        S[j] = S[j] * dA + dtx * sB[tt][n];
+        y += S[j] * sC[tt][n];
+      }
+      y += dpp_f<kDppQuadSwap1>(y);
+      y += dpp_f<kDppQuadSwap2>(y);
+      if (seg == 0) {
+        const float yy = y + Dh * x;
+        a.g[(row0 + t0 + tt) * a.d_inner + (size_t)h * P + p] = yy * silu_f(sz[tt][p]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int n = seg * NPT + j;
+    stb[((size_t)(p >> 4) * N + n) * 16 + (p & 15)] = S[j];
+  }
+}
+
+hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
+  if (a.B <= 0 || a.T <= 0) return hipSuccess;
+  const dim3 grid(a.H, a.B);
+  if (P == 64 && N == 128) hipLaunchKernelGGL((scan_kernel<64, 128>), grid, dim3(256), 0, st, a);
+  else if (P == 32 && N == 16) hipLaunchKernelGGL((scan_kernel<32, 16>), grid, dim3(128), 0, st, a);
+  else if (P == 64 && N == 64) hipLaunchKernelGGL((scan_kernel<64, 64>), grid, dim3(256), 0, st, a);
+  else if (P == 32 && N == 128) hipLaunchKernelGGL((scan_kernel<32, 128>), grid, dim3(128), 0, st, a);
+  else if (P == 64 && N == 16) hipLaunchKernelGGL((scan_kernel<64, 16>), grid, dim3(256), 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+bool scan_supported(int P, int N) {
+  return (P == 64 && (N == 128 || N == 64 || N == 16)) || (P == 32 && (N == 16 || N == 128));
+}
+
+// ---------------------------------------------------------------------------
+// embedding of a chunk of tokens: row m = b * T + t reads tok[b * tok_stride + t0 + t]
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void embed_rows_kernel(const int32_t* __restrict__ tok, int tok_stride, int t0, int T,
+                                                         const int8_t* __restrict__ E, const float* __restrict__ sE,
+                                                         int dm, int V, float* __restrict__ h, int* err) {
+  const int m = blockIdx.x;
+  const int b = m / T, t = m % T;
+  int tk = tok[(size_t)b * tok_stride + t0 + t];
+  if (tk < 0 || tk >= V) {
+    if (threadIdx.x == 0) atomicOr(err, 1);
+    tk = 0;
+  }
+  const float sc = sE[tk];
+  const int8_t* er = E + (size_t)tk * dm;
+  for (int i = threadIdx.x; i < dm; i += 256) h[(size_t)m * dm + i] = (float)er[i] * sc;
+}
+
+hipError_t launch_embed_rows(const int32_t* tok, int tok_stride, int t0, int B, int T, const int8_t* E,
+                             const float* sE, int dm, int V, float* h, int* err, hipStream_t st) {
+  if (B * T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(embed_rows_kernel, dim3(B * T), dim3(256), 0, st, tok, tok_stride, t0, T, E, sE, dm, V, h, err);
+  return hipGetLastError();
+}
+
+}  // namespace dfssm

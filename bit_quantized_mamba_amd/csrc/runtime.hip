@@ -77,6 +77,16 @@ struct dfssm_ctx {
   // graphs keyed by (B, d_tok, d_out)
   std::map<std::tuple<int, const void*, const void*>, hipGraphExec_t> graphs;
 
+  // batched path (decode with B > 1, prefill): rows of tokens per layer
+  struct GemmWs {
+    size_t rows = 0;  // capacity in token rows
+    size_t bytes = 0;
+    char* buf = nullptr;
+    float *h = nullptr, *s = nullptr, *t = nullptr, *zx = nullptr, *xc = nullptr, *g = nullptr;
+    int8_t* q = nullptr;
+    int32_t* qsum = nullptr;
+  } gw;
+
   // persistent batch-1 path
   int path = DFSSM_PATH_AUTO;
   bool persist_ok = false;
@@ -288,10 +298,130 @@ dfssm_status enqueue_step(dfssm_ctx* c, const int32_t* tok, int tok_stride, int 
   return DFSSM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// batched path: every layer on all B * T token rows at once
+// ---------------------------------------------------------------------------
+constexpr size_t kPrefillChunkRows = 4096;  // token rows per prefill chunk (bounds the workspace)
+
+// Grow the batched-path workspace to at least `rows` token rows.  Cached
+// graphs hold pointers into it, so they are dropped when it moves.
+dfssm_status ensure_gemm_ws(dfssm_ctx* c, size_t rows) {
+  if (rows <= c->gw.rows) return DFSSM_OK;
+  rows = std::max(rows, (size_t)c->maxB);
+  const size_t mx = (size_t)std::max(c->dm, c->di);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  const size_t o_h = take(4 * rows * c->dm), o_s = take(4 * rows), o_t = take(4 * rows * 16),
+               o_zx = take(4 * rows * c->dproj), o_xc = take(4 * rows * c->cdim), o_g = take(4 * rows * c->di),
+               o_q = take(rows * mx), o_qs = take(4 * rows);
+  char* buf = nullptr;
+  if (hipMalloc(&buf, off) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DFSSM_E_OOM, "batched-path workspace allocation failed");
+  }
+  if (c->gw.buf) {
+    HIP_TRY(hipDeviceSynchronize());
+    (void)hipFree(c->gw.buf);
+  }
+  for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+  c->graphs.clear();
+  c->gw.rows = rows;
+  c->gw.bytes = off;
+  c->gw.buf = buf;
+  c->gw.h = (float*)(buf + o_h);
+  c->gw.s = (float*)(buf + o_s);
+  c->gw.t = (float*)(buf + o_t);
+  c->gw.zx = (float*)(buf + o_zx);
+  c->gw.xc = (float*)(buf + o_xc);
+  c->gw.g = (float*)(buf + o_g);
+  c->gw.q = (int8_t*)(buf + o_q);
+  c->gw.qsum = (int32_t*)(buf + o_qs);
+  return DFSSM_OK;
+}
+
+// One layer on rows m = b * T + t of the batched workspace (B sequences in
+// state slots 0..B-1, T tokens each, in order).
+dfssm_status enqueue_layer_gemm(dfssm_ctx* c, int l, int B, int T, hipStream_t st, int8_t* q1_out,
+                                int8_t* q2_out) {
+  auto& w = c->gw;
+  const int M = B * T;
+  RowsArgs ra{w.h, c->dm, c->lt<float>(l, DFSSM_T_NORM_W), M, c->eps, c->lt<int8_t>(l, DFSSM_T_IN_A),
+              c->lt<float>(l, DFSSM_T_IN_SA), w.q, w.s, w.qsum, w.t};
+  HIP_TRY(launch_rows_quant(ra, c->dm, st));
+  if (q1_out) HIP_TRY(hipMemcpyAsync(q1_out, w.q, (size_t)M * c->dm, hipMemcpyDeviceToDevice, st));
+  GemmArgs gi{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_IN_BITS), c->lt<float>(l, DFSSM_T_IN_SW),
+              c->lt<int8_t>(l, DFSSM_T_IN_B), c->lt<float>(l, DFSSM_T_IN_SB), M, c->dproj, c->dm, w.zx, c->dproj,
+              nullptr};
+  HIP_TRY(launch_bitgemm(gi, GEMM_EPI_STORE, st));
+  ConvSeqArgs ca{w.zx, c->dproj, c->di, w.xc, c->conv + (size_t)l * (c->K - 1) * c->cdim, c->conv_bstride,
+                 c->lt<float>(l, DFSSM_T_CONV_W), c->lt<float>(l, DFSSM_T_CONV_B), B, T, c->cdim};
+  HIP_TRY(launch_conv_seq(ca, st));
+  ScanArgs sa{w.xc, w.zx, c->dproj, 2 * c->di + 2 * c->N, c->lt<float>(l, DFSSM_T_A_LOG),
+              c->lt<float>(l, DFSSM_T_DT_BIAS), c->lt<float>(l, DFSSM_T_D),
+              c->ssm + (size_t)l * c->H * c->P * c->N, c->ssm_bstride, w.g, B, T, c->H, c->di, c->cdim};
+  HIP_TRY(launch_scan(sa, c->P, c->N, st));
+  RowsArgs rb{w.g, c->di, c->lt<float>(l, DFSSM_T_GNORM_W), M, c->eps, c->lt<int8_t>(l, DFSSM_T_OUT_A),
+              c->lt<float>(l, DFSSM_T_OUT_SA), w.q, w.s, w.qsum, w.t};
+  HIP_TRY(launch_rows_quant(rb, c->di, st));
+  if (q2_out) HIP_TRY(hipMemcpyAsync(q2_out, w.q, (size_t)M * c->di, hipMemcpyDeviceToDevice, st));
+  GemmArgs go{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_OUT_BITS), c->lt<float>(l, DFSSM_T_OUT_SW),
+              c->lt<int8_t>(l, DFSSM_T_OUT_B), c->lt<float>(l, DFSSM_T_OUT_SB), M, c->dm, c->di, w.h, c->dm, nullptr};
+  HIP_TRY(launch_bitgemm(go, GEMM_EPI_RESIDUAL, st));
+  return DFSSM_OK;
+}
+
+// Tokens tok[b * tok_stride + t0 + t], t < T, of B sequences through every
+// layer; with `head`, the last token of each sequence through the final norm,
+// the LM head and the argmax.  Trace buffers (optional) are indexed by row
+// m = b * T + t: h [L+1][B*T][d_model], q1 [L][B*T][d_model],
+// q2 [L][B*T][d_inner], qf [B][d_model].
+dfssm_status enqueue_step_gemm(dfssm_ctx* c, const int32_t* tok, int tok_stride, int t0, int B, int T, float* logits,
+                               int32_t* next, int32_t* out, const Trace* tr, bool head, hipStream_t st) {
+  auto& w = c->gw;
+  const size_t M = (size_t)B * T;
+  HIP_TRY(launch_embed_rows(tok, tok_stride, t0, B, T, c->lt<int8_t>(-1, DFSSM_G_EMBED),
+                            c->lt<float>(-1, DFSSM_G_EMBED_SCALE), c->dm, c->V, w.h, c->err, st));
+  for (int l = 0; l < c->L; ++l) {
+    if (tr && tr->h)
+      HIP_TRY(hipMemcpyAsync(tr->h + (size_t)l * M * c->dm, w.h, sizeof(float) * M * c->dm,
+                             hipMemcpyDeviceToDevice, st));
+    dfssm_status r = enqueue_layer_gemm(c, l, B, T, st, tr && tr->q1 ? tr->q1 + (size_t)l * M * c->dm : nullptr,
+                                        tr && tr->q2 ? tr->q2 + (size_t)l * M * c->di : nullptr);
+    if (r != DFSSM_OK) return r;
+  }
+  if (tr && tr->h)
+    HIP_TRY(hipMemcpyAsync(tr->h + (size_t)c->L * M * c->dm, w.h, sizeof(float) * M * c->dm,
+                           hipMemcpyDeviceToDevice, st));
+  if (!head) return DFSSM_OK;
+  RowsArgs rf{w.h + (size_t)(T - 1) * c->dm, T * c->dm, c->lt<float>(-1, DFSSM_G_FINAL_NORM), B, c->eps, nullptr,
+              nullptr, w.q, w.s, nullptr, nullptr};
+  HIP_TRY(launch_rows_quant(rf, c->dm, st));
+  if (tr && tr->qf) HIP_TRY(hipMemcpyAsync(tr->qf, w.q, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st));
+  float* lg = logits ? logits : c->logits;
+  HIP_TRY(launch_lm_head(c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), w.q, w.s, c->V,
+                         c->dm, B, lg, st));
+  if (next || out) HIP_TRY(launch_argmax(lg, c->V, B, next ? next : c->next, out, c->counter, st));
+  return DFSSM_OK;
+}
+
+// Whether decode of batch B runs on the batched (GEMM) path.
+bool use_gemm(const dfssm_ctx* c, int B) {
+  if (c->path == DFSSM_PATH_KERNELS) return false;
+  if (c->path == DFSSM_PATH_GEMM) return true;
+  return B > 1;
+}
+
+// one decode step of B sequences on whichever path serves batch B (not the persistent one)
+dfssm_status enqueue_decode(dfssm_ctx* c, const int32_t* tok, int B, float* logits, int32_t* next, int32_t* out,
+                            const Trace* tr, hipStream_t st) {
+  if (use_gemm(c, B)) return enqueue_step_gemm(c, tok, 1, 0, B, 1, logits, next, out, tr, true, st);
+  return enqueue_step(c, tok, 1, B, logits, next, out, tr, true, st);
+}
+
 // Whether batch-B work runs on the persistent kernel; fails when it is required but cannot run.
 dfssm_status use_persistent(const dfssm_ctx* c, int B, bool* yes) {
   *yes = false;
-  if (B != 1 || c->path == DFSSM_PATH_KERNELS) return DFSSM_OK;
+  if (B != 1 || c->path == DFSSM_PATH_KERNELS || c->path == DFSSM_PATH_GEMM) return DFSSM_OK;
   if (!c->persist_ok) {
     if (c->path == DFSSM_PATH_PERSISTENT)
       return fail(DFSSM_E_UNSUPPORTED, "persistent decode unavailable: " + c->persist_why);
@@ -521,13 +651,14 @@ void dfssm_destroy(dfssm_ctx* c) {
   if (c->sbuf) (void)hipFree(c->sbuf);
   if (c->ws) (void)hipFree(c->ws);
   if (c->boxes) (void)hipFree(c->boxes);
+  if (c->gw.buf) (void)hipFree(c->gw.buf);
   if (c->abort_flag) (void)hipFree(c->abort_flag);
   delete c;
 }
 
 dfssm_status dfssm_device_bytes(const dfssm_ctx* c, size_t* bytes) {
   if (!c || !bytes) return fail(DFSSM_E_INVALID, "null argument");
-  *bytes = c->wbytes + c->sbytes + c->wsbytes;
+  *bytes = c->wbytes + c->sbytes + c->wsbytes + c->gw.bytes;
   return DFSSM_OK;
 }
 
@@ -672,7 +803,8 @@ dfssm_status dfssm_decode_step(dfssm_ctx* c, const int32_t* d_tok, int32_t B, fl
   bool pers = false;
   if ((v = use_persistent(c, B, &pers)) != DFSSM_OK) return v;
   if (pers) return run_persistent(c, d_tok, nullptr, d_next, 1, d_logits, nullptr, S(stream));
-  return enqueue_step(c, d_tok, 1, B, d_logits, d_next, nullptr, nullptr, true, S(stream));
+  if (use_gemm(c, B) && (v = ensure_gemm_ws(c, B)) != DFSSM_OK) return v;
+  return enqueue_decode(c, d_tok, B, d_logits, d_next, nullptr, nullptr, S(stream));
 }
 
 dfssm_status dfssm_generate(dfssm_ctx* c, int32_t* d_tok, int32_t B, int32_t n_steps, int32_t* d_out,
@@ -687,15 +819,16 @@ dfssm_status dfssm_generate(dfssm_ctx* c, int32_t* d_tok, int32_t B, int32_t n_s
   bool pers = false;
   if ((v = use_persistent(c, B, &pers)) != DFSSM_OK) return v;
   if (pers) return run_persistent(c, d_tok, d_tok, d_out, n_steps, nullptr, nullptr, st);
+  if (use_gemm(c, B) && (v = ensure_gemm_ws(c, B)) != DFSSM_OK) return v;
   if (d_out) HIP_TRY(launch_zero(c->counter, 4, st));
   if (!use_graph) {
     for (int i = 0; i < n_steps; ++i) {
-      v = enqueue_step(c, d_tok, 1, B, nullptr, d_tok, d_out, nullptr, true, st);
+      v = enqueue_decode(c, d_tok, B, nullptr, d_tok, d_out, nullptr, st);
       if (v != DFSSM_OK) return v;
     }
     return DFSSM_OK;
   }
-  auto key = std::make_tuple((int)B, (const void*)d_tok, (const void*)d_out);
+  auto key = std::make_tuple((int)B * 4 + (use_gemm(c, B) ? 1 : 0), (const void*)d_tok, (const void*)d_out);
   auto it = c->graphs.find(key);
   hipGraphExec_t exec = nullptr;
   if (it == c->graphs.end()) {
@@ -704,7 +837,7 @@ dfssm_status dfssm_generate(dfssm_ctx* c, int32_t* d_tok, int32_t B, int32_t n_s
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
-      v = enqueue_step(c, d_tok, 1, B, nullptr, d_tok, d_out, nullptr, true, cap);
+      v = enqueue_decode(c, d_tok, B, nullptr, d_tok, d_out, nullptr, cap);
       hipError_t e2 = hipStreamEndCapture(cap, &graph);
       if (v == DFSSM_OK && e2 != hipSuccess) v = fail(DFSSM_E_HIP, std::string("graph capture: ") + hipGetErrorString(e2));
     } else {
@@ -732,6 +865,19 @@ dfssm_status dfssm_prefill(dfssm_ctx* c, const int32_t* d_tok, int32_t B, int32_
   if ((v = check_B(c, B)) != DFSSM_OK) return v;
   if (!d_tok) return fail(DFSSM_E_INVALID, "null token pointer");
   if (T < 1) return fail(DFSSM_E_INVALID, "prompt length must be >= 1");
+  if (c->path != DFSSM_PATH_KERNELS) {
+    // batched path, in chunks of whole token rows across the B sequences
+    const int tc = (int)std::max<size_t>(1, std::min<size_t>((size_t)T, kPrefillChunkRows / (size_t)B));
+    if ((v = ensure_gemm_ws(c, (size_t)B * tc)) != DFSSM_OK) return v;
+    for (int t0 = 0; t0 < T; t0 += tc) {
+      const int n = std::min(tc, T - t0);
+      const bool last = t0 + n == T;
+      v = enqueue_step_gemm(c, d_tok, T, t0, B, n, last ? d_last_logits : nullptr, last ? d_next : nullptr, nullptr,
+                            nullptr, last && (d_last_logits || d_next), S(stream));
+      if (v != DFSSM_OK) return v;
+    }
+    return DFSSM_OK;
+  }
   for (int t = 0; t < T; ++t) {
     const bool last = t == T - 1;
     v = enqueue_step(c, d_tok + t, T, B, last ? d_last_logits : nullptr, last ? d_next : nullptr, nullptr, nullptr,
@@ -770,7 +916,26 @@ dfssm_status dfssm_trace_step(dfssm_ctx* c, const int32_t* d_tok, int32_t B, flo
   bool pers = false;
   if ((v = use_persistent(c, B, &pers)) != DFSSM_OK) return v;
   if (pers) return run_persistent(c, d_tok, nullptr, nullptr, 1, d_logits, &tr, S(stream));
-  return enqueue_step(c, d_tok, 1, B, d_logits, nullptr, nullptr, &tr, true, S(stream));
+  if (use_gemm(c, B) && (v = ensure_gemm_ws(c, B)) != DFSSM_OK) return v;
+  return enqueue_decode(c, d_tok, B, d_logits, nullptr, nullptr, &tr, S(stream));
+}
+
+dfssm_status dfssm_trace_prefill(dfssm_ctx* c, const int32_t* d_tok, int32_t B, int32_t T, float* d_h_trace,
+                                 int8_t* d_q1_trace, int8_t* d_q2_trace, int8_t* d_qf, float* d_logits,
+                                 void* stream) {
+  dfssm_status v = check_ctx(c);
+  if (v != DFSSM_OK) return v;
+  if ((v = check_B(c, B)) != DFSSM_OK) return v;
+  if (!d_tok || !d_h_trace) return fail(DFSSM_E_INVALID, "null pointer");
+  if (T < 1 || (size_t)B * T > kPrefillChunkRows)
+    return fail(DFSSM_E_INVALID, "traced prefill takes 1 <= B * T <= " + std::to_string(kPrefillChunkRows) + " rows");
+  if ((v = ensure_gemm_ws(c, (size_t)B * T)) != DFSSM_OK) return v;
+  Trace tr;
+  tr.h = d_h_trace;
+  tr.q1 = d_q1_trace;
+  tr.q2 = d_q2_trace;
+  tr.qf = d_qf;
+  return enqueue_step_gemm(c, d_tok, T, 0, B, T, d_logits, nullptr, nullptr, &tr, true, S(stream));
 }
 
 dfssm_status dfssm_time_kernel(dfssm_ctx* c, int32_t kernel, int32_t B, int32_t iters, float* avg_us, void* stream) {
@@ -840,7 +1005,9 @@ dfssm_status dfssm_profile_persistent(dfssm_ctx* c, int32_t* d_tok, int32_t n_to
 
 dfssm_status dfssm_set_path(dfssm_ctx* c, int32_t path) {
   if (!c) return fail(DFSSM_E_INVALID, "null context");
-  if (path < DFSSM_PATH_AUTO || path > DFSSM_PATH_PERSISTENT) return fail(DFSSM_E_INVALID, "unknown path");
+  if (path < DFSSM_PATH_AUTO || path > DFSSM_PATH_GEMM) return fail(DFSSM_E_INVALID, "unknown path");
+  if (path == DFSSM_PATH_GEMM && !scan_supported(c->P, c->N))
+    return fail(DFSSM_E_UNSUPPORTED, "the batched path is not compiled for this headdim / d_state");
   if (path == DFSSM_PATH_PERSISTENT && !c->persist_ok)
     return fail(DFSSM_E_UNSUPPORTED, "persistent decode unavailable: " + c->persist_why);
   c->path = path;
@@ -889,6 +1056,33 @@ dfssm_status dfssm_k_proj(const uint32_t* d_bits, const float* d_sw, const int8_
   hipError_t e2 = hipFreeAsync(tmp, st);
   if (e != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_proj: ") + hipGetErrorString(e));
   if (e2 != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_proj free: ") + hipGetErrorString(e2));
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_k_gemm(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
+                          const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out, const int8_t* d_q,
+                          const float* d_s, int32_t M, int32_t* d_acc, float* d_y, void* stream) {
+  if (!d_bits || !d_sw || !d_A || !d_sA || !d_B || !d_sB || !d_q || !d_s || !d_y)
+    return fail(DFSSM_E_INVALID, "null pointer");
+  if (d_in < 128 || d_in % 128 || (d_in / 128) > 64 || ((d_in / 128) & (d_in / 128 - 1)))
+    return fail(DFSSM_E_UNSUPPORTED, "d_in must be 128 * 2^k <= 8192");
+  if (d_out < 1 || M < 1 || M > 65535) return fail(DFSSM_E_INVALID, "bad d_out / M");
+  hipStream_t st = S(stream);
+  const size_t pl_bytes = sizeof(uint32_t) * (size_t)M * (d_in / 32) * 8;
+  char* tmp = nullptr;
+  const size_t tbytes = align_up(pl_bytes) + align_up(4 * (size_t)M) + align_up(4 * (size_t)M * 16);
+  HIP_TRY(hipMallocAsync((void**)&tmp, tbytes, st));
+  uint32_t* planes = (uint32_t*)tmp;
+  int32_t* qsum = (int32_t*)(tmp + align_up(pl_bytes));
+  float* t = (float*)(tmp + align_up(pl_bytes) + align_up(4 * (size_t)M));
+  hipError_t e = launch_qprep(d_q, d_s, d_in, M, d_A, d_sA, 16, planes, qsum, t, st);
+  if (e == hipSuccess) {
+    GemmArgs a{d_q, d_s, qsum, t, d_bits, d_sw, d_B, d_sB, M, d_out, d_in, d_y, d_out, d_acc};
+    e = launch_bitgemm(a, GEMM_EPI_STORE, st);
+  }
+  hipError_t e2 = hipFreeAsync(tmp, st);
+  if (e != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_gemm: ") + hipGetErrorString(e));
+  if (e2 != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_gemm free: ") + hipGetErrorString(e2));
   return DFSSM_OK;
 }
 

@@ -110,14 +110,19 @@ const char* dfssm_last_error(const dfssm_ctx* ctx);
 dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** out);
 void dfssm_destroy(dfssm_ctx* ctx);
 
-/* Execution path of batch-1 decode.  DFSSM_PATH_AUTO (default) runs batch-1
- * decode_step / generate / trace_step as one persistent kernel (every
- * workgroup resident across all layers and tokens, hops between workgroups
- * through device memory) when the shape and device allow it, and every
- * other call as a sequence of per-layer kernels; DFSSM_PATH_KERNELS forces
- * the per-layer kernels; DFSSM_PATH_PERSISTENT requires the persistent
- * kernel for batch 1 and fails with DFSSM_E_UNSUPPORTED where it cannot run. */
-enum { DFSSM_PATH_AUTO = 0, DFSSM_PATH_KERNELS = 1, DFSSM_PATH_PERSISTENT = 2 };
+/* Execution path.  DFSSM_PATH_AUTO (default) runs batch-1 decode_step /
+ * generate / trace_step as one persistent kernel (every workgroup resident
+ * across all layers and tokens, hops between workgroups through device
+ * memory) when the shape and device allow it, decode of B > 1 sequences and
+ * every prefill on the batched path (each layer on all token rows at once:
+ * int8 matrix-core GEMMs for the projections, a causal conv over the tokens
+ * of each sequence and a sequential SSM scan; prefill in chunks of at most
+ * 4096 token rows).  DFSSM_PATH_KERNELS runs everything as per-layer GEMV
+ * kernels, one token at a time.  DFSSM_PATH_PERSISTENT is AUTO but fails
+ * with DFSSM_E_UNSUPPORTED where batch 1 cannot use the persistent kernel.
+ * DFSSM_PATH_GEMM runs every decode (batch 1 included) and prefill on the
+ * batched path.                                                             */
+enum { DFSSM_PATH_AUTO = 0, DFSSM_PATH_KERNELS = 1, DFSSM_PATH_PERSISTENT = 2, DFSSM_PATH_GEMM = 3 };
 dfssm_status dfssm_set_path(dfssm_ctx* ctx, int32_t path);
 
 /* Device bytes the context holds (weights + state + workspace). */
@@ -191,6 +196,17 @@ dfssm_status dfssm_trace_step(dfssm_ctx* ctx, const int32_t* d_tok, int32_t B, f
                               int8_t* d_q1_trace, int8_t* d_q2_trace, int8_t* d_qf, float* d_logits,
                               void* stream);
 
+/* Prefill of sequences [0, B) on the batched path (one chunk: 1 <= B T <=
+ * 4096) that also records its intermediate results, row m = b T + t:
+ * d_h_trace fp32 [n_layer + 1][B T][d_model], d_q1_trace int8
+ * [n_layer][B T][d_model], d_q2_trace int8 [n_layer][B T][d_inner] (each
+ * may be NULL but d_h_trace), d_qf int8 [B][d_model] (LM-head input of the
+ * last position) and d_logits fp32 [B][vocab] (last position), each may be
+ * NULL.  Leaves the state after the last token.  Enqueued.                 */
+dfssm_status dfssm_trace_prefill(dfssm_ctx* ctx, const int32_t* d_tok, int32_t B, int32_t T, float* d_h_trace,
+                                 int8_t* d_q1_trace, int8_t* d_q2_trace, int8_t* d_qf, float* d_logits,
+                                 void* stream);
+
 /* Kernel timing for roofline reports.  Launches one kernel of the batch-B
  * decode step `iters` times back to back on `stream` (layer i % n_layer on
  * launch i, same arguments as inside the step) between two HIP events and
@@ -243,6 +259,16 @@ dfssm_status dfssm_k_proj(const uint32_t* d_bits, const float* d_sw, const int8_
                           const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out, int32_t r,
                           const int8_t* d_q, const float* d_s, int32_t B, int32_t* d_acc, float* d_y,
                           void* stream);
+
+/* The same projection on the batched path's matrix-core GEMM, M rows
+ * (gist.science summary §2.B/§2.C): r is 16; d_A int8 [16][d_in], d_B int8
+ * [d_out][16]; d_q int8 [M][d_in], d_s fp32 [M]; outputs d_acc int32
+ * [M][d_out] (or NULL) and d_y fp32 [M][d_out], as for dfssm_k_proj.
+ * d_in is 128 * 2^k <= 8192.  Enqueued; uses stream-ordered temporary
+ * memory.                                                                   */
+dfssm_status dfssm_k_gemm(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
+                          const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out, const int8_t* d_q,
+                          const float* d_s, int32_t M, int32_t* d_acc, float* d_y, void* stream);
 
 #ifdef __cplusplus
 }
