@@ -1,16 +1,20 @@
 #!/usr/bin/env python3
-"""Decode throughput of the 48-layer DF-SSM model (Mamba-2 1.3B shape) at batch 1
-on one MI355X.
+"""Decode throughput of the 48-layer DF-SSM model (Mamba-2 1.3B shape) on one
+MI355X.
 
-Workload: seeded synthetic weights (1-bit scaffold + int8 LoRA r=16, int8 tied
-embedding / LM head, vocab 50288), a 16-token seeded prompt prefilled, then
-greedy decoding where every step is one replay of the captured HIP graph of
-the whole step and the argmax is fed back on the device.  A step is one token
-through all 48 layers, the LM head and the argmax.
+Default workload (the headline): batch 1.  Seeded synthetic weights (1-bit
+scaffold + int8 LoRA r=16, int8 tied embedding / LM head, vocab 50288), a
+16-token seeded prompt prefilled, then greedy decoding.  The timed region is
+one launch of the persistent decode kernel that runs every timed token (all
+48 layers, the LM head and the argmax fed back on the device).
 
-Prints one JSON line: tokens/s, the roofline of the dominant kernel (HIP-event
-timing of that kernel, algorithmic bytes per launch), the whole-step HBM
-roofline, and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: tokens/s, the roofline of that kernel (HIP-event time of
+the launch, algorithmic bytes per token x tokens), and the CPU oracle timed on
+a bounded sample of the same workload.
+
+--workload decode-b32 and prefill-8x2048 measure the batched path instead
+(32 sequences decoding after an 8-token prefill; a prefill of 8 x 2048
+tokens); their lines carry step-level rooflines.
 """
 import argparse
 import json
@@ -83,6 +87,107 @@ def step_bytes(s):
     return s.n_layer * per_layer + once
 
 
+def batched_step_bytes(s, B):
+    """Algorithmic HBM bytes of one batch-B decode step: weights once, state and logits per sequence."""
+    dm, di, N, H, P, V, r = s.d_model, s.d_inner, s.d_state, s.n_heads, s.headdim, s.vocab, s.rank
+    dp, cd, K = s.d_in_proj, s.conv_dim, s.d_conv
+    f = 4
+    weights = s.n_layer * (dp * dm // 8 + dm * di // 8 + (dp + dm) * f + r * (dm + dp + di + dm)
+                           + (2 * r + dp + dm) * f + cd * (K + 1) * f + (3 * H + dm + di) * f) \
+        + V * dm + V * f + dm * f
+    per_seq = s.n_layer * (K * cd * f + 2 * H * P * N * f) + dm + V * f
+    return weights + B * per_seq
+
+
+def prefill_work(s, B, T):
+    """int8 matrix-core ops of the scaffold + LoRA GEMMs and fp32 flops of the scan for a B x T prefill."""
+    M = B * T
+    dm, di, dp, r = s.d_model, s.d_inner, s.d_in_proj, s.rank
+    gemm_ops = 2 * M * s.n_layer * (dp * dm + dm * di + r * (dm + dp + di + dm))
+    scan_flops = 5 * s.n_heads * s.headdim * s.d_state * M * s.n_layer
+    return gemm_ops, scan_flops
+
+
+def bench_batched(args):
+    import torch
+    import synth
+    from bit_quantized_mamba_amd import Engine
+
+    s = synth.FULL_1P3B
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    common = {"n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "int8/1-bit weights, int32 accumulation, f32 state", "data": "synthetic (seeded weights and tokens)",
+              "cpu_baseline": None}
+    if args.workload == "decode-b32":
+        B, T = 32, 8
+        seed = synth.SEED_BASE + 3
+        eng = Engine.from_shape(s, max_batch=B, device=0)
+        eng.load_synthetic(seed)
+        toks = synth.gen_tokens(seed, 0, B * T, s.vocab).reshape(B, T)
+        _, nxt = eng.prefill(torch.from_numpy(toks.astype("int32")).to(dev))
+        tok = nxt.clone()
+        out = torch.empty((max(args.steps, args.warmup, 1), B), dtype=torch.int32, device=dev)
+        if args.warmup:
+            eng.generate(tok, args.warmup, out=out, use_graph=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        eng.generate(tok, args.steps, out=out, use_graph=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eng.check()
+        ms = e0.elapsed_time(e1)
+        sb = batched_step_bytes(s, B)
+        gbs = sb * args.steps / (ms / 1e3) / 1e9
+        res = {"metric": "decode tokens/s, batch=32, 48-layer 1.3B shape; % of HBM roofline",
+               "value": round(B * args.steps / (ms / 1e3), 1), "unit": "tokens/s", "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4),
+               "config": {"workload": "DF-SSM 48-layer 1.3B shape, batch 32, 8-token prefill then greedy decode "
+                                      f"of {args.steps} steps (one hipGraph replay per step)", "batch": B},
+               "roofline": {"bound": "hbm", "scope": "whole step", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "bytes_per_step": sb}}
+    else:
+        B, T = 8, 2048
+        seed = synth.SEED_BASE + 4
+        eng = Engine.from_shape(s, max_batch=B, device=0)
+        eng.load_synthetic(seed)
+        toks = torch.from_numpy(synth.gen_tokens(seed, 0, B * T, s.vocab).reshape(B, T).astype("int32")).to(dev)
+        for _ in range(max(args.warmup, 1)):
+            eng.reset_state(B)
+            eng.prefill(toks)
+        torch.cuda.synchronize()
+        reps = max(1, args.steps)
+        tot = 0.0
+        for _ in range(reps):
+            eng.reset_state(B)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            eng.prefill(toks)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        eng.check()
+        ms = tot / reps
+        gops, sflops = prefill_work(s, B, T)
+        res = {"metric": "prefill tokens/s, 8 x 2048 tokens, 48-layer 1.3B shape",
+               "value": round(B * T / (ms / 1e3), 1), "unit": "tokens/s", "steps": reps, "warmup": args.warmup,
+               "ms_per_step": round(ms, 3),
+               "config": {"workload": "DF-SSM 48-layer 1.3B shape, prefill of 8 sequences x 2048 tokens from a "
+                                      "zero state (last-position logits)", "batch": B, "seq_len": T},
+               "roofline": {"bound": "mfma+alu", "scope": "whole prefill",
+                            "int8_gemm_TOPs": round(gops / 1e12, 2), "scan_TFLOPs": round(sflops / 1e12, 2),
+                            "int8_peak_TOPS": 5000.0, "fp32_vector_peak_TFLOPS": 157.3,
+                            "bound_ms": round(max(gops / 5000e12, sflops / 157.3e12) * 1e3, 2),
+                            "frac": round(max(gops / 5000e12, sflops / 157.3e12) * 1e3 / ms, 4)}}
+    eng.close()
+    res.update(common)
+    print(json.dumps(res))
+
+
 def cpu_baseline(shape, seed, prompt, budget_s):
     """The CPU oracle decoding the same model, timed on a bounded number of steps."""
     import numpy as np
@@ -115,7 +220,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-breakdown", action="store_true",
                     help="also time each kernel of the per-layer (multi-kernel) path")
-    ap.add_argument("--path", choices=["auto", "kernels", "persistent"], default="auto")
+    ap.add_argument("--path", choices=["auto", "kernels", "persistent", "gemm"], default="auto")
+    ap.add_argument("--workload", choices=["decode-b1", "decode-b32", "prefill-8x2048"], default="decode-b1")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy (read + write) of this many MiB, "
                          "a known-size reference for the HBM byte counters of a profiler run")
@@ -124,6 +230,10 @@ def main():
         print(f"bench.py: this build runs on one GPU only (the decode path is per-sequence data-parallel; "
               f"see the sharding notes); --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload != "decode-b1":
+        bench_batched(args)
+        return
 
     import torch
     import synth
@@ -167,7 +277,7 @@ def main():
     # The timed region is one launch of the persistent decode kernel (all steps
     # in one kernel) on the auto/persistent path, so its HIP-event time is that
     # kernel's duration; its algorithmic bytes are steps x the step's bytes.
-    persistent = args.path != "kernels"
+    persistent = args.path in ("auto", "persistent")
     roofline = None
     if persistent:
         achieved = sb * args.steps / (ms / 1e3) / 1e9
@@ -217,7 +327,8 @@ def main():
                                f"{args.steps} tokens",
                    "batch": 1, "prefill": 16,
                    "path": "persistent kernel, one launch for all timed tokens" if persistent else
-                           "per-layer kernels, one hipGraph replay per token"},
+                           ("per-layer kernels" if args.path == "kernels" else "batched GEMM path")
+                           + ", one hipGraph replay per token"},
         "roofline": roofline,
         "step_roofline": {"bound": "hbm", "bytes_per_step": sb, "achieved": round(step_gbs, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4)},

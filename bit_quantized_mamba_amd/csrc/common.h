@@ -165,6 +165,34 @@ struct GemmArgs {
   int32_t* acc;         // [M][N] signed scaffold sums, or null
 };
 
+// M <= 32 rows against N weight rows, one 32 x 32 block per workgroup
+enum SkinnyKind : int {
+  SK_IN = 0,   // scaffold + LoRA -> y (stored); with xc set, columns [x_off, x_off + cdim) also go
+               // through the conv shift register of one decode token (state updated, SiLU output to xc)
+  SK_OUT = 1,  // scaffold + LoRA, residual: y += ...
+  SK_HEAD = 2  // int8 weight rows (the tied LM head): y = float(sum w q) * sw[n] * s[m]
+};
+struct SkinnyArgs {
+  const int8_t* q;      // [M][K]
+  const float* s;       // [M]
+  const int32_t* qsum;  // [M] (scaffold kinds)
+  const float* t;       // [M][16] (scaffold kinds)
+  const void* w;        // scaffold bits uint32 [N][K/32], or int8 [N][K] for SK_HEAD
+  const float* sw;      // [N] row scale
+  const int8_t* Bm;     // [N][16] LoRA up (scaffold kinds)
+  const float* sB;      // [N]
+  int M, N, K;
+  float* y;
+  int ldy;
+  int32_t* acc;         // [M][N] signed scaffold sums, or null
+  float* xc;            // [M][cdim] or null
+  float* conv_state;    // sequence 0's window [3][cdim]; sequence m at + m * conv_bstride
+  size_t conv_bstride;
+  const float* conv_w;  // [cdim][4]
+  const float* conv_b;
+  int x_off, cdim;
+};
+
 // causal depthwise conv over T tokens of B sequences (rows b * T + t)
 struct ConvSeqArgs {
   const float* zx;  // in_proj output rows [B*T][ldzx]; conv inputs at columns x_off + c
@@ -192,6 +220,7 @@ struct ScanArgs {
 
 hipError_t launch_rows_quant(const RowsArgs& a, int K, hipStream_t st);
 hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st);
+hipError_t launch_gemm_skinny(const SkinnyArgs& a, int kind, hipStream_t st);
 hipError_t launch_conv_seq(const ConvSeqArgs& a, hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st);
 bool scan_supported(int P, int N);

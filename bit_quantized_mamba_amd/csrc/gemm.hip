@@ -112,9 +112,10 @@ hipError_t launch_rows_quant(const RowsArgs& a, int K, hipStream_t st) {
 // bitgemm
 // ---------------------------------------------------------------------------
 
-// 0/1 bytes of nibble x (bits 0..3): byte j = bit j.  The shifted copies of
-// the four bits land on distinct positions (bit j at 8 j and at 7 i + j for
-// the others), so the 24-bit multiply makes no carries.
+// 0/1 bytes of nibble x (bits 0..3): byte j = bit j.  The multiply copies
+// bit i to positions i, i + 7, i + 14 and i + 21; those 16 positions are all
+// distinct (so nothing carries) and bit j's copy at 7 j + j = 8 j is the one
+// the mask keeps.
 __device__ __forceinline__ uint32_t spread_nibble(uint32_t x) { return __umul24(x & 15u, 0x00204081u) & 0x01010101u; }
 
 constexpr int kGemmKB = 64;       // k per LDS stage
@@ -303,6 +304,129 @@ hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st) {
   if (a.K % kGemmKB) return hipErrorInvalidValue;
   if (a.M <= 32) return launch_bitgemm_t<32, 128>(a, epi, st);
   return launch_bitgemm_t<128, 256>(a, epi, st);
+}
+
+// ---------------------------------------------------------------------------
+// skinny GEMM (M <= 32 rows: batched decode, the LM head of a few sequences).
+// One 32 x 32 output block per workgroup; the four waves take a quarter of K
+// each and sum their accumulators through LDS.  Operands go straight from
+// global memory (the weights streamed once, the codes from L2) into MFMA
+// registers: lane l holds row / column l % 32 and k-half l / 32 of each
+// 32-wide k-step, and 16 scaffold bits become 16 0/1 bytes in registers.
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyUnroll = 8;  // k-steps whose loads are issued together
+
+template <int KIND>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
+  __shared__ int red[3][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 32;
+  const int col = lane & 31, kg = lane >> 5;
+  const int n = n0 + col;
+  const bool nok = n < a.N, mok = col < a.M;  // this lane's B column and A row
+  const int K = a.K, ks = K / 4;              // k slice of this wave
+  const int kbeg = wave * ks;
+  const int8_t* qrow = a.q + (size_t)(mok ? col : 0) * K + 16 * kg;
+  v16i acc = (v16i){};
+  const int kend = kbeg + ks;
+  for (int k0 = kbeg; k0 < kend; k0 += 32 * kSkinnyUnroll) {
+    v4i af[kSkinnyUnroll], bf[kSkinnyUnroll];
+    uint32_t bw[kSkinnyUnroll];
+#pragma unroll
+    for (int u = 0; u < kSkinnyUnroll; ++u) {
+      const int k = k0 + 32 * u;
+      const bool kin = k < kend;  // uniform
+      af[u] = mok && kin ? *(const v4i*)(qrow + k) : (v4i){};
+      if (KIND == SK_HEAD)
+        bf[u] = nok && kin ? *(const v4i*)((const int8_t*)a.w + (size_t)n * K + k + 16 * kg) : (v4i){};
+      else
+        bw[u] = nok && kin ? ((const uint32_t*)a.w)[(size_t)n * (K / 32) + k / 32] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kSkinnyUnroll; ++u) {
+      if (k0 + 32 * u >= kend) break;
+      if (KIND != SK_HEAD) {
+        const uint32_t h = bw[u] >> (16 * kg);
+        bf[u] = (v4i){(int)spread_nibble(h), (int)spread_nibble(h >> 4), (int)spread_nibble(h >> 8),
+                      (int)spread_nibble(h >> 12)};
+      }
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[u], bf[u], acc, 0, 0, 0);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave - 1][r][lane] = acc[r];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] += red[0][r][lane] + red[1][r][lane] + red[2][r][lane];
+
+  if (KIND == SK_HEAD) {
+    const float sc = nok ? a.sw[n] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 8 * (r >> 2) + 4 * kg + (r & 3);
+      if (m < a.M && nok) a.y[(size_t)m * a.ldy + n] = (float)acc[r] * sc * a.s[m];
+    }
+    return;
+  }
+  // LoRA up on the fp32 matrix core: lo[m][n] = sum_j t[m][j] B[n][j]
+  const float sw = nok ? a.sw[n] : 0.0f, sb = nok ? a.sB[n] : 0.0f;
+  const uint4 bq = nok ? *(const uint4*)(a.Bm + (size_t)n * 16) : make_uint4(0, 0, 0, 0);
+  const uint32_t bwv[4] = {bq.x, bq.y, bq.z, bq.w};
+  v16f lo = (v16f){};
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int j = 2 * p + kg;
+    const float bj = (float)(int8_t)(bwv[j >> 2] >> (8 * (j & 3)));
+    const float tj = mok ? a.t[(size_t)col * 16 + j] : 0.0f;
+    lo = __builtin_amdgcn_mfma_f32_32x32x2f32(tj, bj, lo, 0, 0, 0);
+  }
+  const bool conv_col = KIND == SK_IN && a.xc && n >= a.x_off && n < a.x_off + a.cdim;
+  const int c = n - a.x_off;
+  float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f, cb = 0.f;
+  if (conv_col) {
+    const float4 wv = *(const float4*)(a.conv_w + (size_t)c * 4);
+    cw0 = wv.x; cw1 = wv.y; cw2 = wv.z; cw3 = wv.w;
+    cb = a.conv_b[c];
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = 8 * (r >> 2) + 4 * kg + (r & 3);
+    if (m >= a.M || !nok) continue;
+    const int sacc = 2 * acc[r] - a.qsum[m];
+    const float y = (float)sacc * sw * a.s[m] + sb * lo[r];
+    if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
+    float* yp = a.y + (size_t)m * a.ldy + n;
+    if (KIND == SK_OUT) {
+      *yp += y;
+    } else {
+      *yp = y;
+      if (conv_col) {  // one decode token: the conv shift register of channel c
+        float* st = a.conv_state + (size_t)m * a.conv_bstride + c;
+        const float s0 = st[0], s1 = st[a.cdim], s2 = st[2 * a.cdim];
+        const float v = cb + cw0 * s0 + cw1 * s1 + cw2 * s2 + cw3 * y;
+        a.xc[(size_t)m * a.cdim + c] = silu_f(v);
+        st[0] = s1;
+        st[a.cdim] = s2;
+        st[2 * a.cdim] = y;
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_skinny(const SkinnyArgs& a, int kind, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.M > 32 || a.K % 128) return hipErrorInvalidValue;
+  const dim3 grid((a.N + 31) / 32), block(256);
+  switch (kind) {
+    case SK_IN: hipLaunchKernelGGL(gemm_skinny_kernel<SK_IN>, grid, block, 0, st, a); break;
+    case SK_OUT: hipLaunchKernelGGL(gemm_skinny_kernel<SK_OUT>, grid, block, 0, st, a); break;
+    case SK_HEAD: hipLaunchKernelGGL(gemm_skinny_kernel<SK_HEAD>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -341,21 +341,42 @@ dfssm_status ensure_gemm_ws(dfssm_ctx* c, size_t rows) {
 
 // One layer on rows m = b * T + t of the batched workspace (B sequences in
 // state slots 0..B-1, T tokens each, in order).
+// Decode (one token per sequence) of at most 32 sequences uses the skinny
+// GEMM, with the conv shift register in the in_proj epilogue.
+bool skinny_decode(int B, int T) { return T == 1 && B <= 32; }
+
 dfssm_status enqueue_layer_gemm(dfssm_ctx* c, int l, int B, int T, hipStream_t st, int8_t* q1_out,
                                 int8_t* q2_out) {
   auto& w = c->gw;
   const int M = B * T;
+  const bool skinny = skinny_decode(B, T);
   RowsArgs ra{w.h, c->dm, c->lt<float>(l, DFSSM_T_NORM_W), M, c->eps, c->lt<int8_t>(l, DFSSM_T_IN_A),
               c->lt<float>(l, DFSSM_T_IN_SA), w.q, w.s, w.qsum, w.t};
   HIP_TRY(launch_rows_quant(ra, c->dm, st));
   if (q1_out) HIP_TRY(hipMemcpyAsync(q1_out, w.q, (size_t)M * c->dm, hipMemcpyDeviceToDevice, st));
-  GemmArgs gi{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_IN_BITS), c->lt<float>(l, DFSSM_T_IN_SW),
-              c->lt<int8_t>(l, DFSSM_T_IN_B), c->lt<float>(l, DFSSM_T_IN_SB), M, c->dproj, c->dm, w.zx, c->dproj,
-              nullptr};
-  HIP_TRY(launch_bitgemm(gi, GEMM_EPI_STORE, st));
-  ConvSeqArgs ca{w.zx, c->dproj, c->di, w.xc, c->conv + (size_t)l * (c->K - 1) * c->cdim, c->conv_bstride,
-                 c->lt<float>(l, DFSSM_T_CONV_W), c->lt<float>(l, DFSSM_T_CONV_B), B, T, c->cdim};
-  HIP_TRY(launch_conv_seq(ca, st));
+  float* conv_l = c->conv + (size_t)l * (c->K - 1) * c->cdim;
+  if (skinny) {
+    SkinnyArgs si{};
+    si.q = w.q; si.s = w.s; si.qsum = w.qsum; si.t = w.t;
+    si.w = c->lt<uint32_t>(l, DFSSM_T_IN_BITS);
+    si.sw = c->lt<float>(l, DFSSM_T_IN_SW);
+    si.Bm = c->lt<int8_t>(l, DFSSM_T_IN_B);
+    si.sB = c->lt<float>(l, DFSSM_T_IN_SB);
+    si.M = M; si.N = c->dproj; si.K = c->dm;
+    si.y = w.zx; si.ldy = c->dproj;
+    si.xc = w.xc; si.conv_state = conv_l; si.conv_bstride = c->conv_bstride;
+    si.conv_w = c->lt<float>(l, DFSSM_T_CONV_W); si.conv_b = c->lt<float>(l, DFSSM_T_CONV_B);
+    si.x_off = c->di; si.cdim = c->cdim;
+    HIP_TRY(launch_gemm_skinny(si, SK_IN, st));
+  } else {
+    GemmArgs gi{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_IN_BITS), c->lt<float>(l, DFSSM_T_IN_SW),
+                c->lt<int8_t>(l, DFSSM_T_IN_B), c->lt<float>(l, DFSSM_T_IN_SB), M, c->dproj, c->dm, w.zx, c->dproj,
+                nullptr};
+    HIP_TRY(launch_bitgemm(gi, GEMM_EPI_STORE, st));
+    ConvSeqArgs ca{w.zx, c->dproj, c->di, w.xc, conv_l, c->conv_bstride,
+                   c->lt<float>(l, DFSSM_T_CONV_W), c->lt<float>(l, DFSSM_T_CONV_B), B, T, c->cdim};
+    HIP_TRY(launch_conv_seq(ca, st));
+  }
   ScanArgs sa{w.xc, w.zx, c->dproj, 2 * c->di + 2 * c->N, c->lt<float>(l, DFSSM_T_A_LOG),
               c->lt<float>(l, DFSSM_T_DT_BIAS), c->lt<float>(l, DFSSM_T_D),
               c->ssm + (size_t)l * c->H * c->P * c->N, c->ssm_bstride, w.g, B, T, c->H, c->di, c->cdim};
@@ -364,9 +385,21 @@ dfssm_status enqueue_layer_gemm(dfssm_ctx* c, int l, int B, int T, hipStream_t s
               c->lt<float>(l, DFSSM_T_OUT_SA), w.q, w.s, w.qsum, w.t};
   HIP_TRY(launch_rows_quant(rb, c->di, st));
   if (q2_out) HIP_TRY(hipMemcpyAsync(q2_out, w.q, (size_t)M * c->di, hipMemcpyDeviceToDevice, st));
-  GemmArgs go{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_OUT_BITS), c->lt<float>(l, DFSSM_T_OUT_SW),
-              c->lt<int8_t>(l, DFSSM_T_OUT_B), c->lt<float>(l, DFSSM_T_OUT_SB), M, c->dm, c->di, w.h, c->dm, nullptr};
-  HIP_TRY(launch_bitgemm(go, GEMM_EPI_RESIDUAL, st));
+  if (skinny) {
+    SkinnyArgs so{};
+    so.q = w.q; so.s = w.s; so.qsum = w.qsum; so.t = w.t;
+    so.w = c->lt<uint32_t>(l, DFSSM_T_OUT_BITS);
+    so.sw = c->lt<float>(l, DFSSM_T_OUT_SW);
+    so.Bm = c->lt<int8_t>(l, DFSSM_T_OUT_B);
+    so.sB = c->lt<float>(l, DFSSM_T_OUT_SB);
+    so.M = M; so.N = c->dm; so.K = c->di;
+    so.y = w.h; so.ldy = c->dm;
+    HIP_TRY(launch_gemm_skinny(so, SK_OUT, st));
+  } else {
+    GemmArgs go{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_OUT_BITS), c->lt<float>(l, DFSSM_T_OUT_SW),
+                c->lt<int8_t>(l, DFSSM_T_OUT_B), c->lt<float>(l, DFSSM_T_OUT_SB), M, c->dm, c->di, w.h, c->dm, nullptr};
+    HIP_TRY(launch_bitgemm(go, GEMM_EPI_RESIDUAL, st));
+  }
   return DFSSM_OK;
 }
 
@@ -398,8 +431,18 @@ dfssm_status enqueue_step_gemm(dfssm_ctx* c, const int32_t* tok, int tok_stride,
   HIP_TRY(launch_rows_quant(rf, c->dm, st));
   if (tr && tr->qf) HIP_TRY(hipMemcpyAsync(tr->qf, w.q, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st));
   float* lg = logits ? logits : c->logits;
-  HIP_TRY(launch_lm_head(c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), w.q, w.s, c->V,
-                         c->dm, B, lg, st));
+  if (B <= 32 && c->dm % 128 == 0) {
+    SkinnyArgs sh{};
+    sh.q = w.q; sh.s = w.s;
+    sh.w = c->lt<int8_t>(-1, DFSSM_G_EMBED);
+    sh.sw = c->lt<float>(-1, DFSSM_G_EMBED_SCALE);
+    sh.M = B; sh.N = c->V; sh.K = c->dm;
+    sh.y = lg; sh.ldy = c->V;
+    HIP_TRY(launch_gemm_skinny(sh, SK_HEAD, st));
+  } else {
+    HIP_TRY(launch_lm_head(c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), w.q, w.s, c->V,
+                           c->dm, B, lg, st));
+  }
   if (next || out) HIP_TRY(launch_argmax(lg, c->V, B, next ? next : c->next, out, c->counter, st));
   return DFSSM_OK;
 }
@@ -1076,7 +1119,14 @@ dfssm_status dfssm_k_gemm(const uint32_t* d_bits, const float* d_sw, const int8_
   int32_t* qsum = (int32_t*)(tmp + align_up(pl_bytes));
   float* t = (float*)(tmp + align_up(pl_bytes) + align_up(4 * (size_t)M));
   hipError_t e = launch_qprep(d_q, d_s, d_in, M, d_A, d_sA, 16, planes, qsum, t, st);
-  if (e == hipSuccess) {
+  if (e == hipSuccess && M <= 32) {  // the decode-sized kernel
+    SkinnyArgs a{};
+    a.q = d_q; a.s = d_s; a.qsum = qsum; a.t = t;
+    a.w = d_bits; a.sw = d_sw; a.Bm = d_B; a.sB = d_sB;
+    a.M = M; a.N = d_out; a.K = d_in;
+    a.y = d_y; a.ldy = d_out; a.acc = d_acc;
+    e = launch_gemm_skinny(a, SK_IN, st);
+  } else if (e == hipSuccess) {
     GemmArgs a{d_q, d_s, qsum, t, d_bits, d_sw, d_B, d_sB, M, d_out, d_in, d_y, d_out, d_acc};
     e = launch_bitgemm(a, GEMM_EPI_STORE, st);
   }

@@ -264,8 +264,9 @@ dfssm_status dfssm_k_proj(const uint32_t* d_bits, const float* d_sw, const int8_
  * (gist.science summary §2.B/§2.C): r is 16; d_A int8 [16][d_in], d_B int8
  * [d_out][16]; d_q int8 [M][d_in], d_s fp32 [M]; outputs d_acc int32
  * [M][d_out] (or NULL) and d_y fp32 [M][d_out], as for dfssm_k_proj.
- * d_in is 128 * 2^k <= 8192.  Enqueued; uses stream-ordered temporary
- * memory.                                                                   */
+ * d_in is 128 * 2^k <= 8192.  M <= 32 runs the decode-sized kernel (one
+ * 32 x 32 block per workgroup, K split over its waves), larger M the tiled
+ * one.  Enqueued; uses stream-ordered temporary memory.                    */
 dfssm_status dfssm_k_gemm(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
                           const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out, const int8_t* d_q,
                           const float* d_s, int32_t M, int32_t* d_acc, float* d_y, void* stream);
