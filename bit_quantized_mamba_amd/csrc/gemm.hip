@@ -25,26 +25,33 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // rows_quant: one wave per row, four rows per workgroup.  Lane L holds the
-// float4 groups i = 4 L + 256 m (m < K / 256), so every load and store of the
-// row is one coalesced 1 KB access per m.
+// 16-element chunks j = L + 64 mm of the row (chunk j = elements 16 j ..
+// 16 j + 15), so its codes form whole 16-byte words and each LoRA-down row
+// is read as one 16-byte load per chunk.
 // ---------------------------------------------------------------------------
 template <int K>
 __global__ __launch_bounds__(256) void rows_quant_kernel(RowsArgs a) {
-  constexpr int MQ = K / 256;
+  constexpr int NCH = K / 16, MM = (NCH + 63) / 64;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.M) return;  // whole wave leaves together
   const float4* x4 = (const float4*)(a.x + (size_t)row * a.ldx);
   const float4* w4 = (const float4*)a.w;
-  float4 p[MQ];
+  float4 p[MM][4];
   float ss = 0.0f, pm = 0.0f;
 #pragma unroll
-  for (int m = 0; m < MQ; ++m) {
-    const float4 xv = x4[lane + 64 * m];
-    const float4 wv = w4[lane + 64 * m];
-    ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
-    p[m] = make_float4(xv.x * wv.x, xv.y * wv.y, xv.z * wv.z, xv.w * wv.w);
-    pm = fmaxf(pm, fmaxf(fmaxf(fabsf(p[m].x), fabsf(p[m].y)), fmaxf(fabsf(p[m].z), fabsf(p[m].w))));
+  for (int mm = 0; mm < MM; ++mm) {
+    const int j = lane + 64 * mm;
+    const bool live = j < NCH;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 xv = live ? x4[4 * j + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 wv = live ? w4[4 * j + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+      p[mm][i] = make_float4(xv.x * wv.x, xv.y * wv.y, xv.z * wv.z, xv.w * wv.w);
+      pm = fmaxf(pm, fmaxf(fmaxf(fabsf(p[mm][i].x), fabsf(p[mm][i].y)),
+                           fmaxf(fabsf(p[mm][i].z), fabsf(p[mm][i].w))));
+    }
   }
   ss = wave_sum(ss);
   pm = wave_max(pm);
@@ -57,15 +64,20 @@ __global__ __launch_bounds__(256) void rows_quant_kernel(RowsArgs a) {
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return (uint32_t)(uint8_t)(int8_t)(int)r;
   };
-  uint32_t qd[MQ];
+  uint4 qd[MM];
   int qsum = 0;
-  uint32_t* qrow = (uint32_t*)(a.q + (size_t)row * K);
 #pragma unroll
-  for (int m = 0; m < MQ; ++m) {
-    const uint32_t b0 = qz(p[m].x), b1 = qz(p[m].y), b2 = qz(p[m].z), b3 = qz(p[m].w);
-    qd[m] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-    qsum += (int)(int8_t)b0 + (int)(int8_t)b1 + (int)(int8_t)b2 + (int)(int8_t)b3;
-    qrow[lane + 64 * m] = qd[m];
+  for (int mm = 0; mm < MM; ++mm) {
+    uint32_t d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t b0 = qz(p[mm][i].x), b1 = qz(p[mm][i].y), b2 = qz(p[mm][i].z), b3 = qz(p[mm][i].w);
+      d[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      qsum += (int)(int8_t)b0 + (int)(int8_t)b1 + (int)(int8_t)b2 + (int)(int8_t)b3;
+    }
+    qd[mm] = make_uint4(d[0], d[1], d[2], d[3]);
+    const int j = lane + 64 * mm;
+    if (j < NCH) *(uint4*)(a.q + (size_t)row * K + 16 * j) = qd[mm];
   }
   qsum = wave_sum_i(qsum);
   if (lane == 0) {
@@ -77,10 +89,16 @@ __global__ __launch_bounds__(256) void rows_quant_kernel(RowsArgs a) {
   int acc[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const uint32_t* ar = (const uint32_t*)(a.A + (size_t)k * K);
     int v = 0;
 #pragma unroll
-    for (int m = 0; m < MQ; ++m) v = __builtin_amdgcn_sdot4((int)ar[lane + 64 * m], (int)qd[m], v, false);
+    for (int mm = 0; mm < MM; ++mm) {
+      const int j = lane + 64 * mm;
+      const uint4 av = j < NCH ? *(const uint4*)(a.A + (size_t)k * K + 16 * j) : make_uint4(0, 0, 0, 0);
+      v = __builtin_amdgcn_sdot4((int)av.x, (int)qd[mm].x, v, false);
+      v = __builtin_amdgcn_sdot4((int)av.y, (int)qd[mm].y, v, false);
+      v = __builtin_amdgcn_sdot4((int)av.z, (int)qd[mm].z, v, false);
+      v = __builtin_amdgcn_sdot4((int)av.w, (int)qd[mm].w, v, false);
+    }
     acc[k] = v;
   }
 #pragma unroll
@@ -266,6 +284,13 @@ __global__ __launch_bounds__(256) void bitgemm_kernel(GemmArgs a) {
       for (int p = 0; p < 8; ++p)
         lo = __builtin_amdgcn_mfma_f32_32x32x2f32(s_t[(rb + (lane & 31)) * 16 + 2 * p + (lane >> 5)], bcol[p], lo, 0,
                                                    0, 0);
+      // residual values loaded before any store of the block (see the skinny kernel)
+      float prev[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        prev[r] = (EPI == GEMM_EPI_RESIDUAL && m < a.M && nok) ? a.y[(size_t)m * a.ldy + n] : 0.0f;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ml = rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -273,11 +298,7 @@ __global__ __launch_bounds__(256) void bitgemm_kernel(GemmArgs a) {
         if (m < a.M && nok) {
           const int sacc = 2 * acc[i][j][r] - s_qs[ml];
           const float y = (float)sacc * sw * s_s[ml] + sb * lo[r];
-          float* yp = a.y + (size_t)m * a.ldy + n;
-          if (EPI == GEMM_EPI_RESIDUAL)
-            *yp += y;
-          else
-            *yp = y;
+          a.y[(size_t)m * a.ldy + n] = prev[r] + y;
           if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
         }
       }
@@ -314,7 +335,7 @@ hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st) {
 // registers: lane l holds row / column l % 32 and k-half l / 32 of each
 // 32-wide k-step, and 16 scaffold bits become 16 0/1 bytes in registers.
 // ---------------------------------------------------------------------------
-constexpr int kSkinnyUnroll = 8;  // k-steps whose loads are issued together
+constexpr int kSkinnyUnroll = 16;  // k-steps whose loads are issued together
 
 template <int KIND>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
@@ -327,6 +348,44 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
   const int K = a.K, ks = K / 4;              // k slice of this wave
   const int kbeg = wave * ks;
   const int8_t* qrow = a.q + (size_t)(mok ? col : 0) * K + 16 * kg;
+
+  // Operands of the epilogue (wave 0), loaded before the main loop so that
+  // their latency hides under it.  Nothing the epilogue stores is read here
+  // after a store, so no load waits on a possibly aliasing store.
+  const bool conv_col = KIND == SK_IN && a.xc && n >= a.x_off && n < a.x_off + a.cdim;
+  const int c = n - a.x_off;
+  float sm[16], prev[16], w0[16], w1[16], w2[16], tj[8];
+  int qm[16];
+  float sw = 0.f, sb = 0.f, cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f, cb = 0.f;
+  uint4 bq = make_uint4(0, 0, 0, 0);
+  if (wave == 0) {
+    sw = nok ? a.sw[n] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 8 * (r >> 2) + 4 * kg + (r & 3);
+      const bool ok = m < a.M && nok;
+      sm[r] = ok ? a.s[m] : 0.0f;
+      qm[r] = (KIND != SK_HEAD && ok) ? a.qsum[m] : 0;
+      prev[r] = (KIND == SK_OUT && ok) ? a.y[(size_t)m * a.ldy + n] : 0.0f;
+      const bool cv = ok && conv_col;
+      const float* st = a.conv_state + (size_t)m * a.conv_bstride + c;
+      w0[r] = cv ? st[0] : 0.0f;
+      w1[r] = cv ? st[a.cdim] : 0.0f;
+      w2[r] = cv ? st[2 * a.cdim] : 0.0f;
+    }
+    if (KIND != SK_HEAD) {
+      sb = nok ? a.sB[n] : 0.0f;
+      bq = nok ? *(const uint4*)(a.Bm + (size_t)n * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) tj[p] = mok ? a.t[(size_t)col * 16 + 2 * p + kg] : 0.0f;
+    }
+    if (conv_col) {
+      const float4 wv = *(const float4*)(a.conv_w + (size_t)c * 4);
+      cw0 = wv.x; cw1 = wv.y; cw2 = wv.z; cw3 = wv.w;
+      cb = a.conv_b[c];
+    }
+  }
+
   v16i acc = (v16i){};
   const int kend = kbeg + ks;
   for (int k0 = kbeg; k0 < kend; k0 += 32 * kSkinnyUnroll) {
@@ -363,53 +422,40 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
   for (int r = 0; r < 16; ++r) acc[r] += red[0][r][lane] + red[1][r][lane] + red[2][r][lane];
 
   if (KIND == SK_HEAD) {
-    const float sc = nok ? a.sw[n] : 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = 8 * (r >> 2) + 4 * kg + (r & 3);
-      if (m < a.M && nok) a.y[(size_t)m * a.ldy + n] = (float)acc[r] * sc * a.s[m];
+      if (m < a.M && nok) a.y[(size_t)m * a.ldy + n] = (float)acc[r] * sw * sm[r];
     }
     return;
   }
   // LoRA up on the fp32 matrix core: lo[m][n] = sum_j t[m][j] B[n][j]
-  const float sw = nok ? a.sw[n] : 0.0f, sb = nok ? a.sB[n] : 0.0f;
-  const uint4 bq = nok ? *(const uint4*)(a.Bm + (size_t)n * 16) : make_uint4(0, 0, 0, 0);
   const uint32_t bwv[4] = {bq.x, bq.y, bq.z, bq.w};
   v16f lo = (v16f){};
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int j = 2 * p + kg;
     const float bj = (float)(int8_t)(bwv[j >> 2] >> (8 * (j & 3)));
-    const float tj = mok ? a.t[(size_t)col * 16 + j] : 0.0f;
-    lo = __builtin_amdgcn_mfma_f32_32x32x2f32(tj, bj, lo, 0, 0, 0);
-  }
-  const bool conv_col = KIND == SK_IN && a.xc && n >= a.x_off && n < a.x_off + a.cdim;
-  const int c = n - a.x_off;
-  float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f, cb = 0.f;
-  if (conv_col) {
-    const float4 wv = *(const float4*)(a.conv_w + (size_t)c * 4);
-    cw0 = wv.x; cw1 = wv.y; cw2 = wv.z; cw3 = wv.w;
-    cb = a.conv_b[c];
+    lo = __builtin_amdgcn_mfma_f32_32x32x2f32(tj[p], bj, lo, 0, 0, 0);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int m = 8 * (r >> 2) + 4 * kg + (r & 3);
     if (m >= a.M || !nok) continue;
-    const int sacc = 2 * acc[r] - a.qsum[m];
-    const float y = (float)sacc * sw * a.s[m] + sb * lo[r];
+    const int sacc = 2 * acc[r] - qm[r];
+    const float y = (float)sacc * sw * sm[r] + sb * lo[r];
     if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
     float* yp = a.y + (size_t)m * a.ldy + n;
     if (KIND == SK_OUT) {
-      *yp += y;
+      *yp = prev[r] + y;
     } else {
       *yp = y;
       if (conv_col) {  // one decode token: the conv shift register of channel c
         float* st = a.conv_state + (size_t)m * a.conv_bstride + c;
-        const float s0 = st[0], s1 = st[a.cdim], s2 = st[2 * a.cdim];
-        const float v = cb + cw0 * s0 + cw1 * s1 + cw2 * s2 + cw3 * y;
+        const float v = cb + cw0 * w0[r] + cw1 * w1[r] + cw2 * w2[r] + cw3 * y;
         a.xc[(size_t)m * a.cdim + c] = silu_f(v);
-        st[0] = s1;
-        st[a.cdim] = s2;
+        st[0] = w1[r];
+        st[a.cdim] = w2[r];
         st[2 * a.cdim] = y;
       }
     }
@@ -555,9 +601,70 @@ __global__ __launch_bounds__(4 * P) void scan_kernel(ScanArgs a) {
   }
 }
 
+// One decode token per sequence (T = 1), headdim 64, d_state 128.  Workgroup
+// (head, sequence) of 256 threads: thread t owns channels 16 pb + 4 pq + 0..3
+// (pq = t & 3, pb = (t >> 2) & 3) and states 8 ns .. 8 ns + 7 (ns = t >> 4),
+// read and written as float4 along the channels of the [P/16][N][16] block
+// layout (16 lanes cover 256 contiguous bytes).  The sum over states crosses
+// the 16 state segments once, through LDS.
+__global__ __launch_bounds__(256) void scan1_kernel(ScanArgs a) {
+  constexpr int P = 64, N = 128, NPT = 8;
+  __shared__ float red[16][P];
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int pq = t & 3, pb = (t >> 2) & 3, ns = t >> 4;
+  const int p0 = pb * 16 + pq * 4;
+  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;
+  const float* xr = a.xc + (size_t)b * a.cdim;
+  float4 S[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) S[i] = *(const float4*)(stb + ((size_t)(pb * N + ns * NPT + i) * 16 + pq * 4));
+  const float4 xv = *(const float4*)(xr + h * P + p0);
+  const float4 b0 = *(const float4*)(xr + a.d_inner + ns * NPT), b1 = *(const float4*)(xr + a.d_inner + ns * NPT + 4);
+  const float4 c0 = *(const float4*)(xr + a.d_inner + N + ns * NPT),
+               c1 = *(const float4*)(xr + a.d_inner + N + ns * NPT + 4);
+  const float dt = softplus_f(a.zx[(size_t)b * a.ldzx + a.dt_off + h] + a.dt_bias[h]);
+  const float dA = __expf(-dt * __expf(a.A_log[h]));
+  const float bn[NPT] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  const float cn[NPT] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float dx0 = dt * xv.x, dx1 = dt * xv.y, dx2 = dt * xv.z, dx3 = dt * xv.w;
+  float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    float4 v = S[i];
+    v.x = v.x * dA + dx0 * bn[i];
+    v.y = v.y * dA + dx1 * bn[i];
+    v.z = v.z * dA + dx2 * bn[i];
+    v.w = v.w * dA + dx3 * bn[i];
+    S[i] = v;
+    y0 += v.x * cn[i];
+    y1 += v.y * cn[i];
+    y2 += v.z * cn[i];
+    y3 += v.w * cn[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) *(float4*)(stb + ((size_t)(pb * N + ns * NPT + i) * 16 + pq * 4)) = S[i];
+  red[ns][p0 + 0] = y0;
+  red[ns][p0 + 1] = y1;
+  red[ns][p0 + 2] = y2;
+  red[ns][p0 + 3] = y3;
+  __syncthreads();
+  if (t < P) {
+    float yy = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) yy += red[k][t];
+    const float x = xr[h * P + t];
+    const float z = a.zx[(size_t)b * a.ldzx + h * P + t];
+    a.g[(size_t)b * a.d_inner + h * P + t] = (yy + a.D[h] * x) * silu_f(z);
+  }
+}
+
 hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
   const dim3 grid(a.H, a.B);
+  if (a.T == 1 && P == 64 && N == 128) {
+    hipLaunchKernelGGL(scan1_kernel, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (P == 64 && N == 128) hipLaunchKernelGGL((scan_kernel<64, 128>), grid, dim3(256), 0, st, a);
   else if (P == 32 && N == 16) hipLaunchKernelGGL((scan_kernel<32, 16>), grid, dim3(128), 0, st, a);
   else if (P == 64 && N == 64) hipLaunchKernelGGL((scan_kernel<64, 64>), grid, dim3(256), 0, st, a);

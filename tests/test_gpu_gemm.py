@@ -114,6 +114,33 @@ def test_tiny_decode_on_gemm_path(B, steps):
     eng.close()
 
 
+@pytest.mark.parametrize("B", [1, 3])
+def test_1p3b_layer_decode_on_gemm_path(B):
+    # one 1.3B-shaped layer: the decode-sized GEMM (K 2048 / 4096, conv in its
+    # epilogue) and the single-token scan at headdim 64, d_state 128
+    s = synth.LAYER_1P3B
+    seed = synth.SEED_BASE + 5
+    eng = engine(s, max_batch=B)
+    eng.set_path("gemm")
+    eng.load_synthetic(seed)
+    om = oracle.Model(s, synth.gen_model(s, seed))
+    sts = [oracle.State(s) for _ in range(B)]
+    toks = [int(t) for t in synth.gen_tokens(seed, 11, B, s.vocab)]
+    for step in range(6):
+        tr = trace_to_numpy(eng.trace_step(_i32(toks)))
+        for b in range(B):
+            hs, ol, otok = oracle_follow_step(om, sts[b], toks[b], tr, b)
+            assert_close(tr["h"][1, b], hs[1], what=f"h step {step} seq {b}")
+            assert_close(tr["logits"][b], ol, what=f"logits step {step} seq {b}")
+            toks[b] = int(np.argmax(tr["logits"][b]))
+    for b in range(B):
+        conv_g, ssm_g = eng.get_state(b)
+        assert_close(conv_g, sts[b].conv, what=f"conv state seq {b}")
+        assert_close(ssm_g, sts[b].ssm, what=f"ssm state seq {b}")
+    eng.check()
+    eng.close()
+
+
 # ---------------------------------------------------------------------------
 # traced prefill
 # ---------------------------------------------------------------------------
