@@ -230,7 +230,8 @@ class Engine:
         on the persistent kernel) or "gemm" (every decode and prefill on the batched GEMM path)."""
         call("dfssm_set_path", self._h, self.PATHS[path])
 
-    KERNELS = {"in_proj": 0, "ssm": 1, "out_proj": 2, "lm_head": 3, "norm_quant": 4}
+    KERNELS = {"in_proj": 0, "ssm": 1, "out_proj": 2, "lm_head": 3, "norm_quant": 4,
+               "b_rows_in": 5, "b_in_proj": 6, "b_scan": 7, "b_rows_out": 8, "b_out_proj": 9, "b_lm_head": 10}
 
     def time_kernel(self, kernel: str, batch: int = 1, iters: int = 480, stream=None) -> float:
         """Mean microseconds per launch of one decode-step kernel (leaves the state undefined)."""

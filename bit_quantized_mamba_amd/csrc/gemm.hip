@@ -345,41 +345,45 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
   const int col = lane & 31, kg = lane >> 5;
   const int n = n0 + col;
   const bool nok = n < a.N, mok = col < a.M;  // this lane's B column and A row
+  // Out-of-range rows and columns read a valid row and are zeroed by a
+  // select: no load sits behind a branch, so none of them serialises.
+  const int nc = nok ? n : a.N - 1, mc = mok ? col : a.M - 1;
   const int K = a.K, ks = K / 4;              // k slice of this wave
-  const int kbeg = wave * ks;
-  const int8_t* qrow = a.q + (size_t)(mok ? col : 0) * K + 16 * kg;
+  const int kbeg = wave * ks, kend = kbeg + ks;
+  const int8_t* qrow = a.q + (size_t)mc * K + 16 * kg;
 
   // Operands of the epilogue (wave 0), loaded before the main loop so that
-  // their latency hides under it.  Nothing the epilogue stores is read here
-  // after a store, so no load waits on a possibly aliasing store.
+  // their latency hides under it.
   const bool conv_col = KIND == SK_IN && a.xc && n >= a.x_off && n < a.x_off + a.cdim;
-  const int c = n - a.x_off;
+  const int c = min(max(n - a.x_off, 0), a.cdim - 1);
   float sm[16], prev[16], w0[16], w1[16], w2[16], tj[8];
   int qm[16];
   float sw = 0.f, sb = 0.f, cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f, cb = 0.f;
   uint4 bq = make_uint4(0, 0, 0, 0);
   if (wave == 0) {
-    sw = nok ? a.sw[n] : 0.0f;
+    sw = a.sw[nc];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = 8 * (r >> 2) + 4 * kg + (r & 3);
-      const bool ok = m < a.M && nok;
-      sm[r] = ok ? a.s[m] : 0.0f;
-      qm[r] = (KIND != SK_HEAD && ok) ? a.qsum[m] : 0;
-      prev[r] = (KIND == SK_OUT && ok) ? a.y[(size_t)m * a.ldy + n] : 0.0f;
-      const bool cv = ok && conv_col;
-      const float* st = a.conv_state + (size_t)m * a.conv_bstride + c;
-      w0[r] = cv ? st[0] : 0.0f;
-      w1[r] = cv ? st[a.cdim] : 0.0f;
-      w2[r] = cv ? st[2 * a.cdim] : 0.0f;
+      const int m = min(8 * (r >> 2) + 4 * kg + (r & 3), a.M - 1);
+      sm[r] = a.s[m];
+      qm[r] = KIND != SK_HEAD ? a.qsum[m] : 0;
+      prev[r] = KIND == SK_OUT ? a.y[(size_t)m * a.ldy + nc] : 0.0f;
+      if (KIND == SK_IN && a.xc) {
+        const float* st = a.conv_state + (size_t)m * a.conv_bstride + c;
+        w0[r] = st[0];
+        w1[r] = st[a.cdim];
+        w2[r] = st[2 * a.cdim];
+      } else {
+        w0[r] = w1[r] = w2[r] = 0.0f;
+      }
     }
     if (KIND != SK_HEAD) {
-      sb = nok ? a.sB[n] : 0.0f;
-      bq = nok ? *(const uint4*)(a.Bm + (size_t)n * 16) : make_uint4(0, 0, 0, 0);
+      sb = a.sB[nc];
+      bq = *(const uint4*)(a.Bm + (size_t)nc * 16);
 #pragma unroll
-      for (int p = 0; p < 8; ++p) tj[p] = mok ? a.t[(size_t)col * 16 + 2 * p + kg] : 0.0f;
+      for (int p = 0; p < 8; ++p) tj[p] = a.t[(size_t)mc * 16 + 2 * p + kg];
     }
-    if (conv_col) {
+    if (KIND == SK_IN && a.xc) {
       const float4 wv = *(const float4*)(a.conv_w + (size_t)c * 4);
       cw0 = wv.x; cw1 = wv.y; cw2 = wv.z; cw3 = wv.w;
       cb = a.conv_b[c];
@@ -387,27 +391,28 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
   }
 
   v16i acc = (v16i){};
-  const int kend = kbeg + ks;
   for (int k0 = kbeg; k0 < kend; k0 += 32 * kSkinnyUnroll) {
     v4i af[kSkinnyUnroll], bf[kSkinnyUnroll];
     uint32_t bw[kSkinnyUnroll];
 #pragma unroll
     for (int u = 0; u < kSkinnyUnroll; ++u) {
-      const int k = k0 + 32 * u;
-      const bool kin = k < kend;  // uniform
-      af[u] = mok && kin ? *(const v4i*)(qrow + k) : (v4i){};
+      const int k = min(k0 + 32 * u, kend - 32);  // a partial last group re-reads valid data, zeroed below
+      af[u] = *(const v4i*)(qrow + k);
       if (KIND == SK_HEAD)
-        bf[u] = nok && kin ? *(const v4i*)((const int8_t*)a.w + (size_t)n * K + k + 16 * kg) : (v4i){};
+        bf[u] = *(const v4i*)((const int8_t*)a.w + (size_t)nc * K + k + 16 * kg);
       else
-        bw[u] = nok && kin ? ((const uint32_t*)a.w)[(size_t)n * (K / 32) + k / 32] : 0u;
+        bw[u] = ((const uint32_t*)a.w)[(size_t)nc * (K / 32) + k / 32];
     }
 #pragma unroll
     for (int u = 0; u < kSkinnyUnroll; ++u) {
-      if (k0 + 32 * u >= kend) break;
+      const bool live = mok && k0 + 32 * u < kend;
+      if (!live) af[u] = (v4i){};
       if (KIND != SK_HEAD) {
-        const uint32_t h = bw[u] >> (16 * kg);
+        const uint32_t h = nok ? bw[u] >> (16 * kg) : 0u;
         bf[u] = (v4i){(int)spread_nibble(h), (int)spread_nibble(h >> 4), (int)spread_nibble(h >> 8),
                       (int)spread_nibble(h >> 12)};
+      } else if (!nok) {
+        bf[u] = (v4i){};
       }
       acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[u], bf[u], acc, 0, 0, 0);
     }
@@ -435,8 +440,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int j = 2 * p + kg;
-    const float bj = (float)(int8_t)(bwv[j >> 2] >> (8 * (j & 3)));
-    lo = __builtin_amdgcn_mfma_f32_32x32x2f32(tj[p], bj, lo, 0, 0, 0);
+    const float bj = nok ? (float)(int8_t)(bwv[j >> 2] >> (8 * (j & 3))) : 0.0f;
+    lo = __builtin_amdgcn_mfma_f32_32x32x2f32(mok ? tj[p] : 0.0f, bj, lo, 0, 0, 0);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {

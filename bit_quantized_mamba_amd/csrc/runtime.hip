@@ -345,17 +345,18 @@ dfssm_status ensure_gemm_ws(dfssm_ctx* c, size_t rows) {
 // GEMM, with the conv shift register in the in_proj epilogue.
 bool skinny_decode(int B, int T) { return T == 1 && B <= 32; }
 
-dfssm_status enqueue_layer_gemm(dfssm_ctx* c, int l, int B, int T, hipStream_t st, int8_t* q1_out,
-                                int8_t* q2_out) {
+hipError_t b_rows_in(dfssm_ctx* c, int l, int M, hipStream_t st) {
   auto& w = c->gw;
-  const int M = B * T;
-  const bool skinny = skinny_decode(B, T);
   RowsArgs ra{w.h, c->dm, c->lt<float>(l, DFSSM_T_NORM_W), M, c->eps, c->lt<int8_t>(l, DFSSM_T_IN_A),
               c->lt<float>(l, DFSSM_T_IN_SA), w.q, w.s, w.qsum, w.t};
-  HIP_TRY(launch_rows_quant(ra, c->dm, st));
-  if (q1_out) HIP_TRY(hipMemcpyAsync(q1_out, w.q, (size_t)M * c->dm, hipMemcpyDeviceToDevice, st));
+  return launch_rows_quant(ra, c->dm, st);
+}
+
+hipError_t b_in_proj(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
+  auto& w = c->gw;
+  const int M = B * T;
   float* conv_l = c->conv + (size_t)l * (c->K - 1) * c->cdim;
-  if (skinny) {
+  if (skinny_decode(B, T)) {
     SkinnyArgs si{};
     si.q = w.q; si.s = w.s; si.qsum = w.qsum; si.t = w.t;
     si.w = c->lt<uint32_t>(l, DFSSM_T_IN_BITS);
@@ -367,25 +368,37 @@ dfssm_status enqueue_layer_gemm(dfssm_ctx* c, int l, int B, int T, hipStream_t s
     si.xc = w.xc; si.conv_state = conv_l; si.conv_bstride = c->conv_bstride;
     si.conv_w = c->lt<float>(l, DFSSM_T_CONV_W); si.conv_b = c->lt<float>(l, DFSSM_T_CONV_B);
     si.x_off = c->di; si.cdim = c->cdim;
-    HIP_TRY(launch_gemm_skinny(si, SK_IN, st));
-  } else {
-    GemmArgs gi{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_IN_BITS), c->lt<float>(l, DFSSM_T_IN_SW),
-                c->lt<int8_t>(l, DFSSM_T_IN_B), c->lt<float>(l, DFSSM_T_IN_SB), M, c->dproj, c->dm, w.zx, c->dproj,
-                nullptr};
-    HIP_TRY(launch_bitgemm(gi, GEMM_EPI_STORE, st));
-    ConvSeqArgs ca{w.zx, c->dproj, c->di, w.xc, conv_l, c->conv_bstride,
-                   c->lt<float>(l, DFSSM_T_CONV_W), c->lt<float>(l, DFSSM_T_CONV_B), B, T, c->cdim};
-    HIP_TRY(launch_conv_seq(ca, st));
+    return launch_gemm_skinny(si, SK_IN, st);
   }
+  GemmArgs gi{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_IN_BITS), c->lt<float>(l, DFSSM_T_IN_SW),
+              c->lt<int8_t>(l, DFSSM_T_IN_B), c->lt<float>(l, DFSSM_T_IN_SB), M, c->dproj, c->dm, w.zx, c->dproj,
+              nullptr};
+  hipError_t e = launch_bitgemm(gi, GEMM_EPI_STORE, st);
+  if (e != hipSuccess) return e;
+  ConvSeqArgs ca{w.zx, c->dproj, c->di, w.xc, conv_l, c->conv_bstride,
+                 c->lt<float>(l, DFSSM_T_CONV_W), c->lt<float>(l, DFSSM_T_CONV_B), B, T, c->cdim};
+  return launch_conv_seq(ca, st);
+}
+
+hipError_t b_scan(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
+  auto& w = c->gw;
   ScanArgs sa{w.xc, w.zx, c->dproj, 2 * c->di + 2 * c->N, c->lt<float>(l, DFSSM_T_A_LOG),
               c->lt<float>(l, DFSSM_T_DT_BIAS), c->lt<float>(l, DFSSM_T_D),
               c->ssm + (size_t)l * c->H * c->P * c->N, c->ssm_bstride, w.g, B, T, c->H, c->di, c->cdim};
-  HIP_TRY(launch_scan(sa, c->P, c->N, st));
+  return launch_scan(sa, c->P, c->N, st);
+}
+
+hipError_t b_rows_out(dfssm_ctx* c, int l, int M, hipStream_t st) {
+  auto& w = c->gw;
   RowsArgs rb{w.g, c->di, c->lt<float>(l, DFSSM_T_GNORM_W), M, c->eps, c->lt<int8_t>(l, DFSSM_T_OUT_A),
               c->lt<float>(l, DFSSM_T_OUT_SA), w.q, w.s, w.qsum, w.t};
-  HIP_TRY(launch_rows_quant(rb, c->di, st));
-  if (q2_out) HIP_TRY(hipMemcpyAsync(q2_out, w.q, (size_t)M * c->di, hipMemcpyDeviceToDevice, st));
-  if (skinny) {
+  return launch_rows_quant(rb, c->di, st);
+}
+
+hipError_t b_out_proj(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
+  auto& w = c->gw;
+  const int M = B * T;
+  if (skinny_decode(B, T)) {
     SkinnyArgs so{};
     so.q = w.q; so.s = w.s; so.qsum = w.qsum; so.t = w.t;
     so.w = c->lt<uint32_t>(l, DFSSM_T_OUT_BITS);
@@ -394,12 +407,44 @@ dfssm_status enqueue_layer_gemm(dfssm_ctx* c, int l, int B, int T, hipStream_t s
     so.sB = c->lt<float>(l, DFSSM_T_OUT_SB);
     so.M = M; so.N = c->dm; so.K = c->di;
     so.y = w.h; so.ldy = c->dm;
-    HIP_TRY(launch_gemm_skinny(so, SK_OUT, st));
-  } else {
-    GemmArgs go{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_OUT_BITS), c->lt<float>(l, DFSSM_T_OUT_SW),
-                c->lt<int8_t>(l, DFSSM_T_OUT_B), c->lt<float>(l, DFSSM_T_OUT_SB), M, c->dm, c->di, w.h, c->dm, nullptr};
-    HIP_TRY(launch_bitgemm(go, GEMM_EPI_RESIDUAL, st));
+    return launch_gemm_skinny(so, SK_OUT, st);
   }
+  GemmArgs go{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_OUT_BITS), c->lt<float>(l, DFSSM_T_OUT_SW),
+              c->lt<int8_t>(l, DFSSM_T_OUT_B), c->lt<float>(l, DFSSM_T_OUT_SB), M, c->dm, c->di, w.h, c->dm, nullptr};
+  return launch_bitgemm(go, GEMM_EPI_RESIDUAL, st);
+}
+
+// final norm + quantise of the last token row of each sequence, then the LM head
+hipError_t b_head(dfssm_ctx* c, int B, int T, float* lg, int8_t* qf_out, hipStream_t st) {
+  auto& w = c->gw;
+  RowsArgs rf{w.h + (size_t)(T - 1) * c->dm, T * c->dm, c->lt<float>(-1, DFSSM_G_FINAL_NORM), B, c->eps, nullptr,
+              nullptr, w.q, w.s, nullptr, nullptr};
+  hipError_t e = launch_rows_quant(rf, c->dm, st);
+  if (e == hipSuccess && qf_out) e = hipMemcpyAsync(qf_out, w.q, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return e;
+  if (B <= 32 && c->dm % 128 == 0) {
+    SkinnyArgs sh{};
+    sh.q = w.q; sh.s = w.s;
+    sh.w = c->lt<int8_t>(-1, DFSSM_G_EMBED);
+    sh.sw = c->lt<float>(-1, DFSSM_G_EMBED_SCALE);
+    sh.M = B; sh.N = c->V; sh.K = c->dm;
+    sh.y = lg; sh.ldy = c->V;
+    return launch_gemm_skinny(sh, SK_HEAD, st);
+  }
+  return launch_lm_head(c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), w.q, w.s, c->V,
+                        c->dm, B, lg, st);
+}
+
+dfssm_status enqueue_layer_gemm(dfssm_ctx* c, int l, int B, int T, hipStream_t st, int8_t* q1_out,
+                                int8_t* q2_out) {
+  const int M = B * T;
+  HIP_TRY(b_rows_in(c, l, M, st));
+  if (q1_out) HIP_TRY(hipMemcpyAsync(q1_out, c->gw.q, (size_t)M * c->dm, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(b_in_proj(c, l, B, T, st));
+  HIP_TRY(b_scan(c, l, B, T, st));
+  HIP_TRY(b_rows_out(c, l, M, st));
+  if (q2_out) HIP_TRY(hipMemcpyAsync(q2_out, c->gw.q, (size_t)M * c->di, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(b_out_proj(c, l, B, T, st));
   return DFSSM_OK;
 }
 
@@ -426,23 +471,8 @@ dfssm_status enqueue_step_gemm(dfssm_ctx* c, const int32_t* tok, int tok_stride,
     HIP_TRY(hipMemcpyAsync(tr->h + (size_t)c->L * M * c->dm, w.h, sizeof(float) * M * c->dm,
                            hipMemcpyDeviceToDevice, st));
   if (!head) return DFSSM_OK;
-  RowsArgs rf{w.h + (size_t)(T - 1) * c->dm, T * c->dm, c->lt<float>(-1, DFSSM_G_FINAL_NORM), B, c->eps, nullptr,
-              nullptr, w.q, w.s, nullptr, nullptr};
-  HIP_TRY(launch_rows_quant(rf, c->dm, st));
-  if (tr && tr->qf) HIP_TRY(hipMemcpyAsync(tr->qf, w.q, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st));
   float* lg = logits ? logits : c->logits;
-  if (B <= 32 && c->dm % 128 == 0) {
-    SkinnyArgs sh{};
-    sh.q = w.q; sh.s = w.s;
-    sh.w = c->lt<int8_t>(-1, DFSSM_G_EMBED);
-    sh.sw = c->lt<float>(-1, DFSSM_G_EMBED_SCALE);
-    sh.M = B; sh.N = c->V; sh.K = c->dm;
-    sh.y = lg; sh.ldy = c->V;
-    HIP_TRY(launch_gemm_skinny(sh, SK_HEAD, st));
-  } else {
-    HIP_TRY(launch_lm_head(c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), w.q, w.s, c->V,
-                           c->dm, B, lg, st));
-  }
+  HIP_TRY(b_head(c, B, T, lg, tr ? tr->qf : nullptr, st));
   if (next || out) HIP_TRY(launch_argmax(lg, c->V, B, next ? next : c->next, out, c->counter, st));
   return DFSSM_OK;
 }
@@ -986,7 +1016,9 @@ dfssm_status dfssm_time_kernel(dfssm_ctx* c, int32_t kernel, int32_t B, int32_t 
   if (v != DFSSM_OK) return v;
   if ((v = check_B(c, B)) != DFSSM_OK) return v;
   if (iters < 1 || !avg_us) return fail(DFSSM_E_INVALID, "iters must be >= 1 and avg_us non-null");
-  if (kernel < DFSSM_K_IN_PROJ || kernel > DFSSM_K_NORM_QUANT) return fail(DFSSM_E_INVALID, "unknown kernel id");
+  if (kernel < DFSSM_K_IN_PROJ || kernel > DFSSM_K_B_LM_HEAD) return fail(DFSSM_E_INVALID, "unknown kernel id");
+  const bool batched = kernel >= DFSSM_K_B_ROWS_IN;
+  if (batched && (v = ensure_gemm_ws(c, B)) != DFSSM_OK) return v;
   hipStream_t st = S(stream);
   auto launch = [&](int i) -> hipError_t {
     const int l = i % c->L;
@@ -995,11 +1027,24 @@ dfssm_status dfssm_time_kernel(dfssm_ctx* c, int32_t kernel, int32_t B, int32_t 
       case DFSSM_K_SSM: return ssm_step(c, l, B, st);
       case DFSSM_K_OUT_PROJ: return out_proj(c, l, B, st);
       case DFSSM_K_LM_HEAD: return lm_head(c, B, c->logits, st);
-      default: return norm_quant_in(c, l, B, st);
+      case DFSSM_K_NORM_QUANT: return norm_quant_in(c, l, B, st);
+      case DFSSM_K_B_ROWS_IN: return b_rows_in(c, l, B, st);
+      case DFSSM_K_B_IN_PROJ: return b_in_proj(c, l, B, 1, st);
+      case DFSSM_K_B_SCAN: return b_scan(c, l, B, 1, st);
+      case DFSSM_K_B_ROWS_OUT: return b_rows_out(c, l, B, st);
+      case DFSSM_K_B_OUT_PROJ: return b_out_proj(c, l, B, 1, st);
+      default: return b_head(c, B, 1, c->logits, nullptr, st);
     }
   };
-  // operands of the in_proj / LM head kernels come from the norm kernel
-  HIP_TRY(norm_quant_in(c, 0, B, st));
+  // operands of the projection / LM head kernels come from the norm kernels
+  if (batched) {
+    HIP_TRY(b_rows_in(c, 0, B, st));
+    HIP_TRY(b_in_proj(c, 0, B, 1, st));
+    HIP_TRY(b_scan(c, 0, B, 1, st));
+    HIP_TRY(b_rows_out(c, 0, B, st));
+  } else {
+    HIP_TRY(norm_quant_in(c, 0, B, st));
+  }
   for (int i = 0; i < 3; ++i) HIP_TRY(launch(i));
   hipEvent_t e0, e1;
   HIP_TRY(hipEventCreate(&e0));

@@ -214,11 +214,19 @@ dfssm_status dfssm_trace_prefill(dfssm_ctx* ctx, const int32_t* d_tok, int32_t B
  * Leaves the recurrent state and the workspace undefined: reset the state
  * before decoding again.                                                   */
 enum {
+  /* per-layer GEMV path */
   DFSSM_K_IN_PROJ = 0,    /* norm-quantised input -> 1-bit GEMV + LoRA + conv epilogue */
   DFSSM_K_SSM = 1,        /* SSM state update + gate                                  */
   DFSSM_K_OUT_PROJ = 2,   /* 1-bit GEMV + LoRA + residual                             */
   DFSSM_K_LM_HEAD = 3,    /* tied int8 LM head GEMV                                   */
-  DFSSM_K_NORM_QUANT = 4  /* RMSNorm + quantise + operand prep of the in_proj input    */
+  DFSSM_K_NORM_QUANT = 4, /* RMSNorm + quantise + operand prep of the in_proj input    */
+  /* batched path, one decode token for each of B sequences */
+  DFSSM_K_B_ROWS_IN = 5,   /* RMSNorm + quantise + LoRA down of the residual rows       */
+  DFSSM_K_B_IN_PROJ = 6,   /* scaffold + LoRA GEMM of in_proj (+ conv)                  */
+  DFSSM_K_B_SCAN = 7,      /* SSM state update + gate                                   */
+  DFSSM_K_B_ROWS_OUT = 8,  /* gated RMSNorm + quantise + LoRA down                      */
+  DFSSM_K_B_OUT_PROJ = 9,  /* scaffold + LoRA GEMM of out_proj + residual               */
+  DFSSM_K_B_LM_HEAD = 10   /* final norm + int8 LM head                                 */
 };
 dfssm_status dfssm_time_kernel(dfssm_ctx* ctx, int32_t kernel, int32_t B, int32_t iters, float* avg_us,
                                void* stream);
