@@ -58,6 +58,18 @@ __device__ __forceinline__ KArgs kargs() {
   return (KArgs)v;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences
+// global memory, which on this target waits for every outstanding vector
+// memory operation -- every prefetch in flight -- at every barrier.  No
+// barrier here publishes global memory to the workgroup: values that cross
+// threads go through LDS, and global data (weights, state) is prefetched into
+// the registers of the thread that uses it.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ bool aborted(const int* flag) {
   return __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
@@ -124,25 +136,9 @@ __device__ bool gather(const uint64_t* box, int n, unsigned e, float* dst, int* 
   } else {
     *s_stop = 1;
   }
-  __syncthreads();
+  wg_barrier();
   const bool stop = *s_stop != 0;
   return !stop;
-}
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glob_void_t;
-
-// Asynchronous copy of nchunks 16-byte chunks (nchunks % 64 == 0) from global
-// memory into LDS, chunk f -> lds[f], without passing through registers.  The
-// data is in LDS once this thread's earlier loads have completed (vmcnt) and
-// the workgroup has synchronised.
-__device__ __forceinline__ void lds_prefetch(const uint4* src, uint4* lds, int nchunks) {
-  const int lane = threadIdx.x & 63;
-  for (int m = 0; m * kPT < nchunks; ++m) {
-    const int f0 = (threadIdx.x - lane) + m * kPT;  // first chunk of this wave's batch
-    if (f0 < nchunks)
-      __builtin_amdgcn_global_load_lds((glob_void_t*)(src + f0 + lane), (lds_void_t*)(lds + f0), 16, 0, 0);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -175,7 +171,7 @@ __device__ float p_norm_quant(const float* xs, const float (&wr)[MW], int n, flo
     red[wave] = ss;
     red[kPW + wave] = pm;
   }
-  __syncthreads();
+  wg_barrier();
   float tss = 0.0f, tpm = 0.0f;
 #pragma unroll
   for (int v = 0; v < kPW; ++v) {
@@ -195,35 +191,34 @@ __device__ float p_norm_quant(const float* xs, const float (&wr)[MW], int n, flo
       qs[i] = (int8_t)(int)rq;
     }
   }
-  __syncthreads();
+  wg_barrier();
   return amax > 0.0f ? amax / 127.0f : 0.0f;
 }
 
-// LoRA down-projection, rank 16, A staged in LDS as 16-byte chunks (C = n/16
-// per row).  16 lanes per row: thread t takes row k = t/16 and chunks
-// c = t%16 + 16*m, sums them locally, then a 16-lane DPP reduction.
-// tout[k] = float(sum_i A[k][i] q_i) * sA[k] * s;  sA_row = sA[t/16].
+// LoRA down-projection, rank 16.  16 lanes per row: thread t takes row
+// k = t/16 and the 16-byte chunks c = t%16 + 16*m of that row (C = n/16 per
+// row), prefetched into registers (av[m]); local sums, then a 16-lane DPP
+// reduction.  tout[k] = float(sum_i A[k][i] q_i) * sA[k] * s;  sA_row = sA[t/16].
 template <int MC>
-__device__ void p_lora_down(const uint4* alds, int n, const int8_t* qs, float sA_row, float s, float* tout) {
+__device__ void p_lora_down(const uint4 (&av)[MC], int n, const int8_t* qs, float sA_row, float s, float* tout) {
   const int k = threadIdx.x >> 4, c0 = threadIdx.x & 15;
   const int C = n >> 4;
   const uint4* q4 = (const uint4*)qs;
-  const uint4* ar = alds + (size_t)k * C;
   int acc = 0;
 #pragma unroll
   for (int m = 0; m < MC; ++m) {
     const int c = c0 + 16 * m;
     if (c < C) {
-      const uint4 av = ar[c], q = q4[c];
-      acc = __builtin_amdgcn_sdot4((int)av.x, (int)q.x, acc, false);
-      acc = __builtin_amdgcn_sdot4((int)av.y, (int)q.y, acc, false);
-      acc = __builtin_amdgcn_sdot4((int)av.z, (int)q.z, acc, false);
-      acc = __builtin_amdgcn_sdot4((int)av.w, (int)q.w, acc, false);
+      const uint4 q = q4[c];
+      acc = __builtin_amdgcn_sdot4((int)av[m].x, (int)q.x, acc, false);
+      acc = __builtin_amdgcn_sdot4((int)av[m].y, (int)q.y, acc, false);
+      acc = __builtin_amdgcn_sdot4((int)av[m].z, (int)q.z, acc, false);
+      acc = __builtin_amdgcn_sdot4((int)av[m].w, (int)q.w, acc, false);
     }
   }
   acc = group_sum_i(acc, 16);
   if (c0 == 0) tout[k] = (float)acc * sA_row * s;
-  __syncthreads();
+  wg_barrier();
 }
 
 
@@ -278,13 +273,24 @@ __device__ __forceinline__ void load_codes(const int8_t* qs, int j, uint32_t (&q
     qd[4 * k + 3] = v.w;
   }
 }
-__device__ __forceinline__ float lora_up(const uint4 b, const float* t) {
-  // sum_k B[k] t[k] over the 16 int8 of one LoRA up row, k in order
-  const uint32_t wv[4] = {b.x, b.y, b.z, b.w};
-  float lo = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) lo += (float)(int8_t)(wv[k >> 2] >> (8 * (k & 3))) * t[k];
-  return lo;
+// Marks a prefetched register value as used here: the compiler cannot move
+// work on it (a conversion, say) up to the load, where it would make the
+// prefetch wait for its own data.
+__device__ __forceinline__ int at_use(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// float sum over aligned groups of U lanes, the same DPP pattern (and result
+// lanes) as group_sum_i
+__device__ __forceinline__ float group_sum_f(float v, int U) {
+  if (U >= 2) v += dpp_f<kDppQuadSwap1>(v);
+  if (U >= 4) v += dpp_f<kDppQuadSwap2>(v);
+  if (U >= 8) v += dpp_f<kDppRowHalfMirror>(v);
+  if (U >= 16) v += dpp_f<kDppRowMirror>(v);
+  if (U >= 32) v += dpp_f<kDppRowBcast15, 0xA>(v);
+  if (U >= 64) v += dpp_f<kDppRowBcast31, 0x8>(v);
+  return v;
 }
 
 // (value, index) argmax over the wave, larger value first, then lower index
@@ -334,6 +340,8 @@ struct PShape {
   static constexpr int UO = DI / 128, RPPO = 64 / UO, NGO_T = (OUT_PER + RPPO - 1) / RPPO,
                        NGO = (NGO_T + kPW - 1) / kPW;
   static constexpr int MW1 = DM / kPT, MW2 = DI / kPT;
+  // LoRA-up ranks per lane of a row group (lane j takes ranks j, j + U, ...)
+  static constexpr int RLI = (16 + UI - 1) / UI, RLO = (16 + UO - 1) / UO;
   static constexpr int MC1 = (DM / 16 + 15) / 16, MC2 = (DI / 16 + 15) / 16;
   static constexpr int NST = (NS + 63) / 64;
   static constexpr int CH = DM / 16, LH = CH < 64 ? CH : 64, MH = CH / LH, RPPH = 64 / LH, STEPH = kPW * RPPH;
@@ -380,11 +388,9 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
   int* s_stop = (int*)(red + 2 * kPW);          // [1]
   int* s_tok = s_stop + 1;                      // [1]
   float* s_arg = (float*)(s_tok + 2);           // [2*kPW]
-  uint4* ains = (uint4*)(((uintptr_t)(s_arg + 2 * kPW) + 15) & ~(uintptr_t)15);  // [16 * DM/16] LoRA-down A, in_proj
-  uint4* aouts = ains + 16 * (DM / 16);         // [16 * DI/16] LoRA-down A, out_proj
   if (threadIdx.x == 0) *s_stop = 0;
   for (int f = threadIdx.x; f < 256 * kLutCopies; f += kPT) lut[f] = sign_entry((uint32_t)(f / kLutCopies));
-  __syncthreads();
+  wg_barrier();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint2* lut_l = lut + (lane % kLutCopies);
@@ -415,17 +421,20 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
   uint4 win[S::NGI];
   float nw[S::MW1];
   float isw[S::NGI], isb[S::NGI];
-  uint4 ib[S::NGI];
+  int ib[S::NGI][S::RLI];  // LoRA-up weights of this lane's ranks (converted at use: a conversion
+                           // here would make the prefetch wait for its own load)
   float cw[4], cb, cst[3];
   float sAi;
+  uint4 ain[S::MC1];  // LoRA-down A chunks of this thread (row t/16)
   // ---- registers prefetched for phases S and B (SSM, out_proj) of a layer
   uint4 wout[S::NGO];
   float gw[S::MW2];
   float osw[S::NGO], osb[S::NGO];
-  uint4 ob[S::NGO];
+  int ob[S::NGO][S::RLO];
   float4 st[S::NST];  // state float4 (n = lane + 64 m, channels 4*wave ..) of the block [NS][16]
   float dtb, alog, dval;
   float sAo;
+  uint4 aout[S::MC2];
 
   auto lp = [&](int l, int k) -> const char* { return wb + (size_t)l * S::LSTRIDE + S::OFF(k); };
 
@@ -441,15 +450,25 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       const bool live = g < S::NGI_T && k < S::NROWS;
       const int row = live ? in_row(k) : 0;
       win[m] = live ? b4[(size_t)row * S::UI + ji] : make_uint4(0, 0, 0, 0);
-      const bool lead = live && lead_i;
-      isw[m] = lead ? sw[row] : 0.0f;
-      isb[m] = lead ? sb[row] : 0.0f;
-      ib[m] = lead ? *(const uint4*)(bm + (size_t)row * 16) : make_uint4(0, 0, 0, 0);
+      isw[m] = live ? sw[row] : 0.0f;
+      isb[m] = live ? sb[row] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < S::RLI; ++r) {
+        const int kk = ji + S::UI * r;
+        ib[m][r] = live && kk < 16 ? (int)bm[(size_t)row * 16 + kk] : 0;
+      }
     }
     const float* nwp = (const float*)lp(l, DFSSM_PK_NORM_W);
 #pragma unroll
     for (int m = 0; m < S::MW1; ++m) nw[m] = nwp[threadIdx.x + m * kPT];
-    lds_prefetch((const uint4*)lp(l, DFSSM_PK_IN_A), ains, 16 * (DM / 16));
+    {
+      const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_IN_A) + (size_t)(threadIdx.x >> 4) * (DM / 16);
+#pragma unroll
+      for (int m = 0; m < S::MC1; ++m) {
+        const int c = (threadIdx.x & 15) + 16 * m;
+        ain[m] = c < DM / 16 ? A4[c] : make_uint4(0, 0, 0, 0);
+      }
+    }
     sAi = ((const float*)lp(l, DFSSM_PK_IN_SA))[threadIdx.x >> 4];
     if (conv_thread) {
       const float* wc = (const float*)lp(l, DFSSM_PK_CONV_W) + (size_t)conv_c * 4;
@@ -471,15 +490,25 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       const bool live = g < S::NGO_T && k < S::OUT_PER;
       const int row = w * S::OUT_PER + k;
       wout[m] = live ? b4[(size_t)row * S::UO + jo] : make_uint4(0, 0, 0, 0);
-      const bool lead = live && lead_o;
-      osw[m] = lead ? sw[row] : 0.0f;
-      osb[m] = lead ? sb[row] : 0.0f;
-      ob[m] = lead ? *(const uint4*)(bm + (size_t)row * 16) : make_uint4(0, 0, 0, 0);
+      osw[m] = live ? sw[row] : 0.0f;
+      osb[m] = live ? sb[row] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < S::RLO; ++r) {
+        const int kk = jo + S::UO * r;
+        ob[m][r] = live && kk < 16 ? (int)bm[(size_t)row * 16 + kk] : 0;
+      }
     }
     const float* gwp = (const float*)lp(l, DFSSM_PK_GNORM_W);
 #pragma unroll
     for (int m = 0; m < S::MW2; ++m) gw[m] = gwp[threadIdx.x + m * kPT];
-    lds_prefetch((const uint4*)lp(l, DFSSM_PK_OUT_A), aouts, 16 * (DI / 16));
+    {
+      const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_OUT_A) + (size_t)(threadIdx.x >> 4) * (DI / 16);
+#pragma unroll
+      for (int m = 0; m < S::MC2; ++m) {
+        const int c = (threadIdx.x & 15) + 16 * m;
+        aout[m] = c < DI / 16 ? A4[c] : make_uint4(0, 0, 0, 0);
+      }
+    }
     sAo = ((const float*)lp(l, DFSSM_PK_OUT_SA))[threadIdx.x >> 4];
     const float4* s4 = (const float4*)(a.ssm + (size_t)l * S::H * HP * NS + (size_t)w * NS * 16);
 #pragma unroll
@@ -501,6 +530,11 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     }
   };
 
+  // The next operands are prefetched just before a hop: the wave would idle
+  // while polling anyway, and a burst of loads issued inside a compute phase
+  // stalls that phase's instruction stream once the memory queue is full.
+  // (The hop's polls then also wait for the prefetch to land: the vector
+  // memory counter completes in order.)
   load_A(0);
   load_B(0);
   const int T = a.n_tokens;
@@ -522,7 +556,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         const int i = threadIdx.x + m * kPT;
         hs[i] = (float)er[i] * sc;
       }
-      __syncthreads();
+      wg_barrier();
     }
     for (int l = 0; l < Lm && ok; ++l) {
       prof(t, l, 0);
@@ -545,22 +579,33 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         if (tq && w == 0)
           for (int i = threadIdx.x; i < DM; i += kPT) tq[(size_t)l * DM + i] = qs[i];
       }
-      p_lora_down<S::MC1>(ains, DM, qs, sAi, s1, tls);
+      p_lora_down<S::MC1>(ain, DM, qs, sAi, s1, tls);
       prof(t, l, 3);
       {
+        // Every row group is computed (a wave's unused group has zero weights
+        // and is not stored), so the table lookups of all groups are in flight
+        // together.  The LoRA-up term is spread over the row's lanes.
         uint32_t qd[32];
         load_codes(qs, ji, qd);
+        float tl[S::RLI];
+#pragma unroll
+        for (int r = 0; r < S::RLI; ++r) tl[r] = ji + S::UI * r < 16 ? tls[ji + S::UI * r] : 0.0f;
+        int part[S::NGI];
+#pragma unroll
+        for (int m = 0; m < S::NGI; ++m) part[m] = p_sign_dot(win[m], qd, lut_l);
 #pragma unroll
         for (int m = 0; m < S::NGI; ++m) {
+          const int acc = group_sum_i(part[m], S::UI);
+          float lo = 0.0f;
+#pragma unroll
+          for (int r = 0; r < S::RLI; ++r) lo += (float)at_use(ib[m][r]) * tl[r];
+          lo = group_sum_f(lo, S::UI);
           const int g = wave + m * kPW;
-          if (g < S::NGI_T) {  // uniform per wave
-            const int acc = group_sum_i(p_sign_dot(win[m], qd, lut_l), S::UI);
-            const int k = g * S::RPPI + subi;
-            if (lead_i && k < S::NROWS) rowv[k] = (float)acc * isw[m] * s1 + isb[m] * lora_up(ib[m], tls);
-          }
+          const int k = g * S::RPPI + subi;
+          if (lead_i && g < S::NGI_T && k < S::NROWS) rowv[k] = (float)acc * isw[m] * s1 + isb[m] * lo;
         }
       }
-      __syncthreads();
+      wg_barrier();
       prof(t, l, 4);
       if (conv_thread) {
         const float y = rowv[conv_k];
@@ -568,26 +613,24 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         const float xv = silu_f(v);
         rowv[conv_k] = xv;
         if (conv_k >= 33) publish(bcbox, 2 * NS, conv_c - DI, xv, e);
-        cst[0] = cst[1];  // shifted window, written back after the next hop
+        cst[0] = cst[1];  // shifted window, written back after the B/C hop
         cst[1] = cst[2];
         cst[2] = y;
       }
       prof(t, l, 5);
       // keep this layer's new conv window: load_A below refills cst for the next layer
-      float cst_prev[3] = {cst[0], cst[1], cst[2]};
-      // the next layer's phase-A operands stream in during the two hops below
-      // (after the last layer: layer 0 of the next token)
-      load_A(l + 1 < Lm ? l + 1 : 0);
+      const float cst_new[3] = {cst[0], cst[1], cst[2]};
+      load_A(l + 1 < Lm ? l + 1 : 0);  // after the last layer: layer 0 of the next token
       ok = gather<(2 * NS + kPT - 1) / kPT>(bcbox, 2 * NS, e, bcs, a.abort_flag, s_stop);
       ++e;
       if (!ok) break;
       prof(t, l, 6);
-      // stores go out after the hop: a hop's polling load waits for every earlier memory operation
+      // stores go out after the hop, for the same reason as the prefetches
       if (conv_thread) {
         float* cs = a.conv + (size_t)l * 3 * CDIM;
-        cs[conv_c] = cst_prev[0];
-        cs[CDIM + conv_c] = cst_prev[1];
-        cs[2 * CDIM + conv_c] = cst_prev[2];
+        cs[conv_c] = cst_new[0];
+        cs[CDIM + conv_c] = cst_new[1];
+        cs[2 * CDIM + conv_c] = cst_new[2];
       }
       // ---- phase S: SSM on the state block [hd][j*16 .. +16][0 .. NS), gate.
       // Wave v owns channels 4v .. 4v+3, its lanes the state rows n = lane + 64 m.
@@ -638,6 +681,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
           if (n < NS) s4[n * 4 + wave] = st[m];
         }
       }
+
       // ---- phase B: gated norm, quantise, LoRA down, 1-bit GEMV of own rows, residual
       {
         const float s2 = p_norm_quant<S::MW2>(gs, gw, DI, a.eps, qs, red);
@@ -646,26 +690,34 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
           if (tq && w == 0)
             for (int i = threadIdx.x; i < DI; i += kPT) tq[(size_t)l * DI + i] = qs[i];
         }
-        p_lora_down<S::MC2>(aouts, DI, qs, sAo, s2, tls);
+        p_lora_down<S::MC2>(aout, DI, qs, sAo, s2, tls);
         uint32_t qd[32];
         load_codes(qs, jo, qd);
+        float tl[S::RLO];
+#pragma unroll
+        for (int r = 0; r < S::RLO; ++r) tl[r] = jo + S::UO * r < 16 ? tls[jo + S::UO * r] : 0.0f;
+        int part[S::NGO];
+#pragma unroll
+        for (int m = 0; m < S::NGO; ++m) part[m] = p_sign_dot(wout[m], qd, lut_l);
 #pragma unroll
         for (int m = 0; m < S::NGO; ++m) {
+          const int acc = group_sum_i(part[m], S::UO);
+          float lo = 0.0f;
+#pragma unroll
+          for (int r = 0; r < S::RLO; ++r) lo += (float)at_use(ob[m][r]) * tl[r];
+          lo = group_sum_f(lo, S::UO);
           const int g = wave + m * kPW;
-          if (g < S::NGO_T) {
-            const int acc = group_sum_i(p_sign_dot(wout[m], qd, lut_l), S::UO);
-            const int k = g * S::RPPO + subo;
-            if (lead_o && k < S::OUT_PER) {
-              const int row = w * S::OUT_PER + k;
-              const float y = (float)acc * osw[m] * s2 + osb[m] * lora_up(ob[m], tls);
-              publish(hbox, DM, row, hs[row] + y, e);
-            }
+          const int k = g * S::RPPO + subo;
+          if (lead_o && g < S::NGO_T && k < S::OUT_PER) {
+            const int row = w * S::OUT_PER + k;
+            const float y = (float)acc * osw[m] * s2 + osb[m] * lo;
+            publish(hbox, DM, row, hs[row] + y, e);
           }
         }
       }
       prof(t, l, 9);
       load_B(l + 1 < Lm ? l + 1 : 0);
-      __syncthreads();
+      wg_barrier();
     }
     if (!ok) break;
     // ---- final norm + LM head + argmax
@@ -757,7 +809,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         s_arg[wave] = best;
         ((int*)s_arg)[kPW + wave] = bidx;
       }
-      __syncthreads();
+      wg_barrier();
       if (threadIdx.x == 0) {
         for (int wv = 1; wv < kPW; ++wv) argmax_step(best, bidx, s_arg[wv], ((int*)s_arg)[kPW + wv]);
         // argmax candidates: value word and index word per workgroup
@@ -784,7 +836,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
           if (w == 0 && to) to[t] = bidx;
         }
       }
-      __syncthreads();
+      wg_barrier();
       tok = *s_tok;
       prof(t, Lm, 4);
     }
@@ -806,7 +858,7 @@ using Shape1p3b = PShape<2048, 4096, 128, 64>;
 static size_t lds_bytes(int dm, int di, int ns) {
   const int mx = dm > di ? dm : di;
   return (size_t)dm * 4 + (size_t)di * 4 + (size_t)mx + 256 * kLutCopies * 8 + (size_t)2 * ns * 4 + 16 * 4 +
-         kMaxInRows * 4 + 2 * kPW * 4 + 16 + 2 * kPW * 4 + 16 + (size_t)16 * (dm + di);
+         kMaxInRows * 4 + 2 * kPW * 4 + 16 + 2 * kPW * 4 + 16;
 }
 
 template <class S>
