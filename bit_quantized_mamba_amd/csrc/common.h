@@ -10,10 +10,18 @@ namespace dfssm {
 // device helpers
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+__device__ __forceinline__ float silu_f(float v) { return __fdividef(v, 1.0f + __expf(-v)); }
+
+// log(1 + x) for x >= 0 from the natural log of u = fl(1 + x): log(u) * x / (u - 1)
+// corrects the rounding of 1 + x (D. Goldberg, "What every computer scientist
+// should know about floating-point arithmetic", 1991, Theorem 4).
+__device__ __forceinline__ float log1p_pos(float x) {
+  const float u = 1.0f + x;
+  return u == 1.0f ? x : __logf(u) * __fdividef(x, u - 1.0f);
+}
 
 // softplus with the usual linear branch above 20 (log1p(e^a) - a < 2.1e-9 there)
-__device__ __forceinline__ float softplus_f(float a) { return a > 20.0f ? a : log1pf(__expf(a)); }
+__device__ __forceinline__ float softplus_f(float a) { return a > 20.0f ? a : log1p_pos(__expf(a)); }
 
 // ---------------------------------------------------------------------------
 // cross-lane reductions on DPP (data movement inside the VALU; no LDS round

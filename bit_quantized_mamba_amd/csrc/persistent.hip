@@ -661,6 +661,8 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         y1 = wave_sum(y1);
         y2 = wave_sum(y2);
         y3 = wave_sum(y3);
+        // (one store instruction per replica: writing all replicas with one
+        // instruction from 32 lanes measured ~5 % slower per token)
         if (lane < 4) {
           const int c = wave * 4 + lane;  // channel within the slice
           const float y = (lane == 0 ? y0 : lane == 1 ? y1 : lane == 2 ? y2 : y3) + dval * rowv[16 + c];
