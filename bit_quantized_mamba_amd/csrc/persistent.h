@@ -22,7 +22,8 @@ struct PersistArgs {
   const float* final_norm;
   float* conv;  // sequence slot 0: [n_layer][d_conv-1][conv_dim]
   float* ssm;   // sequence slot 0: [n_layer][H][P/16][N][16]
-  // mailboxes, one block: h [8][d_model] | B,C [8][2 d_state] | g [8][d_inner] | argmax [8][2 grid]
+  // mailboxes, one block (R replicas each): h [R][d_model] | B,C [R][2 d_state] | g [R][d_inner] |
+  // argmax [R][2 grid]
   uint64_t* boxes;
   unsigned epoch0;  // first epoch of this launch (host-assigned, never reused)
   int* abort_flag;
