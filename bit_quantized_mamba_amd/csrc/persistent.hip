@@ -361,6 +361,7 @@ struct PShape {
   static constexpr size_t LSTRIDE = OFF(19);
   static_assert(2 * NS % G == 0 && DM % G == 0 && DM % kPT == 0 && DI % kPT == 0, "unsupported shape");
   static_assert(NROWS <= kMaxInRows, "too many in_proj rows per workgroup");
+  static_assert(NBC <= RPPI, "the B/C rows must sit in row group 0 of wave 0");
 };
 
 constexpr int kHeadDepth = 8;  // LM-head rows in flight per wave
@@ -402,19 +403,27 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
   uint64_t* const gbox = bcbox + kR * 2 * NS;
   uint64_t* const abox = gbox + kR * DI;
 
+  // own in_proj rows, B/C first: their conv outputs are published while the
+  // other rows are still being computed
+  constexpr int KZ = S::NBC, KX = S::NBC + 16, KDT = S::NBC + 32;
   auto in_row = [&](int k) -> int {
-    if (k < 16) return hd * HP + j * 16 + k;                 // z
-    if (k < 32) return DI + hd * HP + j * 16 + (k - 16);     // x
-    if (k == 32) return 2 * DI + 2 * NS + hd;                // dt
-    return 2 * DI + (w + (k - 33) * G);                      // B/C
+    if (k < KZ) return 2 * DI + (w + k * G);                  // B/C
+    if (k < KX) return hd * HP + j * 16 + (k - KZ);           // z
+    if (k < KDT) return DI + hd * HP + j * 16 + (k - KX);     // x
+    return 2 * DI + 2 * NS + hd;                              // dt
   };
 
   const int ji = lane & (S::UI - 1), subi = lane / S::UI;
   const bool lead_i = lane == group_sum_lane(subi * S::UI, S::UI);
   const int jo = lane & (S::UO - 1), subo = lane / S::UO;
   const bool lead_o = lane == group_sum_lane(subo * S::UO, S::UO);
-  const bool conv_thread = threadIdx.x < 16 + S::NBC;
-  const int conv_k = threadIdx.x < 16 ? 16 + threadIdx.x : 33 + (threadIdx.x - 16);
+  // conv threads: the lane that reduces B/C row k (< NBC, row group 0 of wave
+  // 0) convolves and publishes it right away; lanes 0..15 of wave 1 convolve
+  // the 16 x channels after the GEMV
+  const bool bc_thread = wave == 0 && lead_i && subi < S::NBC;
+  const bool x_thread = wave == 1 && lane < 16;
+  const bool conv_thread = bc_thread || x_thread;
+  const int conv_k = bc_thread ? subi : KX + (lane & 15);
   const int conv_c = conv_thread ? in_row(conv_k) - DI : 0;
 
   // ---- registers prefetched for phase A (in_proj) of a layer
@@ -461,14 +470,6 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     const float* nwp = (const float*)lp(l, DFSSM_PK_NORM_W);
 #pragma unroll
     for (int m = 0; m < S::MW1; ++m) nw[m] = nwp[threadIdx.x + m * kPT];
-    {
-      const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_IN_A) + (size_t)(threadIdx.x >> 4) * (DM / 16);
-#pragma unroll
-      for (int m = 0; m < S::MC1; ++m) {
-        const int c = (threadIdx.x & 15) + 16 * m;
-        ain[m] = c < DM / 16 ? A4[c] : make_uint4(0, 0, 0, 0);
-      }
-    }
     sAi = ((const float*)lp(l, DFSSM_PK_IN_SA))[threadIdx.x >> 4];
     if (conv_thread) {
       const float* wc = (const float*)lp(l, DFSSM_PK_CONV_W) + (size_t)conv_c * 4;
@@ -501,14 +502,6 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     const float* gwp = (const float*)lp(l, DFSSM_PK_GNORM_W);
 #pragma unroll
     for (int m = 0; m < S::MW2; ++m) gw[m] = gwp[threadIdx.x + m * kPT];
-    {
-      const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_OUT_A) + (size_t)(threadIdx.x >> 4) * (DI / 16);
-#pragma unroll
-      for (int m = 0; m < S::MC2; ++m) {
-        const int c = (threadIdx.x & 15) + 16 * m;
-        aout[m] = c < DI / 16 ? A4[c] : make_uint4(0, 0, 0, 0);
-      }
-    }
     sAo = ((const float*)lp(l, DFSSM_PK_OUT_SA))[threadIdx.x >> 4];
     const float4* s4 = (const float4*)(a.ssm + (size_t)l * S::H * HP * NS + (size_t)w * NS * 16);
 #pragma unroll
@@ -519,6 +512,33 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     dtb = ((const float*)lp(l, DFSSM_PK_DT_BIAS))[hd];
     alog = ((const float*)lp(l, DFSSM_PK_A_LOG))[hd];
     dval = ((const float*)lp(l, DFSSM_PK_D))[hd];
+  };
+
+  // the LoRA-down matrices (the bulk of the prefetched bytes), chunks of row t/16
+  auto load_ain = [&](int l) {
+    const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_IN_A) + (size_t)(threadIdx.x >> 4) * (DM / 16);
+#pragma unroll
+    for (int m = 0; m < S::MC1; ++m) {
+      const int c = (threadIdx.x & 15) + 16 * m;
+      ain[m] = c < DM / 16 ? A4[c] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto load_aout = [&](int l) {
+    const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_OUT_A) + (size_t)(threadIdx.x >> 4) * (DI / 16);
+#pragma unroll
+    for (int m = 0; m < S::MC2; ++m) {
+      const int c = (threadIdx.x & 15) + 16 * m;
+      aout[m] = c < DI / 16 ? A4[c] : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  // conv shift register of this thread's channel (window written back after the B/C hop)
+  auto conv_step = [&](float y) -> float {
+    const float v = cb + cw[0] * cst[0] + cw[1] * cst[1] + cw[2] * cst[2] + cw[3] * y;
+    cst[0] = cst[1];
+    cst[1] = cst[2];
+    cst[2] = y;
+    return silu_f(v);
   };
 
   // phase timestamps (100 MHz device clock) for performance analysis
@@ -533,9 +553,13 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
   // The next operands are prefetched just before a hop: the wave would idle
   // while polling anyway, and a burst of loads issued inside a compute phase
   // stalls that phase's instruction stream once the memory queue is full.
-  // (The hop's polls then also wait for the prefetch to land: the vector
-  // memory counter completes in order.)
+  // The hop's polls then also wait for the prefetch to land (the vector
+  // memory counter completes in order), so the bytes go where the wait is
+  // longest: the g hop carries the out-proj LoRA-down matrix and the next
+  // layer's in-proj operands, the h hop the out-proj operands, the SSM state
+  // and the in-proj LoRA-down matrix, and the short B/C hop nothing.
   load_A(0);
+  load_ain(0);
   load_B(0);
   const int T = a.n_tokens;
   const int Lm = a.n_layer;
@@ -590,37 +614,37 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         float tl[S::RLI];
 #pragma unroll
         for (int r = 0; r < S::RLI; ++r) tl[r] = ji + S::UI * r < 16 ? tls[ji + S::UI * r] : 0.0f;
-        int part[S::NGI];
-#pragma unroll
-        for (int m = 0; m < S::NGI; ++m) part[m] = p_sign_dot(win[m], qd, lut_l);
-#pragma unroll
-        for (int m = 0; m < S::NGI; ++m) {
-          const int acc = group_sum_i(part[m], S::UI);
+        auto row_out = [&](int m, int part) -> float {
+          const int acc = group_sum_i(part, S::UI);
           float lo = 0.0f;
 #pragma unroll
           for (int r = 0; r < S::RLI; ++r) lo += (float)at_use(ib[m][r]) * tl[r];
           lo = group_sum_f(lo, S::UI);
+          return (float)acc * isw[m] * s1 + isb[m] * lo;
+        };
+        // row group 0 first: it holds the B/C row, whose conv output is
+        // published before the remaining groups are computed
+        {
+          const float y = row_out(0, p_sign_dot(win[0], qd, lut_l));
+          const int k = wave * S::RPPI + subi;
+          if (lead_i && wave < S::NGI_T && k < S::NROWS) rowv[k] = y;
+          if (bc_thread) publish(bcbox, 2 * NS, conv_c - DI, conv_step(y), e);
+        }
+        int part[S::NGI];
+#pragma unroll
+        for (int m = 1; m < S::NGI; ++m) part[m] = p_sign_dot(win[m], qd, lut_l);
+#pragma unroll
+        for (int m = 1; m < S::NGI; ++m) {
+          const float y = row_out(m, part[m]);
           const int g = wave + m * kPW;
           const int k = g * S::RPPI + subi;
-          if (lead_i && g < S::NGI_T && k < S::NROWS) rowv[k] = (float)acc * isw[m] * s1 + isb[m] * lo;
+          if (lead_i && g < S::NGI_T && k < S::NROWS) rowv[k] = y;
         }
       }
       wg_barrier();
       prof(t, l, 4);
-      if (conv_thread) {
-        const float y = rowv[conv_k];
-        const float v = cb + cw[0] * cst[0] + cw[1] * cst[1] + cw[2] * cst[2] + cw[3] * y;
-        const float xv = silu_f(v);
-        rowv[conv_k] = xv;
-        if (conv_k >= 33) publish(bcbox, 2 * NS, conv_c - DI, xv, e);
-        cst[0] = cst[1];  // shifted window, written back after the B/C hop
-        cst[1] = cst[2];
-        cst[2] = y;
-      }
+      if (x_thread) rowv[conv_k] = conv_step(rowv[conv_k]);
       prof(t, l, 5);
-      // keep this layer's new conv window: load_A below refills cst for the next layer
-      const float cst_new[3] = {cst[0], cst[1], cst[2]};
-      load_A(l + 1 < Lm ? l + 1 : 0);  // after the last layer: layer 0 of the next token
       ok = gather<(2 * NS + kPT - 1) / kPT>(bcbox, 2 * NS, e, bcs, a.abort_flag, s_stop);
       ++e;
       if (!ok) break;
@@ -628,16 +652,16 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       // stores go out after the hop, for the same reason as the prefetches
       if (conv_thread) {
         float* cs = a.conv + (size_t)l * 3 * CDIM;
-        cs[conv_c] = cst_new[0];
-        cs[CDIM + conv_c] = cst_new[1];
-        cs[2 * CDIM + conv_c] = cst_new[2];
+        cs[conv_c] = cst[0];
+        cs[CDIM + conv_c] = cst[1];
+        cs[2 * CDIM + conv_c] = cst[2];
       }
       // ---- phase S: SSM on the state block [hd][j*16 .. +16][0 .. NS), gate.
       // Wave v owns channels 4v .. 4v+3, its lanes the state rows n = lane + 64 m.
       {
-        const float dt = softplus_f(rowv[32] + dtb);
+        const float dt = softplus_f(rowv[KDT] + dtb);
         const float dA = __expf(-dt * __expf(alog));
-        const float* xr = rowv + 16 + wave * 4;
+        const float* xr = rowv + KX + wave * 4;
         const float x0 = dt * xr[0], x1 = dt * xr[1], x2 = dt * xr[2], x3 = dt * xr[3];
         float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
 #pragma unroll
@@ -665,12 +689,14 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         // instruction from 32 lanes measured ~5 % slower per token)
         if (lane < 4) {
           const int c = wave * 4 + lane;  // channel within the slice
-          const float y = (lane == 0 ? y0 : lane == 1 ? y1 : lane == 2 ? y2 : y3) + dval * rowv[16 + c];
-          const float g = y * silu_f(rowv[c]);
+          const float y = (lane == 0 ? y0 : lane == 1 ? y1 : lane == 2 ? y2 : y3) + dval * rowv[KX + c];
+          const float g = y * silu_f(rowv[KZ + c]);
           publish(gbox, DI, hd * HP + j * 16 + c, g, e);
         }
       }
       prof(t, l, 7);
+      load_aout(l);
+      load_A(l + 1 < Lm ? l + 1 : 0);  // after the last layer: layer 0 of the next token
       ok = gather<S::MW2>(gbox, DI, e, gs, a.abort_flag, s_stop);
       ++e;
       if (!ok) break;
@@ -719,6 +745,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       }
       prof(t, l, 9);
       load_B(l + 1 < Lm ? l + 1 : 0);
+      load_ain(l + 1 < Lm ? l + 1 : 0);
       wg_barrier();
     }
     if (!ok) break;
