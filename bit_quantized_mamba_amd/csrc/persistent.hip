@@ -148,21 +148,66 @@ __device__ bool gather(const uint64_t* box, int n, unsigned e, float* dst, int* 
 // LDS when its phase starts.
 // ---------------------------------------------------------------------------
 
-// RMSNorm with weight w fused with the per-token int8 quantiser: thread t holds
-// inputs t + 256 m.  Sum of squares and max |x w| cross the waves in one LDS
-// round; since rstd > 0 scales every |u| = rstd |x w| alike, the absmax of u
-// is rstd * max |x w|.  Codes go to qs (LDS); returns the scale amax / 127.
+// The int8 codes sit in LDS in 16-byte chunks, chunk c at slot qchunk(c): the
+// low four bits of c are XORed with bits 3..6 (a bijection that keeps every
+// 16-chunk block in place).  A GEMV lane reads the 8 chunks of its 128
+// inputs, so the 16 lanes of a row read chunks 8 apart; unswizzled those all
+// fall in the same 2 of the 16 bank groups a 256-byte LDS row has, swizzled
+// they hit 16 different ones (and 16 consecutive chunks stay conflict-free).
+__device__ __forceinline__ int qchunk(int c) { return c ^ ((c >> 3) & 15); }
+__device__ __forceinline__ int qbyte(int i) { return qchunk(i >> 4) * 16 + (i & 15); }
+// Inputs of a thread in the norm phases: element m of thread t is input
+// norm_idx(m).  With MW a multiple of 4 a thread holds runs of 4 consecutive
+// inputs (one 16-byte load each, one 4-byte code store), else inputs t + 256 m.
+template <int MW>
+__device__ __forceinline__ int norm_idx(int m) {
+  constexpr int V = MW % 4 == 0 ? 4 : 1;
+  return V * ((int)threadIdx.x + kPT * (m / V)) + m % V;
+}
+template <int MW>
+__device__ __forceinline__ void load_norm_w(float (&dst)[MW], const float* src) {
+  if constexpr (MW % 4 == 0) {
+#pragma unroll
+    for (int m = 0; m < MW / 4; ++m) {
+      const float4 v = ((const float4*)src)[threadIdx.x + kPT * m];
+      dst[4 * m] = v.x;
+      dst[4 * m + 1] = v.y;
+      dst[4 * m + 2] = v.z;
+      dst[4 * m + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MW; ++m) dst[m] = src[threadIdx.x + kPT * m];
+  }
+}
+
+// RMSNorm with weight w fused with the per-token int8 quantiser over
+// n = 256 MW inputs (thread layout: norm_idx).  Sum of squares and max |x w|
+// cross the waves in one LDS round; since rstd > 0 scales every
+// |u| = rstd |x w| alike, the absmax of u is rstd * max |x w|.  Codes go to qs
+// (LDS, swizzled by qbyte); returns the scale amax / 127.
 template <int MW>
 __device__ float p_norm_quant(const float* xs, const float (&wr)[MW], int n, float eps, int8_t* qs, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float p[MW];
+  float x[MW], p[MW];
+  if constexpr (MW % 4 == 0) {
+#pragma unroll
+    for (int m = 0; m < MW / 4; ++m) {
+      const float4 v = ((const float4*)xs)[threadIdx.x + kPT * m];
+      x[4 * m] = v.x;
+      x[4 * m + 1] = v.y;
+      x[4 * m + 2] = v.z;
+      x[4 * m + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MW; ++m) x[m] = xs[norm_idx<MW>(m)];
+  }
   float ss = 0.0f, pm = 0.0f;
 #pragma unroll
   for (int m = 0; m < MW; ++m) {
-    const int i = threadIdx.x + m * kPT;
-    const float x = i < n ? xs[i] : 0.0f;
-    p[m] = x * wr[m];
-    ss += x * x;
+    p[m] = x[m] * wr[m];
+    ss += x[m] * x[m];
     pm = fmaxf(pm, fabsf(p[m]));
   }
   ss = wave_sum(ss);
@@ -181,15 +226,21 @@ __device__ float p_norm_quant(const float* xs, const float (&wr)[MW], int n, flo
   const float rstd = 1.0f / sqrtf(tss / (float)n + eps);
   const float amax = rstd * tpm;
   const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  auto code = [&](int m) -> int {
+    const float u = rstd * p[m];
+    const float rq = rintf(u * inv);
+    return (int)fminf(fmaxf(rq, -127.0f), 127.0f);
+  };
+  if constexpr (MW % 4 == 0) {
 #pragma unroll
-  for (int m = 0; m < MW; ++m) {
-    const int i = threadIdx.x + m * kPT;
-    if (i < n) {
-      const float u = rstd * p[m];
-      float rq = rintf(u * inv);
-      rq = fminf(fmaxf(rq, -127.0f), 127.0f);
-      qs[i] = (int8_t)(int)rq;
+    for (int m = 0; m < MW / 4; ++m) {
+      const uint32_t pk = ((uint32_t)code(4 * m) & 0xFFu) | (((uint32_t)code(4 * m + 1) & 0xFFu) << 8) |
+                          (((uint32_t)code(4 * m + 2) & 0xFFu) << 16) | ((uint32_t)code(4 * m + 3) << 24);
+      *(uint32_t*)(qs + qbyte(norm_idx<MW>(4 * m))) = pk;
     }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MW; ++m) qs[qbyte(norm_idx<MW>(m))] = (int8_t)code(m);
   }
   wg_barrier();
   return amax > 0.0f ? amax / 127.0f : 0.0f;
@@ -209,7 +260,7 @@ __device__ void p_lora_down(const uint4 (&av)[MC], int n, const int8_t* qs, floa
   for (int m = 0; m < MC; ++m) {
     const int c = c0 + 16 * m;
     if (c < C) {
-      const uint4 q = q4[c];
+      const uint4 q = q4[qchunk(c)];
       acc = __builtin_amdgcn_sdot4((int)av[m].x, (int)q.x, acc, false);
       acc = __builtin_amdgcn_sdot4((int)av[m].y, (int)q.y, acc, false);
       acc = __builtin_amdgcn_sdot4((int)av[m].z, (int)q.z, acc, false);
@@ -263,10 +314,10 @@ __device__ __forceinline__ int p_sign_dot(const uint4 w, const uint32_t (&qd)[32
 }
 // the int8 codes of inputs [128 j, 128 j + 128) as 32 words
 __device__ __forceinline__ void load_codes(const int8_t* qs, int j, uint32_t (&qd)[32]) {
-  const uint4* q4 = (const uint4*)(qs + 128 * j);
+  const uint4* q4 = (const uint4*)qs;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const uint4 v = q4[k];
+    const uint4 v = q4[qchunk(8 * j + k)];
     qd[4 * k + 0] = v.x;
     qd[4 * k + 1] = v.y;
     qd[4 * k + 2] = v.z;
@@ -468,8 +519,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       }
     }
     const float* nwp = (const float*)lp(l, DFSSM_PK_NORM_W);
-#pragma unroll
-    for (int m = 0; m < S::MW1; ++m) nw[m] = nwp[threadIdx.x + m * kPT];
+    load_norm_w<S::MW1>(nw, nwp);
     sAi = ((const float*)lp(l, DFSSM_PK_IN_SA))[threadIdx.x >> 4];
     if (conv_thread) {
       const float* wc = (const float*)lp(l, DFSSM_PK_CONV_W) + (size_t)conv_c * 4;
@@ -500,8 +550,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       }
     }
     const float* gwp = (const float*)lp(l, DFSSM_PK_GNORM_W);
-#pragma unroll
-    for (int m = 0; m < S::MW2; ++m) gw[m] = gwp[threadIdx.x + m * kPT];
+    load_norm_w<S::MW2>(gw, gwp);
     sAo = ((const float*)lp(l, DFSSM_PK_OUT_SA))[threadIdx.x >> 4];
     const float4* s4 = (const float4*)(a.ssm + (size_t)l * S::H * HP * NS + (size_t)w * NS * 16);
 #pragma unroll
@@ -601,7 +650,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       if constexpr (TR) {
         int8_t* tq = kargs()->trace_q1;
         if (tq && w == 0)
-          for (int i = threadIdx.x; i < DM; i += kPT) tq[(size_t)l * DM + i] = qs[i];
+          for (int i = threadIdx.x; i < DM; i += kPT) tq[(size_t)l * DM + i] = qs[qbyte(i)];
       }
       p_lora_down<S::MC1>(ain, DM, qs, sAi, s1, tls);
       prof(t, l, 3);
@@ -716,7 +765,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         if constexpr (TR) {
           int8_t* tq = kargs()->trace_q2;
           if (tq && w == 0)
-            for (int i = threadIdx.x; i < DI; i += kPT) tq[(size_t)l * DI + i] = qs[i];
+            for (int i = threadIdx.x; i < DI; i += kPT) tq[(size_t)l * DI + i] = qs[qbyte(i)];
         }
         p_lora_down<S::MC2>(aout, DI, qs, sAo, s2, tls);
         uint32_t qd[32];
@@ -765,8 +814,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     float fn[S::MW1];
     {
       const float* fnp = kargs()->final_norm;
-#pragma unroll
-      for (int m = 0; m < S::MW1; ++m) fn[m] = fnp[threadIdx.x + m * kPT];
+      load_norm_w<S::MW1>(fn, fnp);
     }
     // kHeadDepth rows per wave in flight: their bytes and their scales
     uint4 eb[kHeadDepth][MH];
@@ -796,13 +844,13 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     if constexpr (TR) {
       int8_t* tq = kargs()->trace_qf;
       if (tq && w == 0)
-        for (int i = threadIdx.x; i < DM; i += kPT) tq[i] = qs[i];
+        for (int i = threadIdx.x; i < DM; i += kPT) tq[i] = qs[qbyte(i)];
     }
     {
       const uint4* q4 = (const uint4*)qs;
       uint4 qv[MH];
 #pragma unroll
-      for (int c = 0; c < MH; ++c) qv[c] = q4[jh + c * LH];
+      for (int c = 0; c < MH; ++c) qv[c] = q4[qchunk(jh + c * LH)];
       float best = -__builtin_huge_valf();
       int bidx = 0x7fffffff;
       for (int base = 0; base < rows_per; base += kHeadDepth * STEPH) {
