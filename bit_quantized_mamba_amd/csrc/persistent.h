@@ -22,10 +22,12 @@ struct PersistArgs {
   const float* final_norm;
   float* conv;  // sequence slot 0: [n_layer][d_conv-1][conv_dim]
   float* ssm;   // sequence slot 0: [n_layer][H][P/16][N][16]
-  // mailboxes, one block (R replicas each): h [R][d_model] | B,C [R][2 d_state] | g [R][d_inner] |
-  // argmax [R][2 grid]
+  // mailboxes, one block (R replicas each): h [R][d_model / 2] (paired) | B,C [R][2 d_state] |
+  // g [R][d_inner / 2] (paired) | argmax [R][2 grid]
   uint64_t* boxes;
   unsigned epoch0;  // first epoch of this launch (host-assigned, never reused)
+  unsigned pair0;   // write count of the paired boxes at the first write of this launch (mod 4 differs
+                    // from the tag every paired word holds when the launch starts)
   int* abort_flag;
   int* err;
   const int32_t* tok_in;  // [1] first input token

@@ -16,15 +16,19 @@
 //   head (computed by the head's slices redundantly), and B/C rows i with
 //   i % G == w; their conv channels; the SSM state block [hd][j*16..+16][:];
 //   out_proj rows [w * d_model/G, +d_model/G).
-// Hops: each value crossing workgroups is published as a 64-bit word
-// {fp32 bits, epoch} with a relaxed device-scope atomic store into R = 4
-// replicas (replica r read by the workgroups with w % 4 == r, which spreads
-// the readers of a line; 4 measured faster per token than 1, 2, 8 or 16); readers poll with relaxed device-scope atomic
-// loads until the epoch matches.  A value and its epoch travel in one
-// single-copy-atomic word, so no fence or flag ordering is involved, and
-// every instance of a hop has its own epoch.  Each box is reused once per
-// layer; a writer can only reach its next use after every reader has passed
-// the hop that follows this one, so one buffer per box suffices.
+// Hops: values crossing workgroups travel in 64-bit words written with a
+// relaxed device-scope atomic store into R = 4 replicas (replica r read by
+// the workgroups with w % 4 == r, which spreads the readers of a line; 4
+// measured faster per token than 1, 2, 8 or 16); readers poll with relaxed
+// device-scope atomic loads until the word is fresh.  The small boxes (B/C,
+// argmax) carry {fp32 bits, epoch}, every hop instance with its own epoch.
+// The residual and gated-output boxes carry two values per word with a
+// 2-bit write-count tag in their lowest mantissa bits (pack2), which halves
+// the bytes every workgroup reads at those hops.  Freshness travels in the
+// same single-copy-atomic word as the data, so no fence or flag ordering is
+// involved.  Each box is reused once per layer; a writer can only reach its
+// next use after every reader has passed the hop that follows this one, so
+// one buffer per box suffices.
 // Every wait is bounded: a workgroup that polls too long sets a device abort
 // flag, which all waits check, so a fault ends the kernel instead of hanging.
 #include "common.h"
@@ -45,6 +49,21 @@ __device__ __forceinline__ void st64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t pack(float v, unsigned e) { return ((uint64_t)e << 32) | __float_as_uint(v); }
+
+// Paired words (the residual and gated-output boxes, whose per-hop volume is
+// large): two fp32 values in one 64-bit word, the lowest mantissa bit of each
+// replaced by one bit of a 2-bit tag, the count of that box's writes mod 4
+// (a 1-ulp perturbation of each value).  Every reader reads every word of its
+// replica at every write, so by per-location coherence it can only see the
+// current write or the one before, whose tag differs.  The host keeps the
+// count across launches and clears the boxes when it cannot vouch for it.
+constexpr uint64_t kTagMask = 0x0000000100000001ull;
+__device__ __forceinline__ uint64_t tag_bits(unsigned c) {
+  return (uint64_t)(c & 1u) | ((uint64_t)((c >> 1) & 1u) << 32);
+}
+__device__ __forceinline__ uint64_t pack2(float v0, float v1, unsigned c) {
+  return ((((uint64_t)__float_as_uint(v1) << 32) | __float_as_uint(v0)) & ~kTagMask) | tag_bits(c);
+}
 
 // The launch's arguments re-read from the kernel-argument segment at the point
 // of use.  The pointer passes through an empty asm so the compiler cannot keep
@@ -81,6 +100,14 @@ __device__ __forceinline__ void publish(uint64_t* box, int n, int i, float v, un
   for (int r = 0; r < kR; ++r) st64(box + (size_t)r * n + i, w);
 }
 
+// publish values v0, v1 (entries 2i, 2i + 1) as paired word i of a box of n
+// words (all replicas), write count c
+__device__ __forceinline__ void publish2(uint64_t* box, int n, int i, float v0, float v1, unsigned c) {
+  const uint64_t w = pack2(v0, v1, c);
+#pragma unroll 1
+  for (int r = 0; r < kR; ++r) st64(box + (size_t)r * n + i, w);
+}
+
 // Read words [0, n) of this workgroup's replica into LDS.  A thread issues
 // all of its loads before checking any.  While some are stale it waits on the
 // first stale one alone (a single poll in flight per thread keeps the polling
@@ -89,14 +116,18 @@ __device__ __forceinline__ void publish(uint64_t* box, int n, int i, float v, un
 // time, so the words missing when the first one lands arrive together and one
 // parallel round picks them up.  Returns false (for every thread of the
 // workgroup) on abort.
-template <int MAXW>
-__device__ bool gather(const uint64_t* box, int n, unsigned e, float* dst, int* abort_flag, int* s_stop) {
+// PAIRED: paired words, fresh when their tag is tag_bits(key), two floats each
+// to dst; else {value, epoch} words, fresh when the epoch is key.
+template <int MAXW, bool PAIRED>
+__device__ bool gather_words(const uint64_t* box, int n, unsigned key, float* dst, int* abort_flag, int* s_stop) {
   const uint64_t* src = box + (size_t)(blockIdx.x % kR) * n;
+  const uint64_t tb = tag_bits(key);
+  auto fresh = [&](uint64_t v) { return PAIRED ? (v & kTagMask) == tb : (unsigned)(v >> 32) == key; };
   uint64_t w[MAXW];
 #pragma unroll
   for (int m = 0; m < MAXW; ++m) {
     const int i = threadIdx.x + m * kPT;
-    w[m] = i < n ? ld64(src + i) : pack(0.0f, e);
+    w[m] = i < n ? ld64(src + i) : (PAIRED ? tb : pack(0.0f, key));
   }
   bool ok = true;
   long spins = 0;
@@ -104,12 +135,12 @@ __device__ bool gather(const uint64_t* box, int n, unsigned e, float* dst, int* 
     int first = -1;
 #pragma unroll
     for (int m = MAXW - 1; m >= 0; --m)
-      if ((unsigned)(w[m] >> 32) != e) first = m;
+      if (!fresh(w[m])) first = m;
     if (first < 0) break;
     // wait on the first stale word
     const uint64_t* p = src + threadIdx.x + first * kPT;
     uint64_t v = ld64(p);
-    while ((unsigned)(v >> 32) != e) {
+    while (!fresh(v)) {
       if (++spins > kSpinLimit) {
         __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ok = false;
@@ -125,13 +156,18 @@ __device__ bool gather(const uint64_t* box, int n, unsigned e, float* dst, int* 
     // then one parallel round over every word still stale (including that one)
 #pragma unroll
     for (int m = 0; m < MAXW; ++m)
-      if ((unsigned)(w[m] >> 32) != e) w[m] = ld64(src + threadIdx.x + m * kPT);
+      if (!fresh(w[m])) w[m] = ld64(src + threadIdx.x + m * kPT);
   }
   if (ok) {
 #pragma unroll
     for (int m = 0; m < MAXW; ++m) {
       const int i = threadIdx.x + m * kPT;
-      if (i < n) dst[i] = __uint_as_float((unsigned)w[m]);
+      if (i < n) {
+        if (PAIRED)
+          ((float2*)dst)[i] = make_float2(__uint_as_float((unsigned)w[m]), __uint_as_float((unsigned)(w[m] >> 32)));
+        else
+          dst[i] = __uint_as_float((unsigned)w[m]);
+      }
     }
   } else {
     *s_stop = 1;
@@ -139,6 +175,15 @@ __device__ bool gather(const uint64_t* box, int n, unsigned e, float* dst, int* 
   wg_barrier();
   const bool stop = *s_stop != 0;
   return !stop;
+}
+template <int MAXW>
+__device__ bool gather(const uint64_t* box, int n, unsigned e, float* dst, int* abort_flag, int* s_stop) {
+  return gather_words<MAXW, false>(box, n, e, dst, abort_flag, s_stop);
+}
+// paired box of n words (2 n floats), write count c
+template <int MAXW>
+__device__ bool gather2(const uint64_t* box, int n, unsigned c, float* dst, int* abort_flag, int* s_stop) {
+  return gather_words<MAXW, true>(box, n, c, dst, abort_flag, s_stop);
 }
 
 // ---------------------------------------------------------------------------
@@ -246,32 +291,40 @@ __device__ float p_norm_quant(const float* xs, const float (&wr)[MW], int n, flo
   return amax > 0.0f ? amax / 127.0f : 0.0f;
 }
 
-// LoRA down-projection, rank 16.  16 lanes per row: thread t takes row
-// k = t/16 and the 16-byte chunks c = t%16 + 16*m of that row (C = n/16 per
-// row), prefetched into registers (av[m]); local sums, then a 16-lane DPP
-// reduction.  tout[k] = float(sum_i A[k][i] q_i) * sA[k] * s;  sA_row = sA[t/16].
-template <int MC>
-__device__ void p_lora_down(const uint4 (&av)[MC], int n, const int8_t* qs, float sA_row, float s, float* tout) {
-  const int k = threadIdx.x >> 4, c0 = threadIdx.x & 15;
+// LoRA down-projection, rank 16: wave v computes rows 4v .. 4v+3.  Lane l
+// takes the 16-byte input chunks l + 64 j (C = n/16 chunks) and holds
+// A[4v + r][chunk l + 64 j] in av[r J + j] (prefetched), so every code chunk
+// is read from LDS once per wave and feeds 4 independent accumulators; four
+// wave reductions follow.  tout[k] = float(sum_i A[k][i] q_i) * sA[k] * s;
+// sA_lane = sA[4v + (l & 3)].
+template <int J>
+__device__ void p_lora_down(const uint4 (&av)[4 * J], int n, const int8_t* qs, float sA_lane, float s, float* tout) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int C = n >> 4;
   const uint4* q4 = (const uint4*)qs;
-  int acc = 0;
+  uint4 qv[J];
 #pragma unroll
-  for (int m = 0; m < MC; ++m) {
-    const int c = c0 + 16 * m;
-    if (c < C) {
-      const uint4 q = q4[qchunk(c)];
-      acc = __builtin_amdgcn_sdot4((int)av[m].x, (int)q.x, acc, false);
-      acc = __builtin_amdgcn_sdot4((int)av[m].y, (int)q.y, acc, false);
-      acc = __builtin_amdgcn_sdot4((int)av[m].z, (int)q.z, acc, false);
-      acc = __builtin_amdgcn_sdot4((int)av[m].w, (int)q.w, acc, false);
+  for (int j = 0; j < J; ++j) qv[j] = lane + 64 * j < C ? q4[qchunk(lane + 64 * j)] : make_uint4(0, 0, 0, 0);
+  int acc[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint4 a = av[r * J + j];
+      acc[r] = __builtin_amdgcn_sdot4((int)a.x, (int)qv[j].x, acc[r], false);
+      acc[r] = __builtin_amdgcn_sdot4((int)a.y, (int)qv[j].y, acc[r], false);
+      acc[r] = __builtin_amdgcn_sdot4((int)a.z, (int)qv[j].z, acc[r], false);
+      acc[r] = __builtin_amdgcn_sdot4((int)a.w, (int)qv[j].w, acc[r], false);
     }
+  int tot[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) tot[r] = wave_sum_i(acc[r]);
+  if (lane < 4) {
+    const int t = lane == 0 ? tot[0] : lane == 1 ? tot[1] : lane == 2 ? tot[2] : tot[3];
+    tout[4 * wave + lane] = (float)t * sA_lane * s;
   }
-  acc = group_sum_i(acc, 16);
-  if (c0 == 0) tout[k] = (float)acc * sA_row * s;
   wg_barrier();
 }
-
 
 // Sign table: entry v (one byte of scaffold bits, input k at bit k) holds the
 // eight signs +1 / -1 of those inputs as int8, inputs 0..3 in .x and 4..7 in
@@ -391,9 +444,11 @@ struct PShape {
   static constexpr int UO = DI / 128, RPPO = 64 / UO, NGO_T = (OUT_PER + RPPO - 1) / RPPO,
                        NGO = (NGO_T + kPW - 1) / kPW;
   static constexpr int MW1 = DM / kPT, MW2 = DI / kPT;
+  static constexpr int GW1 = (DM / 2 + kPT - 1) / kPT, GW2 = (DI / 2 + kPT - 1) / kPT;  // paired words per thread
   // LoRA-up ranks per lane of a row group (lane j takes ranks j, j + U, ...)
   static constexpr int RLI = (16 + UI - 1) / UI, RLO = (16 + UO - 1) / UO;
-  static constexpr int MC1 = (DM / 16 + 15) / 16, MC2 = (DI / 16 + 15) / 16;
+  // LoRA-down operands per thread: 4 rows x J chunks (J = chunks per lane)
+  static constexpr int J1 = (DM / 16 + 63) / 64, J2 = (DI / 16 + 63) / 64, MC1 = 4 * J1, MC2 = 4 * J2;
   static constexpr int NST = (NS + 63) / 64;
   static constexpr int CH = DM / 16, LH = CH < 64 ? CH : 64, MH = CH / LH, RPPH = 64 / LH, STEPH = kPW * RPPH;
   // one layer's tensors in kind order, each 256-byte aligned (the runtime's weight layout)
@@ -413,6 +468,7 @@ struct PShape {
   static_assert(2 * NS % G == 0 && DM % G == 0 && DM % kPT == 0 && DI % kPT == 0, "unsupported shape");
   static_assert(NROWS <= kMaxInRows, "too many in_proj rows per workgroup");
   static_assert(NBC <= RPPI, "the B/C rows must sit in row group 0 of wave 0");
+  static_assert(RPPO % 2 == 0 && OUT_PER % 2 == 0, "out_proj rows are published in pairs from one wave");
 };
 
 constexpr int kHeadDepth = 8;  // LM-head rows in flight per wave
@@ -449,10 +505,11 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
   unsigned e = a.epoch0;  // same value in every workgroup
   int tok = kargs()->tok_in[0];
   const char* wb = a.wbase;
-  uint64_t* const hbox = a.boxes;
-  uint64_t* const bcbox = hbox + kR * DM;
-  uint64_t* const gbox = bcbox + kR * 2 * NS;
-  uint64_t* const abox = gbox + kR * DI;
+  unsigned pc = a.pair0;  // write count of the paired boxes (one write per layer)
+  uint64_t* const hbox = a.boxes;            // paired, DM / 2 words
+  uint64_t* const bcbox = hbox + kR * DM / 2;
+  uint64_t* const gbox = bcbox + kR * 2 * NS;  // paired, DI / 2 words
+  uint64_t* const abox = gbox + kR * DI / 2;
 
   // own in_proj rows, B/C first: their conv outputs are published while the
   // other rows are still being computed
@@ -485,7 +542,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
                            // here would make the prefetch wait for its own load)
   float cw[4], cb, cst[3];
   float sAi;
-  uint4 ain[S::MC1];  // LoRA-down A chunks of this thread (row t/16)
+  uint4 ain[S::MC1];  // LoRA-down A chunks of this thread (see p_lora_down)
   // ---- registers prefetched for phases S and B (SSM, out_proj) of a layer
   uint4 wout[S::NGO];
   float gw[S::MW2];
@@ -520,7 +577,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     }
     const float* nwp = (const float*)lp(l, DFSSM_PK_NORM_W);
     load_norm_w<S::MW1>(nw, nwp);
-    sAi = ((const float*)lp(l, DFSSM_PK_IN_SA))[threadIdx.x >> 4];
+    sAi = ((const float*)lp(l, DFSSM_PK_IN_SA))[4 * wave + (lane & 3)];
     if (conv_thread) {
       const float* wc = (const float*)lp(l, DFSSM_PK_CONV_W) + (size_t)conv_c * 4;
       cw[0] = wc[0]; cw[1] = wc[1]; cw[2] = wc[2]; cw[3] = wc[3];
@@ -551,7 +608,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     }
     const float* gwp = (const float*)lp(l, DFSSM_PK_GNORM_W);
     load_norm_w<S::MW2>(gw, gwp);
-    sAo = ((const float*)lp(l, DFSSM_PK_OUT_SA))[threadIdx.x >> 4];
+    sAo = ((const float*)lp(l, DFSSM_PK_OUT_SA))[4 * wave + (lane & 3)];
     const float4* s4 = (const float4*)(a.ssm + (size_t)l * S::H * HP * NS + (size_t)w * NS * 16);
 #pragma unroll
     for (int m = 0; m < S::NST; ++m) {
@@ -563,22 +620,27 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     dval = ((const float*)lp(l, DFSSM_PK_D))[hd];
   };
 
-  // the LoRA-down matrices (the bulk of the prefetched bytes), chunks of row t/16
+  // the LoRA-down matrices (the bulk of the prefetched bytes): rows
+  // 4 wave + r, chunks lane + 64 j (the p_lora_down layout)
   auto load_ain = [&](int l) {
-    const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_IN_A) + (size_t)(threadIdx.x >> 4) * (DM / 16);
+    const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_IN_A);
 #pragma unroll
-    for (int m = 0; m < S::MC1; ++m) {
-      const int c = (threadIdx.x & 15) + 16 * m;
-      ain[m] = c < DM / 16 ? A4[c] : make_uint4(0, 0, 0, 0);
-    }
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < S::J1; ++j) {
+        const int c = lane + 64 * j;
+        ain[r * S::J1 + j] = c < DM / 16 ? A4[(size_t)(4 * wave + r) * (DM / 16) + c] : make_uint4(0, 0, 0, 0);
+      }
   };
   auto load_aout = [&](int l) {
-    const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_OUT_A) + (size_t)(threadIdx.x >> 4) * (DI / 16);
+    const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_OUT_A);
 #pragma unroll
-    for (int m = 0; m < S::MC2; ++m) {
-      const int c = (threadIdx.x & 15) + 16 * m;
-      aout[m] = c < DI / 16 ? A4[c] : make_uint4(0, 0, 0, 0);
-    }
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < S::J2; ++j) {
+        const int c = lane + 64 * j;
+        aout[r * S::J2 + j] = c < DI / 16 ? A4[(size_t)(4 * wave + r) * (DI / 16) + c] : make_uint4(0, 0, 0, 0);
+      }
   };
 
   // conv shift register of this thread's channel (window written back after the B/C hop)
@@ -634,7 +696,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     for (int l = 0; l < Lm && ok; ++l) {
       prof(t, l, 0);
       if (l > 0) {
-        ok = gather<S::MW1>(hbox, DM, e, hs, a.abort_flag, s_stop);
+        ok = gather2<S::GW1>(hbox, DM / 2, pc - 1, hs, a.abort_flag, s_stop);
         ++e;
         if (!ok) break;
       }
@@ -652,7 +714,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         if (tq && w == 0)
           for (int i = threadIdx.x; i < DM; i += kPT) tq[(size_t)l * DM + i] = qs[qbyte(i)];
       }
-      p_lora_down<S::MC1>(ain, DM, qs, sAi, s1, tls);
+      p_lora_down<S::J1>(ain, DM, qs, sAi, s1, tls);
       prof(t, l, 3);
       {
         // Every row group is computed (a wave's unused group has zero weights
@@ -736,17 +798,19 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         y3 = wave_sum(y3);
         // (one store instruction per replica: writing all replicas with one
         // instruction from 32 lanes measured ~5 % slower per token)
-        if (lane < 4) {
-          const int c = wave * 4 + lane;  // channel within the slice
-          const float y = (lane == 0 ? y0 : lane == 1 ? y1 : lane == 2 ? y2 : y3) + dval * rowv[KX + c];
+        // lanes 0..3 hold channels 4 wave + lane; lanes 0 and 2 publish pairs
+        {
+          const int c = wave * 4 + (lane & 3);  // channel within the slice
+          const float y = ((lane & 3) == 0 ? y0 : (lane & 3) == 1 ? y1 : (lane & 3) == 2 ? y2 : y3) + dval * rowv[KX + c];
           const float g = y * silu_f(rowv[KZ + c]);
-          publish(gbox, DI, hd * HP + j * 16 + c, g, e);
+          const float gn = dpp_f<kDppQuadSwap1>(g);
+          if (lane == 0 || lane == 2) publish2(gbox, DI / 2, (hd * HP + j * 16 + c) / 2, g, gn, pc);
         }
       }
       prof(t, l, 7);
       load_aout(l);
       load_A(l + 1 < Lm ? l + 1 : 0);  // after the last layer: layer 0 of the next token
-      ok = gather<S::MW2>(gbox, DI, e, gs, a.abort_flag, s_stop);
+      ok = gather2<S::GW2>(gbox, DI / 2, pc, gs, a.abort_flag, s_stop);
       ++e;
       if (!ok) break;
       prof(t, l, 8);
@@ -767,7 +831,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
           if (tq && w == 0)
             for (int i = threadIdx.x; i < DI; i += kPT) tq[(size_t)l * DI + i] = qs[qbyte(i)];
         }
-        p_lora_down<S::MC2>(aout, DI, qs, sAo, s2, tls);
+        p_lora_down<S::J2>(aout, DI, qs, sAo, s2, tls);
         uint32_t qd[32];
         load_codes(qs, jo, qd);
         float tl[S::RLO];
@@ -785,14 +849,16 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
           lo = group_sum_f(lo, S::UO);
           const int g = wave + m * kPW;
           const int k = g * S::RPPO + subo;
-          if (lead_o && g < S::NGO_T && k < S::OUT_PER) {
-            const int row = w * S::OUT_PER + k;
-            const float y = (float)acc * osw[m] * s2 + osb[m] * lo;
-            publish(hbox, DM, row, hs[row] + y, e);
-          }
+          const bool live = g < S::NGO_T && k < S::OUT_PER;
+          const int row = w * S::OUT_PER + (live ? k : 0);
+          const float hv = hs[row] + ((float)acc * osw[m] * s2 + osb[m] * lo);
+          // rows k, k + 1 (k even) sit in one group, row k + 1 lead UO lanes up
+          const float hn = __int_as_float(__builtin_amdgcn_ds_bpermute(((lane + S::UO) & 63) * 4, __float_as_int(hv)));
+          if (lead_o && live && (k & 1) == 0) publish2(hbox, DM / 2, row / 2, hv, hn, pc);
         }
       }
       prof(t, l, 9);
+      ++pc;
       load_B(l + 1 < Lm ? l + 1 : 0);
       load_ain(l + 1 < Lm ? l + 1 : 0);
       wg_barrier();
@@ -830,7 +896,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       for (int c = 0; c < MH; ++c) eb[d][c] = live ? e4[jh + c * LH] : make_uint4(0, 0, 0, 0);
       es[d] = live ? sE[row] : 0.0f;
     }
-    ok = gather<S::MW1>(hbox, DM, e, hs, a.abort_flag, s_stop);
+    ok = gather2<S::GW1>(hbox, DM / 2, pc - 1, hs, a.abort_flag, s_stop);
     ++e;
     if (!ok) break;
     prof(t, Lm, 1);
@@ -1001,7 +1067,7 @@ bool persistent_supported(int d_model, int d_inner, int d_state, int headdim, in
 }
 
 size_t persistent_box_words(int d_model, int d_inner, int d_state, int grid) {
-  return (size_t)kR * ((size_t)d_model + (size_t)d_inner + 2 * (size_t)d_state + 2 * (size_t)grid);
+  return (size_t)kR * ((size_t)d_model / 2 + (size_t)d_inner / 2 + 2 * (size_t)d_state + 2 * (size_t)grid);
 }
 
 }  // namespace dfssm

@@ -96,6 +96,7 @@ struct dfssm_ctx {
   size_t box_words = 0;
   int* abort_flag = nullptr;
   unsigned host_epoch = 1;
+  unsigned pair_count = 1;  // writes of the paired boxes so far + 1 (boxes zeroed: every tag is 0)
 
   void* tensor_ptr(int layer, int kind) const {
     const TensorInfo& t = layer >= 0 ? layer_t[(size_t)layer * DFSSM_T_PER_LAYER + kind] : global_t[kind];
@@ -512,6 +513,7 @@ dfssm_status run_persistent(dfssm_ctx* c, const int32_t* tok_in, int32_t* tok_la
     // epochs are never reused: clear the boxes and start over
     HIP_TRY(launch_zero(c->boxes, sizeof(uint64_t) * c->box_words, st));
     c->host_epoch = 1;
+    c->pair_count = 1;
   }
   PersistArgs a{};
   a.wbase = c->wbuf;
@@ -532,6 +534,7 @@ dfssm_status run_persistent(dfssm_ctx* c, const int32_t* tok_in, int32_t* tok_la
   a.ssm = c->ssm;
   a.boxes = c->boxes;
   a.epoch0 = c->host_epoch;
+  a.pair0 = c->pair_count;
   a.abort_flag = c->abort_flag;
   a.err = c->err;
   a.tok_in = tok_in;
@@ -548,6 +551,7 @@ dfssm_status run_persistent(dfssm_ctx* c, const int32_t* tok_in, int32_t* tok_la
   a.prof = prof;
   a.prof_tokens = prof_tokens;
   c->host_epoch += need;
+  c->pair_count += (unsigned)n_tokens * (unsigned)c->L;
   HIP_TRY(launch_decode_persistent(a, c->persist_grid, st));
   return DFSSM_OK;
 }
@@ -1071,6 +1075,11 @@ dfssm_status dfssm_check_device(dfssm_ctx* c, void* stream) {
   if (flag) {
     HIP_TRY(launch_zero(c->err, 4, nullptr));
     if (c->abort_flag) HIP_TRY(launch_zero(c->abort_flag, 4, nullptr));
+    if (flag & 2) {
+      // an aborted launch leaves the paired boxes with unknown write counts
+      HIP_TRY(launch_zero(c->boxes, sizeof(uint64_t) * c->box_words, nullptr));
+      c->pair_count = 1;
+    }
     HIP_TRY(hipDeviceSynchronize());
     std::string msg;
     if (flag & 1) msg += "a kernel flagged an out-of-range token id; ";
