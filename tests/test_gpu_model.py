@@ -223,6 +223,33 @@ def test_persistent_generate_equals_step_loop(shape):
     eng.close()
 
 
+def test_persistent_launch_sequence_equals_one_launch():
+    # Launches of assorted lengths on a model with an odd layer count (the
+    # residual and gated-output mailboxes carry a write-count tag that the
+    # host continues from launch to launch) give exactly the tokens and state
+    # of one launch over the same tokens.
+    import dataclasses
+    shape = dataclasses.replace(synth.TINY, n_layer=3)
+    seed = synth.SEED_BASE + 5
+    start = int(synth.gen_tokens(seed, 3, 1, shape.vocab)[0])
+    lens = [1, 2, 3, 1, 5, 4]
+    eng = engine(shape)
+    eng.set_path("persistent")
+    eng.load_synthetic(seed)
+    ref = eng.generate(_i32([start]), sum(lens)).cpu().numpy()[:, 0]
+    st_ref = eng.get_state(0)
+    eng.reset_state(1)
+    tok = _i32([start])
+    got = []
+    for n in lens:
+        got += eng.generate(tok, n).cpu().numpy()[:, 0].tolist()
+    st = eng.get_state(0)
+    assert got == ref.tolist()
+    assert np.array_equal(st[0], st_ref[0]) and np.array_equal(st[1], st_ref[1])
+    eng.check()
+    eng.close()
+
+
 def test_state_round_trip_resume():
     s = synth.TINY
     toks = synth.gen_tokens(synth.SEED_BASE, 6, 12, s.vocab)
