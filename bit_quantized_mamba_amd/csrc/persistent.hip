@@ -16,6 +16,11 @@
 //   head (computed by the head's slices redundantly), and B/C rows i with
 //   i % G == w; their conv channels; the SSM state block [hd][j*16..+16][:];
 //   out_proj rows [w * d_model/G, +d_model/G).
+// Waves: a workgroup has 4 compute waves and 4 loader waves (one of each per
+// SIMD).  The loader waves bring in every weight and state a layer needs
+// (staged in LDS for the compute waves, or kept in their own registers for
+// the LoRA down-projections they compute), so the compute waves' instruction
+// streams and polls never wait behind weight traffic.
 // Hops: values crossing workgroups travel in 64-bit words written with a
 // relaxed device-scope atomic store into R = 4 replicas (replica r read by
 // the workgroups with w % 4 == r, which spreads the readers of a line; 4
@@ -34,10 +39,14 @@
 #include "common.h"
 #include "persistent.h"
 
+#include <type_traits>
+
 namespace dfssm {
 
-constexpr int kPT = 256;  // threads per workgroup: one wave per SIMD, so each wave has the full register file
+constexpr int kPT = 256;  // compute threads per workgroup: one compute wave per SIMD
 constexpr int kPW = kPT / 64;
+constexpr int kLT = 256;  // loader threads (waves 4..7): the LoRA down-projections
+constexpr int kBlock = kPT + kLT;
 constexpr int kR = 4;     // replicas of each published word
 constexpr long kSpinLimit = 1 << 21;
 constexpr int kLutCopies = 16;
@@ -187,7 +196,7 @@ __device__ bool gather2(const uint64_t* box, int n, unsigned c, float* dst, int*
 }
 
 // ---------------------------------------------------------------------------
-// compute phases.  One wave per SIMD: nothing hides latency, so every
+// compute phases.  One compute wave per SIMD: nothing hides latency, so every
 // cross-lane step uses DPP, every reduction crosses waves at most once, and
 // every operand that does not depend on the token is already in registers or
 // LDS when its phase starts.
@@ -291,15 +300,15 @@ __device__ float p_norm_quant(const float* xs, const float (&wr)[MW], int n, flo
   return amax > 0.0f ? amax / 127.0f : 0.0f;
 }
 
-// LoRA down-projection, rank 16: wave v computes rows 4v .. 4v+3.  Lane l
-// takes the 16-byte input chunks l + 64 j (C = n/16 chunks) and holds
-// A[4v + r][chunk l + 64 j] in av[r J + j] (prefetched), so every code chunk
-// is read from LDS once per wave and feeds 4 independent accumulators; four
-// wave reductions follow.  tout[k] = float(sum_i A[k][i] q_i) * sA[k] * s;
-// sA_lane = sA[4v + (l & 3)].
+// LoRA down-projection, rank 16, by the loader waves: loader wave v computes
+// rows 4v .. 4v+3.  Lane l takes the 16-byte input chunks l + 64 j (C = n/16
+// chunks) and holds A[4v + r][chunk l + 64 j] in av[r J + j], so every code
+// chunk is read from LDS once per wave and feeds 4 independent accumulators;
+// four wave reductions follow.  tout[k] = float(sum_i A[k][i] q_i) * sA[k]
+// (the code scale s is applied by the reader); sA_lane = sA[4v + (l & 3)].
 template <int J>
-__device__ void p_lora_down(const uint4 (&av)[4 * J], int n, const int8_t* qs, float sA_lane, float s, float* tout) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ void p_lora_down(const uint4 (&av)[4 * J], int n, const int8_t* qs, float sA_lane, float* tout, int lane,
+                            int wave) {
   const int C = n >> 4;
   const uint4* q4 = (const uint4*)qs;
   uint4 qv[J];
@@ -321,9 +330,8 @@ __device__ void p_lora_down(const uint4 (&av)[4 * J], int n, const int8_t* qs, f
   for (int r = 0; r < 4; ++r) tot[r] = wave_sum_i(acc[r]);
   if (lane < 4) {
     const int t = lane == 0 ? tot[0] : lane == 1 ? tot[1] : lane == 2 ? tot[2] : tot[3];
-    tout[4 * wave + lane] = (float)t * sA_lane * s;
+    tout[4 * wave + lane] = (float)t * sA_lane;
   }
-  wg_barrier();
 }
 
 // Sign table: entry v (one byte of scaffold bits, input k at bit k) holds the
@@ -439,6 +447,7 @@ struct PShape {
   static constexpr int H = DI / HP, G = H * (HP / 16), CDIM = DI + 2 * NS, DPROJ = 2 * DI + 2 * NS + H;
   static constexpr int NBC = 2 * NS / G;  // B/C rows per workgroup
   static constexpr int NROWS = 33 + NBC;  // z 16, x 16, dt 1, B/C
+  static constexpr int KZ = NBC, KX = NBC + 16, KDT = NBC + 32;  // first z, x and the dt row among them
   static constexpr int OUT_PER = DM / G;
   static constexpr int UI = DM / 128, RPPI = 64 / UI, NGI_T = (NROWS + RPPI - 1) / RPPI, NGI = (NGI_T + kPW - 1) / kPW;
   static constexpr int UO = DI / 128, RPPO = 64 / UO, NGO_T = (OUT_PER + RPPO - 1) / RPPO,
@@ -472,178 +481,412 @@ struct PShape {
 };
 
 constexpr int kHeadDepth = 8;  // LM-head rows in flight per wave
-static_assert(kPT == 256 && kPW == 4, "one wave per 4 state channels and 16 lanes per LoRA rank row");
+static_assert(kPT == 256 && kPW == 4 && kLT == 256, "one compute wave per 4 state channels, one loader wave per 4 LoRA ranks");
 
-// TR: the variant that also writes traces and phase timestamps (tests and
-// profiling); the plain variant has none of that code.
-template <class S, bool TR>
-__global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a) {
-  extern __shared__ unsigned char smem[];
-  constexpr int DM = S::DM, DI = S::DI, NS = S::NS, HP = S::HP, G = S::G, CDIM = S::CDIM;
-  constexpr int MX = DM > DI ? DM : DI;
-  const int w = blockIdx.x;
-  const int hd = w / (HP / 16), j = w % (HP / 16);
-
-  // LDS carve-up
-  float* hs = (float*)smem;                     // [DM] residual stream
-  float* gs = hs + DM;                          // [DI] gated SSM output (all heads); also argmax candidates
-  int8_t* qs = (int8_t*)(gs + DI);              // [MX] int8 codes
-  uint2* lut = (uint2*)(qs + MX);               // [256][kLutCopies] sign table
-  float* bcs = (float*)(lut + 256 * kLutCopies);  // [2NS] B, C
-  float* tls = bcs + 2 * NS;                    // [16] LoRA down vector
-  float* rowv = tls + 16;                       // [kMaxInRows] outputs of own in_proj rows
-  float* red = rowv + kMaxInRows;               // [2*kPW]
-  int* s_stop = (int*)(red + 2 * kPW);          // [1]
-  int* s_tok = s_stop + 1;                      // [1]
-  float* s_arg = (float*)(s_tok + 2);           // [2*kPW]
-  if (threadIdx.x == 0) *s_stop = 0;
-  for (int f = threadIdx.x; f < 256 * kLutCopies; f += kPT) lut[f] = sign_entry((uint32_t)(f / kLutCopies));
-  wg_barrier();
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint2* lut_l = lut + (lane % kLutCopies);
-  unsigned e = a.epoch0;  // same value in every workgroup
-  int tok = kargs()->tok_in[0];
-  const char* wb = a.wbase;
-  unsigned pc = a.pair0;  // write count of the paired boxes (one write per layer)
-  uint64_t* const hbox = a.boxes;            // paired, DM / 2 words
-  uint64_t* const bcbox = hbox + kR * DM / 2;
-  uint64_t* const gbox = bcbox + kR * 2 * NS;  // paired, DI / 2 words
-  uint64_t* const abox = gbox + kR * DI / 2;
-
+// Where compute thread t (0 .. kPT) of workgroup w sits in the work split;
+// the loader waves stage each compute thread's operands from the same map.
+template <class S>
+struct TMap {
+  int wave, lane, hd, j, w;
+  int ji, subi, jo, subo;
+  bool lead_i, lead_o, bc_thread, x_thread, conv_thread;
+  int conv_k, conv_c, conv_slot;
+  __device__ TMap(int t, int w_) {
+    w = w_;
+    wave = t >> 6;
+    lane = t & 63;
+    hd = w / (S::HP / 16);
+    j = w % (S::HP / 16);
+    ji = lane & (S::UI - 1);
+    subi = lane / S::UI;
+    lead_i = lane == group_sum_lane(subi * S::UI, S::UI);
+    jo = lane & (S::UO - 1);
+    subo = lane / S::UO;
+    lead_o = lane == group_sum_lane(subo * S::UO, S::UO);
+    // conv threads: the lane that reduces B/C row k (< NBC, row group 0 of
+    // wave 0) convolves and publishes it right away; lanes 0..15 of wave 1
+    // convolve the 16 x channels after the GEMV
+    bc_thread = wave == 0 && lead_i && subi < S::NBC;
+    x_thread = wave == 1 && lane < 16;
+    conv_thread = bc_thread || x_thread;
+    conv_k = bc_thread ? subi : S::KX + (lane & 15);
+    conv_c = conv_thread ? in_row(conv_k) - S::DI : 0;
+    conv_slot = bc_thread ? 16 + subi : (lane & 15);
+  }
   // own in_proj rows, B/C first: their conv outputs are published while the
   // other rows are still being computed
-  constexpr int KZ = S::NBC, KX = S::NBC + 16, KDT = S::NBC + 32;
-  auto in_row = [&](int k) -> int {
-    if (k < KZ) return 2 * DI + (w + k * G);                  // B/C
-    if (k < KX) return hd * HP + j * 16 + (k - KZ);           // z
-    if (k < KDT) return DI + hd * HP + j * 16 + (k - KX);     // x
-    return 2 * DI + 2 * NS + hd;                              // dt
-  };
+  __device__ int in_row(int k) const {
+    if (k < S::KZ) return 2 * S::DI + (w + k * S::G);                       // B/C
+    if (k < S::KX) return hd * S::HP + j * 16 + (k - S::KZ);                // z
+    if (k < S::KDT) return S::DI + hd * S::HP + j * 16 + (k - S::KX);       // x
+    return 2 * S::DI + 2 * S::NS + hd;                                      // dt
+  }
+};
 
-  const int ji = lane & (S::UI - 1), subi = lane / S::UI;
-  const bool lead_i = lane == group_sum_lane(subi * S::UI, S::UI);
-  const int jo = lane & (S::UO - 1), subo = lane / S::UO;
-  const bool lead_o = lane == group_sum_lane(subo * S::UO, S::UO);
-  // conv threads: the lane that reduces B/C row k (< NBC, row group 0 of wave
-  // 0) convolves and publishes it right away; lanes 0..15 of wave 1 convolve
-  // the 16 x channels after the GEMV
-  const bool bc_thread = wave == 0 && lead_i && subi < S::NBC;
-  const bool x_thread = wave == 1 && lane < 16;
-  const bool conv_thread = bc_thread || x_thread;
-  const int conv_k = bc_thread ? subi : KX + (lane & 15);
-  const int conv_c = conv_thread ? in_row(conv_k) - DI : 0;
+// LDS carve-up.  The operand images (a layer's weights, scales and state as
+// the compute threads use them, [item][thread]) are written by the loader
+// waves and read by the compute waves.
+template <class S>
+struct Lds {
+  static constexpr int DM = S::DM, DI = S::DI, NS = S::NS, MX = DM > DI ? DM : DI;
+  static constexpr size_t O_WIN = 0;                                          // uint4 [NGI][kPT]
+  static constexpr size_t O_WOUT = O_WIN + (size_t)S::NGI * kPT * 16;         // uint4 [NGO][kPT]
+  static constexpr size_t O_ST = O_WOUT + (size_t)S::NGO * kPT * 16;          // float4 [NST][kPT]
+  static constexpr size_t O_HS = O_ST + (size_t)S::NST * kPT * 16;            // float [DM] residual stream
+  static constexpr size_t O_GS = O_HS + (size_t)DM * 4;                       // float [DI] gated SSM output
+  static constexpr size_t O_NW = O_GS + (size_t)DI * 4;                       // float [DM] norm weight
+  static constexpr size_t O_GW = O_NW + (size_t)DM * 4;                       // float [DI] gated norm weight
+  static constexpr size_t O_LUT = O_GW + (size_t)DI * 4;                      // uint2 [256][kLutCopies]
+  static constexpr size_t O_QS = O_LUT + (size_t)256 * kLutCopies * 8;        // int8 [MX] codes
+  static constexpr size_t O_ISW = O_QS + ((size_t)MX + 15) / 16 * 16;         // float [NGI][kPT]
+  static constexpr size_t O_ISB = O_ISW + (size_t)S::NGI * kPT * 4;           // float [NGI][kPT]
+  static constexpr size_t O_IB = O_ISB + (size_t)S::NGI * kPT * 4;            // int [NGI * RLI][kPT]
+  static constexpr size_t O_OSW = O_IB + (size_t)S::NGI * S::RLI * kPT * 4;   // float [NGO][kPT]
+  static constexpr size_t O_OSB = O_OSW + (size_t)S::NGO * kPT * 4;           // float [NGO][kPT]
+  static constexpr size_t O_OB = O_OSB + (size_t)S::NGO * kPT * 4;            // int [NGO * RLO][kPT]
+  static constexpr size_t O_CONV = O_OB + (size_t)S::NGO * S::RLO * kPT * 4;  // float [8][32] conv w, b, window
+  static constexpr size_t O_HP = O_CONV + 8 * 32 * 4;                         // float [4] dt bias, A_log, D
+  static constexpr size_t O_BCS = O_HP + 16;                                  // float [2 NS] B, C
+  static constexpr size_t O_TLS = O_BCS + (size_t)2 * NS * 4;                 // float [16] LoRA-down vector
+  static constexpr size_t O_ROWV = O_TLS + 16 * 4;                            // float [kMaxInRows] own in_proj rows
+  static constexpr size_t O_RED = O_ROWV + kMaxInRows * 4;                    // float [2 kPW]
+  static constexpr size_t O_STOP = O_RED + 2 * kPW * 4;                       // int [1], token int [1] (+ pad)
+  static constexpr size_t O_ARG = O_STOP + 16;                                // float [2 kPW]
+  static constexpr size_t BYTES = O_ARG + 2 * kPW * 4;
 
-  // ---- registers prefetched for phase A (in_proj) of a layer
-  uint4 win[S::NGI];
-  float nw[S::MW1];
-  float isw[S::NGI], isb[S::NGI];
-  int ib[S::NGI][S::RLI];  // LoRA-up weights of this lane's ranks (converted at use: a conversion
-                           // here would make the prefetch wait for its own load)
-  float cw[4], cb, cst[3];
-  float sAi;
-  uint4 ain[S::MC1];  // LoRA-down A chunks of this thread (see p_lora_down)
-  // ---- registers prefetched for phases S and B (SSM, out_proj) of a layer
-  uint4 wout[S::NGO];
-  float gw[S::MW2];
-  float osw[S::NGO], osb[S::NGO];
-  int ob[S::NGO][S::RLO];
-  float4 st[S::NST];  // state float4 (n = lane + 64 m, channels 4*wave ..) of the block [NS][16]
-  float dtb, alog, dval;
-  float sAo;
-  uint4 aout[S::MC2];
+  uint4 *win, *wout;
+  float4* st;
+  float *hs, *gs, *nw, *gw, *isw, *isb, *osw, *osb, *conv, *hp, *bcs, *tls, *rowv, *red, *arg;
+  int *ib, *ob, *stop, *tok;
+  uint2* lut;
+  int8_t* qs;
+  __device__ explicit Lds(unsigned char* m) {
+    win = (uint4*)(m + O_WIN);
+    wout = (uint4*)(m + O_WOUT);
+    st = (float4*)(m + O_ST);
+    hs = (float*)(m + O_HS);
+    gs = (float*)(m + O_GS);
+    nw = (float*)(m + O_NW);
+    gw = (float*)(m + O_GW);
+    lut = (uint2*)(m + O_LUT);
+    qs = (int8_t*)(m + O_QS);
+    isw = (float*)(m + O_ISW);
+    isb = (float*)(m + O_ISB);
+    ib = (int*)(m + O_IB);
+    osw = (float*)(m + O_OSW);
+    osb = (float*)(m + O_OSB);
+    ob = (int*)(m + O_OB);
+    conv = (float*)(m + O_CONV);
+    hp = (float*)(m + O_HP);
+    bcs = (float*)(m + O_BCS);
+    tls = (float*)(m + O_TLS);
+    rowv = (float*)(m + O_ROWV);
+    red = (float*)(m + O_RED);
+    stop = (int*)(m + O_STOP);
+    tok = stop + 1;
+    arg = (float*)(m + O_ARG);
+  }
+};
 
+// The loader waves (threads kPT .. kPT + kLT).  Loader thread lt stages the
+// operands of compute thread lt: per layer, the in_proj image (scaffold bits
+// of its rows, scales, LoRA-up weights, conv weights and window, the norm
+// weight) and the out_proj / SSM image (scaffold bits, scales, LoRA-up
+// weights, the SSM state block, the gated norm weight, the head's dt bias,
+// A_log and D).  It also holds the LoRA-down matrices (96 KB per layer at the
+// 1.3B shape, the bulk of what a workgroup reads) in registers and forms
+// t = A q while the compute waves run the scaffold GEMV.  So the compute
+// waves issue no weight or state loads at all: their instruction stream never
+// stalls behind a full memory queue, and their polls wait for nothing but the
+// hop (the vector memory counter is per wave).  Global loads are issued a
+// phase or more before their LDS writes, so the data has landed by then.
+// The loaders take no part in the hops: they pass the workgroup barriers in
+// the same sequence as the compute waves (listed at the kernel) and stop
+// where a hop reports an abort.
+//
+// Image timing (layer l): the compute waves read the in_proj image at the
+// start of the layer and the out_proj image after the B/C hop.  The loaders
+// issue the in_proj and out_proj loads of layer l+1 after the B/C hop (the
+// SSM phase) and write the in_proj image between the gated-output hop and the
+// gated norm, the out_proj image in layer l+1 between "in_proj rows done" and
+// the B/C hop; the out_proj LoRA-down matrix of layer l goes out in the norm
+// phase of layer l, the in_proj one of layer l+1 after the in_proj
+// LoRA-down.  Both images
+// are single-buffered: each write lands after the compute waves' last read
+// of the previous layer's image and before their first read of the new one.  Conv and SSM state written back by the
+// compute waves in layer l is re-read for layer l of the next token, at
+// least one layer later (n_layer >= 2), after the compute waves' polls have
+// completed those stores.
+template <int V>
+using I = std::integral_constant<int, V>;
+
+template <class S>
+__device__ void loader_waves(const PersistArgs& a, const Lds<S>& L) {
+  constexpr int DM = S::DM, DI = S::DI, NS = S::NS, HP = S::HP, CDIM = S::CDIM;
+  constexpr int NV1 = (DM / 4 + kLT - 1) / kLT, NV2 = (DI / 4 + kLT - 1) / kLT;  // float4 of a norm weight per thread
+  const int lt = (int)threadIdx.x - kPT, lane = lt & 63, lw = lt >> 6;
+  const TMap<S> tm(lt, blockIdx.x);
+  const int w = tm.w;
+  const char* wb = a.wbase;
   auto lp = [&](int l, int k) -> const char* { return wb + (size_t)l * S::LSTRIDE + S::OFF(k); };
 
-  auto load_A = [&](int l) {
+  // in flight: in_proj image, out_proj image, LoRA-down matrices
+  uint4 r_win[S::NGI];
+  float r_isw[S::NGI], r_isb[S::NGI];
+  int r_ib[S::NGI][S::RLI];
+  float r_conv[8];
+  float4 r_nw[NV1];
+  uint4 r_wout[S::NGO];
+  float r_osw[S::NGO], r_osb[S::NGO];
+  int r_ob[S::NGO][S::RLO];
+  float4 r_st[S::NST];
+  float4 r_gw[NV2];
+  float r_hp[3];
+  uint4 ain[S::MC1], aout[S::MC2];
+  float sAi, sAo;
+
+  auto load_in = [&](int l) {
     const uint4* b4 = (const uint4*)lp(l, DFSSM_PK_IN_BITS);
     const float* sw = (const float*)lp(l, DFSSM_PK_IN_SW);
     const float* sb = (const float*)lp(l, DFSSM_PK_IN_SB);
     const int8_t* bm = (const int8_t*)lp(l, DFSSM_PK_IN_B);
 #pragma unroll
     for (int m = 0; m < S::NGI; ++m) {
-      const int g = wave + m * kPW;
-      const int k = g * S::RPPI + subi;
+      const int g = tm.wave + m * kPW;
+      const int k = g * S::RPPI + tm.subi;
       const bool live = g < S::NGI_T && k < S::NROWS;
-      const int row = live ? in_row(k) : 0;
-      win[m] = live ? b4[(size_t)row * S::UI + ji] : make_uint4(0, 0, 0, 0);
-      isw[m] = live ? sw[row] : 0.0f;
-      isb[m] = live ? sb[row] : 0.0f;
+      const int row = live ? tm.in_row(k) : 0;
+      r_win[m] = live ? b4[(size_t)row * S::UI + tm.ji] : make_uint4(0, 0, 0, 0);
+      r_isw[m] = live ? sw[row] : 0.0f;
+      r_isb[m] = live ? sb[row] : 0.0f;
 #pragma unroll
       for (int r = 0; r < S::RLI; ++r) {
-        const int kk = ji + S::UI * r;
-        ib[m][r] = live && kk < 16 ? (int)bm[(size_t)row * 16 + kk] : 0;
+        const int kk = tm.ji + S::UI * r;
+        r_ib[m][r] = live && kk < 16 ? (int)bm[(size_t)row * 16 + kk] : 0;
       }
     }
-    const float* nwp = (const float*)lp(l, DFSSM_PK_NORM_W);
-    load_norm_w<S::MW1>(nw, nwp);
-    sAi = ((const float*)lp(l, DFSSM_PK_IN_SA))[4 * wave + (lane & 3)];
-    if (conv_thread) {
-      const float* wc = (const float*)lp(l, DFSSM_PK_CONV_W) + (size_t)conv_c * 4;
-      cw[0] = wc[0]; cw[1] = wc[1]; cw[2] = wc[2]; cw[3] = wc[3];
-      cb = ((const float*)lp(l, DFSSM_PK_CONV_B))[conv_c];
+    if (tm.conv_thread) {
+      const float* wc = (const float*)lp(l, DFSSM_PK_CONV_W) + (size_t)tm.conv_c * 4;
       const float* cs = a.conv + (size_t)l * 3 * CDIM;
-      cst[0] = cs[conv_c]; cst[1] = cs[CDIM + conv_c]; cst[2] = cs[2 * CDIM + conv_c];
+      r_conv[0] = wc[0]; r_conv[1] = wc[1]; r_conv[2] = wc[2]; r_conv[3] = wc[3];
+      r_conv[4] = ((const float*)lp(l, DFSSM_PK_CONV_B))[tm.conv_c];
+      r_conv[5] = cs[tm.conv_c]; r_conv[6] = cs[CDIM + tm.conv_c]; r_conv[7] = cs[2 * CDIM + tm.conv_c];
+    }
+    const float4* n4 = (const float4*)lp(l, DFSSM_PK_NORM_W);
+#pragma unroll
+    for (int m = 0; m < NV1; ++m) {
+      const int q = lt + kLT * m;
+      r_nw[m] = q < DM / 4 ? n4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  auto load_B = [&](int l) {
+  auto write_in = [&]() {
+#pragma unroll
+    for (int m = 0; m < S::NGI; ++m) {
+      L.win[m * kPT + lt] = r_win[m];
+      L.isw[m * kPT + lt] = r_isw[m];
+      L.isb[m * kPT + lt] = r_isb[m];
+#pragma unroll
+      for (int r = 0; r < S::RLI; ++r) L.ib[(m * S::RLI + r) * kPT + lt] = r_ib[m][r];
+    }
+    if (tm.conv_thread)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) L.conv[e * 32 + tm.conv_slot] = r_conv[e];
+#pragma unroll
+    for (int m = 0; m < NV1; ++m) {
+      const int q = lt + kLT * m;
+      if (q < DM / 4) ((float4*)L.nw)[q] = r_nw[m];
+    }
+  };
+  auto load_out = [&](int l) {
     const uint4* b4 = (const uint4*)lp(l, DFSSM_PK_OUT_BITS);
     const float* sw = (const float*)lp(l, DFSSM_PK_OUT_SW);
     const float* sb = (const float*)lp(l, DFSSM_PK_OUT_SB);
     const int8_t* bm = (const int8_t*)lp(l, DFSSM_PK_OUT_B);
 #pragma unroll
     for (int m = 0; m < S::NGO; ++m) {
-      const int g = wave + m * kPW;
-      const int k = g * S::RPPO + subo;
+      const int g = tm.wave + m * kPW;
+      const int k = g * S::RPPO + tm.subo;
       const bool live = g < S::NGO_T && k < S::OUT_PER;
-      const int row = w * S::OUT_PER + k;
-      wout[m] = live ? b4[(size_t)row * S::UO + jo] : make_uint4(0, 0, 0, 0);
-      osw[m] = live ? sw[row] : 0.0f;
-      osb[m] = live ? sb[row] : 0.0f;
+      const int row = w * S::OUT_PER + (live ? k : 0);
+      r_wout[m] = live ? b4[(size_t)row * S::UO + tm.jo] : make_uint4(0, 0, 0, 0);
+      r_osw[m] = live ? sw[row] : 0.0f;
+      r_osb[m] = live ? sb[row] : 0.0f;
 #pragma unroll
       for (int r = 0; r < S::RLO; ++r) {
-        const int kk = jo + S::UO * r;
-        ob[m][r] = live && kk < 16 ? (int)bm[(size_t)row * 16 + kk] : 0;
+        const int kk = tm.jo + S::UO * r;
+        r_ob[m][r] = live && kk < 16 ? (int)bm[(size_t)row * 16 + kk] : 0;
       }
     }
-    const float* gwp = (const float*)lp(l, DFSSM_PK_GNORM_W);
-    load_norm_w<S::MW2>(gw, gwp);
-    sAo = ((const float*)lp(l, DFSSM_PK_OUT_SA))[4 * wave + (lane & 3)];
     const float4* s4 = (const float4*)(a.ssm + (size_t)l * S::H * HP * NS + (size_t)w * NS * 16);
 #pragma unroll
     for (int m = 0; m < S::NST; ++m) {
-      const int n = lane + 64 * m;
-      st[m] = n < NS ? s4[n * 4 + wave] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int n = tm.lane + 64 * m;
+      r_st[m] = n < NS ? s4[n * 4 + tm.wave] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    dtb = ((const float*)lp(l, DFSSM_PK_DT_BIAS))[hd];
-    alog = ((const float*)lp(l, DFSSM_PK_A_LOG))[hd];
-    dval = ((const float*)lp(l, DFSSM_PK_D))[hd];
+    const float4* g4 = (const float4*)lp(l, DFSSM_PK_GNORM_W);
+#pragma unroll
+    for (int m = 0; m < NV2; ++m) {
+      const int q = lt + kLT * m;
+      r_gw[m] = q < DI / 4 ? g4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (lt == 0) {
+      r_hp[0] = ((const float*)lp(l, DFSSM_PK_DT_BIAS))[tm.hd];
+      r_hp[1] = ((const float*)lp(l, DFSSM_PK_A_LOG))[tm.hd];
+      r_hp[2] = ((const float*)lp(l, DFSSM_PK_D))[tm.hd];
+    }
   };
-
-  // the LoRA-down matrices (the bulk of the prefetched bytes): rows
-  // 4 wave + r, chunks lane + 64 j (the p_lora_down layout)
+  auto write_out = [&]() {
+#pragma unroll
+    for (int m = 0; m < S::NGO; ++m) {
+      L.wout[m * kPT + lt] = r_wout[m];
+      L.osw[m * kPT + lt] = r_osw[m];
+      L.osb[m * kPT + lt] = r_osb[m];
+#pragma unroll
+      for (int r = 0; r < S::RLO; ++r) L.ob[(m * S::RLO + r) * kPT + lt] = r_ob[m][r];
+    }
+#pragma unroll
+    for (int m = 0; m < S::NST; ++m) L.st[m * kPT + lt] = r_st[m];
+#pragma unroll
+    for (int m = 0; m < NV2; ++m) {
+      const int q = lt + kLT * m;
+      if (q < DI / 4) ((float4*)L.gw)[q] = r_gw[m];
+    }
+    if (lt == 0) {
+      L.hp[0] = r_hp[0];
+      L.hp[1] = r_hp[1];
+      L.hp[2] = r_hp[2];
+    }
+  };
+  // LoRA-down matrices: rows 4 lw + r, chunks lane + 64 j (the p_lora_down layout)
   auto load_ain = [&](int l) {
     const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_IN_A);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int j = 0; j < S::J1; ++j) {
-        const int c = lane + 64 * j;
-        ain[r * S::J1 + j] = c < DM / 16 ? A4[(size_t)(4 * wave + r) * (DM / 16) + c] : make_uint4(0, 0, 0, 0);
+      for (int jj = 0; jj < S::J1; ++jj) {
+        const int c = lane + 64 * jj;
+        ain[r * S::J1 + jj] = c < DM / 16 ? A4[(size_t)(4 * lw + r) * (DM / 16) + c] : make_uint4(0, 0, 0, 0);
       }
+    sAi = ((const float*)lp(l, DFSSM_PK_IN_SA))[4 * lw + (lane & 3)];
   };
-  auto load_aout = [&](int l) {
+  // rows 4 lw + r for r in [R0, R1) (compile-time bounds: no branches around the loads)
+  auto load_aout = [&](int l, auto r0c, auto r1c) {
+    constexpr int R0 = decltype(r0c)::value, R1 = decltype(r1c)::value;
     const uint4* A4 = (const uint4*)lp(l, DFSSM_PK_OUT_A);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = R0; r < R1; ++r)
 #pragma unroll
-      for (int j = 0; j < S::J2; ++j) {
-        const int c = lane + 64 * j;
-        aout[r * S::J2 + j] = c < DI / 16 ? A4[(size_t)(4 * wave + r) * (DI / 16) + c] : make_uint4(0, 0, 0, 0);
+      for (int jj = 0; jj < S::J2; ++jj) {
+        const int c = lane + 64 * jj;
+        aout[r * S::J2 + jj] = c < DI / 16 ? A4[(size_t)(4 * lw + r) * (DI / 16) + c] : make_uint4(0, 0, 0, 0);
       }
+    if constexpr (R0 == 0) sAo = ((const float*)lp(l, DFSSM_PK_OUT_SA))[4 * lw + (lane & 3)];
   };
+  auto stopped = [&]() { return *L.stop != 0; };
 
-  // conv shift register of this thread's channel (window written back after the B/C hop)
+  const int T = a.n_tokens, Lm = a.n_layer;
+  // A workgroup's loads share one memory pipeline, so a compute wave's poll
+  // queues behind any loader bytes issued just before it; and a loader wave
+  // that is still issuing loads when the compute waves reach a barrier holds
+  // them there.  So the loads go out in pieces that each fit the compute
+  // phase between two barriers, in the phases without a poll at their end.
+  load_in(0);
+  load_ain(0);
+  load_out(0);
+  load_aout(0, I<0>{}, I<2>{});
+  write_in();
+  for (int t = 0; t < T; ++t) {
+    wg_barrier();  // embedding row in LDS
+    for (int l = 0; l < Lm; ++l) {
+      const int ln = l + 1 < Lm ? l + 1 : 0;  // after the last layer: layer 0 of the next token
+      if (l > 0) {
+        wg_barrier();  // residual hop
+        if (stopped()) return;
+      }
+      load_aout(l, I<2>{}, I<4>{});
+      wg_barrier();  // norm statistics
+      wg_barrier();  // in_proj codes in LDS
+      p_lora_down<S::J1>(ain, DM, L.qs, sAi, L.tls, lane, lw);
+      wg_barrier();  // LoRA-down vector ready
+      load_in(ln);
+      load_ain(ln);
+      wg_barrier();  // in_proj rows done
+      write_out();   // this layer's out_proj image
+      wg_barrier();  // B/C hop
+      if (stopped()) return;
+      wg_barrier();  // gated-output hop
+      if (stopped()) return;
+      write_in();    // the next layer's in_proj image
+      wg_barrier();  // gated norm statistics
+      wg_barrier();  // out_proj codes in LDS
+      p_lora_down<S::J2>(aout, DI, L.qs, sAo, L.tls, lane, lw);
+      wg_barrier();  // LoRA-down vector ready
+      load_out(ln);
+      load_aout(ln, I<0>{}, I<2>{});
+      wg_barrier();  // end of layer
+    }
+    wg_barrier();  // final residual hop
+    if (stopped()) return;
+    wg_barrier();  // final norm statistics
+    wg_barrier();  // final codes
+    wg_barrier();  // per-wave argmax candidates
+    wg_barrier();  // argmax hop
+    if (stopped()) return;
+    wg_barrier();  // next token chosen
+  }
+}
+
+// TR: the variant that also writes traces and phase timestamps (tests and
+// profiling); the plain variant has none of that code.
+//
+// Workgroup barriers per token, the same sequence in the compute and loader
+// waves: embedding; per layer [residual hop (layers > 0)], norm statistics,
+// codes, LoRA-down vector ready, in_proj rows done, B/C hop, gated-output
+// hop, gated norm statistics, codes, LoRA-down vector ready, end of layer;
+// then final residual hop, final norm statistics, codes, per-wave argmax
+// candidates, argmax hop, next token chosen.
+template <class S, bool TR>
+__global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArgs a) {
+  extern __shared__ unsigned char smem[];
+  constexpr int DM = S::DM, DI = S::DI, NS = S::NS, HP = S::HP, G = S::G, CDIM = S::CDIM;
+  constexpr int KZ = S::KZ, KX = S::KX, KDT = S::KDT;
+  const Lds<S> L(smem);
+  float* const hs = L.hs;
+  float* const gs = L.gs;
+  int8_t* const qs = L.qs;
+  float* const bcs = L.bcs;
+  float* const tls = L.tls;
+  float* const rowv = L.rowv;
+  float* const red = L.red;
+  int* const s_stop = L.stop;
+  int* const s_tok = L.tok;
+  float* const s_arg = L.arg;
+  if (threadIdx.x == 0) *s_stop = 0;
+  for (int f = threadIdx.x; f < 256 * kLutCopies; f += kBlock) L.lut[f] = sign_entry((uint32_t)(f / kLutCopies));
+  wg_barrier();
+  if (threadIdx.x >= kPT) {
+    loader_waves<S>(a, L);
+    return;
+  }
+
+  const int w = blockIdx.x;
+  const TMap<S> tm(threadIdx.x, w);
+  const int lane = tm.lane, wave = tm.wave, hd = tm.hd, j = tm.j;
+  const int ji = tm.ji, subi = tm.subi, jo = tm.jo, subo = tm.subo;
+  const bool lead_i = tm.lead_i, lead_o = tm.lead_o, bc_thread = tm.bc_thread, x_thread = tm.x_thread;
+  const bool conv_thread = tm.conv_thread;
+  const int conv_k = tm.conv_k, conv_c = tm.conv_c;
+  const uint2* lut_l = L.lut + (lane % kLutCopies);
+  unsigned e = a.epoch0;  // same value in every workgroup
+  int tok = kargs()->tok_in[0];
+  unsigned pc = a.pair0;  // write count of the paired boxes (one write per layer)
+  uint64_t* const hbox = a.boxes;            // paired, DM / 2 words
+  uint64_t* const bcbox = hbox + kR * DM / 2;
+  uint64_t* const gbox = bcbox + kR * 2 * NS;  // paired, DI / 2 words
+  uint64_t* const abox = gbox + kR * DI / 2;
+
+  // conv weights and window of this thread's channel (conv threads)
+  float cw[4], cb, cst[3];
   auto conv_step = [&](float y) -> float {
     const float v = cb + cw[0] * cst[0] + cw[1] * cst[1] + cw[2] * cst[2] + cw[3] * y;
     cst[0] = cst[1];
@@ -661,17 +904,6 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     }
   };
 
-  // The next operands are prefetched just before a hop: the wave would idle
-  // while polling anyway, and a burst of loads issued inside a compute phase
-  // stalls that phase's instruction stream once the memory queue is full.
-  // The hop's polls then also wait for the prefetch to land (the vector
-  // memory counter completes in order), so the bytes go where the wait is
-  // longest: the g hop carries the out-proj LoRA-down matrix and the next
-  // layer's in-proj operands, the h hop the out-proj operands, the SSM state
-  // and the in-proj LoRA-down matrix, and the short B/C hop nothing.
-  load_A(0);
-  load_ain(0);
-  load_B(0);
   const int T = a.n_tokens;
   const int Lm = a.n_layer;
   bool ok = true;
@@ -695,6 +927,24 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
     }
     for (int l = 0; l < Lm && ok; ++l) {
       prof(t, l, 0);
+      // this layer's in_proj image (staged by the loader waves)
+      uint4 win[S::NGI];
+      float isw[S::NGI], isb[S::NGI];
+      int ib[S::NGI][S::RLI];
+#pragma unroll
+      for (int m = 0; m < S::NGI; ++m) {
+        win[m] = L.win[m * kPT + threadIdx.x];
+        isw[m] = L.isw[m * kPT + threadIdx.x];
+        isb[m] = L.isb[m * kPT + threadIdx.x];
+#pragma unroll
+        for (int r = 0; r < S::RLI; ++r) ib[m][r] = L.ib[(m * S::RLI + r) * kPT + threadIdx.x];
+      }
+      if (conv_thread) {
+        const float* cv = L.conv + tm.conv_slot;
+        cw[0] = cv[0]; cw[1] = cv[32]; cw[2] = cv[64]; cw[3] = cv[96];
+        cb = cv[128];
+        cst[0] = cv[160]; cst[1] = cv[192]; cst[2] = cv[224];
+      }
       if (l > 0) {
         ok = gather2<S::GW1>(hbox, DM / 2, pc - 1, hs, a.abort_flag, s_stop);
         ++e;
@@ -706,7 +956,9 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         if (th && w == 0)
           for (int i = threadIdx.x; i < DM; i += kPT) th[(size_t)l * DM + i] = hs[i];
       }
-      // ---- phase A: norm, quantise, LoRA down, 1-bit GEMV of own rows, conv
+      // ---- phase A: norm, quantise, 1-bit GEMV of own rows (LoRA down by the loaders), conv
+      float nw[S::MW1];
+      load_norm_w<S::MW1>(nw, L.nw);
       const float s1 = p_norm_quant<S::MW1>(hs, nw, DM, a.eps, qs, red);
       prof(t, l, 2);
       if constexpr (TR) {
@@ -714,36 +966,37 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         if (tq && w == 0)
           for (int i = threadIdx.x; i < DM; i += kPT) tq[(size_t)l * DM + i] = qs[qbyte(i)];
       }
-      p_lora_down<S::J1>(ain, DM, qs, sAi, s1, tls);
-      prof(t, l, 3);
       {
         // Every row group is computed (a wave's unused group has zero weights
         // and is not stored), so the table lookups of all groups are in flight
-        // together.  The LoRA-up term is spread over the row's lanes.
+        // together; the loader waves form the LoRA-down vector meanwhile.  The
+        // LoRA-up term is spread over the row's lanes.
         uint32_t qd[32];
         load_codes(qs, ji, qd);
+        int part[S::NGI];
+#pragma unroll
+        for (int m = 0; m < S::NGI; ++m) part[m] = p_sign_dot(win[m], qd, lut_l);
+        wg_barrier();  // LoRA-down vector ready
+        prof(t, l, 3);
         float tl[S::RLI];
 #pragma unroll
-        for (int r = 0; r < S::RLI; ++r) tl[r] = ji + S::UI * r < 16 ? tls[ji + S::UI * r] : 0.0f;
+        for (int r = 0; r < S::RLI; ++r) tl[r] = ji + S::UI * r < 16 ? tls[ji + S::UI * r] * s1 : 0.0f;
         auto row_out = [&](int m, int part) -> float {
           const int acc = group_sum_i(part, S::UI);
           float lo = 0.0f;
 #pragma unroll
-          for (int r = 0; r < S::RLI; ++r) lo += (float)at_use(ib[m][r]) * tl[r];
+          for (int r = 0; r < S::RLI; ++r) lo += (float)ib[m][r] * tl[r];
           lo = group_sum_f(lo, S::UI);
           return (float)acc * isw[m] * s1 + isb[m] * lo;
         };
         // row group 0 first: it holds the B/C row, whose conv output is
-        // published before the remaining groups are computed
+        // published before the remaining groups are finished
         {
-          const float y = row_out(0, p_sign_dot(win[0], qd, lut_l));
+          const float y = row_out(0, part[0]);
           const int k = wave * S::RPPI + subi;
           if (lead_i && wave < S::NGI_T && k < S::NROWS) rowv[k] = y;
           if (bc_thread) publish(bcbox, 2 * NS, conv_c - DI, conv_step(y), e);
         }
-        int part[S::NGI];
-#pragma unroll
-        for (int m = 1; m < S::NGI; ++m) part[m] = p_sign_dot(win[m], qd, lut_l);
 #pragma unroll
         for (int m = 1; m < S::NGI; ++m) {
           const float y = row_out(m, part[m]);
@@ -752,7 +1005,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
           if (lead_i && g < S::NGI_T && k < S::NROWS) rowv[k] = y;
         }
       }
-      wg_barrier();
+      wg_barrier();  // in_proj rows done
       prof(t, l, 4);
       if (x_thread) rowv[conv_k] = conv_step(rowv[conv_k]);
       prof(t, l, 5);
@@ -760,16 +1013,31 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       ++e;
       if (!ok) break;
       prof(t, l, 6);
-      // stores go out after the hop, for the same reason as the prefetches
       if (conv_thread) {
         float* cs = a.conv + (size_t)l * 3 * CDIM;
         cs[conv_c] = cst[0];
         cs[CDIM + conv_c] = cst[1];
         cs[2 * CDIM + conv_c] = cst[2];
       }
+      // this layer's out_proj image (staged by the loader waves)
+      uint4 wout[S::NGO];
+      float osw[S::NGO], osb[S::NGO];
+      int ob[S::NGO][S::RLO];
+      float4 st[S::NST];  // state float4 (n = lane + 64 m, channels 4*wave ..) of the block [NS][16]
+#pragma unroll
+      for (int m = 0; m < S::NGO; ++m) {
+        wout[m] = L.wout[m * kPT + threadIdx.x];
+        osw[m] = L.osw[m * kPT + threadIdx.x];
+        osb[m] = L.osb[m * kPT + threadIdx.x];
+#pragma unroll
+        for (int r = 0; r < S::RLO; ++r) ob[m][r] = L.ob[(m * S::RLO + r) * kPT + threadIdx.x];
+      }
+#pragma unroll
+      for (int m = 0; m < S::NST; ++m) st[m] = L.st[m * kPT + threadIdx.x];
       // ---- phase S: SSM on the state block [hd][j*16 .. +16][0 .. NS), gate.
       // Wave v owns channels 4v .. 4v+3, its lanes the state rows n = lane + 64 m.
       {
+        const float dtb = L.hp[0], alog = L.hp[1], dval = L.hp[2];
         const float dt = softplus_f(rowv[KDT] + dtb);
         const float dA = __expf(-dt * __expf(alog));
         const float* xr = rowv + KX + wave * 4;
@@ -808,8 +1076,6 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         }
       }
       prof(t, l, 7);
-      load_aout(l);
-      load_A(l + 1 < Lm ? l + 1 : 0);  // after the last layer: layer 0 of the next token
       ok = gather2<S::GW2>(gbox, DI / 2, pc, gs, a.abort_flag, s_stop);
       ++e;
       if (!ok) break;
@@ -823,29 +1089,31 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
         }
       }
 
-      // ---- phase B: gated norm, quantise, LoRA down, 1-bit GEMV of own rows, residual
+      // ---- phase B: gated norm, quantise, 1-bit GEMV of own rows (LoRA down by the loaders), residual
       {
+        float gw[S::MW2];
+        load_norm_w<S::MW2>(gw, L.gw);
         const float s2 = p_norm_quant<S::MW2>(gs, gw, DI, a.eps, qs, red);
         if constexpr (TR) {
           int8_t* tq = kargs()->trace_q2;
           if (tq && w == 0)
             for (int i = threadIdx.x; i < DI; i += kPT) tq[(size_t)l * DI + i] = qs[qbyte(i)];
         }
-        p_lora_down<S::J2>(aout, DI, qs, sAo, s2, tls);
         uint32_t qd[32];
         load_codes(qs, jo, qd);
-        float tl[S::RLO];
-#pragma unroll
-        for (int r = 0; r < S::RLO; ++r) tl[r] = jo + S::UO * r < 16 ? tls[jo + S::UO * r] : 0.0f;
         int part[S::NGO];
 #pragma unroll
         for (int m = 0; m < S::NGO; ++m) part[m] = p_sign_dot(wout[m], qd, lut_l);
+        wg_barrier();  // LoRA-down vector ready
+        float tl[S::RLO];
+#pragma unroll
+        for (int r = 0; r < S::RLO; ++r) tl[r] = jo + S::UO * r < 16 ? tls[jo + S::UO * r] * s2 : 0.0f;
 #pragma unroll
         for (int m = 0; m < S::NGO; ++m) {
           const int acc = group_sum_i(part[m], S::UO);
           float lo = 0.0f;
 #pragma unroll
-          for (int r = 0; r < S::RLO; ++r) lo += (float)at_use(ob[m][r]) * tl[r];
+          for (int r = 0; r < S::RLO; ++r) lo += (float)ob[m][r] * tl[r];
           lo = group_sum_f(lo, S::UO);
           const int g = wave + m * kPW;
           const int k = g * S::RPPO + subo;
@@ -859,9 +1127,7 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
       }
       prof(t, l, 9);
       ++pc;
-      load_B(l + 1 < Lm ? l + 1 : 0);
-      load_ain(l + 1 < Lm ? l + 1 : 0);
-      wg_barrier();
+      wg_barrier();  // end of layer
     }
     if (!ok) break;
     // ---- final norm + LM head + argmax
@@ -998,12 +1264,6 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(PersistArgs a
 using ShapeTiny = PShape<256, 512, 16, 32>;
 using Shape1p3b = PShape<2048, 4096, 128, 64>;
 
-static size_t lds_bytes(int dm, int di, int ns) {
-  const int mx = dm > di ? dm : di;
-  return (size_t)dm * 4 + (size_t)di * 4 + (size_t)mx + 256 * kLutCopies * 8 + (size_t)2 * ns * 4 + 16 * 4 +
-         kMaxInRows * 4 + 2 * kPW * 4 + 16 + 2 * kPW * 4 + 16;
-}
-
 template <class S>
 static const void* kernel_of(bool tr) {
   return tr ? (const void*)decode_persistent_kernel<S, true> : (const void*)decode_persistent_kernel<S, false>;
@@ -1012,6 +1272,12 @@ static const void* kernel_of(bool tr) {
 template <class S>
 static bool shape_is(int dm, int di, int ns, int hp) {
   return dm == S::DM && di == S::DI && ns == S::NS && hp == S::HP;
+}
+
+static size_t lds_bytes(int dm, int di, int ns, int hp) {
+  if (shape_is<Shape1p3b>(dm, di, ns, hp)) return Lds<Shape1p3b>::BYTES;
+  if (shape_is<ShapeTiny>(dm, di, ns, hp)) return Lds<ShapeTiny>::BYTES;
+  return 0;
 }
 
 static const void* select_kernel(int dm, int di, int ns, int hp, size_t* stride, bool tr = false) {
@@ -1039,8 +1305,8 @@ hipError_t launch_decode_persistent(const PersistArgs& a, int grid, hipStream_t 
   if (!k) return hipErrorInvalidValue;
   PersistArgs args = a;
   void* params[] = {&args};
-  return hipLaunchCooperativeKernel(k, dim3(grid), dim3(kPT), params,
-                                    (unsigned)lds_bytes(a.d_model, a.d_inner, a.d_state), st);
+  return hipLaunchCooperativeKernel(k, dim3(grid), dim3(kBlock), params,
+                                    (unsigned)lds_bytes(a.d_model, a.d_inner, a.d_state, a.headdim), st);
 }
 
 // Whether the persistent kernel can run for these dimensions with `grid`
@@ -1058,7 +1324,10 @@ bool persistent_supported(int d_model, int d_inner, int d_state, int headdim, in
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return no("no CU count");
   for (int tr = 0; tr < 2; ++tr) {  // both variants (plain, tracing) must fit
     k = select_kernel(d_model, d_inner, d_state, headdim, &stride, tr != 0);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kPT, lds_bytes(d_model, d_inner, d_state)) !=
+    const size_t lds = lds_bytes(d_model, d_inner, d_state, headdim);
+    if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return no("the kernel's LDS carve-up does not fit a workgroup on this device");
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kBlock, lds) !=
         hipSuccess)
       return no("occupancy query failed");
     if ((long)per_cu * cus < grid) return no("grid does not fit co-resident on this device");

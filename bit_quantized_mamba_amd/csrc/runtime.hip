@@ -689,6 +689,11 @@ dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** o
   const char* why = "";
   c->persist_ok = persistent_supported(c->dm, c->di, c->N, c->P, c->H, c->r, c->persist_grid, &why);
   c->persist_why = why;
+  if (c->persist_ok && c->L < 2) {
+    // the kernel re-reads a layer's conv and SSM state one layer after writing it back
+    c->persist_ok = false;
+    c->persist_why = "the persistent kernel needs at least 2 layers";
+  }
   if (c->persist_ok) {
     // the kernel addresses layer l, kind k as base + l * stride + offset(k): check that this is our layout
     size_t stride = 0, offs[DFSSM_T_PER_LAYER];
