@@ -33,9 +33,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # (FETCH_SIZE reads 0.5 GiB for it: factor 2.0; WRITE_SIZE reads 1 GiB: 1.0).
 # Valid only for the kernel sources they were taken from (hash below).
 COUNTED_TRAFFIC = {
-    "sources_sha256": "0f676bdd6764a47a63b184503f04d27b45acd10396627b231dea5a861667524c",
-    "fetch_bytes_per_token": 466470432,
-    "write_bytes_per_token": 132648156,
+    "sources_sha256": "a50e104bbabc2b87b9b79af83c9a62e001c0d977daeee5f89fedd73fcebff1f7",
+    "fetch_bytes_per_token": 459930201,
+    "write_bytes_per_token": 118426850,
 }
 KERNEL_SOURCES = ("bit_quantized_mamba_amd/csrc/persistent.hip", "bit_quantized_mamba_amd/csrc/persistent.h",
                   "bit_quantized_mamba_amd/csrc/common.h")
