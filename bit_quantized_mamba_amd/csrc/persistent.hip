@@ -128,11 +128,10 @@ __device__ __forceinline__ void publish2(uint64_t* box, int n, int i, float v0, 
 // PAIRED: paired words, fresh when their tag is tag_bits(key), two floats each
 // to dst; else {value, epoch} words, fresh when the epoch is key.
 template <int MAXW, bool PAIRED>
-__device__ bool gather_words(const uint64_t* box, int n, unsigned key, float* dst, int* abort_flag, int* s_stop) {
+__device__ bool poll_words(const uint64_t* box, int n, unsigned key, uint64_t (&w)[MAXW], int* abort_flag) {
   const uint64_t* src = box + (size_t)(blockIdx.x % kR) * n;
   const uint64_t tb = tag_bits(key);
   auto fresh = [&](uint64_t v) { return PAIRED ? (v & kTagMask) == tb : (unsigned)(v >> 32) == key; };
-  uint64_t w[MAXW];
 #pragma unroll
   for (int m = 0; m < MAXW; ++m) {
     const int i = threadIdx.x + m * kPT;
@@ -167,6 +166,12 @@ __device__ bool gather_words(const uint64_t* box, int n, unsigned key, float* ds
     for (int m = 0; m < MAXW; ++m)
       if (!fresh(w[m])) w[m] = ld64(src + threadIdx.x + m * kPT);
   }
+  return ok;
+}
+template <int MAXW, bool PAIRED>
+__device__ bool gather_words(const uint64_t* box, int n, unsigned key, float* dst, int* abort_flag, int* s_stop) {
+  uint64_t w[MAXW];
+  const bool ok = poll_words<MAXW, PAIRED>(box, n, key, w, abort_flag);
   if (ok) {
 #pragma unroll
     for (int m = 0; m < MAXW; ++m) {
@@ -295,6 +300,61 @@ __device__ float p_norm_quant(const float* xs, const float (&wr)[MW], int n, flo
   } else {
 #pragma unroll
     for (int m = 0; m < MW; ++m) qs[qbyte(norm_idx<MW>(m))] = (int8_t)code(m);
+  }
+  wg_barrier();
+  return amax > 0.0f ? amax / 127.0f : 0.0f;
+}
+
+// The residual and gated-output hops fused with the first half of their
+// RMSNorm + quantiser: the thread that polled paired words i = t + 256 m
+// keeps their values (inputs 2i, 2i+1, held in x) and forms p = x w, the
+// partial sum of squares and max |p| (wave totals into red), so the hop's
+// closing barrier is also the norm's statistics barrier and the values never
+// take an LDS round trip.  np = number of pairs.
+template <int MP>
+__device__ __forceinline__ void pair_stats(const float (&x)[2 * MP], const float* wts, int np, float (&p)[2 * MP],
+                                           float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float ss = 0.0f, pm = 0.0f;
+#pragma unroll
+  for (int m = 0; m < MP; ++m) {
+    const int i = threadIdx.x + m * kPT;
+    const float2 w2 = i < np ? ((const float2*)wts)[i] : make_float2(0.0f, 0.0f);
+    p[2 * m] = x[2 * m] * w2.x;
+    p[2 * m + 1] = x[2 * m + 1] * w2.y;
+    ss += x[2 * m] * x[2 * m];
+    ss += x[2 * m + 1] * x[2 * m + 1];
+    pm = fmaxf(pm, fmaxf(fabsf(p[2 * m]), fabsf(p[2 * m + 1])));
+  }
+  ss = wave_sum(ss);
+  pm = wave_max(pm);
+  if (lane == 0) {
+    red[wave] = ss;
+    red[kPW + wave] = pm;
+  }
+}
+// Second half (after the statistics barrier): the scale, then the codes of
+// the held pairs into qs (swizzled), then the codes barrier.  n = 2 np
+// inputs; returns amax / 127 as p_norm_quant does.
+template <int MP>
+__device__ float pair_quant(const float (&p)[2 * MP], int np, float eps, const float* red, int8_t* qs) {
+  float tss = 0.0f, tpm = 0.0f;
+#pragma unroll
+  for (int v = 0; v < kPW; ++v) {
+    tss += red[v];
+    tpm = fmaxf(tpm, red[kPW + v]);
+  }
+  const float rstd = 1.0f / sqrtf(tss / (float)(2 * np) + eps);
+  const float amax = rstd * tpm;
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  auto code = [&](float pv) -> uint32_t {
+    const float rq = rintf((rstd * pv) * inv);
+    return (uint32_t)(int)fminf(fmaxf(rq, -127.0f), 127.0f) & 0xFFu;
+  };
+#pragma unroll
+  for (int m = 0; m < MP; ++m) {
+    const int i = threadIdx.x + m * kPT;
+    if (i < np) *(uint16_t*)(qs + qbyte(2 * i)) = (uint16_t)(code(p[2 * m]) | (code(p[2 * m + 1]) << 8));
   }
   wg_barrier();
   return amax > 0.0f ? amax / 127.0f : 0.0f;
@@ -799,12 +859,9 @@ __device__ void loader_waves(const PersistArgs& a, const Lds<S>& L) {
     wg_barrier();  // embedding row in LDS
     for (int l = 0; l < Lm; ++l) {
       const int ln = l + 1 < Lm ? l + 1 : 0;  // after the last layer: layer 0 of the next token
-      if (l > 0) {
-        wg_barrier();  // residual hop
-        if (stopped()) return;
-      }
+      wg_barrier();  // residual hop (layers > 0) and norm statistics
+      if (stopped()) return;
       load_aout(l, I<2>{}, I<4>{});
-      wg_barrier();  // norm statistics
       wg_barrier();  // in_proj codes in LDS
       p_lora_down<S::J1>(ain, DM, L.qs, sAi, L.tls, lane, lw);
       wg_barrier();  // LoRA-down vector ready
@@ -814,10 +871,9 @@ __device__ void loader_waves(const PersistArgs& a, const Lds<S>& L) {
       write_out();   // this layer's out_proj image
       wg_barrier();  // B/C hop
       if (stopped()) return;
-      wg_barrier();  // gated-output hop
+      wg_barrier();  // gated-output hop and gated norm statistics
       if (stopped()) return;
       write_in();    // the next layer's in_proj image
-      wg_barrier();  // gated norm statistics
       wg_barrier();  // out_proj codes in LDS
       p_lora_down<S::J2>(aout, DI, L.qs, sAo, L.tls, lane, lw);
       wg_barrier();  // LoRA-down vector ready
@@ -840,11 +896,11 @@ __device__ void loader_waves(const PersistArgs& a, const Lds<S>& L) {
 // profiling); the plain variant has none of that code.
 //
 // Workgroup barriers per token, the same sequence in the compute and loader
-// waves: embedding; per layer [residual hop (layers > 0)], norm statistics,
-// codes, LoRA-down vector ready, in_proj rows done, B/C hop, gated-output
-// hop, gated norm statistics, codes, LoRA-down vector ready, end of layer;
-// then final residual hop, final norm statistics, codes, per-wave argmax
-// candidates, argmax hop, next token chosen.
+// waves: embedding; per layer residual hop (layers > 0) with the norm
+// statistics, codes, LoRA-down vector ready, in_proj rows done, B/C hop,
+// gated-output hop with the gated norm statistics, codes, LoRA-down vector
+// ready, end of layer; then final residual hop, final norm statistics, codes,
+// per-wave argmax candidates, argmax hop, next token chosen.
 template <class S, bool TR>
 __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArgs a) {
   extern __shared__ unsigned char smem[];
@@ -927,6 +983,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArg
     }
     for (int l = 0; l < Lm && ok; ++l) {
       prof(t, l, 0);
+      float s1;
       // this layer's in_proj image (staged by the loader waves)
       uint4 win[S::NGI];
       float isw[S::NGI], isb[S::NGI];
@@ -945,21 +1002,47 @@ __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArg
         cb = cv[128];
         cst[0] = cv[160]; cst[1] = cv[192]; cst[2] = cv[224];
       }
-      if (l > 0) {
-        ok = gather2<S::GW1>(hbox, DM / 2, pc - 1, hs, a.abort_flag, s_stop);
-        ++e;
-        if (!ok) break;
+      // ---- residual hop (layers > 0; layer 0 starts from the embedding row) fused
+      // with the norm statistics
+      {
+        float xa[2 * S::GW1], pa[2 * S::GW1];
+        bool got = true;
+        if (l > 0) {
+          uint64_t wv[S::GW1];
+          got = poll_words<S::GW1, true>(hbox, DM / 2, pc - 1, wv, a.abort_flag);
+#pragma unroll
+          for (int m = 0; m < S::GW1; ++m) {
+            const int i = threadIdx.x + m * kPT;
+            xa[2 * m] = __uint_as_float((unsigned)wv[m]);
+            xa[2 * m + 1] = __uint_as_float((unsigned)(wv[m] >> 32));
+            if (i < DM / 2) ((float2*)hs)[i] = make_float2(xa[2 * m], xa[2 * m + 1]);
+          }
+          ++e;
+        } else {
+#pragma unroll
+          for (int m = 0; m < S::GW1; ++m) {
+            const int i = threadIdx.x + m * kPT;
+            const float2 v = i < DM / 2 ? ((const float2*)hs)[i] : make_float2(0.0f, 0.0f);
+            xa[2 * m] = v.x;
+            xa[2 * m + 1] = v.y;
+          }
+        }
+        pair_stats<S::GW1>(xa, L.nw, DM / 2, pa, red);
+        if (!got) *s_stop = 1;
+        wg_barrier();  // residual hop and norm statistics
+        if (*s_stop) {
+          ok = false;
+          break;
+        }
+        prof(t, l, 1);
+        if constexpr (TR) {
+          float* th = kargs()->trace_h;
+          if (th && w == 0)
+            for (int i = threadIdx.x; i < DM; i += kPT) th[(size_t)l * DM + i] = hs[i];
+        }
+        s1 = pair_quant<S::GW1>(pa, DM / 2, a.eps, red, qs);
       }
-      prof(t, l, 1);
-      if constexpr (TR) {
-        float* th = kargs()->trace_h;
-        if (th && w == 0)
-          for (int i = threadIdx.x; i < DM; i += kPT) th[(size_t)l * DM + i] = hs[i];
-      }
-      // ---- phase A: norm, quantise, 1-bit GEMV of own rows (LoRA down by the loaders), conv
-      float nw[S::MW1];
-      load_norm_w<S::MW1>(nw, L.nw);
-      const float s1 = p_norm_quant<S::MW1>(hs, nw, DM, a.eps, qs, red);
+      // ---- phase A: 1-bit GEMV of own rows (LoRA down by the loaders), conv
       prof(t, l, 2);
       if constexpr (TR) {
         int8_t* tq = kargs()->trace_q1;
@@ -1076,9 +1159,26 @@ __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArg
         }
       }
       prof(t, l, 7);
-      ok = gather2<S::GW2>(gbox, DI / 2, pc, gs, a.abort_flag, s_stop);
-      ++e;
-      if (!ok) break;
+      // ---- gated-output hop fused with the gated norm statistics
+      float pg[2 * S::GW2];
+      {
+        float xg[2 * S::GW2];
+        uint64_t wv[S::GW2];
+        const bool got = poll_words<S::GW2, true>(gbox, DI / 2, pc, wv, a.abort_flag);
+#pragma unroll
+        for (int m = 0; m < S::GW2; ++m) {
+          xg[2 * m] = __uint_as_float((unsigned)wv[m]);
+          xg[2 * m + 1] = __uint_as_float((unsigned)(wv[m] >> 32));
+        }
+        pair_stats<S::GW2>(xg, L.gw, DI / 2, pg, red);
+        if (!got) *s_stop = 1;
+        wg_barrier();  // gated-output hop and gated norm statistics
+        ++e;
+        if (*s_stop) {
+          ok = false;
+          break;
+        }
+      }
       prof(t, l, 8);
       {
         float4* s4 = (float4*)(a.ssm + (size_t)l * S::H * HP * NS + (size_t)w * NS * 16);
@@ -1091,9 +1191,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArg
 
       // ---- phase B: gated norm, quantise, 1-bit GEMV of own rows (LoRA down by the loaders), residual
       {
-        float gw[S::MW2];
-        load_norm_w<S::MW2>(gw, L.gw);
-        const float s2 = p_norm_quant<S::MW2>(gs, gw, DI, a.eps, qs, red);
+        const float s2 = pair_quant<S::GW2>(pg, DI / 2, a.eps, red, qs);
         if constexpr (TR) {
           int8_t* tq = kargs()->trace_q2;
           if (tq && w == 0)
