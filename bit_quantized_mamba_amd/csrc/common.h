@@ -65,6 +65,15 @@ __device__ __forceinline__ int group_sum_lane(int g0, int U) {
   return U <= 16 ? g0 : (U == 32 ? g0 + 16 : 48);
 }
 
+// sum over each row of 16 lanes, in every lane of the row
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<kDppQuadSwap1>(v);
+  v += dpp_f<kDppQuadSwap2>(v);
+  v += dpp_f<kDppRowHalfMirror>(v);
+  v += dpp_f<kDppRowMirror>(v);
+  return v;
+}
+
 // row (16-lane) all-reduce, then the four rows combined through readlane:
 // the result is uniform across the wave.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -151,6 +151,74 @@ struct GemmTile {
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
 };
 
+// Epilogue of a batched scaffold GEMM tile: 2 acc - sum(q) gives the signed
+// scaffold sum, scaled by the column and row scales; the LoRA-up term runs on
+// the f32 matrix cores; store or residual add.  acc[i][j] is the 32 x 32 block
+// at tile rows wm0 + 32 i, columns wn0 + 32 j.  gsm: at least TM * 72 bytes
+// of LDS (reused after the first barrier here).
+template <int TM, int BM, int BN, int EPI>
+__device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i (&acc)[BM][BN], int m0, int n0,
+                                                   int wm0, int wn0, unsigned char* gsm) {
+  const int lane = threadIdx.x & 63;
+  // row data of the tile into LDS
+  __syncthreads();
+  float* s_s = (float*)gsm;              // [TM]
+  int* s_qs = (int*)(s_s + TM);          // [TM]
+  float* s_t = (float*)(s_qs + TM);      // [TM][16]
+  for (int i = threadIdx.x; i < TM; i += 256) {
+    const int m = m0 + i;
+    s_s[i] = m < a.M ? a.s[m] : 0.0f;
+    s_qs[i] = m < a.M ? a.qsum[m] : 0;
+  }
+  for (int i = threadIdx.x; i < TM * 16; i += 256) {
+    const int m = m0 + i / 16;
+    s_t[i] = m < a.M ? a.t[(size_t)m * 16 + (i & 15)] : 0.0f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < BN; ++j) {
+    const int n = n0 + wn0 + 32 * j + (lane & 31);
+    const bool nok = n < a.N;
+    const float sw = nok ? a.sw[n] : 0.0f, sb = nok ? a.sB[n] : 0.0f;
+    // LoRA up operands of this column: B[n][2p + lane/32], p = 0..7
+    const uint4 bq = nok ? *(const uint4*)(a.Bm + (size_t)n * 16) : make_uint4(0, 0, 0, 0);
+    const uint32_t bw[4] = {bq.x, bq.y, bq.z, bq.w};
+    float bcol[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int k = 2 * p + (lane >> 5);
+      bcol[p] = (float)(int8_t)(bw[k >> 2] >> (8 * (k & 3)));
+    }
+#pragma unroll
+    for (int i = 0; i < BM; ++i) {
+      const int rb = wm0 + 32 * i;  // tile-local first row of the block
+      v16f lo = (v16f){};
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        lo = __builtin_amdgcn_mfma_f32_32x32x2f32(s_t[(rb + (lane & 31)) * 16 + 2 * p + (lane >> 5)], bcol[p], lo, 0,
+                                                   0, 0);
+      // residual values loaded before any store of the block (see the skinny kernel)
+      float prev[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        prev[r] = (EPI == GEMM_EPI_RESIDUAL && m < a.M && nok) ? a.y[(size_t)m * a.ldy + n] : 0.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ml = rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int m = m0 + ml;
+        if (m < a.M && nok) {
+          const int sacc = 2 * acc[i][j][r] - s_qs[ml];
+          const float y = (float)sacc * sw * s_s[ml] + sb * lo[r];
+          a.y[(size_t)m * a.ldy + n] = prev[r] + y;
+          if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
+        }
+      }
+    }
+  }
+}
+
 template <int TM, int TN, int EPI>
 __global__ __launch_bounds__(256) void bitgemm_kernel(GemmArgs a) {
   using T = GemmTile<TM, TN>;
@@ -247,63 +315,118 @@ __global__ __launch_bounds__(256) void bitgemm_kernel(GemmArgs a) {
     }
   }
 
-  // ---- epilogue.  Row data of the tile into LDS (stage 0 is free after a barrier).
-  __syncthreads();
-  float* s_s = (float*)gsm;              // [TM]
-  int* s_qs = (int*)(s_s + TM);          // [TM]
-  float* s_t = (float*)(s_qs + TM);      // [TM][16]
-  for (int i = threadIdx.x; i < TM; i += 256) {
-    const int m = m0 + i;
-    s_s[i] = m < a.M ? a.s[m] : 0.0f;
-    s_qs[i] = m < a.M ? a.qsum[m] : 0;
+  gemm_tile_epilogue<TM, T::BM, T::BN, EPI>(a, acc, m0, n0, wm0, wn0, gsm);
+}
+
+// The scaffold GEMM for many rows (prefill), second form.  Tile 128 x 256,
+// k-tiles of 64; four waves, each 128 rows x 64 columns (4 x 2 blocks of
+// v_mfma_i32_32x32x32_i8, so a wave expands only its own two column blocks).
+// LDS holds the A tile (int8 codes) and the scaffold *bits* of the B tile
+// (2 KB a stage instead of 16 KB of expanded bytes); each lane expands the 16
+// bits of its B operand to 0/1 bytes in registers right before the multiply.
+// Global loads run two k-tiles ahead in two register sets, LDS is double
+// buffered: one barrier per k-tile, and each tile's loads have two tiles of
+// matrix work to land.
+constexpr int kG2TM = 128, kG2TN = 256, kG2KB = 64, kG2ARow = 80;
+constexpr int kG2A = kG2TM * kG2ARow, kG2B = kG2TN * 8, kG2Stage = kG2A + kG2B;
+
+__device__ __forceinline__ v4i expand16(uint32_t b) {
+  return (v4i){(int)spread_nibble(b), (int)spread_nibble(b >> 4), (int)spread_nibble(b >> 8),
+               (int)spread_nibble(b >> 12)};
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void bitgemm2_kernel(GemmArgs a) {
+  constexpr int TM = kG2TM, TN = kG2TN, KB = kG2KB, BM = 4, BN = 2;
+  extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // XCD-aware tile order: workgroups are dealt to the 8 XCDs round-robin, so
+  // workgroup g runs on XCD g % 8; XCD x takes a contiguous run of tiles in
+  // row-block-major order, and the tiles that share a row block of A (and
+  // every column block of B) share that XCD's L2.
+  int n0, m0;
+  {
+    const int ntn = gridDim.x, T = gridDim.x * gridDim.y;
+    const int g = blockIdx.x + ntn * blockIdx.y;
+    const int q = T / 8, r = T % 8, x = g % 8;
+    const int tile = x * q + min(x, r) + g / 8;
+    n0 = (tile % ntn) * TN;
+    m0 = (tile / ntn) * TM;
   }
-  for (int i = threadIdx.x; i < TM * 16; i += 256) {
-    const int m = m0 + i / 16;
-    s_t[i] = m < a.M ? a.t[(size_t)m * 16 + (i & 15)] : 0.0f;
-  }
-  __syncthreads();
+  const int wn0 = wave * 64;
+  const int K = a.K, KW = K / 32, nk = K / KB;
+  // a thread's share of a k-tile: A chunks c = t, t + 256 (row c / 4, 16-byte
+  // chunk c % 4), B words c = t, t + 256 (column c / 2, word c % 2)
+  struct Tile {
+    uint4 a[2];
+    uint32_t b[2];
+  };
+  auto load = [&](int kt, Tile& R) {
 #pragma unroll
-  for (int j = 0; j < T::BN; ++j) {
-    const int n = n0 + wn0 + 32 * j + (lane & 31);
-    const bool nok = n < a.N;
-    const float sw = nok ? a.sw[n] : 0.0f, sb = nok ? a.sB[n] : 0.0f;
-    // LoRA up operands of this column: B[n][2p + lane/32], p = 0..7
-    const uint4 bq = nok ? *(const uint4*)(a.Bm + (size_t)n * 16) : make_uint4(0, 0, 0, 0);
-    const uint32_t bw[4] = {bq.x, bq.y, bq.z, bq.w};
-    float bcol[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int k = 2 * p + (lane >> 5);
-      bcol[p] = (float)(int8_t)(bw[k >> 2] >> (8 * (k & 3)));
+    for (int i = 0; i < 2; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int m = m0 + (c >> 2);
+      R.a[i] = m < a.M ? *(const uint4*)(a.q + (size_t)m * K + (size_t)kt * KB + (c & 3) * 16) : make_uint4(0, 0, 0, 0);
+      const int n = n0 + (c >> 1);
+      R.b[i] = n < a.N ? a.bits[(size_t)n * KW + kt * 2 + (c & 1)] : 0u;
     }
+  };
+  auto store = [&](int stg, const Tile& R) {
+    unsigned char* As = gsm + stg * kG2Stage;
+    uint32_t* Bw = (uint32_t*)(As + kG2A);
 #pragma unroll
-    for (int i = 0; i < T::BM; ++i) {
-      const int rb = wm0 + 32 * i;  // tile-local first row of the block
-      v16f lo = (v16f){};
+    for (int i = 0; i < 2; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      *(uint4*)(As + (c >> 2) * kG2ARow + (c & 3) * 16) = R.a[i];
+      Bw[c] = R.b[i];
+    }
+  };
+  v16i acc[BM][BN];
 #pragma unroll
-      for (int p = 0; p < 8; ++p)
-        lo = __builtin_amdgcn_mfma_f32_32x32x2f32(s_t[(rb + (lane & 31)) * 16 + 2 * p + (lane >> 5)], bcol[p], lo, 0,
-                                                   0, 0);
-      // residual values loaded before any store of the block (see the skinny kernel)
-      float prev[16];
+  for (int i = 0; i < BM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        prev[r] = (EPI == GEMM_EPI_RESIDUAL && m < a.M && nok) ? a.y[(size_t)m * a.ldy + n] : 0.0f;
+    for (int j = 0; j < BN; ++j) acc[i][j] = (v16i){};
+  auto compute = [&](int stg) {
+    const unsigned char* As = gsm + stg * kG2Stage;
+    const unsigned char* Bb = As + kG2A;
+#pragma unroll
+    for (int kk = 0; kk < KB / 32; ++kk) {
+      const int koff = kk * 32 + 16 * (lane >> 5);
+      v4i af[BM], bf[BN];
+#pragma unroll
+      for (int j = 0; j < BN; ++j) {
+        const int col = wn0 + 32 * j + (lane & 31);
+        bf[j] = expand16(*(const uint16_t*)(Bb + col * 8 + kk * 4 + 2 * (lane >> 5)));
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ml = rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int m = m0 + ml;
-        if (m < a.M && nok) {
-          const int sacc = 2 * acc[i][j][r] - s_qs[ml];
-          const float y = (float)sacc * sw * s_s[ml] + sb * lo[r];
-          a.y[(size_t)m * a.ldy + n] = prev[r] + y;
-          if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
-        }
-      }
+      for (int i = 0; i < BM; ++i) af[i] = *(const v4i*)(As + (32 * i + (lane & 31)) * kG2ARow + koff);
+#pragma unroll
+      for (int i = 0; i < BM; ++i)
+#pragma unroll
+        for (int j = 0; j < BN; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
+  };
+
+  Tile R0, R1;
+  load(0, R0);
+  if (nk > 1) load(1, R1);
+  store(0, R0);
+  if (nk > 2) load(2, R0);
+  __syncthreads();
+  // invariant at step kt: LDS stage kt % 2 holds k-tile kt; the register set
+  // of parity (kt + 1) % 2 holds tile kt + 1 and the other one tile kt + 2
+  for (int kt = 0; kt < nk; kt += 2) {
+    compute(0);
+    if (kt + 1 < nk) store(1, R1);
+    __syncthreads();
+    if (kt + 3 < nk) load(kt + 3, R1);
+    if (kt + 1 >= nk) break;
+    compute(1);
+    if (kt + 2 < nk) store(0, R0);
+    __syncthreads();
+    if (kt + 4 < nk) load(kt + 4, R0);
   }
+  gemm_tile_epilogue<TM, BM, BN, EPI>(a, acc, m0, n0, 0, wn0, gsm);
 }
 
 template <int TM, int TN>
@@ -324,6 +447,15 @@ hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % kGemmKB) return hipErrorInvalidValue;
   if (a.M <= 32) return launch_bitgemm_t<32, 128>(a, epi, st);
+  if (a.K % kG2KB == 0) {
+    const dim3 grid((a.N + kG2TN - 1) / kG2TN, (a.M + kG2TM - 1) / kG2TM), block(256);
+    const size_t lds = 2 * (size_t)kG2Stage;
+    if (epi == GEMM_EPI_RESIDUAL)
+      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_RESIDUAL>), grid, block, lds, st, a);
+    else
+      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_STORE>), grid, block, lds, st, a);
+    return hipGetLastError();
+  }
   return launch_bitgemm_t<128, 256>(a, epi, st);
 }
 
@@ -606,6 +738,110 @@ __global__ __launch_bounds__(4 * P) void scan_kernel(ScanArgs a) {
   }
 }
 
+// The scan over T tokens for headdim 64, d_state 128.  Workgroup (head,
+// sequence) of 256 threads; thread t owns channels 4c .. 4c+3 (c = t >> 4)
+// and states 8s .. 8s+7 (s = t & 15) as float4 over the channels, i.e. one
+// float4 of the [P/16][N][16] state block per state.  A token then costs a
+// thread two float4 of B, two of C and one of x from LDS for 64 FMAs (the
+// one-channel-per-thread layout reads 64 floats of B and C per token), and the
+// sum over states is one 16-lane DPP reduction per channel.  dt and the decay
+// of each staged token are computed once, by the first kScan2Chunk threads.
+constexpr int kScan2Chunk = 32;
+__global__ __launch_bounds__(256) void scan64x128_kernel(ScanArgs a) {
+  constexpr int P = 64, N = 128, Q = kScan2Chunk;
+  __shared__ float4 sB[Q][N / 4], sC[Q][N / 4], sx[Q][P / 4], sz[Q][P / 4];
+  __shared__ float sdt[Q], sdA[Q];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int c = tid >> 4, s = tid & 15;
+  const int pb = c >> 2, pq = c & 3;
+  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;  // [P/16][N][16]
+  float4 S[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) S[k] = *(const float4*)(stb + ((size_t)(pb * N + 8 * s + k) * 16 + pq * 4));
+  const float dtb = a.dt_bias[h], ea = __expf(a.A_log[h]), Dh = a.D[h];
+  const size_t row0 = (size_t)b * a.T;
+  for (int t0 = 0; t0 < a.T; t0 += Q) {
+    const int tc = min(Q, a.T - t0);
+    __syncthreads();  // the previous chunk is consumed
+    for (int i = tid; i < tc * (N / 4); i += 256) {
+      const int tt = i / (N / 4), q = i % (N / 4);
+      const float4* xr = (const float4*)(a.xc + (row0 + t0 + tt) * a.cdim + a.d_inner);
+      sB[tt][q] = xr[q];
+      sC[tt][q] = xr[N / 4 + q];
+    }
+    for (int i = tid; i < tc * (P / 4); i += 256) {
+      const int tt = i / (P / 4), q = i % (P / 4);
+      sx[tt][q] = ((const float4*)(a.xc + (row0 + t0 + tt) * a.cdim + (size_t)h * P))[q];
+      sz[tt][q] = ((const float4*)(a.zx + (row0 + t0 + tt) * a.ldzx + (size_t)h * P))[q];
+    }
+    if (tid < tc) {
+      const float dt = softplus_f(a.zx[(row0 + t0 + tid) * a.ldzx + a.dt_off + h] + dtb);
+      sdt[tid] = dt;
+      sdA[tid] = __expf(-dt * ea);
+    }
+    __syncthreads();
+    // Tokens go in groups of UT: the state update is sequential over tokens,
+    // but the output sums are not, so a group's 4 UT sums reduce together
+    // (independent DPP chains instead of one dependent chain per token).
+    constexpr int UT = 4;
+    for (int tb = 0; tb < tc; tb += UT) {
+      float y[UT][4];
+#pragma unroll
+      for (int u = 0; u < UT; ++u) {
+        const int tt = min(tb + u, tc - 1);  // a short last group repeats a token; its update is skipped
+        const bool live = tb + u < tc;
+        const float dt = sdt[tt], dA = live ? sdA[tt] : 1.0f;
+        const float4 xv = sx[tt][c];
+        const float dx0 = live ? dt * xv.x : 0.f, dx1 = live ? dt * xv.y : 0.f;
+        const float dx2 = live ? dt * xv.z : 0.f, dx3 = live ? dt * xv.w : 0.f;
+        const float4 b0 = sB[tt][2 * s], b1 = sB[tt][2 * s + 1];
+        const float4 c0 = sC[tt][2 * s], c1 = sC[tt][2 * s + 1];
+        const float bn[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const float cn[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float4 v = S[k];
+          v.x = v.x * dA + dx0 * bn[k];
+          v.y = v.y * dA + dx1 * bn[k];
+          v.z = v.z * dA + dx2 * bn[k];
+          v.w = v.w * dA + dx3 * bn[k];
+          S[k] = v;
+          y0 += v.x * cn[k];
+          y1 += v.y * cn[k];
+          y2 += v.z * cn[k];
+          y3 += v.w * cn[k];
+        }
+        y[u][0] = y0;
+        y[u][1] = y1;
+        y[u][2] = y2;
+        y[u][3] = y3;
+      }
+#pragma unroll
+      for (int u = 0; u < UT; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[u][i] = row_sum16(y[u][i]);
+      if (s == 0) {
+#pragma unroll
+        for (int u = 0; u < UT; ++u) {
+          const int tt = tb + u;
+          if (tt < tc) {
+            const float4 xv = sx[tt][c], zv = sz[tt][c];
+            float4 g;
+            g.x = (y[u][0] + Dh * xv.x) * silu_f(zv.x);
+            g.y = (y[u][1] + Dh * xv.y) * silu_f(zv.y);
+            g.z = (y[u][2] + Dh * xv.z) * silu_f(zv.z);
+            g.w = (y[u][3] + Dh * xv.w) * silu_f(zv.w);
+            *(float4*)(a.g + (row0 + t0 + tt) * a.d_inner + (size_t)h * P + 4 * c) = g;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) *(float4*)(stb + ((size_t)(pb * N + 8 * s + k) * 16 + pq * 4)) = S[k];
+}
+
 // One decode token per sequence (T = 1), headdim 64, d_state 128.  Workgroup
 // (head, sequence) of 256 threads: thread t owns channels 16 pb + 4 pq + 0..3
 // (pq = t & 3, pb = (t >> 2) & 3) and states 8 ns .. 8 ns + 7 (ns = t >> 4),
@@ -670,7 +906,7 @@ hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
     hipLaunchKernelGGL(scan1_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  if (P == 64 && N == 128) hipLaunchKernelGGL((scan_kernel<64, 128>), grid, dim3(256), 0, st, a);
+  if (P == 64 && N == 128) hipLaunchKernelGGL(scan64x128_kernel, grid, dim3(256), 0, st, a);
   else if (P == 32 && N == 16) hipLaunchKernelGGL((scan_kernel<32, 16>), grid, dim3(128), 0, st, a);
   else if (P == 64 && N == 64) hipLaunchKernelGGL((scan_kernel<64, 64>), grid, dim3(256), 0, st, a);
   else if (P == 32 && N == 128) hipLaunchKernelGGL((scan_kernel<32, 128>), grid, dim3(128), 0, st, a);
