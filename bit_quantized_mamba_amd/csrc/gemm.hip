@@ -780,61 +780,40 @@ __global__ __launch_bounds__(256) void scan64x128_kernel(ScanArgs a) {
       sdA[tid] = __expf(-dt * ea);
     }
     __syncthreads();
-    // Tokens go in groups of UT: the state update is sequential over tokens,
-    // but the output sums are not, so a group's 4 UT sums reduce together
-    // (independent DPP chains instead of one dependent chain per token).
-    constexpr int UT = 4;
-    for (int tb = 0; tb < tc; tb += UT) {
-      float y[UT][4];
+    for (int tt = 0; tt < tc; ++tt) {
+      const float dt = sdt[tt], dA = sdA[tt];
+      const float4 xv = sx[tt][c];
+      const float dx0 = dt * xv.x, dx1 = dt * xv.y, dx2 = dt * xv.z, dx3 = dt * xv.w;
+      const float4 b0 = sB[tt][2 * s], b1 = sB[tt][2 * s + 1];
+      const float4 c0 = sC[tt][2 * s], c1 = sC[tt][2 * s + 1];
+      const float bn[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      const float cn[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
 #pragma unroll
-      for (int u = 0; u < UT; ++u) {
-        const int tt = min(tb + u, tc - 1);  // a short last group repeats a token; its update is skipped
-        const bool live = tb + u < tc;
-        const float dt = sdt[tt], dA = live ? sdA[tt] : 1.0f;
-        const float4 xv = sx[tt][c];
-        const float dx0 = live ? dt * xv.x : 0.f, dx1 = live ? dt * xv.y : 0.f;
-        const float dx2 = live ? dt * xv.z : 0.f, dx3 = live ? dt * xv.w : 0.f;
-        const float4 b0 = sB[tt][2 * s], b1 = sB[tt][2 * s + 1];
-        const float4 c0 = sC[tt][2 * s], c1 = sC[tt][2 * s + 1];
-        const float bn[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        const float cn[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          float4 v = S[k];
-          v.x = v.x * dA + dx0 * bn[k];
-          v.y = v.y * dA + dx1 * bn[k];
-          v.z = v.z * dA + dx2 * bn[k];
-          v.w = v.w * dA + dx3 * bn[k];
-          S[k] = v;
-          y0 += v.x * cn[k];
-          y1 += v.y * cn[k];
-          y2 += v.z * cn[k];
-          y3 += v.w * cn[k];
-        }
-        y[u][0] = y0;
-        y[u][1] = y1;
-        y[u][2] = y2;
-        y[u][3] = y3;
+      for (int k = 0; k < 8; ++k) {
+        float4 v = S[k];
+        v.x = v.x * dA + dx0 * bn[k];
+        v.y = v.y * dA + dx1 * bn[k];
+        v.z = v.z * dA + dx2 * bn[k];
+        v.w = v.w * dA + dx3 * bn[k];
+        S[k] = v;
+        y0 += v.x * cn[k];
+        y1 += v.y * cn[k];
+        y2 += v.z * cn[k];
+        y3 += v.w * cn[k];
       }
-#pragma unroll
-      for (int u = 0; u < UT; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y[u][i] = row_sum16(y[u][i]);
+      y0 = row_sum16(y0);
+      y1 = row_sum16(y1);
+      y2 = row_sum16(y2);
+      y3 = row_sum16(y3);
       if (s == 0) {
-#pragma unroll
-        for (int u = 0; u < UT; ++u) {
-          const int tt = tb + u;
-          if (tt < tc) {
-            const float4 xv = sx[tt][c], zv = sz[tt][c];
-            float4 g;
-            g.x = (y[u][0] + Dh * xv.x) * silu_f(zv.x);
-            g.y = (y[u][1] + Dh * xv.y) * silu_f(zv.y);
-            g.z = (y[u][2] + Dh * xv.z) * silu_f(zv.z);
-            g.w = (y[u][3] + Dh * xv.w) * silu_f(zv.w);
-            *(float4*)(a.g + (row0 + t0 + tt) * a.d_inner + (size_t)h * P + 4 * c) = g;
-          }
-        }
+        const float4 zv = sz[tt][c];
+        float4 g;
+        g.x = (y0 + Dh * xv.x) * silu_f(zv.x);
+        g.y = (y1 + Dh * xv.y) * silu_f(zv.y);
+        g.z = (y2 + Dh * xv.z) * silu_f(zv.z);
+        g.w = (y3 + Dh * xv.w) * silu_f(zv.w);
+        *(float4*)(a.g + (row0 + t0 + tt) * a.d_inner + (size_t)h * P + 4 * c) = g;
       }
     }
   }
