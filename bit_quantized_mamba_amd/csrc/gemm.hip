@@ -361,14 +361,17 @@ __global__ __launch_bounds__(256, 1) void bitgemm2_kernel(GemmArgs a) {
     uint4 a[2];
     uint32_t b[2];
   };
+  // branch-free loads: rows and columns past the end read the last one and
+  // are zeroed by a select, so the compiler can count the loads in flight
+  // exactly (a branch around a load makes it wait for all of them)
   auto load = [&](int kt, Tile& R) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = threadIdx.x + 256 * i;
       const int m = m0 + (c >> 2);
-      R.a[i] = m < a.M ? *(const uint4*)(a.q + (size_t)m * K + (size_t)kt * KB + (c & 3) * 16) : make_uint4(0, 0, 0, 0);
+      R.a[i] = *(const uint4*)(a.q + (size_t)min(m, a.M - 1) * K + (size_t)kt * KB + (c & 3) * 16);
       const int n = n0 + (c >> 1);
-      R.b[i] = n < a.N ? a.bits[(size_t)n * KW + kt * 2 + (c & 1)] : 0u;
+      R.b[i] = a.bits[(size_t)min(n, a.N - 1) * KW + kt * 2 + (c & 1)];
     }
   };
   auto store = [&](int stg, const Tile& R) {
@@ -377,8 +380,9 @@ __global__ __launch_bounds__(256, 1) void bitgemm2_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = threadIdx.x + 256 * i;
-      *(uint4*)(As + (c >> 2) * kG2ARow + (c & 3) * 16) = R.a[i];
-      Bw[c] = R.b[i];
+      const bool mok = m0 + (c >> 2) < a.M, nok = n0 + (c >> 1) < a.N;
+      *(uint4*)(As + (c >> 2) * kG2ARow + (c & 3) * 16) = mok ? R.a[i] : make_uint4(0, 0, 0, 0);
+      Bw[c] = nok ? R.b[i] : 0u;
     }
   };
   v16i acc[BM][BN];
@@ -407,24 +411,27 @@ __global__ __launch_bounds__(256, 1) void bitgemm2_kernel(GemmArgs a) {
     }
   };
 
+  // nk is even (K % 128 == 0), so the loop runs whole pairs of k-tiles with
+  // no exit in between, and the loads are unconditional (indexes clamped to
+  // the last tile): the compiler keeps one accumulator set and waits only
+  // for the tile being stored, not for the one still in flight.
   Tile R0, R1;
   load(0, R0);
-  if (nk > 1) load(1, R1);
+  load(1, R1);
   store(0, R0);
-  if (nk > 2) load(2, R0);
+  load(min(2, nk - 1), R0);
   __syncthreads();
-  // invariant at step kt: LDS stage kt % 2 holds k-tile kt; the register set
-  // of parity (kt + 1) % 2 holds tile kt + 1 and the other one tile kt + 2
+  // at step kt: LDS stage kt % 2 holds k-tile kt; the register set of parity
+  // (kt + 1) % 2 holds tile kt + 1 and the other one tile kt + 2
   for (int kt = 0; kt < nk; kt += 2) {
     compute(0);
-    if (kt + 1 < nk) store(1, R1);
+    store(1, R1);
     __syncthreads();
-    if (kt + 3 < nk) load(kt + 3, R1);
-    if (kt + 1 >= nk) break;
+    load(min(kt + 3, nk - 1), R1);
     compute(1);
-    if (kt + 2 < nk) store(0, R0);
+    store(0, R0);  // after the last pair: a copy of the last tile nobody reads
     __syncthreads();
-    if (kt + 4 < nk) load(kt + 4, R0);
+    load(min(kt + 4, nk - 1), R0);
   }
   gemm_tile_epilogue<TM, BM, BN, EPI>(a, acc, m0, n0, 0, wn0, gsm);
 }
@@ -447,7 +454,7 @@ hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % kGemmKB) return hipErrorInvalidValue;
   if (a.M <= 32) return launch_bitgemm_t<32, 128>(a, epi, st);
-  if (a.K % kG2KB == 0) {
+  if (a.K % (2 * kG2KB) == 0) {
     const dim3 grid((a.N + kG2TN - 1) / kG2TN, (a.M + kG2TM - 1) / kG2TM), block(256);
     const size_t lds = 2 * (size_t)kG2Stage;
     if (epi == GEMM_EPI_RESIDUAL)
