@@ -22,6 +22,20 @@ namespace dfssm {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// v = p1 + p2 + p3 exactly, each part a bf16: p1 keeps the top 8 significant
+// bits of v (truncation), p2 the top 8 of the remainder, p3 the remaining at
+// most 8 bits.  The remainders are exact fp32 differences.
+__device__ __forceinline__ void bf16_split3(float v, __bf16& p1, __bf16& p2, __bf16& p3) {
+  const uint32_t u1 = __float_as_uint(v) & 0xFFFF0000u;
+  const float r1 = v - __uint_as_float(u1);
+  const uint32_t u2 = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(u2);
+  p1 = __builtin_bit_cast(__bf16, (unsigned short)(u1 >> 16));
+  p2 = __builtin_bit_cast(__bf16, (unsigned short)(u2 >> 16));
+  p3 = __builtin_bit_cast(__bf16, (unsigned short)(__float_as_uint(r2) >> 16));
+}
 
 // ---------------------------------------------------------------------------
 // rows_quant: one wave per row, four rows per workgroup.  Lane L holds the
@@ -180,23 +194,32 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
     const int n = n0 + wn0 + 32 * j + (lane & 31);
     const bool nok = n < a.N;
     const float sw = nok ? a.sw[n] : 0.0f, sb = nok ? a.sB[n] : 0.0f;
-    // LoRA up operands of this column: B[n][2p + lane/32], p = 0..7
+    // LoRA up operand of this column: B[n][8 h + e], h = lane / 32 (int8, exact in bf16)
     const uint4 bq = nok ? *(const uint4*)(a.Bm + (size_t)n * 16) : make_uint4(0, 0, 0, 0);
-    const uint32_t bw[4] = {bq.x, bq.y, bq.z, bq.w};
-    float bcol[8];
+    const uint32_t bw2[2] = {(lane >> 5) ? bq.z : bq.x, (lane >> 5) ? bq.w : bq.y};
+    v8bf bB;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int k = 2 * p + (lane >> 5);
-      bcol[p] = (float)(int8_t)(bw[k >> 2] >> (8 * (k & 3)));
-    }
+    for (int e = 0; e < 8; ++e) bB[e] = (__bf16)(float)(int8_t)(bw2[e >> 2] >> (8 * (e & 3)));
 #pragma unroll
     for (int i = 0; i < BM; ++i) {
       const int rb = wm0 + 32 * i;  // tile-local first row of the block
-      v16f lo = (v16f){};
+      // t of row rb + lane % 32, ranks 8 h .. 8 h + 7, split exactly into three
+      // bf16 parts (each part is the top 8 significant bits of what is left), so
+      // the rank-16 product is three bf16 matrix-core steps with exact products
+      const float* tr = s_t + (rb + (lane & 31)) * 16 + 8 * (lane >> 5);
+      v8bf t1, t2, t3;
 #pragma unroll
-      for (int p = 0; p < 8; ++p)
-        lo = __builtin_amdgcn_mfma_f32_32x32x2f32(s_t[(rb + (lane & 31)) * 16 + 2 * p + (lane >> 5)], bcol[p], lo, 0,
-                                                   0, 0);
+      for (int e = 0; e < 8; ++e) {
+        __bf16 p1, p2, p3;
+        bf16_split3(tr[e], p1, p2, p3);
+        t1[e] = p1;
+        t2[e] = p2;
+        t3[e] = p3;
+      }
+      v16f lo = (v16f){};
+      lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t1, bB, lo, 0, 0, 0);
+      lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t2, bB, lo, 0, 0, 0);
+      lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t3, bB, lo, 0, 0, 0);
       // residual values loaded before any store of the block (see the skinny kernel)
       float prev[16];
 #pragma unroll
@@ -319,16 +342,19 @@ __global__ __launch_bounds__(256) void bitgemm_kernel(GemmArgs a) {
 }
 
 // The scaffold GEMM for many rows (prefill), second form.  Tile 128 x 256,
-// k-tiles of 64; four waves, each 128 rows x 64 columns (4 x 2 blocks of
+// k-tiles of 128; four waves, each 128 rows x 64 columns (4 x 2 blocks of
 // v_mfma_i32_32x32x32_i8, so a wave expands only its own two column blocks).
 // LDS holds the A tile (int8 codes) and the scaffold *bits* of the B tile
-// (2 KB a stage instead of 16 KB of expanded bytes); each lane expands the 16
+// (4 KB a stage instead of 32 KB of expanded bytes); each lane expands the 16
 // bits of its B operand to 0/1 bytes in registers right before the multiply.
 // Global loads run two k-tiles ahead in two register sets, LDS is double
 // buffered: one barrier per k-tile, and each tile's loads have two tiles of
 // matrix work to land.
-constexpr int kG2TM = 128, kG2TN = 256, kG2KB = 64, kG2ARow = 80;
-constexpr int kG2A = kG2TM * kG2ARow, kG2B = kG2TN * 8, kG2Stage = kG2A + kG2B;
+constexpr int kG2TM = 128, kG2TN = 256, kG2KB = 128, kG2ARow = kG2KB + 16;
+constexpr int kG2CW = kG2KB / 32;  // scaffold words per column of a k-tile
+constexpr int kG2AC = kG2KB / 16;  // 16-byte A chunks per row of a k-tile
+constexpr int kG2A = kG2TM * kG2ARow, kG2B = kG2TN * kG2CW * 4, kG2Stage = kG2A + kG2B;
+constexpr int kG2PT = kG2TM * kG2AC / 256;  // A chunks (and B words) per thread and k-tile
 
 __device__ __forceinline__ v4i expand16(uint32_t b) {
   return (v4i){(int)spread_nibble(b), (int)spread_nibble(b >> 4), (int)spread_nibble(b >> 8),
@@ -358,30 +384,30 @@ __global__ __launch_bounds__(256, 1) void bitgemm2_kernel(GemmArgs a) {
   // a thread's share of a k-tile: A chunks c = t, t + 256 (row c / 4, 16-byte
   // chunk c % 4), B words c = t, t + 256 (column c / 2, word c % 2)
   struct Tile {
-    uint4 a[2];
-    uint32_t b[2];
+    uint4 a[kG2PT];
+    uint32_t b[kG2PT];
   };
   // branch-free loads: rows and columns past the end read the last one and
   // are zeroed by a select, so the compiler can count the loads in flight
   // exactly (a branch around a load makes it wait for all of them)
   auto load = [&](int kt, Tile& R) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kG2PT; ++i) {
       const int c = threadIdx.x + 256 * i;
-      const int m = m0 + (c >> 2);
-      R.a[i] = *(const uint4*)(a.q + (size_t)min(m, a.M - 1) * K + (size_t)kt * KB + (c & 3) * 16);
-      const int n = n0 + (c >> 1);
-      R.b[i] = a.bits[(size_t)min(n, a.N - 1) * KW + kt * 2 + (c & 1)];
+      const int m = m0 + c / kG2AC;
+      R.a[i] = *(const uint4*)(a.q + (size_t)min(m, a.M - 1) * K + (size_t)kt * KB + (c % kG2AC) * 16);
+      const int n = n0 + c / kG2CW;
+      R.b[i] = a.bits[(size_t)min(n, a.N - 1) * KW + kt * kG2CW + c % kG2CW];
     }
   };
   auto store = [&](int stg, const Tile& R) {
     unsigned char* As = gsm + stg * kG2Stage;
     uint32_t* Bw = (uint32_t*)(As + kG2A);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kG2PT; ++i) {
       const int c = threadIdx.x + 256 * i;
-      const bool mok = m0 + (c >> 2) < a.M, nok = n0 + (c >> 1) < a.N;
-      *(uint4*)(As + (c >> 2) * kG2ARow + (c & 3) * 16) = mok ? R.a[i] : make_uint4(0, 0, 0, 0);
+      const bool mok = m0 + c / kG2AC < a.M, nok = n0 + c / kG2CW < a.N;
+      *(uint4*)(As + (c / kG2AC) * kG2ARow + (c % kG2AC) * 16) = mok ? R.a[i] : make_uint4(0, 0, 0, 0);
       Bw[c] = nok ? R.b[i] : 0u;
     }
   };
@@ -400,7 +426,7 @@ __global__ __launch_bounds__(256, 1) void bitgemm2_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < BN; ++j) {
         const int col = wn0 + 32 * j + (lane & 31);
-        bf[j] = expand16(*(const uint16_t*)(Bb + col * 8 + kk * 4 + 2 * (lane >> 5)));
+        bf[j] = expand16(*(const uint16_t*)(Bb + col * (kG2CW * 4) + kk * 4 + 2 * (lane >> 5)));
       }
 #pragma unroll
       for (int i = 0; i < BM; ++i) af[i] = *(const v4i*)(As + (32 * i + (lane & 31)) * kG2ARow + koff);
