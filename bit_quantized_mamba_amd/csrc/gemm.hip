@@ -7,14 +7,18 @@
 //  * bitgemm: the 1-bit scaffold GEMM on the int8 matrix cores.  The 0/1
 //    bytes of the scaffold bits (bit 1 -> 1) multiply the int8 codes on
 //    v_mfma_i32_32x32x32_i8, giving pos[m][n] = sum of q over the +1 weights;
-//    the signed product is 2 pos - sum(q).  Each k-tile of scaffold bits is
-//    expanded once per workgroup into LDS.  The LoRA up-projection is a
-//    rank-16 fp32 product on v_mfma_f32_32x32x2f32 in the epilogue, then row
-//    scales and either a plain store (in_proj) or the residual add (out_proj).
+//    the signed product is 2 pos - sum(q).  The scaffold bits are expanded to
+//    bytes in LDS once per k-tile (first form) or in registers per operand
+//    (second form).  The LoRA up-projection is a rank-16 product on
+//    v_mfma_f32_32x32x16_bf16 over an exact three-way bf16 split of t, in the
+//    epilogue, then row scales and either a plain store (in_proj) or the
+//    residual add (out_proj).
 //  * conv_seq / conv_state_update: the depthwise causal conv over T tokens of
 //    each sequence, with the stored window as the history before t = 0.
 //  * scan: the SSM recurrence over T tokens, one workgroup per (sequence,
-//    head), state in registers, B and C staged through LDS; gated output.
+//    head), state in registers (carried divided by its running decay, so an
+//    element costs one FMA per token), B and C staged through LDS; gated
+//    output.
 #include "common.h"
 
 namespace dfssm {
@@ -546,7 +550,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
       sb = a.sB[nc];
       bq = *(const uint4*)(a.Bm + (size_t)nc * 16);
 #pragma unroll
-      for (int p = 0; p < 8; ++p) tj[p] = a.t[(size_t)mc * 16 + 2 * p + kg];
+      for (int e = 0; e < 8; ++e) tj[e] = a.t[(size_t)mc * 16 + 8 * kg + e];
     }
     if (KIND == SK_IN && a.xc) {
       const float4 wv = *(const float4*)(a.conv_w + (size_t)c * 4);
@@ -599,15 +603,24 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
     }
     return;
   }
-  // LoRA up on the fp32 matrix core: lo[m][n] = sum_j t[m][j] B[n][j]
-  const uint32_t bwv[4] = {bq.x, bq.y, bq.z, bq.w};
-  v16f lo = (v16f){};
+  // LoRA up, lo[m][n] = sum_j t[m][j] B[n][j]: three bf16 matrix-core steps on
+  // the exact three-way split of t (the arithmetic of gemm_tile_epilogue, so a
+  // row gets the same value on either GEMM)
+  const uint32_t bw2[2] = {kg ? bq.z : bq.x, kg ? bq.w : bq.y};
+  v8bf bB, t1, t2, t3;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int j = 2 * p + kg;
-    const float bj = nok ? (float)(int8_t)(bwv[j >> 2] >> (8 * (j & 3))) : 0.0f;
-    lo = __builtin_amdgcn_mfma_f32_32x32x2f32(mok ? tj[p] : 0.0f, bj, lo, 0, 0, 0);
+  for (int e = 0; e < 8; ++e) {
+    bB[e] = (__bf16)(nok ? (float)(int8_t)(bw2[e >> 2] >> (8 * (e & 3))) : 0.0f);
+    __bf16 p1, p2, p3;
+    bf16_split3(mok ? tj[e] : 0.0f, p1, p2, p3);
+    t1[e] = p1;
+    t2[e] = p2;
+    t3[e] = p3;
   }
+  v16f lo = (v16f){};
+  lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t1, bB, lo, 0, 0, 0);
+  lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t2, bB, lo, 0, 0, 0);
+  lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t3, bB, lo, 0, 0, 0);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int m = 8 * (r >> 2) + 4 * kg + (r & 3);
@@ -780,10 +793,21 @@ __global__ __launch_bounds__(4 * P) void scan_kernel(ScanArgs a) {
 // sum over states is one 16-lane DPP reduction per channel.  dt and the decay
 // of each staged token are computed once, by the first kScan2Chunk threads.
 constexpr int kScan2Chunk = 32;
+// Rescaled recurrence: with P_t the product of the decays since the last
+// rescale point, S_t = P_t * R_t where R_t = R_{t-1} + (dt_t x_t / P_t) B_t,
+// and y_t = P_t * (C_t . R_t).  A state element then costs one FMA for the
+// update and one for the output (the direct form needs a multiply more).  The
+// state is brought back to S at every chunk boundary, and a token at which P
+// would fall below kScanPMin becomes a rescale point: R is multiplied by the
+// decay up to and including that token (R * P_{t-1} * dA_t = dA_t S_{t-1}),
+// and P restarts at 1.
+constexpr float kScanPMin = 0x1p-40f;
 __global__ __launch_bounds__(256) void scan64x128_kernel(ScanArgs a) {
   constexpr int P = 64, N = 128, Q = kScan2Chunk;
   __shared__ float4 sB[Q][N / 4], sC[Q][N / 4], sx[Q][P / 4], sz[Q][P / 4];
-  __shared__ float sdt[Q], sdA[Q];
+  __shared__ float sdt[Q], sdA[Q], sP[Q], sW[Q], sRen[Q];
+  __shared__ int smode[Q];  // 1: rescale point (R *= sRen[t] before the update)
+  __shared__ float sPend;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int c = tid >> 4, s = tid & 15;
   const int pb = c >> 2, pq = c & 3;
@@ -813,41 +837,77 @@ __global__ __launch_bounds__(256) void scan64x128_kernel(ScanArgs a) {
       sdA[tid] = __expf(-dt * ea);
     }
     __syncthreads();
+    if (tid == 0) {
+      // the rescale schedule of the chunk (R = S at its start)
+      float pr = 1.0f;
+      for (int tt = 0; tt < tc; ++tt) {
+        const float np = pr * sdA[tt];
+        const bool re = np < kScanPMin;
+        smode[tt] = re;
+        sRen[tt] = np;
+        pr = re ? 1.0f : np;
+        sP[tt] = pr;
+        sW[tt] = sdt[tt] / pr;
+      }
+      sPend = pr;
+    }
+    __syncthreads();
     for (int tt = 0; tt < tc; ++tt) {
-      const float dt = sdt[tt], dA = sdA[tt];
+      const int mode = __builtin_amdgcn_readfirstlane(smode[tt]);
       const float4 xv = sx[tt][c];
-      const float dx0 = dt * xv.x, dx1 = dt * xv.y, dx2 = dt * xv.z, dx3 = dt * xv.w;
       const float4 b0 = sB[tt][2 * s], b1 = sB[tt][2 * s + 1];
       const float4 c0 = sC[tt][2 * s], c1 = sC[tt][2 * s + 1];
       const float bn[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       const float cn[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      if (mode != 0) {
+        const float r = sRen[tt];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          S[k].x *= r;
+          S[k].y *= r;
+          S[k].z *= r;
+          S[k].w *= r;
+        }
+      }
+      const float wdt = sW[tt];
+      const float w0 = wdt * xv.x, w1 = wdt * xv.y, w2 = wdt * xv.z, w3 = wdt * xv.w;
       float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         float4 v = S[k];
-        v.x = v.x * dA + dx0 * bn[k];
-        v.y = v.y * dA + dx1 * bn[k];
-        v.z = v.z * dA + dx2 * bn[k];
-        v.w = v.w * dA + dx3 * bn[k];
+        v.x += w0 * bn[k];
+        v.y += w1 * bn[k];
+        v.z += w2 * bn[k];
+        v.w += w3 * bn[k];
         S[k] = v;
-        y0 += v.x * cn[k];
-        y1 += v.y * cn[k];
-        y2 += v.z * cn[k];
-        y3 += v.w * cn[k];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        y0 += S[k].x * cn[k];
+        y1 += S[k].y * cn[k];
+        y2 += S[k].z * cn[k];
+        y3 += S[k].w * cn[k];
       }
       y0 = row_sum16(y0);
       y1 = row_sum16(y1);
       y2 = row_sum16(y2);
       y3 = row_sum16(y3);
-      if (s == 0) {
-        const float4 zv = sz[tt][c];
-        float4 g;
-        g.x = (y0 + Dh * xv.x) * silu_f(zv.x);
-        g.y = (y1 + Dh * xv.y) * silu_f(zv.y);
-        g.z = (y2 + Dh * xv.z) * silu_f(zv.z);
-        g.w = (y3 + Dh * xv.w) * silu_f(zv.w);
-        *(float4*)(a.g + (row0 + t0 + tt) * a.d_inner + (size_t)h * P + 4 * c) = g;
+      // the row sums sit in all 16 lanes of the row: lanes s = 0..3 gate one channel each
+      if (s < 4) {
+        const float yv = s == 0 ? y0 : s == 1 ? y1 : s == 2 ? y2 : y3;
+        const float xs = s == 0 ? xv.x : s == 1 ? xv.y : s == 2 ? xv.z : xv.w;
+        const float zs = ((const float*)sz[tt])[4 * c + s];
+        a.g[(row0 + t0 + tt) * a.d_inner + (size_t)h * P + 4 * c + s] = (sP[tt] * yv + Dh * xs) * silu_rcp(zs);
       }
+    }
+    // back to S at the chunk boundary
+    const float pe = sPend;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      S[k].x *= pe;
+      S[k].y *= pe;
+      S[k].z *= pe;
+      S[k].w *= pe;
     }
   }
 #pragma unroll
