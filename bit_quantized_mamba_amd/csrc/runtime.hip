@@ -302,7 +302,7 @@ dfssm_status enqueue_step(dfssm_ctx* c, const int32_t* tok, int tok_stride, int 
 // ---------------------------------------------------------------------------
 // batched path: every layer on all B * T token rows at once
 // ---------------------------------------------------------------------------
-constexpr size_t kPrefillChunkRows = 4096;  // token rows per prefill chunk (bounds the workspace)
+constexpr size_t kPrefillChunkRows = 16384;  // token rows per prefill chunk (bounds the workspace)
 
 // Grow the batched-path workspace to at least `rows` token rows.  Cached
 // graphs hold pointers into it, so they are dropped when it moves.
