@@ -33,9 +33,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # (FETCH_SIZE reads 0.5 GiB for it: factor 2.0; WRITE_SIZE reads 1 GiB: 1.0).
 # Valid only for the kernel sources they were taken from (hash below).
 COUNTED_TRAFFIC = {
-    "sources_sha256": "970051d5046cfd2547d7e05b7cb765c3b345fd281cc556254db26d6d1b31edf3",
-    "fetch_bytes_per_token": 461142914,
-    "write_bytes_per_token": 118426852,
+    "sources_sha256": "2f36a5837f492f8369cec756fc891993ea23c3c3a1f2e87ff00855e0d1925f85",
+    "fetch_bytes_per_token": 461084478,
+    "write_bytes_per_token": 118426850,
 }
 KERNEL_SOURCES = ("bit_quantized_mamba_amd/csrc/persistent.hip", "bit_quantized_mamba_amd/csrc/persistent.h",
                   "bit_quantized_mamba_amd/csrc/common.h")
