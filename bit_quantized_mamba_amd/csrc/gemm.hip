@@ -129,16 +129,120 @@ __global__ __launch_bounds__(256) void rows_quant_kernel(RowsArgs a) {
   }
 }
 
+// rows_quant_row: the same operation with one workgroup per row (K >= 2048),
+// thread i holding the E = K / 256 consecutive elements E i .. E i + E - 1:
+// a few rows (batched decode) spread over as many CUs as there are rows, and
+// each thread's LoRA-down operands (8 bytes per rank and pair of code words)
+// are loaded together with its inputs.
+template <int K>
+__global__ __launch_bounds__(256) void rows_quant_row_kernel(RowsArgs a) {
+  constexpr int E = K / 256, E4 = E / 4;
+  static_assert(E % 8 == 0, "8, 16 or 32 elements per thread");
+  __shared__ float red_f[2][4];
+  __shared__ int red_i[4][17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  const float4* x4 = (const float4*)(a.x + (size_t)row * a.ldx) + E4 * tid;
+  const float4* w4 = (const float4*)a.w + E4 * tid;
+  float4 xs[E4], ws[E4];
+#pragma unroll
+  for (int i = 0; i < E4; ++i) {
+    xs[i] = x4[i];
+    ws[i] = w4[i];
+  }
+  // the LoRA-down rows this thread needs, loaded with the row so that both
+  // latencies overlap
+  uint2 av[16][E4 / 2];
+  if (a.A) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint2* ar = (const uint2*)(a.A + (size_t)k * K + E * tid);
+#pragma unroll
+      for (int i = 0; i < E4 / 2; ++i) av[k][i] = ar[i];
+    }
+  }
+  float4 p[E4];
+  float ss = 0.0f, pm = 0.0f;
+#pragma unroll
+  for (int i = 0; i < E4; ++i) {
+    const float4 xv = xs[i], wv = ws[i];
+    ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+    p[i] = make_float4(xv.x * wv.x, xv.y * wv.y, xv.z * wv.z, xv.w * wv.w);
+    pm = fmaxf(pm, fmaxf(fmaxf(fabsf(p[i].x), fabsf(p[i].y)), fmaxf(fabsf(p[i].z), fabsf(p[i].w))));
+  }
+  ss = wave_sum(ss);
+  pm = wave_max(pm);
+  if (lane == 0) {
+    red_f[0][wave] = ss;
+    red_f[1][wave] = pm;
+  }
+  __syncthreads();
+  ss = (red_f[0][0] + red_f[0][1]) + (red_f[0][2] + red_f[0][3]);
+  pm = fmaxf(fmaxf(red_f[1][0], red_f[1][1]), fmaxf(red_f[1][2], red_f[1][3]));
+  const float rstd = 1.0f / sqrtf(ss / (float)K + a.eps);
+  const float amax = rstd * pm;
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  const float s = amax > 0.0f ? amax / 127.0f : 0.0f;
+  auto qz = [&](float v) -> uint32_t {
+    float r = rintf(rstd * v * inv);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (uint32_t)(uint8_t)(int8_t)(int)r;
+  };
+  uint32_t d[E4];
+  int qsum = 0;
+#pragma unroll
+  for (int i = 0; i < E4; ++i) {
+    const uint32_t b0 = qz(p[i].x), b1 = qz(p[i].y), b2 = qz(p[i].z), b3 = qz(p[i].w);
+    d[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    qsum += (int)(int8_t)b0 + (int)(int8_t)b1 + (int)(int8_t)b2 + (int)(int8_t)b3;
+  }
+  int8_t* qrow = a.q + (size_t)row * K + E * tid;
+#pragma unroll
+  for (int i = 0; i < E4; i += 2) *(uint2*)(qrow + 4 * i) = make_uint2(d[i], d[i + 1]);
+  // LoRA down: t[k] = float(sum_i A[k][i] q_i) * sA[k] * s
+  int acc[17];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    int v = 0;
+#pragma unroll
+    for (int i = 0; i < E4; i += 2) {
+      v = __builtin_amdgcn_sdot4((int)av[k][i / 2].x, (int)d[i], v, false);
+      v = __builtin_amdgcn_sdot4((int)av[k][i / 2].y, (int)d[i + 1], v, false);
+    }
+    acc[k] = a.A ? v : 0;
+  }
+  acc[16] = qsum;
+#pragma unroll
+  for (int k = 0; k < 17; ++k) acc[k] = wave_sum_i(acc[k]);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 17; ++k) red_i[wave][k] = acc[k];
+  }
+  __syncthreads();
+  if (tid < 17) {
+    const int v = red_i[0][tid] + red_i[1][tid] + red_i[2][tid] + red_i[3][tid];
+    if (tid == 16) {
+      a.s[row] = s;
+      if (a.qsum) a.qsum[row] = v;
+    } else if (a.A) {
+      a.t[(size_t)row * 16 + tid] = (float)v * a.sA[tid] * s;
+    }
+  }
+}
+
 hipError_t launch_rows_quant(const RowsArgs& a, int K, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
   const dim3 grid((a.M + 3) / 4), block(256);
   switch (K) {
+    case 2048: hipLaunchKernelGGL(rows_quant_row_kernel<2048>, dim3(a.M), block, 0, st, a); return hipGetLastError();
+    case 4096: hipLaunchKernelGGL(rows_quant_row_kernel<4096>, dim3(a.M), block, 0, st, a); return hipGetLastError();
+    case 8192: hipLaunchKernelGGL(rows_quant_row_kernel<8192>, dim3(a.M), block, 0, st, a); return hipGetLastError();
+    default: break;
+  }
+  switch (K) {
     case 256: hipLaunchKernelGGL(rows_quant_kernel<256>, grid, block, 0, st, a); break;
     case 512: hipLaunchKernelGGL(rows_quant_kernel<512>, grid, block, 0, st, a); break;
     case 1024: hipLaunchKernelGGL(rows_quant_kernel<1024>, grid, block, 0, st, a); break;
-    case 2048: hipLaunchKernelGGL(rows_quant_kernel<2048>, grid, block, 0, st, a); break;
-    case 4096: hipLaunchKernelGGL(rows_quant_kernel<4096>, grid, block, 0, st, a); break;
-    case 8192: hipLaunchKernelGGL(rows_quant_kernel<8192>, grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
