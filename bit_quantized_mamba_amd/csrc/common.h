@@ -237,6 +237,7 @@ struct ScanArgs {
   size_t ssm_bstride;
   float* g;         // [B*T][d_inner]
   int B, T, H, d_inner, cdim;
+  float* gram;      // chunked scan workspace, B * ceil(T / 64) * 64 * 64 floats, or null
 };
 
 hipError_t launch_rows_quant(const RowsArgs& a, int K, hipStream_t st);

@@ -1,9 +1,9 @@
 // Kernels of the batched path: many token rows per layer (batched decode, one
 // row per sequence; prefill, B x T rows), gfx950.
 //
-//  * rows_quant: RMSNorm + per-token int8 quantisation of one row per wave,
-//    plus the row sum of the codes and the LoRA down-projection
-//    t = float(A q) * sA * s.
+//  * rows_quant: RMSNorm + per-token int8 quantisation of a row (one wave per
+//    row, or one workgroup per row from K = 2048), plus the row sum of the
+//    codes and the LoRA down-projection t = float(A q) * sA * s.
 //  * bitgemm: the 1-bit scaffold GEMM on the int8 matrix cores.  The 0/1
 //    bytes of the scaffold bits (bit 1 -> 1) multiply the int8 codes on
 //    v_mfma_i32_32x32x32_i8, giving pos[m][n] = sum of q over the +1 weights;
@@ -15,10 +15,9 @@
 //    residual add (out_proj).
 //  * conv_seq / conv_state_update: the depthwise causal conv over T tokens of
 //    each sequence, with the stored window as the history before t = 0.
-//  * scan: the SSM recurrence over T tokens, one workgroup per (sequence,
-//    head), state in registers (carried divided by its running decay, so an
-//    element costs one FMA per token), B and C staged through LDS; gated
-//    output.
+//  * embed_rows: the embedding rows of a chunk of tokens.
+//
+// The SSM scans over T tokens are in scan.hip.
 #include "common.h"
 
 namespace dfssm {
@@ -39,6 +38,19 @@ __device__ __forceinline__ void bf16_split3(float v, __bf16& p1, __bf16& p2, __b
   p1 = __builtin_bit_cast(__bf16, (unsigned short)(u1 >> 16));
   p2 = __builtin_bit_cast(__bf16, (unsigned short)(u2 >> 16));
   p3 = __builtin_bit_cast(__bf16, (unsigned short)(__float_as_uint(r2) >> 16));
+}
+
+// The projection output float(sacc) * sw * s + sB * lo and the causal conv
+// sum, each rounded in one fixed order (two products, then a fused
+// multiply-add; a chain of fused multiply-adds) whatever the compiler would
+// contract: every kernel that produces them gives a row the same value.
+__device__ __forceinline__ float proj_out(int sacc, float sw, float s, float sb, float lo) {
+#pragma clang fp contract(off)
+  return __builtin_fmaf(sb, lo, ((float)sacc * sw) * s);
+}
+__device__ __forceinline__ float conv4(float bias, float w0, float x0, float w1, float x1, float w2, float x2,
+                                       float w3, float x3) {
+  return __builtin_fmaf(w3, x3, __builtin_fmaf(w2, x2, __builtin_fmaf(w1, x1, __builtin_fmaf(w0, x0, bias))));
 }
 
 // ---------------------------------------------------------------------------
@@ -341,7 +353,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
         const int m = m0 + ml;
         if (m < a.M && nok) {
           const int sacc = 2 * acc[i][j][r] - s_qs[ml];
-          const float y = (float)sacc * sw * s_s[ml] + sb * lo[r];
+          const float y = proj_out(sacc, sw, s_s[ml], sb, lo[r]);
           a.y[(size_t)m * a.ldy + n] = prev[r] + y;
           if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
         }
@@ -730,7 +742,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
     const int m = 8 * (r >> 2) + 4 * kg + (r & 3);
     if (m >= a.M || !nok) continue;
     const int sacc = 2 * acc[r] - qm[r];
-    const float y = (float)sacc * sw * sm[r] + sb * lo[r];
+    const float y = proj_out(sacc, sw, sm[r], sb, lo[r]);
     if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
     float* yp = a.y + (size_t)m * a.ldy + n;
     if (KIND == SK_OUT) {
@@ -739,7 +751,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
       *yp = y;
       if (conv_col) {  // one decode token: the conv shift register of channel c
         float* st = a.conv_state + (size_t)m * a.conv_bstride + c;
-        const float v = cb + cw0 * w0[r] + cw1 * w1[r] + cw2 * w2[r] + cw3 * y;
+        const float v = conv4(cb, cw0, w0[r], cw1, w1[r], cw2, w2[r], cw3, y);
         a.xc[(size_t)m * a.cdim + c] = silu_f(v);
         st[0] = w1[r];
         st[a.cdim] = w2[r];
@@ -783,7 +795,7 @@ __global__ __launch_bounds__(256) void conv_seq_kernel(ConvSeqArgs a) {
   float x0 = raw(t0 - 3), x1 = raw(t0 - 2), x2 = raw(t0 - 1);
   for (int t = t0; t < t1; ++t) {
     const float x3 = raw(t);
-    const float v = bias + w0 * x0 + w1 * x1 + w2 * x2 + w3 * x3;
+    const float v = conv4(bias, w0, x0, w1, x1, w2, x2, w3, x3);
     a.xc[(size_t)((size_t)b * a.T + t) * a.cdim + c] = silu_f(v);
     x0 = x1;
     x1 = x2;
@@ -818,281 +830,6 @@ hipError_t launch_conv_seq(const ConvSeqArgs& a, hipStream_t st) {
   const dim3 g2((a.cdim + 255) / 256, a.B);
   hipLaunchKernelGGL(conv_state_update_kernel, g2, dim3(256), 0, st, a);
   return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// SSM scan over T tokens.  Workgroup (head h, sequence b) of 4 P threads:
-// thread (p = tid / 4, seg = tid % 4) holds S[p][seg N/4 .. +N/4) in
-// registers.  B, C, x, z and dt of kScanChunk tokens are staged in LDS; y[p]
-// is the sum over the four threads of a quad (DPP).
-// ---------------------------------------------------------------------------
-constexpr int kScanChunk = 16;
-
-template <int P, int N>
-__global__ __launch_bounds__(4 * P) void scan_kernel(ScanArgs a) {
-  constexpr int NPT = N / 4;
-  constexpr int NT = 4 * P;
-  __shared__ float sB[kScanChunk][N], sC[kScanChunk][N], sx[kScanChunk][P], sz[kScanChunk][P], sdt[kScanChunk];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int p = tid >> 2, seg = tid & 3;
-  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;  // [P/16][N][16]
-  float S[NPT];
-#pragma unroll
-  for (int j = 0; j < NPT; ++j) {
-    const int n = seg * NPT + j;
-    S[j] = stb[((size_t)(p >> 4) * N + n) * 16 + (p & 15)];
-  }
-  const float dtb = a.dt_bias[h], ea = __expf(a.A_log[h]), Dh = a.D[h];
-  const size_t row0 = (size_t)b * a.T;
-  for (int t0 = 0; t0 < a.T; t0 += kScanChunk) {
-    const int tc = min(kScanChunk, a.T - t0);
-    __syncthreads();  // previous chunk fully consumed
-    for (int i = tid; i < tc * N; i += NT) {
-      const int tt = i / N, n = i % N;
-      const float* xr = a.xc + (row0 + t0 + tt) * a.cdim;
-      sB[tt][n] = xr[a.d_inner + n];
-      sC[tt][n] = xr[a.d_inner + N + n];
-    }
-    for (int i = tid; i < tc * P; i += NT) {
-      const int tt = i / P, pp = i % P;
-      sx[tt][pp] = a.xc[(row0 + t0 + tt) * a.cdim + (size_t)h * P + pp];
-      sz[tt][pp] = a.zx[(row0 + t0 + tt) * a.ldzx + (size_t)h * P + pp];
-    }
-    for (int i = tid; i < tc; i += NT) sdt[i] = a.zx[(row0 + t0 + i) * a.ldzx + a.dt_off + h];
-    __syncthreads();
-    for (int tt = 0; tt < tc; ++tt) {
-      const float dt = softplus_f(sdt[tt] + dtb);
-      const float dA = __expf(-dt * ea);
-      const float x = sx[tt][p];
-      const float dtx = dt * x;
-      float y = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NPT; ++j) {
-        const int n = seg * NPT + j;
-        S[j] = S[j] * dA + dtx * sB[tt][n];
-        y += S[j] * sC[tt][n];
-      }
-      y += dpp_f<kDppQuadSwap1>(y);
-      y += dpp_f<kDppQuadSwap2>(y);
-      if (seg == 0) {
-        const float yy = y + Dh * x;
-        a.g[(row0 + t0 + tt) * a.d_inner + (size_t)h * P + p] = yy * silu_f(sz[tt][p]);
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < NPT; ++j) {
-    const int n = seg * NPT + j;
-    stb[((size_t)(p >> 4) * N + n) * 16 + (p & 15)] = S[j];
-  }
-}
-
-// The scan over T tokens for headdim 64, d_state 128.  Workgroup (head,
-// sequence) of 256 threads; thread t owns channels 4c .. 4c+3 (c = t >> 4)
-// and states 8s .. 8s+7 (s = t & 15) as float4 over the channels, i.e. one
-// float4 of the [P/16][N][16] state block per state.  A token then costs a
-// thread two float4 of B, two of C and one of x from LDS for 64 FMAs (the
-// one-channel-per-thread layout reads 64 floats of B and C per token), and the
-// sum over states is one 16-lane DPP reduction per channel.  dt and the decay
-// of each staged token are computed once, by the first kScan2Chunk threads.
-constexpr int kScan2Chunk = 32;
-// Rescaled recurrence: with P_t the product of the decays since the last
-// rescale point, S_t = P_t * R_t where R_t = R_{t-1} + (dt_t x_t / P_t) B_t,
-// and y_t = P_t * (C_t . R_t).  A state element then costs one FMA for the
-// update and one for the output (the direct form needs a multiply more).  The
-// state is brought back to S at every chunk boundary, and a token at which P
-// would fall below kScanPMin becomes a rescale point: R is multiplied by the
-// decay up to and including that token (R * P_{t-1} * dA_t = dA_t S_{t-1}),
-// and P restarts at 1.
-constexpr float kScanPMin = 0x1p-40f;
-__global__ __launch_bounds__(256) void scan64x128_kernel(ScanArgs a) {
-  constexpr int P = 64, N = 128, Q = kScan2Chunk;
-  __shared__ float4 sB[Q][N / 4], sC[Q][N / 4], sx[Q][P / 4], sz[Q][P / 4];
-  __shared__ float sdt[Q], sdA[Q], sP[Q], sW[Q], sRen[Q];
-  __shared__ int smode[Q];  // 1: rescale point (R *= sRen[t] before the update)
-  __shared__ float sPend;
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int c = tid >> 4, s = tid & 15;
-  const int pb = c >> 2, pq = c & 3;
-  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;  // [P/16][N][16]
-  float4 S[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) S[k] = *(const float4*)(stb + ((size_t)(pb * N + 8 * s + k) * 16 + pq * 4));
-  const float dtb = a.dt_bias[h], ea = __expf(a.A_log[h]), Dh = a.D[h];
-  const size_t row0 = (size_t)b * a.T;
-  for (int t0 = 0; t0 < a.T; t0 += Q) {
-    const int tc = min(Q, a.T - t0);
-    __syncthreads();  // the previous chunk is consumed
-    for (int i = tid; i < tc * (N / 4); i += 256) {
-      const int tt = i / (N / 4), q = i % (N / 4);
-      const float4* xr = (const float4*)(a.xc + (row0 + t0 + tt) * a.cdim + a.d_inner);
-      sB[tt][q] = xr[q];
-      sC[tt][q] = xr[N / 4 + q];
-    }
-    for (int i = tid; i < tc * (P / 4); i += 256) {
-      const int tt = i / (P / 4), q = i % (P / 4);
-      sx[tt][q] = ((const float4*)(a.xc + (row0 + t0 + tt) * a.cdim + (size_t)h * P))[q];
-      sz[tt][q] = ((const float4*)(a.zx + (row0 + t0 + tt) * a.ldzx + (size_t)h * P))[q];
-    }
-    if (tid < tc) {
-      const float dt = softplus_f(a.zx[(row0 + t0 + tid) * a.ldzx + a.dt_off + h] + dtb);
-      sdt[tid] = dt;
-      sdA[tid] = __expf(-dt * ea);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      // the rescale schedule of the chunk (R = S at its start)
-      float pr = 1.0f;
-      for (int tt = 0; tt < tc; ++tt) {
-        const float np = pr * sdA[tt];
-        const bool re = np < kScanPMin;
-        smode[tt] = re;
-        sRen[tt] = np;
-        pr = re ? 1.0f : np;
-        sP[tt] = pr;
-        sW[tt] = sdt[tt] / pr;
-      }
-      sPend = pr;
-    }
-    __syncthreads();
-    for (int tt = 0; tt < tc; ++tt) {
-      const int mode = __builtin_amdgcn_readfirstlane(smode[tt]);
-      const float4 xv = sx[tt][c];
-      const float4 b0 = sB[tt][2 * s], b1 = sB[tt][2 * s + 1];
-      const float4 c0 = sC[tt][2 * s], c1 = sC[tt][2 * s + 1];
-      const float bn[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      const float cn[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      if (mode != 0) {
-        const float r = sRen[tt];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          S[k].x *= r;
-          S[k].y *= r;
-          S[k].z *= r;
-          S[k].w *= r;
-        }
-      }
-      const float wdt = sW[tt];
-      const float w0 = wdt * xv.x, w1 = wdt * xv.y, w2 = wdt * xv.z, w3 = wdt * xv.w;
-      float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        float4 v = S[k];
-        v.x += w0 * bn[k];
-        v.y += w1 * bn[k];
-        v.z += w2 * bn[k];
-        v.w += w3 * bn[k];
-        S[k] = v;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        y0 += S[k].x * cn[k];
-        y1 += S[k].y * cn[k];
-        y2 += S[k].z * cn[k];
-        y3 += S[k].w * cn[k];
-      }
-      y0 = row_sum16(y0);
-      y1 = row_sum16(y1);
-      y2 = row_sum16(y2);
-      y3 = row_sum16(y3);
-      // the row sums sit in all 16 lanes of the row: lanes s = 0..3 gate one channel each
-      if (s < 4) {
-        const float yv = s == 0 ? y0 : s == 1 ? y1 : s == 2 ? y2 : y3;
-        const float xs = s == 0 ? xv.x : s == 1 ? xv.y : s == 2 ? xv.z : xv.w;
-        const float zs = ((const float*)sz[tt])[4 * c + s];
-        a.g[(row0 + t0 + tt) * a.d_inner + (size_t)h * P + 4 * c + s] = (sP[tt] * yv + Dh * xs) * silu_rcp(zs);
-      }
-    }
-    // back to S at the chunk boundary
-    const float pe = sPend;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      S[k].x *= pe;
-      S[k].y *= pe;
-      S[k].z *= pe;
-      S[k].w *= pe;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) *(float4*)(stb + ((size_t)(pb * N + 8 * s + k) * 16 + pq * 4)) = S[k];
-}
-
-// One decode token per sequence (T = 1), headdim 64, d_state 128.  Workgroup
-// (head, sequence) of 256 threads: thread t owns channels 16 pb + 4 pq + 0..3
-// (pq = t & 3, pb = (t >> 2) & 3) and states 8 ns .. 8 ns + 7 (ns = t >> 4),
-// read and written as float4 along the channels of the [P/16][N][16] block
-// layout (16 lanes cover 256 contiguous bytes).  The sum over states crosses
-// the 16 state segments once, through LDS.
-__global__ __launch_bounds__(256) void scan1_kernel(ScanArgs a) {
-  constexpr int P = 64, N = 128, NPT = 8;
-  __shared__ float red[16][P];
-  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int pq = t & 3, pb = (t >> 2) & 3, ns = t >> 4;
-  const int p0 = pb * 16 + pq * 4;
-  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;
-  const float* xr = a.xc + (size_t)b * a.cdim;
-  float4 S[NPT];
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) S[i] = *(const float4*)(stb + ((size_t)(pb * N + ns * NPT + i) * 16 + pq * 4));
-  const float4 xv = *(const float4*)(xr + h * P + p0);
-  const float4 b0 = *(const float4*)(xr + a.d_inner + ns * NPT), b1 = *(const float4*)(xr + a.d_inner + ns * NPT + 4);
-  const float4 c0 = *(const float4*)(xr + a.d_inner + N + ns * NPT),
-               c1 = *(const float4*)(xr + a.d_inner + N + ns * NPT + 4);
-  const float dt = softplus_f(a.zx[(size_t)b * a.ldzx + a.dt_off + h] + a.dt_bias[h]);
-  const float dA = __expf(-dt * __expf(a.A_log[h]));
-  const float bn[NPT] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-  const float cn[NPT] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-  const float dx0 = dt * xv.x, dx1 = dt * xv.y, dx2 = dt * xv.z, dx3 = dt * xv.w;
-  float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) {
-    float4 v = S[i];
-    v.x = v.x * dA + dx0 * bn[i];
-    v.y = v.y * dA + dx1 * bn[i];
-    v.z = v.z * dA + dx2 * bn[i];
-    v.w = v.w * dA + dx3 * bn[i];
-    S[i] = v;
-    y0 += v.x * cn[i];
-    y1 += v.y * cn[i];
-    y2 += v.z * cn[i];
-    y3 += v.w * cn[i];
-  }
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) *(float4*)(stb + ((size_t)(pb * N + ns * NPT + i) * 16 + pq * 4)) = S[i];
-  red[ns][p0 + 0] = y0;
-  red[ns][p0 + 1] = y1;
-  red[ns][p0 + 2] = y2;
-  red[ns][p0 + 3] = y3;
-  __syncthreads();
-  if (t < P) {
-    float yy = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) yy += red[k][t];
-    const float x = xr[h * P + t];
-    const float z = a.zx[(size_t)b * a.ldzx + h * P + t];
-    a.g[(size_t)b * a.d_inner + h * P + t] = (yy + a.D[h] * x) * silu_f(z);
-  }
-}
-
-hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
-  if (a.B <= 0 || a.T <= 0) return hipSuccess;
-  const dim3 grid(a.H, a.B);
-  if (a.T == 1 && P == 64 && N == 128) {
-    hipLaunchKernelGGL(scan1_kernel, grid, dim3(256), 0, st, a);
-    return hipGetLastError();
-  }
-  if (P == 64 && N == 128) hipLaunchKernelGGL(scan64x128_kernel, grid, dim3(256), 0, st, a);
-  else if (P == 32 && N == 16) hipLaunchKernelGGL((scan_kernel<32, 16>), grid, dim3(128), 0, st, a);
-  else if (P == 64 && N == 64) hipLaunchKernelGGL((scan_kernel<64, 64>), grid, dim3(256), 0, st, a);
-  else if (P == 32 && N == 128) hipLaunchKernelGGL((scan_kernel<32, 128>), grid, dim3(128), 0, st, a);
-  else if (P == 64 && N == 16) hipLaunchKernelGGL((scan_kernel<64, 16>), grid, dim3(256), 0, st, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-bool scan_supported(int P, int N) {
-  return (P == 64 && (N == 128 || N == 64 || N == 16)) || (P == 32 && (N == 16 || N == 128));
 }
 
 // ---------------------------------------------------------------------------

@@ -85,6 +85,7 @@ struct dfssm_ctx {
     float *h = nullptr, *s = nullptr, *t = nullptr, *zx = nullptr, *xc = nullptr, *g = nullptr;
     int8_t* q = nullptr;
     int32_t* qsum = nullptr;
+    float* gram = nullptr;  // chunked-scan workspace
   } gw;
 
   // persistent batch-1 path
@@ -314,7 +315,8 @@ dfssm_status ensure_gemm_ws(dfssm_ctx* c, size_t rows) {
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
   const size_t o_h = take(4 * rows * c->dm), o_s = take(4 * rows), o_t = take(4 * rows * 16),
                o_zx = take(4 * rows * c->dproj), o_xc = take(4 * rows * c->cdim), o_g = take(4 * rows * c->di),
-               o_q = take(rows * mx), o_qs = take(4 * rows);
+               o_q = take(rows * mx), o_qs = take(4 * rows),
+               o_gram = take(4 * (rows / 64 + (size_t)c->maxB) * 64 * 64);
   char* buf = nullptr;
   if (hipMalloc(&buf, off) != hipSuccess) {
     (void)hipGetLastError();
@@ -337,6 +339,7 @@ dfssm_status ensure_gemm_ws(dfssm_ctx* c, size_t rows) {
   c->gw.g = (float*)(buf + o_g);
   c->gw.q = (int8_t*)(buf + o_q);
   c->gw.qsum = (int32_t*)(buf + o_qs);
+  c->gw.gram = (float*)(buf + o_gram);
   return DFSSM_OK;
 }
 
@@ -385,7 +388,8 @@ hipError_t b_scan(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
   auto& w = c->gw;
   ScanArgs sa{w.xc, w.zx, c->dproj, 2 * c->di + 2 * c->N, c->lt<float>(l, DFSSM_T_A_LOG),
               c->lt<float>(l, DFSSM_T_DT_BIAS), c->lt<float>(l, DFSSM_T_D),
-              c->ssm + (size_t)l * c->H * c->P * c->N, c->ssm_bstride, w.g, B, T, c->H, c->di, c->cdim};
+              c->ssm + (size_t)l * c->H * c->P * c->N, c->ssm_bstride, w.g, B, T, c->H, c->di, c->cdim,
+              w.gram};
   return launch_scan(sa, c->P, c->N, st);
 }
 

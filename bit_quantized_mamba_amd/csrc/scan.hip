@@ -1,0 +1,612 @@
+// SSM scans of the batched path over T tokens per sequence, gfx950.
+//
+//  * scan_kernel / scan64x128_kernel: the recurrence token by token, one
+//    workgroup per (sequence, head), state in registers (for headdim 64,
+//    d_state 128 carried divided by its running decay, so an element costs
+//    one FMA per token), B and C staged through LDS; gated output.
+//  * scan1_kernel: one decode token per sequence (headdim 64, d_state 128).
+//  * ssd_gram_kernel / ssd_scan_kernel: the same recurrence for headdim 64,
+//    d_state 128 unrolled over chunks of 64 tokens into matrix products on
+//    the fp32 matrix cores (prefill).
+//
+// The recurrence (the Mamba-2 block, per head h and sequence):
+//   dt = softplus(dt_raw + dt_bias), dA = exp(-dt exp(A_log)),
+//   S <- dA S + dt x B^T, y = S C + D x, g = y * silu(z).
+#include "common.h"
+
+namespace dfssm {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// SSM scan over T tokens.  Workgroup (head h, sequence b) of 4 P threads:
+// thread (p = tid / 4, seg = tid % 4) holds S[p][seg N/4 .. +N/4) in
+// registers.  B, C, x, z and dt of kScanChunk tokens are staged in LDS; y[p]
+// is the sum over the four threads of a quad (DPP).
+// ---------------------------------------------------------------------------
+constexpr int kScanChunk = 16;
+
+template <int P, int N>
+__global__ __launch_bounds__(4 * P) void scan_kernel(ScanArgs a) {
+  constexpr int NPT = N / 4;
+  constexpr int NT = 4 * P;
+  __shared__ float sB[kScanChunk][N], sC[kScanChunk][N], sx[kScanChunk][P], sz[kScanChunk][P], sdt[kScanChunk];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int p = tid >> 2, seg = tid & 3;
+  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;  // [P/16][N][16]
+  float S[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int n = seg * NPT + j;
+    S[j] = stb[((size_t)(p >> 4) * N + n) * 16 + (p & 15)];
+  }
+  const float dtb = a.dt_bias[h], ea = __expf(a.A_log[h]), Dh = a.D[h];
+  const size_t row0 = (size_t)b * a.T;
+  for (int t0 = 0; t0 < a.T; t0 += kScanChunk) {
+    const int tc = min(kScanChunk, a.T - t0);
+    __syncthreads();  // previous chunk fully consumed
+    for (int i = tid; i < tc * N; i += NT) {
+      const int tt = i / N, n = i % N;
+      const float* xr = a.xc + (row0 + t0 + tt) * a.cdim;
+      sB[tt][n] = xr[a.d_inner + n];
+      sC[tt][n] = xr[a.d_inner + N + n];
+    }
+    for (int i = tid; i < tc * P; i += NT) {
+      const int tt = i / P, pp = i % P;
+      sx[tt][pp] = a.xc[(row0 + t0 + tt) * a.cdim + (size_t)h * P + pp];
+      sz[tt][pp] = a.zx[(row0 + t0 + tt) * a.ldzx + (size_t)h * P + pp];
+    }
+    for (int i = tid; i < tc; i += NT) sdt[i] = a.zx[(row0 + t0 + i) * a.ldzx + a.dt_off + h];
+    __syncthreads();
+    for (int tt = 0; tt < tc; ++tt) {
+      const float dt = softplus_f(sdt[tt] + dtb);
+      const float dA = __expf(-dt * ea);
+      const float x = sx[tt][p];
+      const float dtx = dt * x;
+      float y = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        const int n = seg * NPT + j;
+        S[j] = S[j] * dA + dtx * sB[tt][n];
+        y += S[j] * sC[tt][n];
+      }
+      y += dpp_f<kDppQuadSwap1>(y);
+      y += dpp_f<kDppQuadSwap2>(y);
+      if (seg == 0) {
+        const float yy = y + Dh * x;
+        a.g[(row0 + t0 + tt) * a.d_inner + (size_t)h * P + p] = yy * silu_f(sz[tt][p]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int n = seg * NPT + j;
+    stb[((size_t)(p >> 4) * N + n) * 16 + (p & 15)] = S[j];
+  }
+}
+
+// The scan over T tokens for headdim 64, d_state 128.  Workgroup (head,
+// sequence) of 256 threads; thread t owns channels 4c .. 4c+3 (c = t >> 4)
+// and states 8s .. 8s+7 (s = t & 15) as float4 over the channels, i.e. one
+// float4 of the [P/16][N][16] state block per state.  A token then costs a
+// thread two float4 of B, two of C and one of x from LDS for 64 FMAs (the
+// one-channel-per-thread layout reads 64 floats of B and C per token), and the
+// sum over states is one 16-lane DPP reduction per channel.  dt and the decay
+// of each staged token are computed once, by the first kScan2Chunk threads.
+constexpr int kScan2Chunk = 32;
+// Rescaled recurrence: with P_t the product of the decays since the last
+// rescale point, S_t = P_t * R_t where R_t = R_{t-1} + (dt_t x_t / P_t) B_t,
+// and y_t = P_t * (C_t . R_t).  A state element then costs one FMA for the
+// update and one for the output (the direct form needs a multiply more).  The
+// state is brought back to S at every chunk boundary, and a token at which P
+// would fall below kScanPMin becomes a rescale point: R is multiplied by the
+// decay up to and including that token (R * P_{t-1} * dA_t = dA_t S_{t-1}),
+// and P restarts at 1.
+constexpr float kScanPMin = 0x1p-40f;
+__global__ __launch_bounds__(256) void scan64x128_kernel(ScanArgs a) {
+  constexpr int P = 64, N = 128, Q = kScan2Chunk;
+  __shared__ float4 sB[Q][N / 4], sC[Q][N / 4], sx[Q][P / 4], sz[Q][P / 4];
+  __shared__ float sdt[Q], sdA[Q], sP[Q], sW[Q], sRen[Q];
+  __shared__ int smode[Q];  // 1: rescale point (R *= sRen[t] before the update)
+  __shared__ float sPend;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int c = tid >> 4, s = tid & 15;
+  const int pb = c >> 2, pq = c & 3;
+  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;  // [P/16][N][16]
+  float4 S[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) S[k] = *(const float4*)(stb + ((size_t)(pb * N + 8 * s + k) * 16 + pq * 4));
+  const float dtb = a.dt_bias[h], ea = __expf(a.A_log[h]), Dh = a.D[h];
+  const size_t row0 = (size_t)b * a.T;
+  for (int t0 = 0; t0 < a.T; t0 += Q) {
+    const int tc = min(Q, a.T - t0);
+    __syncthreads();  // the previous chunk is consumed
+    for (int i = tid; i < tc * (N / 4); i += 256) {
+      const int tt = i / (N / 4), q = i % (N / 4);
+      const float4* xr = (const float4*)(a.xc + (row0 + t0 + tt) * a.cdim + a.d_inner);
+      sB[tt][q] = xr[q];
+      sC[tt][q] = xr[N / 4 + q];
+    }
+    for (int i = tid; i < tc * (P / 4); i += 256) {
+      const int tt = i / (P / 4), q = i % (P / 4);
+      sx[tt][q] = ((const float4*)(a.xc + (row0 + t0 + tt) * a.cdim + (size_t)h * P))[q];
+      sz[tt][q] = ((const float4*)(a.zx + (row0 + t0 + tt) * a.ldzx + (size_t)h * P))[q];
+    }
+    if (tid < tc) {
+      const float dt = softplus_f(a.zx[(row0 + t0 + tid) * a.ldzx + a.dt_off + h] + dtb);
+      sdt[tid] = dt;
+      sdA[tid] = __expf(-dt * ea);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      // the rescale schedule of the chunk (R = S at its start)
+      float pr = 1.0f;
+      for (int tt = 0; tt < tc; ++tt) {
+        const float np = pr * sdA[tt];
+        const bool re = np < kScanPMin;
+        smode[tt] = re;
+        sRen[tt] = np;
+        pr = re ? 1.0f : np;
+        sP[tt] = pr;
+        sW[tt] = sdt[tt] / pr;
+      }
+      sPend = pr;
+    }
+    __syncthreads();
+    for (int tt = 0; tt < tc; ++tt) {
+      const int mode = __builtin_amdgcn_readfirstlane(smode[tt]);
+      const float4 xv = sx[tt][c];
+      const float4 b0 = sB[tt][2 * s], b1 = sB[tt][2 * s + 1];
+      const float4 c0 = sC[tt][2 * s], c1 = sC[tt][2 * s + 1];
+      const float bn[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      const float cn[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      if (mode != 0) {
+        const float r = sRen[tt];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          S[k].x *= r;
+          S[k].y *= r;
+          S[k].z *= r;
+          S[k].w *= r;
+        }
+      }
+      const float wdt = sW[tt];
+      const float w0 = wdt * xv.x, w1 = wdt * xv.y, w2 = wdt * xv.z, w3 = wdt * xv.w;
+      float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float4 v = S[k];
+        v.x += w0 * bn[k];
+        v.y += w1 * bn[k];
+        v.z += w2 * bn[k];
+        v.w += w3 * bn[k];
+        S[k] = v;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        y0 += S[k].x * cn[k];
+        y1 += S[k].y * cn[k];
+        y2 += S[k].z * cn[k];
+        y3 += S[k].w * cn[k];
+      }
+      y0 = row_sum16(y0);
+      y1 = row_sum16(y1);
+      y2 = row_sum16(y2);
+      y3 = row_sum16(y3);
+      // the row sums sit in all 16 lanes of the row: lanes s = 0..3 gate one channel each
+      if (s < 4) {
+        const float yv = s == 0 ? y0 : s == 1 ? y1 : s == 2 ? y2 : y3;
+        const float xs = s == 0 ? xv.x : s == 1 ? xv.y : s == 2 ? xv.z : xv.w;
+        const float zs = ((const float*)sz[tt])[4 * c + s];
+        a.g[(row0 + t0 + tt) * a.d_inner + (size_t)h * P + 4 * c + s] = (sP[tt] * yv + Dh * xs) * silu_rcp(zs);
+      }
+    }
+    // back to S at the chunk boundary
+    const float pe = sPend;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      S[k].x *= pe;
+      S[k].y *= pe;
+      S[k].z *= pe;
+      S[k].w *= pe;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) *(float4*)(stb + ((size_t)(pb * N + 8 * s + k) * 16 + pq * 4)) = S[k];
+}
+
+// One decode token per sequence (T = 1), headdim 64, d_state 128.  Workgroup
+// (head, sequence) of 256 threads: thread t owns channels 16 pb + 4 pq + 0..3
+// (pq = t & 3, pb = (t >> 2) & 3) and states 8 ns .. 8 ns + 7 (ns = t >> 4),
+// read and written as float4 along the channels of the [P/16][N][16] block
+// layout (16 lanes cover 256 contiguous bytes).  The sum over states crosses
+// the 16 state segments once, through LDS.
+__global__ __launch_bounds__(256) void scan1_kernel(ScanArgs a) {
+  constexpr int P = 64, N = 128, NPT = 8;
+  __shared__ float red[16][P];
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int pq = t & 3, pb = (t >> 2) & 3, ns = t >> 4;
+  const int p0 = pb * 16 + pq * 4;
+  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;
+  const float* xr = a.xc + (size_t)b * a.cdim;
+  float4 S[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) S[i] = *(const float4*)(stb + ((size_t)(pb * N + ns * NPT + i) * 16 + pq * 4));
+  const float4 xv = *(const float4*)(xr + h * P + p0);
+  const float4 b0 = *(const float4*)(xr + a.d_inner + ns * NPT), b1 = *(const float4*)(xr + a.d_inner + ns * NPT + 4);
+  const float4 c0 = *(const float4*)(xr + a.d_inner + N + ns * NPT),
+               c1 = *(const float4*)(xr + a.d_inner + N + ns * NPT + 4);
+  const float dt = softplus_f(a.zx[(size_t)b * a.ldzx + a.dt_off + h] + a.dt_bias[h]);
+  const float dA = __expf(-dt * __expf(a.A_log[h]));
+  const float bn[NPT] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  const float cn[NPT] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float dx0 = dt * xv.x, dx1 = dt * xv.y, dx2 = dt * xv.z, dx3 = dt * xv.w;
+  float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    float4 v = S[i];
+    v.x = v.x * dA + dx0 * bn[i];
+    v.y = v.y * dA + dx1 * bn[i];
+    v.z = v.z * dA + dx2 * bn[i];
+    v.w = v.w * dA + dx3 * bn[i];
+    S[i] = v;
+    y0 += v.x * cn[i];
+    y1 += v.y * cn[i];
+    y2 += v.z * cn[i];
+    y3 += v.w * cn[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) *(float4*)(stb + ((size_t)(pb * N + ns * NPT + i) * 16 + pq * 4)) = S[i];
+  red[ns][p0 + 0] = y0;
+  red[ns][p0 + 1] = y1;
+  red[ns][p0 + 2] = y2;
+  red[ns][p0 + 3] = y3;
+  __syncthreads();
+  if (t < P) {
+    float yy = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) yy += red[k][t];
+    const float x = xr[h * P + t];
+    const float z = a.zx[(size_t)b * a.ldzx + h * P + t];
+    a.g[(size_t)b * a.d_inner + h * P + t] = (yy + a.D[h] * x) * silu_f(z);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunked scan on the matrix cores (headdim P = 64, d_state N = 128).
+//
+// Within a chunk of L = 64 tokens, with a_t = -dt_t exp(A_log) and the
+// running sums A_i = a_0 + ... + a_i (positions i, j in the chunk), the
+// recurrence unrolls to
+//   S_i = exp(A_i) S_in + sum_{j<=i} exp(A_i - A_j) dt_j x_j B_j^T
+//   y_i = exp(A_i) S_in C_i + sum_{j<=i} exp(A_i - A_j) dt_j (C_i . B_j) x_j.
+// With G = C B^T (shared by all heads of a sequence) and
+// M[i][j] = G[i][j] exp(A_i - A_j) dt_j for j <= i (0 above the diagonal):
+//   Y     = diag(exp(A)) C S_in^T + M X                        [L][P]
+//   S_out = exp(A_{L-1}) S_in + X^T diag(w) B,  w_j = exp(A_{L-1} - A_j) dt_j
+// The ragged tail of a sequence is padded with tokens of dt = 0 (no decay, no
+// input), which leave the state as it is.  Every product is fp32 on
+// v_mfma_f32_32x32x2f32 (exact products, fp32 sums).
+//
+// ssd_gram_kernel writes G for every chunk; ssd_scan_kernel walks the chunks
+// of one sequence in order for two heads, with the state in registers.
+// ---------------------------------------------------------------------------
+constexpr int kSsdL = 64;                      // tokens per chunk
+constexpr int kSsdRow = kSsdL + 4;             // LDS row of 64 floats (+4 against bank conflicts)
+constexpr int kSsdCRow = 128 + 4;              // LDS row of C (128 floats)
+constexpr int kSsdOC = 0;                      // C       [64 i][kSsdCRow]
+constexpr int kSsdOBt = kSsdOC + 64 * kSsdCRow;  // B^T   [128 n][kSsdRow]
+constexpr int kSsdOX = kSsdOBt + 128 * kSsdRow;  // X^T   [2 heads][64 p][kSsdRow]
+constexpr int kSsdOG = kSsdOX + 128 * kSsdRow;   // G     [64 i][kSsdRow]
+constexpr int kSsdOPar = kSsdOG + 64 * kSsdRow;  // per head: A_i, dt_j, w_j, exp(A_i)  [2][4][64]
+constexpr int kSsdFloats = kSsdOPar + 2 * 4 * 64;
+constexpr size_t kSsdLds = sizeof(float) * kSsdFloats;
+static_assert(8 * 16 * 64 <= 64 * kSsdCRow, "the partial-sum exchange fits in the C buffer");
+
+__device__ __forceinline__ v16f mfma_f32(float a, float b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// G[b][c][i][j] = C_{t0+i} . B_{t0+j} for chunk c of sequence b (rows past the
+// end of the sequence count as zero).  Workgroup (chunk, sequence), wave w
+// computes the 32 x 32 tile (w >> 1, w & 1); the tile above the diagonal is
+// never read and not written.
+__global__ __launch_bounds__(256) void ssd_gram_kernel(ScanArgs a) {
+  constexpr int N = 128;
+  __shared__ __attribute__((aligned(16))) float sC[64 * kSsdRow], sB[64 * kSsdRow];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
+  const int ti = wave >> 1, tj = wave & 1;
+  const int t0 = c * kSsdL, Lc = min(kSsdL, a.T - t0);
+  const size_t row0 = (size_t)b * a.T + t0;
+  v16f acc = (v16f){};
+  for (int nh = 0; nh < 2; ++nh) {  // two halves of d_state
+    if (nh) __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int idx = tid + 256 * k;          // 2048 float4: 64 rows x (B 16, C 16)
+      const int j = idx >> 5, q = idx & 31;   // q < 16: B, else C
+      const int cc = (q & 15) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < Lc) v = *(const float4*)(a.xc + (row0 + j) * a.cdim + a.d_inner + (q >> 4) * N + nh * 64 + cc);
+      *(float4*)((q < 16 ? sB : sC) + j * kSsdRow + cc) = v;
+    }
+    __syncthreads();
+    if (wave != 1) {
+      const float* ar = sC + (32 * ti + col) * kSsdRow + 4 * half;
+      const float* br = sB + (32 * tj + col) * kSsdRow + 4 * half;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 av = *(const float4*)(ar + 8 * q), bv = *(const float4*)(br + 8 * q);
+        acc = mfma_f32(av.x, bv.x, acc);
+        acc = mfma_f32(av.y, bv.y, acc);
+        acc = mfma_f32(av.z, bv.z, acc);
+        acc = mfma_f32(av.w, bv.w, acc);
+      }
+    }
+  }
+  if (wave == 1) return;
+  float* gp = a.gram + ((size_t)b * gridDim.x + c) * (kSsdL * kSsdL);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = 32 * ti + 8 * (r >> 2) + 4 * half + (r & 3);
+    gp[i * kSsdL + 32 * tj + col] = acc[r];
+  }
+}
+
+// Workgroup (head pair, sequence) of 8 waves; wave w serves head 2 hp + (w >> 2),
+// channel block pb = (w >> 1) & 1 (channels 32 pb .. 32 pb + 31) and half
+// h2 = w & 1: it holds the state tiles S^T[n][p] of states 64 h2 .. 64 h2 + 63
+// (two 32 x 32 accumulator tiles: lane = channel, register = state) and
+// produces the outputs of chunk positions 32 h2 .. 32 h2 + 31.  Per chunk:
+//  (a) partial C S_in^T over its 64 states for both position blocks (its own
+//      state tiles are the A operand as they sit in the accumulators), the
+//      partial of the other block handed to the partner wave through LDS;
+//  (b) + M X for its positions;
+//  (c) S <- exp(A_{L-1}) S + X^T diag(w) B for its state tiles.
+// The k index of every product runs over 4-element runs so that each operand
+// comes from LDS as one 16-byte read per four steps: k-step s of half hf is
+// element 8 (s / 4) + 4 hf + s % 4, the order in which the accumulator
+// registers hold the states.
+__global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
+  constexpr int P = 64, N = 128;
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  const int hp = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
+  const int hh = wave >> 2, pb = (wave >> 1) & 1, h2 = wave & 1;
+  const int h = 2 * hp + hh;
+  const int p = 32 * pb + col;  // this lane's channel in (b), (c) and the state tiles
+  const int nch = (a.T + kSsdL - 1) / kSsdL;
+  const size_t rowb = (size_t)b * a.T;
+  float* sPar = sm + kSsdOPar + hh * 256;  // [0] A_i  [64] dt_j  [128] w_j  [192] exp(A_i)
+  const float* sXh = sm + kSsdOX + hh * 64 * kSsdRow;
+
+  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;  // [P/16][N][16]
+  // state element (p, n) of tile t, register r: n = 64 h2 + 32 t + 8 (r / 4) + 4 half + r % 4;
+  // relative to this lane's first element the offsets are compile-time constants
+  float* sp = stb + ((size_t)(p >> 4) * N + 64 * h2 + 4 * half) * 16 + (p & 15);
+  v16f S[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[t][r] = sp[(32 * t + 8 * (r >> 2) + (r & 3)) * 16];
+  const float dtb = a.dt_bias[h], ea = __expf(a.A_log[h]), Dh = a.D[h];
+  const int iy = 32 * h2 + col;  // this lane's output position
+
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = c * kSsdL, Lc = min(kSsdL, a.T - t0);
+    const size_t row0 = rowb + t0;
+    __syncthreads();  // the previous chunk is done with LDS
+    // ---- stage the chunk: x of both heads (transposed), B (transposed), C, G
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + 512 * k;  // 2048 float4: 64 rows x 32
+      const int j = idx >> 5, q = idx & 31;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < Lc) v = *(const float4*)(a.xc + (row0 + j) * a.cdim + (size_t)(2 * hp) * P + 4 * q);
+      float* d = sm + kSsdOX + (4 * q) * kSsdRow + j;  // [hh][p][j] with hh * 64 + p = 4 q
+      d[0] = v.x;
+      d[kSsdRow] = v.y;
+      d[2 * kSsdRow] = v.z;
+      d[3 * kSsdRow] = v.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int idx = tid + 512 * k;  // 4096 float4: 64 rows x (B 32, C 32)
+      const int j = idx >> 6, q = idx & 63;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < Lc) v = *(const float4*)(a.xc + (row0 + j) * a.cdim + a.d_inner + 4 * q);
+      if (q < 32) {
+        float* d = sm + kSsdOBt + (4 * q) * kSsdRow + j;
+        d[0] = v.x;
+        d[kSsdRow] = v.y;
+        d[2 * kSsdRow] = v.z;
+        d[3 * kSsdRow] = v.w;
+      } else {
+        *(float4*)(sm + kSsdOC + j * kSsdCRow + 4 * (q - 32)) = v;
+      }
+    }
+    {
+      const float* gp = a.gram + ((size_t)b * nch + c) * (kSsdL * kSsdL);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int idx = tid + 512 * k;  // 1024 float4
+        const int i = idx >> 4, q = idx & 15;
+        *(float4*)(sm + kSsdOG + i * kSsdRow + 4 * q) = *(const float4*)(gp + i * kSsdL + 4 * q);
+      }
+    }
+    float dtraw = 0.0f;
+    if (wave < 2 && lane < Lc) dtraw = a.zx[(row0 + lane) * a.ldzx + a.dt_off + 2 * hp + wave];
+    // gate inputs of this lane's outputs, loaded now and used at the end
+    float4 zv[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      zv[r4] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (iy < Lc)
+        zv[r4] = *(const float4*)(a.zx + (row0 + iy) * a.ldzx + (size_t)h * P + 32 * pb + 8 * r4 + 4 * half);
+    }
+    __syncthreads();
+    // ---- per-head chunk parameters (wave hh, lane = position j)
+    if (wave < 2) {
+      float* par = sm + kSsdOPar + wave * 256;
+      const int hw = 2 * hp + wave;
+      const float dt = lane < Lc ? softplus_f(dtraw + a.dt_bias[hw]) : 0.0f;
+      float cum = -dt * __expf(a.A_log[hw]);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_up(cum, d);
+        if (lane >= d) cum += o;
+      }
+      const float end = __shfl(cum, 63);
+      par[lane] = cum;
+      par[64 + lane] = dt;
+      par[128 + lane] = __expf(end - cum) * dt;
+      par[192 + lane] = __expf(cum);
+    }
+    __syncthreads();
+
+    // ---- (a) Y_inter^T[p][i] partial over this wave's 64 states, both position blocks
+    v16f Y0 = (v16f){}, Y1 = (v16f){};
+    {
+      const float e0 = sPar[192 + col], e1 = sPar[192 + 32 + col];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int nb = 2 * h2 + t;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 c0 = *(const float4*)(sm + kSsdOC + col * kSsdCRow + 32 * nb + 8 * r4 + 4 * half);
+          const float4 c1 = *(const float4*)(sm + kSsdOC + (32 + col) * kSsdCRow + 32 * nb + 8 * r4 + 4 * half);
+          Y0 = mfma_f32(S[t][4 * r4 + 0], c0.x * e0, Y0);
+          Y1 = mfma_f32(S[t][4 * r4 + 0], c1.x * e1, Y1);
+          Y0 = mfma_f32(S[t][4 * r4 + 1], c0.y * e0, Y0);
+          Y1 = mfma_f32(S[t][4 * r4 + 1], c1.y * e1, Y1);
+          Y0 = mfma_f32(S[t][4 * r4 + 2], c0.z * e0, Y0);
+          Y1 = mfma_f32(S[t][4 * r4 + 2], c1.z * e1, Y1);
+          Y0 = mfma_f32(S[t][4 * r4 + 3], c0.w * e0, Y0);
+          Y1 = mfma_f32(S[t][4 * r4 + 3], c1.w * e1, Y1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    __syncthreads();  // C is no longer read: its space takes the partial sums
+    float* xch = sm + kSsdOC;
+    {
+      const v16f& give = h2 ? Y0 : Y1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[(wave * 16 + r) * 64 + lane] = give[r];
+    }
+    __syncthreads();
+    v16f Yo = h2 ? Y1 : Y0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Yo[r] += xch[((wave ^ 1) * 16 + r) * 64 + lane];
+
+    // ---- (b) + M X for positions 32 h2 .. 32 h2 + 31 (positions j <= i only)
+    float xs[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 v = *(const float4*)(sXh + p * kSsdRow + 8 * q + 4 * half);
+      xs[4 * q + 0] = v.x;
+      xs[4 * q + 1] = v.y;
+      xs[4 * q + 2] = v.z;
+      xs[4 * q + 3] = v.w;
+    }
+    {
+      const float cumi = sPar[iy];
+      const int nq = h2 ? 8 : 4;  // block 0 needs j < 32 only
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (q < nq) {
+          const int j0 = 8 * q + 4 * half;
+          const float4 gv = *(const float4*)(sm + kSsdOG + iy * kSsdRow + j0);
+          const float4 cj = *(const float4*)(sPar + j0);
+          const float4 dj = *(const float4*)(sPar + 64 + j0);
+          const float m0 = j0 + 0 <= iy ? gv.x * __expf(cumi - cj.x) * dj.x : 0.0f;
+          const float m1 = j0 + 1 <= iy ? gv.y * __expf(cumi - cj.y) * dj.y : 0.0f;
+          const float m2 = j0 + 2 <= iy ? gv.z * __expf(cumi - cj.z) * dj.z : 0.0f;
+          const float m3 = j0 + 3 <= iy ? gv.w * __expf(cumi - cj.w) * dj.w : 0.0f;
+          Yo = mfma_f32(xs[4 * q + 0], m0, Yo);
+          Yo = mfma_f32(xs[4 * q + 1], m1, Yo);
+          Yo = mfma_f32(xs[4 * q + 2], m2, Yo);
+          Yo = mfma_f32(xs[4 * q + 3], m3, Yo);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+
+    // ---- (c) S <- exp(A_{L-1}) S + X^T diag(w) B for this wave's state tiles
+    {
+      const float dec = __expf(sPar[63]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        S[t] *= dec;
+        const float* bt = sm + kSsdOBt + (32 * (2 * h2 + t) + col) * kSsdRow + 4 * half;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float4 bv = *(const float4*)(bt + 8 * q);
+          const float4 wv = *(const float4*)(sPar + 128 + 8 * q + 4 * half);
+          S[t] = mfma_f32(bv.x * wv.x, xs[4 * q + 0], S[t]);
+          S[t] = mfma_f32(bv.y * wv.y, xs[4 * q + 1], S[t]);
+          S[t] = mfma_f32(bv.z * wv.z, xs[4 * q + 2], S[t]);
+          S[t] = mfma_f32(bv.w * wv.w, xs[4 * q + 3], S[t]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+
+    // ---- gated output of position iy: lane register r is channel 32 pb + 8 (r / 4) + 4 half + r % 4
+    if (iy < Lc) {
+      float* gr = a.g + (row0 + iy) * a.d_inner + (size_t)h * P;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int p0 = 32 * pb + 8 * r4 + 4 * half;
+        const float* xr = sXh + p0 * kSsdRow + iy;
+        float4 o;
+        o.x = (Yo[4 * r4 + 0] + Dh * xr[0]) * silu_f(zv[r4].x);
+        o.y = (Yo[4 * r4 + 1] + Dh * xr[kSsdRow]) * silu_f(zv[r4].y);
+        o.z = (Yo[4 * r4 + 2] + Dh * xr[2 * kSsdRow]) * silu_f(zv[r4].z);
+        o.w = (Yo[4 * r4 + 3] + Dh * xr[3 * kSsdRow]) * silu_f(zv[r4].w);
+        *(float4*)(gr + p0) = o;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sp[(32 * t + 8 * (r >> 2) + (r & 3)) * 16] = S[t][r];
+}
+
+hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
+  if (a.B <= 0 || a.T <= 0) return hipSuccess;
+  const dim3 grid(a.H, a.B);
+  if (a.T == 1 && P == 64 && N == 128) {
+    hipLaunchKernelGGL(scan1_kernel, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  if (P == 64 && N == 128 && a.gram && a.H % 2 == 0) {
+    static bool lds_set = false;
+    if (!lds_set) {
+      const hipError_t e = hipFuncSetAttribute((const void*)ssd_scan_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSsdLds);
+      if (e != hipSuccess) return e;
+      lds_set = true;
+    }
+    const int nch = (a.T + kSsdL - 1) / kSsdL;
+    hipLaunchKernelGGL(ssd_gram_kernel, dim3(nch, a.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(ssd_scan_kernel, dim3(a.H / 2, a.B), dim3(512), kSsdLds, st, a);
+    return hipGetLastError();
+  }
+  if (P == 64 && N == 128) hipLaunchKernelGGL(scan64x128_kernel, grid, dim3(256), 0, st, a);
+  else if (P == 32 && N == 16) hipLaunchKernelGGL((scan_kernel<32, 16>), grid, dim3(128), 0, st, a);
+  else if (P == 64 && N == 64) hipLaunchKernelGGL((scan_kernel<64, 64>), grid, dim3(256), 0, st, a);
+  else if (P == 32 && N == 128) hipLaunchKernelGGL((scan_kernel<32, 128>), grid, dim3(128), 0, st, a);
+  else if (P == 64 && N == 16) hipLaunchKernelGGL((scan_kernel<64, 16>), grid, dim3(256), 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+bool scan_supported(int P, int N) {
+  return (P == 64 && (N == 128 || N == 64 || N == 16)) || (P == 32 && (N == 16 || N == 128));
+}
+
+}  // namespace dfssm

@@ -1,8 +1,9 @@
 """Parity of the batched path (int8 matrix-core GEMMs, causal conv over T,
-sequential scan) against the CPU oracle: the GEMM kernel bit-exact on its
-integer sums, batched decode and traced prefill teacher-forced on the GPU's
-int8 codes, at the tiny shape, one 1.3B-shaped layer over 2048 tokens, and
-the 48-layer model."""
+the scan token by token or in 64-token chunks on the fp32 matrix cores)
+against the CPU oracle: the GEMM kernel bit-exact on its integer sums,
+batched decode and traced prefill teacher-forced on the GPU's int8 codes, at
+the tiny shape, one 1.3B-shaped layer (2048 tokens; ragged chunks continued
+from a state) and the 48-layer model."""
 import numpy as np
 import pytest
 
@@ -145,11 +146,11 @@ def test_1p3b_layer_decode_on_gemm_path(B):
 # traced prefill
 # ---------------------------------------------------------------------------
 
-def _follow_prefill(om, s, toks, tr, b, T, check_h_at=(), h_tol_what=""):
-    """Oracle run of sequence b over its T prompt tokens, taking the GPU's
-    int8 codes where they are correct roundings.  Returns (state, logits of the
-    last position)."""
-    st = oracle.State(s)
+def _follow_prefill(om, s, toks, tr, b, T, check_h_at=(), h_tol_what="", st=None):
+    """Oracle run of sequence b over its T prompt tokens (from state st, else
+    from zero), taking the GPU's int8 codes where they are correct roundings.
+    Returns (state, logits of the last position)."""
+    st = oracle.State(s) if st is None else st
     h = None
     for t in range(T):
         m = b * T + t
@@ -209,6 +210,35 @@ def test_one_1p3b_layer_prefill_2048_tokens():
         conv_g, ssm_g = eng.get_state(b)
         assert_close(conv_g, st.conv, what=f"conv state seq {b}")
         assert_close(ssm_g, st.ssm, what=f"ssm state seq {b}")
+    eng.close()
+
+
+def test_1p3b_layer_prefill_ragged_chunks_continue_from_state():
+    # Two sequences on one 1.3B-shaped layer: a prefill of 70 tokens (a whole
+    # 64-token chunk of the chunked scan and a ragged one), then 100 more
+    # tokens from the state it left (a nonzero initial state, a ragged last
+    # chunk).  Outputs and states follow the oracle token by token.
+    s = synth.LAYER_1P3B
+    seed = synth.SEED_BASE + 11
+    B, T1, T2 = 2, 70, 100
+    eng = engine(s, max_batch=B)
+    eng.load_synthetic(seed)
+    om = oracle.Model(s, synth.gen_model(s, seed))
+    toks = synth.gen_tokens(seed, 12, B * (T1 + T2), s.vocab).reshape(B, T1 + T2)
+    first, second = np.ascontiguousarray(toks[:, :T1]), np.ascontiguousarray(toks[:, T1:])
+    tr1 = trace_to_numpy(eng.trace_prefill(_i32(first)))
+    mid = [eng.get_state(b) for b in range(B)]
+    tr2 = trace_to_numpy(eng.trace_prefill(_i32(second)))
+    for b in range(B):
+        st, _ = _follow_prefill(om, s, first, tr1, b, T1, check_h_at={0, 1, 63, 64, 69})
+        assert_close(mid[b][1], st.ssm, what=f"ssm state seq {b} after {T1} tokens")
+        assert_close(mid[b][0], st.conv, what=f"conv state seq {b} after {T1} tokens")
+        st, ol = _follow_prefill(om, s, second, tr2, b, T2, check_h_at={0, 1, 63, 64, 99}, st=st)
+        assert_close(tr2["logits"][b], ol, what=f"last logits seq {b}")
+        conv_g, ssm_g = eng.get_state(b)
+        assert_close(ssm_g, st.ssm, what=f"ssm state seq {b} after {T1 + T2} tokens")
+        assert_close(conv_g, st.conv, what=f"conv state seq {b} after {T1 + T2} tokens")
+    eng.check()
     eng.close()
 
 
