@@ -777,29 +777,41 @@ hipError_t launch_gemm_skinny(const SkinnyArgs& a, int kind, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // causal conv over T (depthwise, width 4) + SiLU
 // ---------------------------------------------------------------------------
-constexpr int kConvChunk = 32;  // tokens per thread
+constexpr int kConvChunk = 16;  // tokens per thread
 
+// Thread = four consecutive channels (float4) and kConvChunk tokens: the
+// inputs of its tokens and the three before them are all loaded first (the
+// stored window stands in before t = 0), then the outputs are computed.
 __global__ __launch_bounds__(256) void conv_seq_kernel(ConvSeqArgs a) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = 4 * (blockIdx.x * 256 + threadIdx.x);
   const int b = blockIdx.z;
   if (c >= a.cdim) return;
   const int t0 = blockIdx.y * kConvChunk;
-  const int t1 = min(a.T, t0 + kConvChunk);
-  const float* st = a.state + (size_t)b * a.state_bstride;  // [3][cdim], oldest first
-  const float* xin = a.zx + a.x_off + c;
-  auto raw = [&](int t) -> float {
-    return t >= 0 ? xin[(size_t)((size_t)b * a.T + t) * a.ldzx] : st[(size_t)(t + 3) * a.cdim + c];
-  };
-  const float w0 = a.w[(size_t)c * 4 + 0], w1 = a.w[(size_t)c * 4 + 1], w2 = a.w[(size_t)c * 4 + 2],
-              w3 = a.w[(size_t)c * 4 + 3], bias = a.bias[c];
-  float x0 = raw(t0 - 3), x1 = raw(t0 - 2), x2 = raw(t0 - 1);
-  for (int t = t0; t < t1; ++t) {
-    const float x3 = raw(t);
-    const float v = conv4(bias, w0, x0, w1, x1, w2, x2, w3, x3);
-    a.xc[(size_t)((size_t)b * a.T + t) * a.cdim + c] = silu_f(v);
-    x0 = x1;
-    x1 = x2;
-    x2 = x3;
+  const int nt = min(a.T - t0, kConvChunk);
+  const float* st = a.state + (size_t)b * a.state_bstride + c;  // [3][cdim], oldest first
+  const float* xin = a.zx + (size_t)b * a.T * a.ldzx + a.x_off + c;
+  float4 x[kConvChunk + 3];
+#pragma unroll
+  for (int j = 0; j < kConvChunk + 3; ++j) {
+    const int t = min(t0 - 3 + j, a.T - 1);
+    const float* src = t >= 0 ? xin + (size_t)t * a.ldzx : st + (size_t)(t + 3) * a.cdim;
+    x[j] = *(const float4*)src;
+  }
+  float4 w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = *(const float4*)(a.w + (size_t)(c + k) * 4);
+  const float4 bias = *(const float4*)(a.bias + c);
+  float* out = a.xc + ((size_t)b * a.T + t0) * a.cdim + c;
+#pragma unroll
+  for (int j = 0; j < kConvChunk; ++j) {
+    if (j < nt) {
+      float4 o;
+      o.x = silu_f(conv4(bias.x, w[0].x, x[j].x, w[0].y, x[j + 1].x, w[0].z, x[j + 2].x, w[0].w, x[j + 3].x));
+      o.y = silu_f(conv4(bias.y, w[1].x, x[j].y, w[1].y, x[j + 1].y, w[1].z, x[j + 2].y, w[1].w, x[j + 3].y));
+      o.z = silu_f(conv4(bias.z, w[2].x, x[j].z, w[2].y, x[j + 1].z, w[2].z, x[j + 2].z, w[2].w, x[j + 3].z));
+      o.w = silu_f(conv4(bias.w, w[3].x, x[j].w, w[3].y, x[j + 1].w, w[3].z, x[j + 2].w, w[3].w, x[j + 3].w));
+      *(float4*)(out + (size_t)j * a.cdim) = o;
+    }
   }
 }
 
@@ -823,7 +835,8 @@ __global__ __launch_bounds__(256) void conv_state_update_kernel(ConvSeqArgs a) {
 
 hipError_t launch_conv_seq(const ConvSeqArgs& a, hipStream_t st) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
-  const dim3 g1((a.cdim + 255) / 256, (a.T + kConvChunk - 1) / kConvChunk, a.B);
+  if (a.cdim % 4 || a.x_off % 4 || a.ldzx % 4) return hipErrorInvalidValue;
+  const dim3 g1((a.cdim / 4 + 255) / 256, (a.T + kConvChunk - 1) / kConvChunk, a.B);
   hipLaunchKernelGGL(conv_seq_kernel, g1, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

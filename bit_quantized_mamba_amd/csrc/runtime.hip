@@ -120,6 +120,7 @@ dfssm_status validate(const dfssm_config* c) {
   if (c->d_inner % 128 || !pow2le64(c->d_inner / 128))
     return fail(DFSSM_E_UNSUPPORTED, "d_inner must be 128 * 2^k <= 8192");
   if (c->headdim % 16 || c->d_inner % c->headdim) return fail(DFSSM_E_UNSUPPORTED, "headdim must be a multiple of 16 dividing d_inner");
+  if ((c->d_inner / c->headdim) % 4) return fail(DFSSM_E_UNSUPPORTED, "the head count must be a multiple of 4");
   if (c->d_state % 2) return fail(DFSSM_E_UNSUPPORTED, "d_state must be even");
   if (c->d_conv != 4) return fail(DFSSM_E_UNSUPPORTED, "d_conv must be 4");
   if (c->lora_rank > 32) return fail(DFSSM_E_UNSUPPORTED, "lora_rank must be <= 32");

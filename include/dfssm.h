@@ -58,7 +58,8 @@ typedef enum {
 /* Model dimensions (ngroups = 1).  Derived: n_heads = d_inner / headdim,
  * conv_dim = d_inner + 2 d_state, d_in_proj = 2 d_inner + 2 d_state + n_heads.
  * Supported: d_model and d_inner multiples of 128 with d/128 a power of two
- * <= 64; headdim a multiple of 16; d_conv = 4; 1 <= lora_rank <= 32;
+ * <= 64; headdim a multiple of 16 and n_heads a multiple of 4; d_state
+ * even; d_conv = 4; 1 <= lora_rank <= 32;
  * 1 <= max_batch <= 1024.  norm_eps is the RMSNorm epsilon (1e-5 if 0).   */
 typedef struct {
   int32_t n_layer, d_model, d_inner, d_state, headdim, vocab, d_conv, lora_rank;
