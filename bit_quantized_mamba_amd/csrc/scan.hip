@@ -300,9 +300,19 @@ constexpr int kSsdOBt = kSsdOC + 64 * kSsdCRow;  // B^T   [128 n][kSsdRow]
 constexpr int kSsdOX = kSsdOBt + 128 * kSsdRow;  // X^T   [2 heads][64 p][kSsdRow]
 constexpr int kSsdOG = kSsdOX + 128 * kSsdRow;   // G     [64 i][kSsdRow]
 constexpr int kSsdOPar = kSsdOG + 64 * kSsdRow;  // per head: A_i, dt_j, w_j, exp(A_i)  [2][4][64]
-constexpr int kSsdFloats = kSsdOPar + 2 * 4 * 64;
+constexpr int kSsdOZ = kSsdOPar + 2 * 4 * 64;     // z of both heads [64 i][kSsdCRow]
+constexpr int kSsdFloats = kSsdOZ + 64 * kSsdCRow;
 constexpr size_t kSsdLds = sizeof(float) * kSsdFloats;
 static_assert(8 * 16 * 64 <= 64 * kSsdCRow, "the partial-sum exchange fits in the C buffer");
+
+// Workgroup barrier that orders LDS only: __syncthreads() would also wait for
+// every global load and store in flight (the next chunk's operands, the
+// outputs just written).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ v16f mfma_f32(float a, float b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -355,6 +365,42 @@ __global__ __launch_bounds__(256) void ssd_gram_kernel(ScanArgs a) {
   }
 }
 
+// One chunk's operands in registers: per thread four float4 of x (both
+// heads), B, C and z (rows j = idx / 32, float4 q = idx % 32 of idx = tid +
+// 512 k), two of G, and dt_raw of position `lane` for head 2 hp + wave
+// (waves 0 and 1).  Rows past the sequence end read the last valid row and
+// are zeroed (x, B, C; their G entries are zero already).
+struct SsdStage {
+  float4 x[4], b[4], c[4], z[4], g[2];
+  float dt;
+};
+
+__device__ __forceinline__ void ssd_stage_load(const ScanArgs& a, int hp, int tid, int lane, int wave, size_t row0,
+                                               int Lc, const float* gp, SsdStage& st) {
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = tid + 512 * k;
+    const int j = idx >> 5, q = idx & 31;
+    const bool ok = j < Lc;
+    const size_t r = row0 + min(j, Lc - 1);
+    const float* xr = a.xc + r * a.cdim;
+    const float4 xv = *(const float4*)(xr + (size_t)(2 * hp) * 64 + 4 * q);
+    const float4 bv = *(const float4*)(xr + a.d_inner + 4 * q);
+    const float4 cv = *(const float4*)(xr + a.d_inner + 128 + 4 * q);
+    st.z[k] = *(const float4*)(a.zx + r * a.ldzx + (size_t)(2 * hp) * 64 + 4 * q);
+    st.x[k] = ok ? xv : zero;
+    st.b[k] = ok ? bv : zero;
+    st.c[k] = ok ? cv : zero;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = tid + 512 * k;
+    st.g[k] = *(const float4*)(gp + (idx >> 4) * kSsdL + 4 * (idx & 15));
+  }
+  st.dt = a.zx[(row0 + min(lane, Lc - 1)) * a.ldzx + a.dt_off + 2 * hp + (wave & 1)];
+}
+
 // Workgroup (head pair, sequence) of 8 waves; wave w serves head 2 hp + (w >> 2),
 // channel block pb = (w >> 1) & 1 (channels 32 pb .. 32 pb + 31) and half
 // h2 = w & 1: it holds the state tiles S^T[n][p] of states 64 h2 .. 64 h2 + 63
@@ -391,68 +437,48 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[t][r] = sp[(32 * t + 8 * (r >> 2) + (r & 3)) * 16];
-  const float dtb = a.dt_bias[h], ea = __expf(a.A_log[h]), Dh = a.D[h];
+  const float Dh = a.D[h];
+  // dt bias and exp(A_log) of the head whose chunk parameters this wave computes (waves 0 and 1)
+  const float dtb_w = a.dt_bias[2 * hp + (wave & 1)], ea_w = __expf(a.A_log[2 * hp + (wave & 1)]);
   const int iy = 32 * h2 + col;  // this lane's output position
+
+  SsdStage st;
+  ssd_stage_load(a, hp, tid, lane, wave, rowb, min(kSsdL, a.T), a.gram + (size_t)b * nch * (kSsdL * kSsdL), st);
 
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * kSsdL, Lc = min(kSsdL, a.T - t0);
     const size_t row0 = rowb + t0;
-    __syncthreads();  // the previous chunk is done with LDS
-    // ---- stage the chunk: x of both heads (transposed), B (transposed), C, G
+    lds_barrier();  // the previous chunk is done with LDS
+    // ---- the chunk's operands into LDS: x of both heads (transposed), B (transposed), C, G, z
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int idx = tid + 512 * k;  // 2048 float4: 64 rows x 32
+      const int idx = tid + 512 * k;
       const int j = idx >> 5, q = idx & 31;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < Lc) v = *(const float4*)(a.xc + (row0 + j) * a.cdim + (size_t)(2 * hp) * P + 4 * q);
-      float* d = sm + kSsdOX + (4 * q) * kSsdRow + j;  // [hh][p][j] with hh * 64 + p = 4 q
-      d[0] = v.x;
-      d[kSsdRow] = v.y;
-      d[2 * kSsdRow] = v.z;
-      d[3 * kSsdRow] = v.w;
+      float* dx = sm + kSsdOX + (4 * q) * kSsdRow + j;  // [hh][p][j] with hh * 64 + p = 4 q
+      dx[0] = st.x[k].x;
+      dx[kSsdRow] = st.x[k].y;
+      dx[2 * kSsdRow] = st.x[k].z;
+      dx[3 * kSsdRow] = st.x[k].w;
+      float* db = sm + kSsdOBt + (4 * q) * kSsdRow + j;  // [n][j]
+      db[0] = st.b[k].x;
+      db[kSsdRow] = st.b[k].y;
+      db[2 * kSsdRow] = st.b[k].z;
+      db[3 * kSsdRow] = st.b[k].w;
+      *(float4*)(sm + kSsdOC + j * kSsdCRow + 4 * q) = st.c[k];
+      *(float4*)(sm + kSsdOZ + j * kSsdCRow + 4 * q) = st.z[k];
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int idx = tid + 512 * k;  // 4096 float4: 64 rows x (B 32, C 32)
-      const int j = idx >> 6, q = idx & 63;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < Lc) v = *(const float4*)(a.xc + (row0 + j) * a.cdim + a.d_inner + 4 * q);
-      if (q < 32) {
-        float* d = sm + kSsdOBt + (4 * q) * kSsdRow + j;
-        d[0] = v.x;
-        d[kSsdRow] = v.y;
-        d[2 * kSsdRow] = v.z;
-        d[3 * kSsdRow] = v.w;
-      } else {
-        *(float4*)(sm + kSsdOC + j * kSsdCRow + 4 * (q - 32)) = v;
-      }
+    for (int k = 0; k < 2; ++k) {
+      const int idx = tid + 512 * k;
+      *(float4*)(sm + kSsdOG + (idx >> 4) * kSsdRow + 4 * (idx & 15)) = st.g[k];
     }
-    {
-      const float* gp = a.gram + ((size_t)b * nch + c) * (kSsdL * kSsdL);
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int idx = tid + 512 * k;  // 1024 float4
-        const int i = idx >> 4, q = idx & 15;
-        *(float4*)(sm + kSsdOG + i * kSsdRow + 4 * q) = *(const float4*)(gp + i * kSsdL + 4 * q);
-      }
-    }
-    float dtraw = 0.0f;
-    if (wave < 2 && lane < Lc) dtraw = a.zx[(row0 + lane) * a.ldzx + a.dt_off + 2 * hp + wave];
-    // gate inputs of this lane's outputs, loaded now and used at the end
-    float4 zv[4];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      zv[r4] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (iy < Lc)
-        zv[r4] = *(const float4*)(a.zx + (row0 + iy) * a.ldzx + (size_t)h * P + 32 * pb + 8 * r4 + 4 * half);
-    }
-    __syncthreads();
+    const float dtr = st.dt;
+    lds_barrier();
     // ---- per-head chunk parameters (wave hh, lane = position j)
     if (wave < 2) {
       float* par = sm + kSsdOPar + wave * 256;
-      const int hw = 2 * hp + wave;
-      const float dt = lane < Lc ? softplus_f(dtraw + a.dt_bias[hw]) : 0.0f;
-      float cum = -dt * __expf(a.A_log[hw]);
+      const float dt = lane < Lc ? softplus_f(dtr + dtb_w) : 0.0f;
+      float cum = -dt * ea_w;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
         const float o = __shfl_up(cum, d);
@@ -464,7 +490,10 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
       par[128 + lane] = __expf(end - cum) * dt;
       par[192 + lane] = __expf(cum);
     }
-    __syncthreads();
+    lds_barrier();
+    if (c + 1 < nch)  // loaded while this chunk is computed
+      ssd_stage_load(a, hp, tid, lane, wave, row0 + kSsdL, min(kSsdL, a.T - t0 - kSsdL),
+                     a.gram + ((size_t)b * nch + c + 1) * (kSsdL * kSsdL), st);
 
     // ---- (a) Y_inter^T[p][i] partial over this wave's 64 states, both position blocks
     v16f Y0 = (v16f){}, Y1 = (v16f){};
@@ -485,71 +514,54 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
           Y1 = mfma_f32(S[t][4 * r4 + 2], c1.z * e1, Y1);
           Y0 = mfma_f32(S[t][4 * r4 + 3], c0.w * e0, Y0);
           Y1 = mfma_f32(S[t][4 * r4 + 3], c1.w * e1, Y1);
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-    __syncthreads();  // C is no longer read: its space takes the partial sums
+    lds_barrier();  // C is no longer read: its space takes the partial sums
     float* xch = sm + kSsdOC;
     {
       const v16f& give = h2 ? Y0 : Y1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) xch[(wave * 16 + r) * 64 + lane] = give[r];
     }
-    __syncthreads();
+    lds_barrier();
     v16f Yo = h2 ? Y1 : Y0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) Yo[r] += xch[((wave ^ 1) * 16 + r) * 64 + lane];
 
-    // ---- (b) + M X for positions 32 h2 .. 32 h2 + 31 (positions j <= i only)
-    float xs[32];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float4 v = *(const float4*)(sXh + p * kSsdRow + 8 * q + 4 * half);
-      xs[4 * q + 0] = v.x;
-      xs[4 * q + 1] = v.y;
-      xs[4 * q + 2] = v.z;
-      xs[4 * q + 3] = v.w;
-    }
+    // ---- (b) + M X for positions 32 h2 .. 32 h2 + 31 (positions j <= i only) and
+    // (c) S <- exp(A_{L-1}) S + X^T diag(w) B for this wave's state tiles, one
+    // group of four k-steps at a time (both take the same x operands)
     {
       const float cumi = sPar[iy];
-      const int nq = h2 ? 8 : 4;  // block 0 needs j < 32 only
+      const float dec = __expf(sPar[63]);
+      S[0] *= dec;
+      S[1] *= dec;
+      const float* bt0 = sm + kSsdOBt + (64 * h2 + col) * kSsdRow + 4 * half;
+      const float* bt1 = bt0 + 32 * kSsdRow;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        if (q < nq) {
-          const int j0 = 8 * q + 4 * half;
+        const int j0 = 8 * q + 4 * half;
+        const float4 xv = *(const float4*)(sXh + p * kSsdRow + j0);
+        const float xq[4] = {xv.x, xv.y, xv.z, xv.w};
+        if (q < 4 || h2) {  // positions < 32 need j < 32 only
           const float4 gv = *(const float4*)(sm + kSsdOG + iy * kSsdRow + j0);
           const float4 cj = *(const float4*)(sPar + j0);
           const float4 dj = *(const float4*)(sPar + 64 + j0);
-          const float m0 = j0 + 0 <= iy ? gv.x * __expf(cumi - cj.x) * dj.x : 0.0f;
-          const float m1 = j0 + 1 <= iy ? gv.y * __expf(cumi - cj.y) * dj.y : 0.0f;
-          const float m2 = j0 + 2 <= iy ? gv.z * __expf(cumi - cj.z) * dj.z : 0.0f;
-          const float m3 = j0 + 3 <= iy ? gv.w * __expf(cumi - cj.w) * dj.w : 0.0f;
-          Yo = mfma_f32(xs[4 * q + 0], m0, Yo);
-          Yo = mfma_f32(xs[4 * q + 1], m1, Yo);
-          Yo = mfma_f32(xs[4 * q + 2], m2, Yo);
-          Yo = mfma_f32(xs[4 * q + 3], m3, Yo);
-          __builtin_amdgcn_sched_barrier(0);
+          const float gq[4] = {gv.x, gv.y, gv.z, gv.w}, cq[4] = {cj.x, cj.y, cj.z, cj.w},
+                      dq[4] = {dj.x, dj.y, dj.z, dj.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            Yo = mfma_f32(xq[e], j0 + e <= iy ? gq[e] * __expf(cumi - cq[e]) * dq[e] : 0.0f, Yo);
         }
-      }
-    }
-
-    // ---- (c) S <- exp(A_{L-1}) S + X^T diag(w) B for this wave's state tiles
-    {
-      const float dec = __expf(sPar[63]);
+        const float4 wv = *(const float4*)(sPar + 128 + j0);
+        const float4 b0 = *(const float4*)(bt0 + 8 * q), b1 = *(const float4*)(bt1 + 8 * q);
+        const float wq[4] = {wv.x, wv.y, wv.z, wv.w}, bq0[4] = {b0.x, b0.y, b0.z, b0.w},
+                    bq1[4] = {b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        S[t] *= dec;
-        const float* bt = sm + kSsdOBt + (32 * (2 * h2 + t) + col) * kSsdRow + 4 * half;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 bv = *(const float4*)(bt + 8 * q);
-          const float4 wv = *(const float4*)(sPar + 128 + 8 * q + 4 * half);
-          S[t] = mfma_f32(bv.x * wv.x, xs[4 * q + 0], S[t]);
-          S[t] = mfma_f32(bv.y * wv.y, xs[4 * q + 1], S[t]);
-          S[t] = mfma_f32(bv.z * wv.z, xs[4 * q + 2], S[t]);
-          S[t] = mfma_f32(bv.w * wv.w, xs[4 * q + 3], S[t]);
-          __builtin_amdgcn_sched_barrier(0);
+        for (int e = 0; e < 4; ++e) {
+          S[0] = mfma_f32(bq0[e] * wq[e], xq[e], S[0]);
+          S[1] = mfma_f32(bq1[e] * wq[e], xq[e], S[1]);
         }
       }
     }
@@ -561,11 +573,12 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
       for (int r4 = 0; r4 < 4; ++r4) {
         const int p0 = 32 * pb + 8 * r4 + 4 * half;
         const float* xr = sXh + p0 * kSsdRow + iy;
+        const float4 zq = *(const float4*)(sm + kSsdOZ + iy * kSsdCRow + hh * 64 + p0);
         float4 o;
-        o.x = (Yo[4 * r4 + 0] + Dh * xr[0]) * silu_f(zv[r4].x);
-        o.y = (Yo[4 * r4 + 1] + Dh * xr[kSsdRow]) * silu_f(zv[r4].y);
-        o.z = (Yo[4 * r4 + 2] + Dh * xr[2 * kSsdRow]) * silu_f(zv[r4].z);
-        o.w = (Yo[4 * r4 + 3] + Dh * xr[3 * kSsdRow]) * silu_f(zv[r4].w);
+        o.x = (Yo[4 * r4 + 0] + Dh * xr[0]) * silu_f(zq.x);
+        o.y = (Yo[4 * r4 + 1] + Dh * xr[kSsdRow]) * silu_f(zq.y);
+        o.z = (Yo[4 * r4 + 2] + Dh * xr[2 * kSsdRow]) * silu_f(zq.z);
+        o.w = (Yo[4 * r4 + 3] + Dh * xr[3 * kSsdRow]) * silu_f(zq.w);
         *(float4*)(gr + p0) = o;
       }
     }
