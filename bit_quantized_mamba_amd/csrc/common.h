@@ -237,8 +237,16 @@ struct ScanArgs {
   size_t ssm_bstride;
   float* g;         // [B*T][d_inner]
   int B, T, H, d_inner, cdim;
-  float* gram;      // chunked scan workspace, B * ceil(T / 64) * 64 * 64 floats, or null
+  float* gram;      // chunked scan workspace: B * ceil(T / kSsdL) records of ssd_record_floats(H), or null
 };
+
+// The chunked scan (headdim 64, d_state 128) works on chunks of kSsdL tokens;
+// its workspace record per chunk is G [kSsdL][kSsdL], then per head the
+// chunk parameters A_j, dt_j, w_j, exp(A_j) [H][4][kSsdL].
+constexpr int kSsdL = 64;
+__host__ __device__ constexpr size_t ssd_record_floats(int H) {
+  return (size_t)kSsdL * kSsdL + (size_t)H * 4 * kSsdL;
+}
 
 hipError_t launch_rows_quant(const RowsArgs& a, int K, hipStream_t st);
 hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st);

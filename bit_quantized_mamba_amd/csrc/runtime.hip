@@ -317,7 +317,7 @@ dfssm_status ensure_gemm_ws(dfssm_ctx* c, size_t rows) {
   const size_t o_h = take(4 * rows * c->dm), o_s = take(4 * rows), o_t = take(4 * rows * 16),
                o_zx = take(4 * rows * c->dproj), o_xc = take(4 * rows * c->cdim), o_g = take(4 * rows * c->di),
                o_q = take(rows * mx), o_qs = take(4 * rows),
-               o_gram = take(4 * (rows / 64 + (size_t)c->maxB) * 64 * 64);
+               o_gram = take(4 * (rows / kSsdL + (size_t)c->maxB) * ssd_record_floats(c->H));
   char* buf = nullptr;
   if (hipMalloc(&buf, off) != hipSuccess) {
     (void)hipGetLastError();

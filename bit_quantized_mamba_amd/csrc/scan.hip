@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void scan1_kernel(ScanArgs a) {
 // ssd_gram_kernel writes G for every chunk; ssd_scan_kernel walks the chunks
 // of one sequence in order for two heads, with the state in registers.
 // ---------------------------------------------------------------------------
-constexpr int kSsdL = 64;                      // tokens per chunk
+static_assert(kSsdL == 64, "the chunked scan is written for chunks of 64 tokens");
 constexpr int kSsdRow = kSsdL + 4;             // LDS row of 64 floats (+4 against bank conflicts)
 constexpr int kSsdCRow = 128 + 4;              // LDS row of C (128 floats)
 constexpr int kSsdOC = 0;                      // C       [64 i][kSsdCRow]
@@ -319,9 +319,9 @@ __device__ __forceinline__ v16f mfma_f32(float a, float b, v16f c) {
 }
 
 // G[b][c][i][j] = C_{t0+i} . B_{t0+j} for chunk c of sequence b (rows past the
-// end of the sequence count as zero).  Workgroup (chunk, sequence), wave w
-// computes the 32 x 32 tile (w >> 1, w & 1); the tile above the diagonal is
-// never read and not written.
+// end of the sequence count as zero), and the chunk parameters of every head.
+// Workgroup (chunk, sequence), wave w computes the 32 x 32 tile (w >> 1,
+// w & 1) of G; the tile above the diagonal is never read and not written.
 __global__ __launch_bounds__(256) void ssd_gram_kernel(ScanArgs a) {
   constexpr int N = 128;
   __shared__ __attribute__((aligned(16))) float sC[64 * kSsdRow], sB[64 * kSsdRow];
@@ -356,49 +356,64 @@ __global__ __launch_bounds__(256) void ssd_gram_kernel(ScanArgs a) {
       }
     }
   }
-  if (wave == 1) return;
-  float* gp = a.gram + ((size_t)b * gridDim.x + c) * (kSsdL * kSsdL);
+  float* rec = a.gram + ((size_t)b * gridDim.x + c) * ssd_record_floats(a.H);
+  if (wave != 1) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = 32 * ti + 8 * (r >> 2) + 4 * half + (r & 3);
-    gp[i * kSsdL + 32 * tj + col] = acc[r];
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * ti + 8 * (r >> 2) + 4 * half + (r & 3);
+      rec[i * kSsdL + 32 * tj + col] = acc[r];
+    }
+  }
+  // chunk parameters of every head (wave w: heads w, w + 4, ...; lane = position j):
+  // A_j (running sum of -dt exp(A_log)), dt_j, w_j = exp(A_{L-1} - A_j) dt_j, exp(A_j)
+  float* par = rec + kSsdL * kSsdL;
+  const size_t rj = row0 + min(lane, Lc - 1);
+  for (int h = wave; h < a.H; h += 4) {
+    const float dt = lane < Lc ? softplus_f(a.zx[rj * a.ldzx + a.dt_off + h] + a.dt_bias[h]) : 0.0f;
+    float cum = -dt * __expf(a.A_log[h]);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float o = __shfl_up(cum, d);
+      if (lane >= d) cum += o;
+    }
+    const float end = __shfl(cum, 63);
+    float* ph = par + h * 256;
+    ph[lane] = cum;
+    ph[64 + lane] = dt;
+    ph[128 + lane] = __expf(end - cum) * dt;
+    ph[192 + lane] = __expf(cum);
   }
 }
 
 // One chunk's operands in registers: per thread four float4 of x (both
 // heads), B, C and z (rows j = idx / 32, float4 q = idx % 32 of idx = tid +
-// 512 k), two of G, and dt_raw of position `lane` for head 2 hp + wave
-// (waves 0 and 1).  Rows past the sequence end read the last valid row and
-// are zeroed (x, B, C; their G entries are zero already).
+// 512 k), two of G and (threads < 128) one of the two heads' parameters.
+// Rows past the sequence end read the last valid row; x, B and C of those
+// rows are zeroed when they are written to LDS (their G entries and dt are
+// zero already).
 struct SsdStage {
-  float4 x[4], b[4], c[4], z[4], g[2];
-  float dt;
+  float4 x[4], b[4], c[4], z[4], g[2], par;
 };
 
-__device__ __forceinline__ void ssd_stage_load(const ScanArgs& a, int hp, int tid, int lane, int wave, size_t row0,
-                                               int Lc, const float* gp, SsdStage& st) {
-  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+__device__ __forceinline__ void ssd_stage_load(const ScanArgs& a, int hp, int tid, size_t row0, int Lc,
+                                               const float* rec, SsdStage& st) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int idx = tid + 512 * k;
     const int j = idx >> 5, q = idx & 31;
-    const bool ok = j < Lc;
     const size_t r = row0 + min(j, Lc - 1);
     const float* xr = a.xc + r * a.cdim;
-    const float4 xv = *(const float4*)(xr + (size_t)(2 * hp) * 64 + 4 * q);
-    const float4 bv = *(const float4*)(xr + a.d_inner + 4 * q);
-    const float4 cv = *(const float4*)(xr + a.d_inner + 128 + 4 * q);
+    st.x[k] = *(const float4*)(xr + (size_t)(2 * hp) * 64 + 4 * q);
+    st.b[k] = *(const float4*)(xr + a.d_inner + 4 * q);
+    st.c[k] = *(const float4*)(xr + a.d_inner + 128 + 4 * q);
     st.z[k] = *(const float4*)(a.zx + r * a.ldzx + (size_t)(2 * hp) * 64 + 4 * q);
-    st.x[k] = ok ? xv : zero;
-    st.b[k] = ok ? bv : zero;
-    st.c[k] = ok ? cv : zero;
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int idx = tid + 512 * k;
-    st.g[k] = *(const float4*)(gp + (idx >> 4) * kSsdL + 4 * (idx & 15));
+    st.g[k] = *(const float4*)(rec + (idx >> 4) * kSsdL + 4 * (idx & 15));
   }
-  st.dt = a.zx[(row0 + min(lane, Lc - 1)) * a.ldzx + a.dt_off + 2 * hp + (wave & 1)];
+  st.par = *(const float4*)(rec + kSsdL * kSsdL + (size_t)(2 * hp) * 256 + 4 * (tid & 127));
 }
 
 // Workgroup (head pair, sequence) of 8 waves; wave w serves head 2 hp + (w >> 2),
@@ -438,62 +453,57 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[t][r] = sp[(32 * t + 8 * (r >> 2) + (r & 3)) * 16];
   const float Dh = a.D[h];
-  // dt bias and exp(A_log) of the head whose chunk parameters this wave computes (waves 0 and 1)
-  const float dtb_w = a.dt_bias[2 * hp + (wave & 1)], ea_w = __expf(a.A_log[2 * hp + (wave & 1)]);
   const int iy = 32 * h2 + col;  // this lane's output position
+  const size_t recf = ssd_record_floats(a.H);
 
   SsdStage st;
-  ssd_stage_load(a, hp, tid, lane, wave, rowb, min(kSsdL, a.T), a.gram + (size_t)b * nch * (kSsdL * kSsdL), st);
+  ssd_stage_load(a, hp, tid, rowb, min(kSsdL, a.T), a.gram + (size_t)b * nch * recf, st);
+  // gated outputs of the previous chunk, stored once the next chunk's loads
+  // have been waited for (a store issued after those loads would hold them up)
+  float4 go[4];
+  float* gprev = nullptr;
 
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * kSsdL, Lc = min(kSsdL, a.T - t0);
     const size_t row0 = rowb + t0;
     lds_barrier();  // the previous chunk is done with LDS
-    // ---- the chunk's operands into LDS: x of both heads (transposed), B (transposed), C, G, z
+    // ---- the chunk's operands into LDS: x of both heads (transposed), B (transposed), C, G, z, parameters
+    {
+      const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int idx = tid + 512 * k;
-      const int j = idx >> 5, q = idx & 31;
-      float* dx = sm + kSsdOX + (4 * q) * kSsdRow + j;  // [hh][p][j] with hh * 64 + p = 4 q
-      dx[0] = st.x[k].x;
-      dx[kSsdRow] = st.x[k].y;
-      dx[2 * kSsdRow] = st.x[k].z;
-      dx[3 * kSsdRow] = st.x[k].w;
-      float* db = sm + kSsdOBt + (4 * q) * kSsdRow + j;  // [n][j]
-      db[0] = st.b[k].x;
-      db[kSsdRow] = st.b[k].y;
-      db[2 * kSsdRow] = st.b[k].z;
-      db[3 * kSsdRow] = st.b[k].w;
-      *(float4*)(sm + kSsdOC + j * kSsdCRow + 4 * q) = st.c[k];
-      *(float4*)(sm + kSsdOZ + j * kSsdCRow + 4 * q) = st.z[k];
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int idx = tid + 512 * k;
-      *(float4*)(sm + kSsdOG + (idx >> 4) * kSsdRow + 4 * (idx & 15)) = st.g[k];
-    }
-    const float dtr = st.dt;
-    lds_barrier();
-    // ---- per-head chunk parameters (wave hh, lane = position j)
-    if (wave < 2) {
-      float* par = sm + kSsdOPar + wave * 256;
-      const float dt = lane < Lc ? softplus_f(dtr + dtb_w) : 0.0f;
-      float cum = -dt * ea_w;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float o = __shfl_up(cum, d);
-        if (lane >= d) cum += o;
+      for (int k = 0; k < 4; ++k) {
+        const int idx = tid + 512 * k;
+        const int j = idx >> 5, q = idx & 31;
+        const bool ok = j < Lc;
+        const float4 xv = ok ? st.x[k] : zero, bv = ok ? st.b[k] : zero, cv = ok ? st.c[k] : zero;
+        float* dx = sm + kSsdOX + (4 * q) * kSsdRow + j;  // [hh][p][j] with hh * 64 + p = 4 q
+        dx[0] = xv.x;
+        dx[kSsdRow] = xv.y;
+        dx[2 * kSsdRow] = xv.z;
+        dx[3 * kSsdRow] = xv.w;
+        float* db = sm + kSsdOBt + (4 * q) * kSsdRow + j;  // [n][j]
+        db[0] = bv.x;
+        db[kSsdRow] = bv.y;
+        db[2 * kSsdRow] = bv.z;
+        db[3 * kSsdRow] = bv.w;
+        *(float4*)(sm + kSsdOC + j * kSsdCRow + 4 * q) = cv;
+        *(float4*)(sm + kSsdOZ + j * kSsdCRow + 4 * q) = st.z[k];
       }
-      const float end = __shfl(cum, 63);
-      par[lane] = cum;
-      par[64 + lane] = dt;
-      par[128 + lane] = __expf(end - cum) * dt;
-      par[192 + lane] = __expf(cum);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int idx = tid + 512 * k;
+        *(float4*)(sm + kSsdOG + (idx >> 4) * kSsdRow + 4 * (idx & 15)) = st.g[k];
+      }
+      if (tid < 128) *(float4*)(sm + kSsdOPar + 4 * tid) = st.par;
+    }
+    if (gprev) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) *(float4*)(gprev + 32 * pb + 8 * r4 + 4 * half) = go[r4];
     }
     lds_barrier();
     if (c + 1 < nch)  // loaded while this chunk is computed
-      ssd_stage_load(a, hp, tid, lane, wave, row0 + kSsdL, min(kSsdL, a.T - t0 - kSsdL),
-                     a.gram + ((size_t)b * nch + c + 1) * (kSsdL * kSsdL), st);
+      ssd_stage_load(a, hp, tid, row0 + kSsdL, min(kSsdL, a.T - t0 - kSsdL), a.gram + ((size_t)b * nch + c + 1) * recf,
+                     st);
 
     // ---- (a) Y_inter^T[p][i] partial over this wave's 64 states, both position blocks
     v16f Y0 = (v16f){}, Y1 = (v16f){};
@@ -567,21 +577,21 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
     }
 
     // ---- gated output of position iy: lane register r is channel 32 pb + 8 (r / 4) + 4 half + r % 4
-    if (iy < Lc) {
-      float* gr = a.g + (row0 + iy) * a.d_inner + (size_t)h * P;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int p0 = 32 * pb + 8 * r4 + 4 * half;
-        const float* xr = sXh + p0 * kSsdRow + iy;
-        const float4 zq = *(const float4*)(sm + kSsdOZ + iy * kSsdCRow + hh * 64 + p0);
-        float4 o;
-        o.x = (Yo[4 * r4 + 0] + Dh * xr[0]) * silu_f(zq.x);
-        o.y = (Yo[4 * r4 + 1] + Dh * xr[kSsdRow]) * silu_f(zq.y);
-        o.z = (Yo[4 * r4 + 2] + Dh * xr[2 * kSsdRow]) * silu_f(zq.z);
-        o.w = (Yo[4 * r4 + 3] + Dh * xr[3 * kSsdRow]) * silu_f(zq.w);
-        *(float4*)(gr + p0) = o;
-      }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int p0 = 32 * pb + 8 * r4 + 4 * half;
+      const float* xr = sXh + p0 * kSsdRow + iy;
+      const float4 zq = *(const float4*)(sm + kSsdOZ + iy * kSsdCRow + hh * 64 + p0);
+      go[r4].x = (Yo[4 * r4 + 0] + Dh * xr[0]) * silu_f(zq.x);
+      go[r4].y = (Yo[4 * r4 + 1] + Dh * xr[kSsdRow]) * silu_f(zq.y);
+      go[r4].z = (Yo[4 * r4 + 2] + Dh * xr[2 * kSsdRow]) * silu_f(zq.z);
+      go[r4].w = (Yo[4 * r4 + 3] + Dh * xr[3 * kSsdRow]) * silu_f(zq.w);
     }
+    gprev = iy < Lc ? a.g + (row0 + iy) * a.d_inner + (size_t)h * P : nullptr;
+  }
+  if (gprev) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) *(float4*)(gprev + 32 * pb + 8 * r4 + 4 * half) = go[r4];
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t)
