@@ -294,11 +294,11 @@ __global__ __launch_bounds__(256) void scan1_kernel(ScanArgs a) {
 // ---------------------------------------------------------------------------
 static_assert(kSsdL == 64, "the chunked scan is written for chunks of 64 tokens");
 constexpr int kSsdRow = kSsdL + 4;             // LDS row of 64 floats (+4 against bank conflicts)
-constexpr int kSsdCRow = 128 + 4;              // LDS row of C (128 floats)
+constexpr int kSsdCRow = 128 + 8;              // LDS row of 128 floats (+8: rows 4 apart fall on other banks)
 constexpr int kSsdOC = 0;                      // C       [64 i][kSsdCRow]
-constexpr int kSsdOBt = kSsdOC + 64 * kSsdCRow;  // B^T   [128 n][kSsdRow]
-constexpr int kSsdOX = kSsdOBt + 128 * kSsdRow;  // X^T   [2 heads][64 p][kSsdRow]
-constexpr int kSsdOG = kSsdOX + 128 * kSsdRow;   // G     [64 i][kSsdRow]
+constexpr int kSsdOB = kSsdOC + 64 * kSsdCRow;   // B     [64 j][kSsdCRow]
+constexpr int kSsdOX = kSsdOB + 64 * kSsdCRow;   // x of both heads [64 j][kSsdCRow]
+constexpr int kSsdOG = kSsdOX + 64 * kSsdCRow;   // G     [64 i][kSsdRow]
 constexpr int kSsdOPar = kSsdOG + 64 * kSsdRow;  // per head: A_i, dt_j, w_j, exp(A_i)  [2][4][64]
 constexpr int kSsdOZ = kSsdOPar + 2 * 4 * 64;     // z of both heads [64 i][kSsdCRow]
 constexpr int kSsdFloats = kSsdOZ + 64 * kSsdCRow;
@@ -426,10 +426,10 @@ __device__ __forceinline__ void ssd_stage_load(const ScanArgs& a, int hp, int ti
 //      partial of the other block handed to the partner wave through LDS;
 //  (b) + M X for its positions;
 //  (c) S <- exp(A_{L-1}) S + X^T diag(w) B for its state tiles.
-// The k index of every product runs over 4-element runs so that each operand
-// comes from LDS as one 16-byte read per four steps: k-step s of half hf is
-// element 8 (s / 4) + 4 hf + s % 4, the order in which the accumulator
-// registers hold the states.
+// The k index of every product runs over 4-element runs: k-step s of half hf
+// is element 8 (s / 4) + 4 hf + s % 4, the order in which the accumulator
+// registers hold the states, so that C and G come from LDS as one 16-byte
+// read per four steps (x and B, stored as rows, are read along them).
 __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
   constexpr int P = 64, N = 128;
   extern __shared__ __attribute__((aligned(16))) float sm[];
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
   const int nch = (a.T + kSsdL - 1) / kSsdL;
   const size_t rowb = (size_t)b * a.T;
   float* sPar = sm + kSsdOPar + hh * 256;  // [0] A_i  [64] dt_j  [128] w_j  [192] exp(A_i)
-  const float* sXh = sm + kSsdOX + hh * 64 * kSsdRow;
+  const float* sXh = sm + kSsdOX + hh * 64;  // x of this head: [j][kSsdCRow]
 
   float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;  // [P/16][N][16]
   // state element (p, n) of tile t, register r: n = 64 h2 + 32 t + 8 (r / 4) + 4 half + r % 4;
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
     const int t0 = c * kSsdL, Lc = min(kSsdL, a.T - t0);
     const size_t row0 = rowb + t0;
     lds_barrier();  // the previous chunk is done with LDS
-    // ---- the chunk's operands into LDS: x of both heads (transposed), B (transposed), C, G, z, parameters
+    // ---- the chunk's operands into LDS: x of both heads, B, C, G, z, parameters
     {
       const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -476,16 +476,8 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
         const int j = idx >> 5, q = idx & 31;
         const bool ok = j < Lc;
         const float4 xv = ok ? st.x[k] : zero, bv = ok ? st.b[k] : zero, cv = ok ? st.c[k] : zero;
-        float* dx = sm + kSsdOX + (4 * q) * kSsdRow + j;  // [hh][p][j] with hh * 64 + p = 4 q
-        dx[0] = xv.x;
-        dx[kSsdRow] = xv.y;
-        dx[2 * kSsdRow] = xv.z;
-        dx[3 * kSsdRow] = xv.w;
-        float* db = sm + kSsdOBt + (4 * q) * kSsdRow + j;  // [n][j]
-        db[0] = bv.x;
-        db[kSsdRow] = bv.y;
-        db[2 * kSsdRow] = bv.z;
-        db[3 * kSsdRow] = bv.w;
+        *(float4*)(sm + kSsdOX + j * kSsdCRow + 4 * q) = xv;
+        *(float4*)(sm + kSsdOB + j * kSsdCRow + 4 * q) = bv;
         *(float4*)(sm + kSsdOC + j * kSsdCRow + 4 * q) = cv;
         *(float4*)(sm + kSsdOZ + j * kSsdCRow + 4 * q) = st.z[k];
       }
@@ -502,8 +494,8 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
     }
     lds_barrier();
     if (c + 1 < nch)  // loaded while this chunk is computed
-      ssd_stage_load(a, hp, tid, row0 + kSsdL, min(kSsdL, a.T - t0 - kSsdL), a.gram + ((size_t)b * nch + c + 1) * recf,
-                     st);
+      ssd_stage_load(a, hp, tid, row0 + kSsdL, min(kSsdL, a.T - t0 - kSsdL),
+                     a.gram + ((size_t)b * nch + c + 1) * recf, st);
 
     // ---- (a) Y_inter^T[p][i] partial over this wave's 64 states, both position blocks
     v16f Y0 = (v16f){}, Y1 = (v16f){};
@@ -547,13 +539,13 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
       const float dec = __expf(sPar[63]);
       S[0] *= dec;
       S[1] *= dec;
-      const float* bt0 = sm + kSsdOBt + (64 * h2 + col) * kSsdRow + 4 * half;
-      const float* bt1 = bt0 + 32 * kSsdRow;
+      const float* bt0 = sm + kSsdOB + 64 * h2 + col;  // B[j][n] of this lane's states n = 64 h2 + col (+ 32)
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int j0 = 8 * q + 4 * half;
-        const float4 xv = *(const float4*)(sXh + p * kSsdRow + j0);
-        const float xq[4] = {xv.x, xv.y, xv.z, xv.w};
+        float xq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xq[e] = sXh[(j0 + e) * kSsdCRow + p];
         if (q < 4 || h2) {  // positions < 32 need j < 32 only
           const float4 gv = *(const float4*)(sm + kSsdOG + iy * kSsdRow + j0);
           const float4 cj = *(const float4*)(sPar + j0);
@@ -565,13 +557,12 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
             Yo = mfma_f32(xq[e], j0 + e <= iy ? gq[e] * __expf(cumi - cq[e]) * dq[e] : 0.0f, Yo);
         }
         const float4 wv = *(const float4*)(sPar + 128 + j0);
-        const float4 b0 = *(const float4*)(bt0 + 8 * q), b1 = *(const float4*)(bt1 + 8 * q);
-        const float wq[4] = {wv.x, wv.y, wv.z, wv.w}, bq0[4] = {b0.x, b0.y, b0.z, b0.w},
-                    bq1[4] = {b1.x, b1.y, b1.z, b1.w};
+        const float wq[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          S[0] = mfma_f32(bq0[e] * wq[e], xq[e], S[0]);
-          S[1] = mfma_f32(bq1[e] * wq[e], xq[e], S[1]);
+          const float b0 = bt0[(j0 + e) * kSsdCRow], b1 = bt0[(j0 + e) * kSsdCRow + 32];
+          S[0] = mfma_f32(b0 * wq[e], xq[e], S[0]);
+          S[1] = mfma_f32(b1 * wq[e], xq[e], S[1]);
         }
       }
     }
@@ -580,12 +571,12 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int p0 = 32 * pb + 8 * r4 + 4 * half;
-      const float* xr = sXh + p0 * kSsdRow + iy;
+      const float4 xq = *(const float4*)(sXh + iy * kSsdCRow + p0);
       const float4 zq = *(const float4*)(sm + kSsdOZ + iy * kSsdCRow + hh * 64 + p0);
-      go[r4].x = (Yo[4 * r4 + 0] + Dh * xr[0]) * silu_f(zq.x);
-      go[r4].y = (Yo[4 * r4 + 1] + Dh * xr[kSsdRow]) * silu_f(zq.y);
-      go[r4].z = (Yo[4 * r4 + 2] + Dh * xr[2 * kSsdRow]) * silu_f(zq.z);
-      go[r4].w = (Yo[4 * r4 + 3] + Dh * xr[3 * kSsdRow]) * silu_f(zq.w);
+      go[r4].x = (Yo[4 * r4 + 0] + Dh * xq.x) * silu_f(zq.x);
+      go[r4].y = (Yo[4 * r4 + 1] + Dh * xq.y) * silu_f(zq.y);
+      go[r4].z = (Yo[4 * r4 + 2] + Dh * xq.z) * silu_f(zq.z);
+      go[r4].w = (Yo[4 * r4 + 3] + Dh * xq.w) * silu_f(zq.w);
     }
     gprev = iy < Lc ? a.g + (row0 + iy) * a.d_inner + (size_t)h * P : nullptr;
   }
