@@ -11,10 +11,6 @@ namespace dfssm {
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ float silu_f(float v) { return __fdividef(v, 1.0f + __expf(-v)); }
-// the same through the hardware reciprocal (about 1 ulp; the division above
-// expands to a ten-instruction IEEE sequence on this target).  Used where it
-// measured faster: in the persistent decode kernel it measured slower.
-__device__ __forceinline__ float silu_rcp(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // log(1 + x) for x >= 0 from the natural log of u = fl(1 + x): log(u) * x / (u - 1)
 // corrects the rounding of 1 + x (D. Goldberg, "What every computer scientist

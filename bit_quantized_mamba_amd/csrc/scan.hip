@@ -1,9 +1,8 @@
 // SSM scans of the batched path over T tokens per sequence, gfx950.
 //
-//  * scan_kernel / scan64x128_kernel: the recurrence token by token, one
-//    workgroup per (sequence, head), state in registers (for headdim 64,
-//    d_state 128 carried divided by its running decay, so an element costs
-//    one FMA per token), B and C staged through LDS; gated output.
+//  * scan_kernel: the recurrence token by token, one workgroup per
+//    (sequence, head), state in registers, B and C staged through LDS; gated
+//    output.
 //  * scan1_kernel: one decode token per sequence (headdim 64, d_state 128).
 //  * ssd_gram_kernel / ssd_scan_kernel: the same recurrence for headdim 64,
 //    d_state 128 unrolled over chunks of 64 tokens into matrix products on
@@ -84,136 +83,6 @@ __global__ __launch_bounds__(4 * P) void scan_kernel(ScanArgs a) {
     const int n = seg * NPT + j;
     stb[((size_t)(p >> 4) * N + n) * 16 + (p & 15)] = S[j];
   }
-}
-
-// The scan over T tokens for headdim 64, d_state 128.  Workgroup (head,
-// sequence) of 256 threads; thread t owns channels 4c .. 4c+3 (c = t >> 4)
-// and states 8s .. 8s+7 (s = t & 15) as float4 over the channels, i.e. one
-// float4 of the [P/16][N][16] state block per state.  A token then costs a
-// thread two float4 of B, two of C and one of x from LDS for 64 FMAs (the
-// one-channel-per-thread layout reads 64 floats of B and C per token), and the
-// sum over states is one 16-lane DPP reduction per channel.  dt and the decay
-// of each staged token are computed once, by the first kScan2Chunk threads.
-constexpr int kScan2Chunk = 32;
-// Rescaled recurrence: with P_t the product of the decays since the last
-// rescale point, S_t = P_t * R_t where R_t = R_{t-1} + (dt_t x_t / P_t) B_t,
-// and y_t = P_t * (C_t . R_t).  A state element then costs one FMA for the
-// update and one for the output (the direct form needs a multiply more).  The
-// state is brought back to S at every chunk boundary, and a token at which P
-// would fall below kScanPMin becomes a rescale point: R is multiplied by the
-// decay up to and including that token (R * P_{t-1} * dA_t = dA_t S_{t-1}),
-// and P restarts at 1.
-constexpr float kScanPMin = 0x1p-40f;
-__global__ __launch_bounds__(256) void scan64x128_kernel(ScanArgs a) {
-  constexpr int P = 64, N = 128, Q = kScan2Chunk;
-  __shared__ float4 sB[Q][N / 4], sC[Q][N / 4], sx[Q][P / 4], sz[Q][P / 4];
-  __shared__ float sdt[Q], sdA[Q], sP[Q], sW[Q], sRen[Q];
-  __shared__ int smode[Q];  // 1: rescale point (R *= sRen[t] before the update)
-  __shared__ float sPend;
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int c = tid >> 4, s = tid & 15;
-  const int pb = c >> 2, pq = c & 3;
-  float* stb = a.ssm + (size_t)b * a.ssm_bstride + (size_t)h * P * N;  // [P/16][N][16]
-  float4 S[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) S[k] = *(const float4*)(stb + ((size_t)(pb * N + 8 * s + k) * 16 + pq * 4));
-  const float dtb = a.dt_bias[h], ea = __expf(a.A_log[h]), Dh = a.D[h];
-  const size_t row0 = (size_t)b * a.T;
-  for (int t0 = 0; t0 < a.T; t0 += Q) {
-    const int tc = min(Q, a.T - t0);
-    __syncthreads();  // the previous chunk is consumed
-    for (int i = tid; i < tc * (N / 4); i += 256) {
-      const int tt = i / (N / 4), q = i % (N / 4);
-      const float4* xr = (const float4*)(a.xc + (row0 + t0 + tt) * a.cdim + a.d_inner);
-      sB[tt][q] = xr[q];
-      sC[tt][q] = xr[N / 4 + q];
-    }
-    for (int i = tid; i < tc * (P / 4); i += 256) {
-      const int tt = i / (P / 4), q = i % (P / 4);
-      sx[tt][q] = ((const float4*)(a.xc + (row0 + t0 + tt) * a.cdim + (size_t)h * P))[q];
-      sz[tt][q] = ((const float4*)(a.zx + (row0 + t0 + tt) * a.ldzx + (size_t)h * P))[q];
-    }
-    if (tid < tc) {
-      const float dt = softplus_f(a.zx[(row0 + t0 + tid) * a.ldzx + a.dt_off + h] + dtb);
-      sdt[tid] = dt;
-      sdA[tid] = __expf(-dt * ea);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      // the rescale schedule of the chunk (R = S at its start)
-      float pr = 1.0f;
-      for (int tt = 0; tt < tc; ++tt) {
-        const float np = pr * sdA[tt];
-        const bool re = np < kScanPMin;
-        smode[tt] = re;
-        sRen[tt] = np;
-        pr = re ? 1.0f : np;
-        sP[tt] = pr;
-        sW[tt] = sdt[tt] / pr;
-      }
-      sPend = pr;
-    }
-    __syncthreads();
-    for (int tt = 0; tt < tc; ++tt) {
-      const int mode = __builtin_amdgcn_readfirstlane(smode[tt]);
-      const float4 xv = sx[tt][c];
-      const float4 b0 = sB[tt][2 * s], b1 = sB[tt][2 * s + 1];
-      const float4 c0 = sC[tt][2 * s], c1 = sC[tt][2 * s + 1];
-      const float bn[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      const float cn[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      if (mode != 0) {
-        const float r = sRen[tt];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          S[k].x *= r;
-          S[k].y *= r;
-          S[k].z *= r;
-          S[k].w *= r;
-        }
-      }
-      const float wdt = sW[tt];
-      const float w0 = wdt * xv.x, w1 = wdt * xv.y, w2 = wdt * xv.z, w3 = wdt * xv.w;
-      float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        float4 v = S[k];
-        v.x += w0 * bn[k];
-        v.y += w1 * bn[k];
-        v.z += w2 * bn[k];
-        v.w += w3 * bn[k];
-        S[k] = v;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        y0 += S[k].x * cn[k];
-        y1 += S[k].y * cn[k];
-        y2 += S[k].z * cn[k];
-        y3 += S[k].w * cn[k];
-      }
-      y0 = row_sum16(y0);
-      y1 = row_sum16(y1);
-      y2 = row_sum16(y2);
-      y3 = row_sum16(y3);
-      // the row sums sit in all 16 lanes of the row: lanes s = 0..3 gate one channel each
-      if (s < 4) {
-        const float yv = s == 0 ? y0 : s == 1 ? y1 : s == 2 ? y2 : y3;
-        const float xs = s == 0 ? xv.x : s == 1 ? xv.y : s == 2 ? xv.z : xv.w;
-        const float zs = ((const float*)sz[tt])[4 * c + s];
-        a.g[(row0 + t0 + tt) * a.d_inner + (size_t)h * P + 4 * c + s] = (sP[tt] * yv + Dh * xs) * silu_rcp(zs);
-      }
-    }
-    // back to S at the chunk boundary
-    const float pe = sPend;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      S[k].x *= pe;
-      S[k].y *= pe;
-      S[k].z *= pe;
-      S[k].w *= pe;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) *(float4*)(stb + ((size_t)(pb * N + 8 * s + k) * 16 + pq * 4)) = S[k];
 }
 
 // One decode token per sequence (T = 1), headdim 64, d_state 128.  Workgroup
@@ -597,7 +466,8 @@ hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
     hipLaunchKernelGGL(scan1_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  if (P == 64 && N == 128 && a.gram && a.H % 2 == 0) {
+  if (P == 64 && N == 128) {
+    if (!a.gram || a.H % 2) return hipErrorInvalidValue;
     static bool lds_set = false;
     if (!lds_set) {
       const hipError_t e = hipFuncSetAttribute((const void*)ssd_scan_kernel,
@@ -610,8 +480,7 @@ hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
     hipLaunchKernelGGL(ssd_scan_kernel, dim3(a.H / 2, a.B), dim3(512), kSsdLds, st, a);
     return hipGetLastError();
   }
-  if (P == 64 && N == 128) hipLaunchKernelGGL(scan64x128_kernel, grid, dim3(256), 0, st, a);
-  else if (P == 32 && N == 16) hipLaunchKernelGGL((scan_kernel<32, 16>), grid, dim3(128), 0, st, a);
+  if (P == 32 && N == 16) hipLaunchKernelGGL((scan_kernel<32, 16>), grid, dim3(128), 0, st, a);
   else if (P == 64 && N == 64) hipLaunchKernelGGL((scan_kernel<64, 64>), grid, dim3(256), 0, st, a);
   else if (P == 32 && N == 128) hipLaunchKernelGGL((scan_kernel<32, 128>), grid, dim3(128), 0, st, a);
   else if (P == 64 && N == 16) hipLaunchKernelGGL((scan_kernel<64, 16>), grid, dim3(256), 0, st, a);
