@@ -482,7 +482,7 @@ __device__ __forceinline__ v4i expand16(uint32_t b) {
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void bitgemm2_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, 2) void bitgemm2_kernel(GemmArgs a) {
   constexpr int TM = kG2TM, TN = kG2TN, KB = kG2KB, BM = 4, BN = 2;
   extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
