@@ -242,6 +242,31 @@ def test_1p3b_layer_prefill_ragged_chunks_continue_from_state():
     eng.close()
 
 
+@pytest.mark.parametrize("B,T1,T2", [(1, 2, 64), (3, 65, 129), (2, 64, 1)])
+def test_1p3b_layer_prefill_chunk_edges(B, T1, T2):
+    # Lengths at the edges of the 64-token chunks of the matrix-core scan (2,
+    # 64, 65, 129 tokens), several sequences per launch, and a second prefill
+    # from the state the first one left (T2 = 1 takes the decode-step scan).
+    s = synth.LAYER_1P3B
+    seed = synth.SEED_BASE + 13
+    eng = engine(s, max_batch=B)
+    eng.load_synthetic(seed)
+    om = oracle.Model(s, synth.gen_model(s, seed))
+    toks = synth.gen_tokens(seed, 14 + T1, B * (T1 + T2), s.vocab).reshape(B, T1 + T2)
+    first, second = np.ascontiguousarray(toks[:, :T1]), np.ascontiguousarray(toks[:, T1:])
+    tr1 = trace_to_numpy(eng.trace_prefill(_i32(first)))
+    tr2 = trace_to_numpy(eng.trace_prefill(_i32(second)))
+    for b in range(B):
+        st, _ = _follow_prefill(om, s, first, tr1, b, T1, check_h_at={0, T1 - 1})
+        st, ol = _follow_prefill(om, s, second, tr2, b, T2, check_h_at={0, T2 - 1}, st=st)
+        assert_close(tr2["logits"][b], ol, what=f"last logits seq {b}")
+        conv_g, ssm_g = eng.get_state(b)
+        assert_close(ssm_g, st.ssm, what=f"ssm state seq {b}")
+        assert_close(conv_g, st.conv, what=f"conv state seq {b}")
+    eng.check()
+    eng.close()
+
+
 @pytest.fixture(scope="module")
 def full_model():
     s = synth.FULL_1P3B
