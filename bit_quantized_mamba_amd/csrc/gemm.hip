@@ -320,6 +320,17 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
     v8bf bB;
 #pragma unroll
     for (int e = 0; e < 8; ++e) bB[e] = (__bf16)(float)(int8_t)(bw2[e >> 2] >> (8 * (e & 3)));
+    // residual values of the column block's BM row blocks, all loaded before
+    // any of them is used (one memory round trip per column block, and before
+    // any store of the block: see the skinny kernel)
+    float prev[BM][16];
+#pragma unroll
+    for (int i = 0; i < BM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        prev[i][r] = (EPI == GEMM_EPI_RESIDUAL && m < a.M && nok) ? a.y[(size_t)m * a.ldy + n] : 0.0f;
+      }
 #pragma unroll
     for (int i = 0; i < BM; ++i) {
       const int rb = wm0 + 32 * i;  // tile-local first row of the block
@@ -340,13 +351,6 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
       lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t1, bB, lo, 0, 0, 0);
       lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t2, bB, lo, 0, 0, 0);
       lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t3, bB, lo, 0, 0, 0);
-      // residual values loaded before any store of the block (see the skinny kernel)
-      float prev[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        prev[r] = (EPI == GEMM_EPI_RESIDUAL && m < a.M && nok) ? a.y[(size_t)m * a.ldy + n] : 0.0f;
-      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ml = rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -354,7 +358,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
         if (m < a.M && nok) {
           const int sacc = 2 * acc[i][j][r] - s_qs[ml];
           const float y = proj_out(sacc, sw, s_s[ml], sb, lo[r]);
-          a.y[(size_t)m * a.ldy + n] = prev[r] + y;
+          a.y[(size_t)m * a.ldy + n] = prev[i][r] + y;
           if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
         }
       }
