@@ -16,6 +16,7 @@
 namespace dfssm {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // SSM scan over T tokens.  Workgroup (head h, sequence b) of 4 P threads:
@@ -101,7 +102,11 @@ __global__ __launch_bounds__(256) void scan1_kernel(ScanArgs a) {
   const float* xr = a.xc + (size_t)b * a.cdim;
   float4 S[NPT];
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) S[i] = *(const float4*)(stb + ((size_t)(pb * N + ns * NPT + i) * 16 + pq * 4));
+  // the state is streamed (read once and written once per step): non-temporal accesses
+  for (int i = 0; i < NPT; ++i) {
+    const v4f v = __builtin_nontemporal_load((const v4f*)(stb + ((size_t)(pb * N + ns * NPT + i) * 16 + pq * 4)));
+    S[i] = make_float4(v.x, v.y, v.z, v.w);
+  }
   const float4 xv = *(const float4*)(xr + h * P + p0);
   const float4 b0 = *(const float4*)(xr + a.d_inner + ns * NPT), b1 = *(const float4*)(xr + a.d_inner + ns * NPT + 4);
   const float4 c0 = *(const float4*)(xr + a.d_inner + N + ns * NPT),
@@ -126,7 +131,10 @@ __global__ __launch_bounds__(256) void scan1_kernel(ScanArgs a) {
     y3 += v.w * cn[i];
   }
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) *(float4*)(stb + ((size_t)(pb * N + ns * NPT + i) * 16 + pq * 4)) = S[i];
+  for (int i = 0; i < NPT; ++i) {
+    const v4f v = {S[i].x, S[i].y, S[i].z, S[i].w};
+    __builtin_nontemporal_store(v, (v4f*)(stb + ((size_t)(pb * N + ns * NPT + i) * 16 + pq * 4)));
+  }
   red[ns][p0 + 0] = y0;
   red[ns][p0 + 1] = y1;
   red[ns][p0 + 2] = y2;
