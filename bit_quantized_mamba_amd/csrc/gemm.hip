@@ -465,29 +465,37 @@ __global__ __launch_bounds__(256) void bitgemm_kernel(GemmArgs a) {
   gemm_tile_epilogue<TM, T::BM, T::BN, EPI>(a, acc, m0, n0, wm0, wn0, gsm);
 }
 
-// The scaffold GEMM for many rows (prefill), second form.  Tile 128 x 256,
-// k-tiles of 128; four waves, each 128 rows x 64 columns (4 x 2 blocks of
-// v_mfma_i32_32x32x32_i8, so a wave expands only its own two column blocks).
-// LDS holds the A tile (int8 codes) and the scaffold *bits* of the B tile
-// (4 KB a stage instead of 32 KB of expanded bytes); each lane expands the 16
-// bits of its B operand to 0/1 bytes in registers right before the multiply.
-// Global loads run two k-tiles ahead in two register sets, LDS is double
-// buffered: one barrier per k-tile, and each tile's loads have two tiles of
-// matrix work to land.
-constexpr int kG2TM = 128, kG2TN = 256, kG2KB = 128, kG2ARow = kG2KB + 16;
+// The scaffold GEMM for many rows (prefill), second form.  Tile 128 x TN,
+// k-tiles of 128; four waves in a WR x (4 / WR) grid, each (128 / WR) rows x
+// (TN / (4 / WR)) columns of v_mfma_i32_32x32x32_i8 blocks, so a wave expands
+// only its own column blocks.  LDS holds the A tile (int8 codes) and the
+// scaffold *bits* of the B tile (TN x 16 bytes a stage instead of TN x 128 of
+// expanded bytes); each lane expands the 16 bits of its B operand to 0/1
+// bytes in registers right before the multiply.  Global loads run two k-tiles
+// ahead in two register sets, LDS is double buffered: one barrier per k-tile,
+// and each tile's loads have two tiles of matrix work to land.  OCC
+// workgroups share a CU (the accumulators then live in VGPRs).
+constexpr int kG2TM = 128, kG2KB = 128, kG2ARow = kG2KB + 16;
 constexpr int kG2CW = kG2KB / 32;  // scaffold words per column of a k-tile
 constexpr int kG2AC = kG2KB / 16;  // 16-byte A chunks per row of a k-tile
-constexpr int kG2A = kG2TM * kG2ARow, kG2B = kG2TN * kG2CW * 4, kG2Stage = kG2A + kG2B;
-constexpr int kG2PT = kG2TM * kG2AC / 256;  // A chunks (and B words) per thread and k-tile
+constexpr int kG2A = kG2TM * kG2ARow;
+constexpr int kG2PT = kG2TM * kG2AC / 256;  // A chunks per thread and k-tile
+template <int TN>
+struct G2 {
+  static constexpr int B = TN * kG2CW * 4, STAGE = kG2A + B;
+  static constexpr int PB = TN * kG2CW / 256;  // B words per thread and k-tile
+};
 
 __device__ __forceinline__ v4i expand16(uint32_t b) {
   return (v4i){(int)spread_nibble(b), (int)spread_nibble(b >> 4), (int)spread_nibble(b >> 8),
                (int)spread_nibble(b >> 12)};
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void bitgemm2_kernel(GemmArgs a) {
-  constexpr int TM = kG2TM, TN = kG2TN, KB = kG2KB, BM = 4, BN = 2;
+template <int EPI, int TN, int WR, int OCC>
+__global__ __launch_bounds__(256, OCC) void bitgemm2_kernel(GemmArgs a) {
+  constexpr int TM = kG2TM, KB = kG2KB, WC = 4 / WR;
+  constexpr int BM = TM / WR / 32, BN = TN / WC / 32;
+  constexpr int PB = G2<TN>::PB, STAGE = G2<TN>::STAGE;
   extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // XCD-aware tile order: workgroups are dealt to the 8 XCDs round-robin, so
@@ -503,13 +511,13 @@ __global__ __launch_bounds__(256, 2) void bitgemm2_kernel(GemmArgs a) {
     n0 = (tile % ntn) * TN;
     m0 = (tile / ntn) * TM;
   }
-  const int wn0 = wave * 64;
+  const int wm0 = WR == 1 ? 0 : (wave / WC) * (TM / WR), wn0 = (WC == 4 ? wave : wave % WC) * (TN / WC);
   const int K = a.K, KW = K / 32, nk = K / KB;
-  // a thread's share of a k-tile: A chunks c = t, t + 256 (row c / 4, 16-byte
-  // chunk c % 4), B words c = t, t + 256 (column c / 2, word c % 2)
+  // a thread's share of a k-tile: A chunks c = t + 256 i (row c / 8, 16-byte
+  // chunk c % 8), B words c = t + 256 i (column c / 4, word c % 4)
   struct Tile {
     uint4 a[kG2PT];
-    uint32_t b[kG2PT];
+    uint32_t b[PB];
   };
   // branch-free loads: rows and columns past the end read the last one and
   // are zeroed by a select, so the compiler can count the loads in flight
@@ -520,18 +528,27 @@ __global__ __launch_bounds__(256, 2) void bitgemm2_kernel(GemmArgs a) {
       const int c = threadIdx.x + 256 * i;
       const int m = m0 + c / kG2AC;
       R.a[i] = *(const uint4*)(a.q + (size_t)min(m, a.M - 1) * K + (size_t)kt * KB + (c % kG2AC) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int c = threadIdx.x + 256 * i;
       const int n = n0 + c / kG2CW;
       R.b[i] = a.bits[(size_t)min(n, a.N - 1) * KW + kt * kG2CW + c % kG2CW];
     }
   };
   auto store = [&](int stg, const Tile& R) {
-    unsigned char* As = gsm + stg * kG2Stage;
+    unsigned char* As = gsm + stg * STAGE;
     uint32_t* Bw = (uint32_t*)(As + kG2A);
 #pragma unroll
     for (int i = 0; i < kG2PT; ++i) {
       const int c = threadIdx.x + 256 * i;
-      const bool mok = m0 + c / kG2AC < a.M, nok = n0 + c / kG2CW < a.N;
+      const bool mok = m0 + c / kG2AC < a.M;
       *(uint4*)(As + (c / kG2AC) * kG2ARow + (c % kG2AC) * 16) = mok ? R.a[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const bool nok = n0 + c / kG2CW < a.N;
       Bw[c] = nok ? R.b[i] : 0u;
     }
   };
@@ -541,7 +558,7 @@ __global__ __launch_bounds__(256, 2) void bitgemm2_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < BN; ++j) acc[i][j] = (v16i){};
   auto compute = [&](int stg) {
-    const unsigned char* As = gsm + stg * kG2Stage;
+    const unsigned char* As = gsm + stg * STAGE;
     const unsigned char* Bb = As + kG2A;
 #pragma unroll
     for (int kk = 0; kk < KB / 32; ++kk) {
@@ -553,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void bitgemm2_kernel(GemmArgs a) {
         bf[j] = expand16(*(const uint16_t*)(Bb + col * (kG2CW * 4) + kk * 4 + 2 * (lane >> 5)));
       }
 #pragma unroll
-      for (int i = 0; i < BM; ++i) af[i] = *(const v4i*)(As + (32 * i + (lane & 31)) * kG2ARow + koff);
+      for (int i = 0; i < BM; ++i) af[i] = *(const v4i*)(As + (wm0 + 32 * i + (lane & 31)) * kG2ARow + koff);
 #pragma unroll
       for (int i = 0; i < BM; ++i)
 #pragma unroll
@@ -561,7 +578,7 @@ __global__ __launch_bounds__(256, 2) void bitgemm2_kernel(GemmArgs a) {
     }
   };
 
-  // nk is even (K % 128 == 0), so the loop runs whole pairs of k-tiles with
+  // nk is even (K % 256 == 0), so the loop runs whole pairs of k-tiles with
   // no exit in between, and the loads are unconditional (indexes clamped to
   // the last tile): the compiler keeps one accumulator set and waits only
   // for the tile being stored, not for the one still in flight.
@@ -583,8 +600,11 @@ __global__ __launch_bounds__(256, 2) void bitgemm2_kernel(GemmArgs a) {
     __syncthreads();
     load(min(kt + 4, nk - 1), R0);
   }
-  gemm_tile_epilogue<TM, BM, BN, EPI>(a, acc, m0, n0, 0, wn0, gsm);
+  gemm_tile_epilogue<TM, BM, BN, EPI>(a, acc, m0, n0, wm0, wn0, gsm);
 }
+
+// tile width, wave rows and workgroups per CU of the many-row scaffold GEMM
+constexpr int kG2TN = 128, kG2WR = 1, kG2OCC = 3;
 
 template <int TM, int TN>
 static hipError_t launch_bitgemm_t(const GemmArgs& a, int epi, hipStream_t st) {
@@ -606,11 +626,11 @@ hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st) {
   if (a.M <= 32) return launch_bitgemm_t<32, 128>(a, epi, st);
   if (a.K % (2 * kG2KB) == 0) {
     const dim3 grid((a.N + kG2TN - 1) / kG2TN, (a.M + kG2TM - 1) / kG2TM), block(256);
-    const size_t lds = 2 * (size_t)kG2Stage;
+    const size_t lds = 2 * (size_t)G2<kG2TN>::STAGE;
     if (epi == GEMM_EPI_RESIDUAL)
-      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_RESIDUAL>), grid, block, lds, st, a);
+      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_RESIDUAL, kG2TN, kG2WR, kG2OCC>), grid, block, lds, st, a);
     else
-      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_STORE>), grid, block, lds, st, a);
+      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_STORE, kG2TN, kG2WR, kG2OCC>), grid, block, lds, st, a);
     return hipGetLastError();
   }
   return launch_bitgemm_t<128, 256>(a, epi, st);
