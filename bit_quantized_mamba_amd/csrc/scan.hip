@@ -374,7 +374,7 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
       ssd_stage_load(a, hp, tid, row0 + kSsdL, min(kSsdL, a.T - t0 - kSsdL),
                      a.gram + ((size_t)b * nch + c + 1) * recf, st);
 
-    // ---- (a) Y_inter^T[p][i] partial over this wave's 64 states, both position blocks
+    // ---- (a) Y_inter^T[p][i] = exp(A_i) sum_n S_in[p][n] C[i][n], partial over this wave's 64 states, both position blocks
     v16f Y0 = (v16f){}, Y1 = (v16f){};
     {
       const float e0 = sPar[192 + col], e1 = sPar[192 + 32 + col];
@@ -385,16 +385,19 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
         for (int r4 = 0; r4 < 4; ++r4) {
           const float4 c0 = *(const float4*)(sm + kSsdOC + col * kSsdCRow + 32 * nb + 8 * r4 + 4 * half);
           const float4 c1 = *(const float4*)(sm + kSsdOC + (32 + col) * kSsdCRow + 32 * nb + 8 * r4 + 4 * half);
-          Y0 = mfma_f32(S[t][4 * r4 + 0], c0.x * e0, Y0);
-          Y1 = mfma_f32(S[t][4 * r4 + 0], c1.x * e1, Y1);
-          Y0 = mfma_f32(S[t][4 * r4 + 1], c0.y * e0, Y0);
-          Y1 = mfma_f32(S[t][4 * r4 + 1], c1.y * e1, Y1);
-          Y0 = mfma_f32(S[t][4 * r4 + 2], c0.z * e0, Y0);
-          Y1 = mfma_f32(S[t][4 * r4 + 2], c1.z * e1, Y1);
-          Y0 = mfma_f32(S[t][4 * r4 + 3], c0.w * e0, Y0);
-          Y1 = mfma_f32(S[t][4 * r4 + 3], c1.w * e1, Y1);
+          Y0 = mfma_f32(S[t][4 * r4 + 0], c0.x, Y0);
+          Y1 = mfma_f32(S[t][4 * r4 + 0], c1.x, Y1);
+          Y0 = mfma_f32(S[t][4 * r4 + 1], c0.y, Y0);
+          Y1 = mfma_f32(S[t][4 * r4 + 1], c1.y, Y1);
+          Y0 = mfma_f32(S[t][4 * r4 + 2], c0.z, Y0);
+          Y1 = mfma_f32(S[t][4 * r4 + 2], c1.z, Y1);
+          Y0 = mfma_f32(S[t][4 * r4 + 3], c0.w, Y0);
+          Y1 = mfma_f32(S[t][4 * r4 + 3], c1.w, Y1);
         }
       }
+      // exp(A_i) scales output column i (lane % 32 of either block)
+      Y0 *= e0;
+      Y1 *= e1;
     }
     lds_barrier();  // C is no longer read: its space takes the partial sums
     float* xch = sm + kSsdOC;
