@@ -12,9 +12,9 @@ Prints one JSON line: tokens/s, the roofline of that kernel (HIP-event time of
 the launch, algorithmic bytes per token x tokens), and the CPU oracle timed on
 a bounded sample of the same workload.
 
---workload decode-b32 and prefill-8x2048 measure the batched path instead
-(32 sequences decoding after an 8-token prefill; a prefill of 8 x 2048
-tokens); their lines carry step-level rooflines.
+--workload decode-b32, decode-b512 and prefill-8x2048 measure the batched
+path instead (32 or 512 sequences decoding after an 8-token prefill; a
+prefill of 8 x 2048 tokens); their lines carry step-level rooflines.
 """
 import argparse
 import json
@@ -122,8 +122,8 @@ def bench_batched(args):
     common = {"n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "dtype": "int8/1-bit weights, int32 accumulation, f32 state", "data": "synthetic (seeded weights and tokens)",
               "cpu_baseline": None}
-    if args.workload == "decode-b32":
-        B, T = 32, 8
+    if args.workload in ("decode-b32", "decode-b512"):
+        B, T = (32, 8) if args.workload == "decode-b32" else (512, 8)
         seed = synth.SEED_BASE + 3
         eng = Engine.from_shape(s, max_batch=B, device=0)
         eng.load_synthetic(seed)
@@ -142,10 +142,10 @@ def bench_batched(args):
         ms = e0.elapsed_time(e1)
         sb = batched_step_bytes(s, B)
         gbs = sb * args.steps / (ms / 1e3) / 1e9
-        res = {"metric": "decode tokens/s, batch=32, 48-layer 1.3B shape; % of HBM roofline",
+        res = {"metric": f"decode tokens/s, batch={B}, 48-layer 1.3B shape; % of HBM roofline",
                "value": round(B * args.steps / (ms / 1e3), 1), "unit": "tokens/s", "steps": args.steps,
                "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4),
-               "config": {"workload": "DF-SSM 48-layer 1.3B shape, batch 32, 8-token prefill then greedy decode "
+               "config": {"workload": f"DF-SSM 48-layer 1.3B shape, batch {B}, 8-token prefill then greedy decode "
                                       f"of {args.steps} steps (one hipGraph replay per step)", "batch": B},
                "roofline": {"bound": "hbm", "scope": "whole step", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
@@ -224,7 +224,8 @@ def main():
     ap.add_argument("--kernel-breakdown", action="store_true",
                     help="also time each kernel of the per-layer (multi-kernel) path")
     ap.add_argument("--path", choices=["auto", "kernels", "persistent", "gemm"], default="auto")
-    ap.add_argument("--workload", choices=["decode-b1", "decode-b32", "prefill-8x2048"], default="decode-b1")
+    ap.add_argument("--workload", choices=["decode-b1", "decode-b32", "decode-b512", "prefill-8x2048"],
+                    default="decode-b1")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy (read + write) of this many MiB, "
                          "a known-size reference for the HBM byte counters of a profiler run")

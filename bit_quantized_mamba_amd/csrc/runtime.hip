@@ -428,14 +428,20 @@ hipError_t b_head(dfssm_ctx* c, int B, int T, float* lg, int8_t* qf_out, hipStre
   hipError_t e = launch_rows_quant(rf, c->dm, st);
   if (e == hipSuccess && qf_out) e = hipMemcpyAsync(qf_out, w.q, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st);
   if (e != hipSuccess) return e;
-  if (B <= 32 && c->dm % 128 == 0) {
-    SkinnyArgs sh{};
-    sh.q = w.q; sh.s = w.s;
-    sh.w = c->lt<int8_t>(-1, DFSSM_G_EMBED);
-    sh.sw = c->lt<float>(-1, DFSSM_G_EMBED_SCALE);
-    sh.M = B; sh.N = c->V; sh.K = c->dm;
-    sh.y = lg; sh.ldy = c->V;
-    return launch_gemm_skinny(sh, SK_HEAD, st);
+  if (c->dm % 128 == 0) {
+    // the int8 LM head on the matrix cores, 32 sequences per launch (the
+    // embedding rows, 103 MB at the 1.3B shape, stream once per launch)
+    for (int b0 = 0; b0 < B; b0 += 32) {
+      SkinnyArgs sh{};
+      sh.q = w.q + (size_t)b0 * c->dm; sh.s = w.s + b0;
+      sh.w = c->lt<int8_t>(-1, DFSSM_G_EMBED);
+      sh.sw = c->lt<float>(-1, DFSSM_G_EMBED_SCALE);
+      sh.M = std::min(32, B - b0); sh.N = c->V; sh.K = c->dm;
+      sh.y = lg + (size_t)b0 * c->V; sh.ldy = c->V;
+      const hipError_t e2 = launch_gemm_skinny(sh, SK_HEAD, st);
+      if (e2 != hipSuccess) return e2;
+    }
+    return hipSuccess;
   }
   return launch_lm_head(c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), w.q, w.s, c->V,
                         c->dm, B, lg, st);

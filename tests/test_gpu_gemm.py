@@ -293,16 +293,17 @@ def test_full_model_traced_prefill(full_model):
     eng.close()
 
 
-def test_full_model_batch32_decode_sampled(full_model):
-    # the batch-32 decode workload: 32 sequences prefilled with 8 tokens, then
-    # greedy steps; sequences 0, 13 and 31 are followed by the oracle
+@pytest.mark.parametrize("B,T,follow", [(32, 8, (0, 13, 31)), (512, 2, (0, 257, 511))])
+def test_full_model_batched_decode_sampled(full_model, B, T, follow):
+    # the batch-32 decode workload (32 sequences prefilled with 8 tokens) and
+    # batch 512 (the skinny kernels give way to the tiled GEMMs, the LM head
+    # runs in 16 launches of 32 sequences), then greedy steps; three sequences
+    # are followed by the oracle
     s, seed, w, om = full_model
-    B, T = 32, 8
     eng = engine(s, max_batch=B)
     eng.load_synthetic(seed)
     toks = synth.gen_tokens(seed, 10, B * T, s.vocab).reshape(B, T)
     tr = trace_to_numpy(eng.trace_prefill(_i32(toks)))
-    follow = (0, 13, 31)
     sts, nxt = {}, {}
     for b in follow:
         sts[b], ol = _follow_prefill(om, s, toks, tr, b, T)
