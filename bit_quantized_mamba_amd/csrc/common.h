@@ -180,6 +180,14 @@ struct GemmArgs {
   float* y;             // [M][ldy]
   int ldy;
   int32_t* acc;         // [M][N] signed scaffold sums, or null
+  // one decode token per sequence (row m = sequence m): the conv shift
+  // register of columns [x_off, x_off + cdim) in the epilogue, or xc null
+  float* xc;            // [M][cdim]
+  float* conv_state;    // sequence 0's window [3][cdim]; sequence m at + m * conv_bstride
+  size_t conv_bstride;
+  const float* conv_w;  // [cdim][4]
+  const float* conv_b;
+  int x_off, cdim;
 };
 
 // M <= 32 rows against N weight rows, one 32 x 32 block per workgroup

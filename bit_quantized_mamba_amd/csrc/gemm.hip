@@ -331,6 +331,15 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
         const int m = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         prev[i][r] = (EPI == GEMM_EPI_RESIDUAL && m < a.M && nok) ? a.y[(size_t)m * a.ldy + n] : 0.0f;
       }
+    // conv shift register of this column (one decode token per row), or none
+    const bool conv_col = EPI == GEMM_EPI_STORE && a.xc && nok && n >= a.x_off && n < a.x_off + a.cdim;
+    const int cc = min(max(n - a.x_off, 0), a.cdim - 1);
+    float4 cw = make_float4(0.f, 0.f, 0.f, 0.f);
+    float cb = 0.0f;
+    if (EPI == GEMM_EPI_STORE && a.xc) {
+      cw = *(const float4*)(a.conv_w + (size_t)cc * 4);
+      cb = a.conv_b[cc];
+    }
 #pragma unroll
     for (int i = 0; i < BM; ++i) {
       const int rb = wm0 + 32 * i;  // tile-local first row of the block
@@ -351,6 +360,19 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
       lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t1, bB, lo, 0, 0, 0);
       lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t2, bB, lo, 0, 0, 0);
       lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t3, bB, lo, 0, 0, 0);
+      // the block's conv windows, loaded before any of its stores (rows past
+      // the end read the last one)
+      float w0[16], w1[16], w2[16];
+      if (EPI == GEMM_EPI_STORE && a.xc) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = min(m0 + rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), a.M - 1);
+          const float* st = a.conv_state + (size_t)m * a.conv_bstride + cc;
+          w0[r] = st[0];
+          w1[r] = st[a.cdim];
+          w2[r] = st[2 * a.cdim];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ml = rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -360,6 +382,13 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
           const float y = proj_out(sacc, sw, s_s[ml], sb, lo[r]);
           a.y[(size_t)m * a.ldy + n] = prev[i][r] + y;
           if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
+          if (conv_col) {  // one decode token: the conv shift register of channel cc
+            float* st = a.conv_state + (size_t)m * a.conv_bstride + cc;
+            a.xc[(size_t)m * a.cdim + cc] = silu_f(conv4(cb, cw.x, w0[r], cw.y, w1[r], cw.z, w2[r], cw.w, y));
+            st[0] = w1[r];
+            st[a.cdim] = w2[r];
+            st[2 * a.cdim] = y;
+          }
         }
       }
     }

@@ -378,6 +378,12 @@ hipError_t b_in_proj(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
   GemmArgs gi{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_IN_BITS), c->lt<float>(l, DFSSM_T_IN_SW),
               c->lt<int8_t>(l, DFSSM_T_IN_B), c->lt<float>(l, DFSSM_T_IN_SB), M, c->dproj, c->dm, w.zx, c->dproj,
               nullptr};
+  if (T == 1) {  // one decode token per sequence: the conv shift register in the GEMM epilogue
+    gi.xc = w.xc; gi.conv_state = conv_l; gi.conv_bstride = c->conv_bstride;
+    gi.conv_w = c->lt<float>(l, DFSSM_T_CONV_W); gi.conv_b = c->lt<float>(l, DFSSM_T_CONV_B);
+    gi.x_off = c->di; gi.cdim = c->cdim;
+    return launch_bitgemm(gi, GEMM_EPI_STORE, st);
+  }
   hipError_t e = launch_bitgemm(gi, GEMM_EPI_STORE, st);
   if (e != hipSuccess) return e;
   ConvSeqArgs ca{w.zx, c->dproj, c->di, w.xc, conv_l, c->conv_bstride,
