@@ -34,9 +34,9 @@ PAGES_B512_TOKS = 5081.0  # decode tokens/s at batch 512 (A100), the pages' only
 # (FETCH_SIZE reads 0.5 GiB for it: factor 2.0; WRITE_SIZE reads 1 GiB: 1.0).
 # Valid only for the kernel sources they were taken from (hash below).
 COUNTED_TRAFFIC = {
-    "sources_sha256": "4fda29a3cd4d731bcec2701aacc34539991864e7c788c8d2d0045354f0d53942",
-    "fetch_bytes_per_token": 461136450,
-    "write_bytes_per_token": 118426857,
+    "sources_sha256": "39682a08697673e9fcc4107ec5d4d4abb855e1e51c0ba802b8d2468f35551ea2",
+    "fetch_bytes_per_token": 461174091,
+    "write_bytes_per_token": 118426844,
 }
 KERNEL_SOURCES = ("bit_quantized_mamba_amd/csrc/persistent.hip", "bit_quantized_mamba_amd/csrc/persistent.h",
                   "bit_quantized_mamba_amd/csrc/common.h")
