@@ -293,6 +293,34 @@ def test_full_model_traced_prefill(full_model):
     eng.close()
 
 
+def test_full_model_prefill_8x2048_batch_independence(full_model):
+    # The 8 x 2048 prefill as the bench runs it (48 layers, one 16384-row
+    # chunk): each sequence's last logits and final state equal, bit for bit,
+    # those of a prefill of that sequence alone (every kernel treats rows and
+    # sequences independently; the arithmetic is checked against the oracle
+    # by the shorter prefills above).
+    s, seed, w, om = full_model
+    B, T = 8, 2048
+    toks = synth.gen_tokens(seed, 15, B * T, s.vocab).reshape(B, T)
+    eng = engine(s, max_batch=B)
+    eng.load_synthetic(seed)
+    eng.reset_state(B)
+    lg_b, nx_b = eng.prefill(_i32(toks))
+    lg_b = lg_b.cpu().numpy()
+    st_b = {b: eng.get_state(b) for b in (0, 5, 7)}
+    eng.close()
+    one = engine(s, max_batch=1)
+    one.load_synthetic(seed)
+    for b in (0, 5, 7):
+        one.reset_state(1)
+        lg_1, _ = one.prefill(_i32(toks[b:b + 1]))
+        assert np.array_equal(lg_1.cpu().numpy()[0], lg_b[b]), b
+        conv_1, ssm_1 = one.get_state(0)
+        assert np.array_equal(ssm_1, st_b[b][1]) and np.array_equal(conv_1, st_b[b][0]), b
+        assert np.all(np.isfinite(lg_b[b]))
+    one.close()
+
+
 @pytest.mark.parametrize("B,T,follow", [(32, 8, (0, 13, 31)), (512, 2, (0, 257, 511))])
 def test_full_model_batched_decode_sampled(full_model, B, T, follow):
     # the batch-32 decode workload (32 sequences prefilled with 8 tokens) and
