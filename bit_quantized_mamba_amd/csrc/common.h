@@ -100,6 +100,19 @@ __device__ __forceinline__ int wave_sum_i(int v) {
          (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
+// The projection output float(sacc) * sw * s + sB * lo and the causal conv
+// sum, each rounded in one fixed order (two products, then a fused
+// multiply-add; a chain of fused multiply-adds) whatever the compiler would
+// contract: every kernel that produces them gives a row the same value.
+__device__ __forceinline__ float proj_out(int sacc, float sw, float s, float sb, float lo) {
+#pragma clang fp contract(off)
+  return __builtin_fmaf(sb, lo, ((float)sacc * sw) * s);
+}
+__device__ __forceinline__ float conv4(float bias, float w0, float x0, float w1, float x1, float w2, float x2,
+                                       float w3, float x3) {
+  return __builtin_fmaf(w3, x3, __builtin_fmaf(w2, x2, __builtin_fmaf(w1, x1, __builtin_fmaf(w0, x0, bias))));
+}
+
 // ---------------------------------------------------------------------------
 // kernel argument bundles
 // ---------------------------------------------------------------------------
@@ -242,20 +255,31 @@ struct ScanArgs {
   float* g;         // [B*T][d_inner]
   int B, T, H, d_inner, cdim;
   float* gram;      // chunked scan workspace: B * ceil(T / kSsdL) records of ssd_record_floats(H), or null
+  // The chunked scan takes the conv inputs (the in_proj output x, B, C at
+  // zx columns x_off + c) and applies the causal conv itself, with the stored
+  // window as the history before t = 0; xc is then not read.
+  int x_off;
+  const float* conv_w;      // [cdim][4]
+  const float* conv_b;      // [cdim]
+  const float* conv_state;  // sequence 0's window [3][cdim] (oldest first); sequence b at + b * conv_bstride
+  size_t conv_bstride;
 };
 
 // The chunked scan (headdim 64, d_state 128) works on chunks of kSsdL tokens;
-// its workspace record per chunk is G [kSsdL][kSsdL], then per head the
-// chunk parameters A_j, dt_j, w_j, exp(A_j) [H][4][kSsdL].
+// its workspace record per chunk is G [kSsdL][kSsdL], per head the chunk
+// parameters A_j, dt_j, w_j, exp(A_j) [H][4][kSsdL], then the chunk's conv
+// outputs B [kSsdL][128] and C [kSsdL][128].
 constexpr int kSsdL = 64;
 __host__ __device__ constexpr size_t ssd_record_floats(int H) {
-  return (size_t)kSsdL * kSsdL + (size_t)H * 4 * kSsdL;
+  return (size_t)kSsdL * kSsdL + (size_t)H * 4 * kSsdL + 2 * (size_t)kSsdL * 128;
 }
 
 hipError_t launch_rows_quant(const RowsArgs& a, int K, hipStream_t st);
 hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st);
 hipError_t launch_gemm_skinny(const SkinnyArgs& a, int kind, hipStream_t st);
-hipError_t launch_conv_seq(const ConvSeqArgs& a, hipStream_t st);
+hipError_t launch_conv_seq(const ConvSeqArgs& a, hipStream_t st);  // conv, then the window update
+hipError_t launch_conv_state_update(const ConvSeqArgs& a, hipStream_t st);
+bool scan_takes_conv_inputs(int P, int N);  // the scan applies the conv itself (then run the window update after it)
 hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st);
 bool scan_supported(int P, int N);
 hipError_t launch_embed_rows(const int32_t* tok, int tok_stride, int t0, int B, int T, const int8_t* E,

@@ -40,18 +40,6 @@ __device__ __forceinline__ void bf16_split3(float v, __bf16& p1, __bf16& p2, __b
   p3 = __builtin_bit_cast(__bf16, (unsigned short)(__float_as_uint(r2) >> 16));
 }
 
-// The projection output float(sacc) * sw * s + sB * lo and the causal conv
-// sum, each rounded in one fixed order (two products, then a fused
-// multiply-add; a chain of fused multiply-adds) whatever the compiler would
-// contract: every kernel that produces them gives a row the same value.
-__device__ __forceinline__ float proj_out(int sacc, float sw, float s, float sb, float lo) {
-#pragma clang fp contract(off)
-  return __builtin_fmaf(sb, lo, ((float)sacc * sw) * s);
-}
-__device__ __forceinline__ float conv4(float bias, float w0, float x0, float w1, float x1, float w2, float x2,
-                                       float w3, float x3) {
-  return __builtin_fmaf(w3, x3, __builtin_fmaf(w2, x2, __builtin_fmaf(w1, x1, __builtin_fmaf(w0, x0, bias))));
-}
 
 // ---------------------------------------------------------------------------
 // rows_quant: one wave per row, four rows per workgroup.  Lane L holds the
@@ -886,16 +874,21 @@ __global__ __launch_bounds__(256) void conv_state_update_kernel(ConvSeqArgs a) {
   for (int j = 0; j < 3; ++j) st[(size_t)j * a.cdim + c] = nv[j];
 }
 
+hipError_t launch_conv_state_update(const ConvSeqArgs& a, hipStream_t st) {
+  if (a.B <= 0 || a.T <= 0) return hipSuccess;
+  const dim3 g2((a.cdim + 255) / 256, a.B);
+  hipLaunchKernelGGL(conv_state_update_kernel, g2, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_conv_seq(const ConvSeqArgs& a, hipStream_t st) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
   if (a.cdim % 4 || a.x_off % 4 || a.ldzx % 4) return hipErrorInvalidValue;
   const dim3 g1((a.cdim / 4 + 255) / 256, (a.T + kConvChunk - 1) / kConvChunk, a.B);
   hipLaunchKernelGGL(conv_seq_kernel, g1, dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 g2((a.cdim + 255) / 256, a.B);
-  hipLaunchKernelGGL(conv_state_update_kernel, g2, dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch_conv_state_update(a, st);
 }
 
 // ---------------------------------------------------------------------------

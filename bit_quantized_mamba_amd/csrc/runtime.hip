@@ -385,7 +385,7 @@ hipError_t b_in_proj(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
     return launch_bitgemm(gi, GEMM_EPI_STORE, st);
   }
   hipError_t e = launch_bitgemm(gi, GEMM_EPI_STORE, st);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || scan_takes_conv_inputs(c->P, c->N)) return e;  // else the scan applies the conv
   ConvSeqArgs ca{w.zx, c->dproj, c->di, w.xc, conv_l, c->conv_bstride,
                  c->lt<float>(l, DFSSM_T_CONV_W), c->lt<float>(l, DFSSM_T_CONV_B), B, T, c->cdim};
   return launch_conv_seq(ca, st);
@@ -397,7 +397,20 @@ hipError_t b_scan(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
               c->lt<float>(l, DFSSM_T_DT_BIAS), c->lt<float>(l, DFSSM_T_D),
               c->ssm + (size_t)l * c->H * c->P * c->N, c->ssm_bstride, w.g, B, T, c->H, c->di, c->cdim,
               w.gram};
-  return launch_scan(sa, c->P, c->N, st);
+  if (T == 1 || !scan_takes_conv_inputs(c->P, c->N)) return launch_scan(sa, c->P, c->N, st);
+  // the scan convolves the in_proj output itself, reading the stored window;
+  // the window moves on once the scan is done with it
+  float* conv_l = c->conv + (size_t)l * (c->K - 1) * c->cdim;
+  sa.x_off = c->di;
+  sa.conv_w = c->lt<float>(l, DFSSM_T_CONV_W);
+  sa.conv_b = c->lt<float>(l, DFSSM_T_CONV_B);
+  sa.conv_state = conv_l;
+  sa.conv_bstride = c->conv_bstride;
+  hipError_t e = launch_scan(sa, c->P, c->N, st);
+  if (e != hipSuccess) return e;
+  ConvSeqArgs ca{w.zx, c->dproj, c->di, w.xc, conv_l, c->conv_bstride,
+                 c->lt<float>(l, DFSSM_T_CONV_W), c->lt<float>(l, DFSSM_T_CONV_B), B, T, c->cdim};
+  return launch_conv_state_update(ca, st);
 }
 
 hipError_t b_rows_out(dfssm_ctx* c, int l, int M, hipStream_t st) {

@@ -178,7 +178,9 @@ constexpr int kSsdOX = kSsdOB + 64 * kSsdCRow;   // x of both heads [64 j][kSsdC
 constexpr int kSsdOG = kSsdOX + 64 * kSsdCRow;   // G     [64 i][kSsdRow]
 constexpr int kSsdOPar = kSsdOG + 64 * kSsdRow;  // per head: A_i, dt_j, w_j, exp(A_i)  [2][4][64]
 constexpr int kSsdOZ = kSsdOPar + 2 * 4 * 64;     // z of both heads [64 i][kSsdCRow]
-constexpr int kSsdFloats = kSsdOZ + 64 * kSsdCRow;
+constexpr int kSsdOCW = kSsdOZ + 64 * kSsdCRow;  // conv weights of both heads' x channels [128][4]
+constexpr int kSsdOCB = kSsdOCW + 128 * 4;        // conv biases [128]
+constexpr int kSsdFloats = kSsdOCB + 128;
 constexpr size_t kSsdLds = sizeof(float) * kSsdFloats;
 static_assert(8 * 16 * 64 <= 64 * kSsdCRow, "the partial-sum exchange fits in the C buffer");
 
@@ -195,10 +197,14 @@ __device__ __forceinline__ v16f mfma_f32(float a, float b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// G[b][c][i][j] = C_{t0+i} . B_{t0+j} for chunk c of sequence b (rows past the
-// end of the sequence count as zero), and the chunk parameters of every head.
-// Workgroup (chunk, sequence), wave w computes the 32 x 32 tile (w >> 1,
-// w & 1) of G; the tile above the diagonal is never read and not written.
+// G[b][c][i][j] = C_{t0+i} . B_{t0+j} for chunk c of sequence b, where B and
+// C are the causal conv outputs of the chunk's tokens: computed here from the
+// in_proj output (the three inputs before the chunk from the previous rows or
+// the stored window) and written to the chunk's record for the scan.  Rows
+// past the end of the sequence count as zero.  Then the chunk parameters of
+// every head.  Workgroup (chunk, sequence), wave w computes the 32 x 32 tile
+// (w >> 1, w & 1) of G; the tile above the diagonal is never read and not
+// written.
 __global__ __launch_bounds__(256) void ssd_gram_kernel(ScanArgs a) {
   constexpr int N = 128;
   __shared__ __attribute__((aligned(16))) float sC[64 * kSsdRow], sB[64 * kSsdRow];
@@ -206,18 +212,38 @@ __global__ __launch_bounds__(256) void ssd_gram_kernel(ScanArgs a) {
   const int lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
   const int ti = wave >> 1, tj = wave & 1;
   const int t0 = c * kSsdL, Lc = min(kSsdL, a.T - t0);
-  const size_t row0 = (size_t)b * a.T + t0;
+  const size_t row0 = (size_t)b * a.T + t0, rowb = (size_t)b * a.T;
+  float* const recB = a.gram + ((size_t)b * gridDim.x + c) * ssd_record_floats(a.H) + kSsdL * kSsdL +
+                      (size_t)a.H * 4 * kSsdL;
+  float* const recC = recB + kSsdL * N;
+  // conv: thread = channel ch of this half (0..63 of B, 64..127 of C), tokens 32 rh .. 32 rh + 31
+  const int ch = tid & 127, rh = tid >> 7;
   v16f acc = (v16f){};
   for (int nh = 0; nh < 2; ++nh) {  // two halves of d_state
     if (nh) __syncthreads();
+    {
+      const int n = nh * 64 + (ch & 63);
+      const int cc = a.d_inner + (ch < 64 ? 0 : N) + n;  // conv channel
+      const float4 cw = *(const float4*)(a.conv_w + (size_t)cc * 4);
+      const float cb = a.conv_b[cc];
+      const float* zcol = a.zx + a.x_off + cc;
+      const float* wst = a.conv_state + (size_t)b * a.conv_bstride + cc;
+      float v[32 + 3];  // inputs of tokens t0 + 32 rh - 3 ..
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int idx = tid + 256 * k;          // 2048 float4: 64 rows x (B 16, C 16)
-      const int j = idx >> 5, q = idx & 31;   // q < 16: B, else C
-      const int cc = (q & 15) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < Lc) v = *(const float4*)(a.xc + (row0 + j) * a.cdim + a.d_inner + (q >> 4) * N + nh * 64 + cc);
-      *(float4*)((q < 16 ? sB : sC) + j * kSsdRow + cc) = v;
+      for (int k = 0; k < 35; ++k) {
+        const int t = t0 + 32 * rh - 3 + k;
+        const float* src = t >= 0 ? zcol + (rowb + min(t, a.T - 1)) * a.ldzx : wst + (size_t)(t + 3) * a.cdim;
+        v[k] = *src;
+      }
+      float* dst = (ch < 64 ? sB : sC) + (ch & 63);
+      float* rdst = (ch < 64 ? recB : recC) + n;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const int j = 32 * rh + r;
+        const float o = j < Lc ? silu_f(conv4(cb, cw.x, v[r], cw.y, v[r + 1], cw.z, v[r + 2], cw.w, v[r + 3])) : 0.0f;
+        dst[j * kSsdRow] = o;
+        rdst[(size_t)j * N] = o;
+      }
     }
     __syncthreads();
     if (wave != 1) {
@@ -262,28 +288,40 @@ __global__ __launch_bounds__(256) void ssd_gram_kernel(ScanArgs a) {
   }
 }
 
-// One chunk's operands in registers: per thread four float4 of x (both
-// heads), B, C and z (rows j = idx / 32, float4 q = idx % 32 of idx = tid +
-// 512 k), two of G and (threads < 128) one of the two heads' parameters.
-// Rows past the sequence end read the last valid row; x, B and C of those
-// rows are zeroed when they are written to LDS (their G entries and dt are
-// zero already).
+// One chunk's operands in registers: per thread the in_proj outputs x of
+// channels 4 q .. 4 q + 3 of both heads (q = tid % 32) for tokens 4 rg - 3 ..
+// 4 rg + 3 (rg = tid / 32; before the sequence start the stored conv window),
+// four float4 of the conv outputs B and C (from the chunk's record) and of z
+// (rows j = idx / 32, float4 q = idx % 32 of idx = tid + 512 k), two of G
+// and (threads < 128) one of the two heads' parameters.  Tokens past the
+// sequence end read the last one; their values are zeroed or unused.
 struct SsdStage {
-  float4 x[4], b[4], c[4], z[4], g[2], par;
+  float4 x[7], b[4], c[4], z[4], g[2], par;
 };
 
-__device__ __forceinline__ void ssd_stage_load(const ScanArgs& a, int hp, int tid, size_t row0, int Lc,
-                                               const float* rec, SsdStage& st) {
+__device__ __forceinline__ void ssd_stage_load(const ScanArgs& a, int hp, int tid, int b, int t0, const float* rec,
+                                               SsdStage& st) {
+  const size_t rowb = (size_t)b * a.T;
+  {
+    const int q = tid & 31, rg = tid >> 5;
+    const float* xz = a.zx + a.x_off + (size_t)(2 * hp) * 64 + 4 * q;
+    const float* xw = a.conv_state + (size_t)b * a.conv_bstride + (size_t)(2 * hp) * 64 + 4 * q;
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+      const int t = t0 + 4 * rg - 3 + k;
+      const float* src = t >= 0 ? xz + (rowb + min(t, a.T - 1)) * a.ldzx : xw + (size_t)(t + 3) * a.cdim;
+      st.x[k] = *(const float4*)src;
+    }
+  }
+  const float* recB = rec + kSsdL * kSsdL + (size_t)a.H * 4 * kSsdL;
+  const float* recC = recB + kSsdL * 128;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int idx = tid + 512 * k;
     const int j = idx >> 5, q = idx & 31;
-    const size_t r = row0 + min(j, Lc - 1);
-    const float* xr = a.xc + r * a.cdim;
-    st.x[k] = *(const float4*)(xr + (size_t)(2 * hp) * 64 + 4 * q);
-    st.b[k] = *(const float4*)(xr + a.d_inner + 4 * q);
-    st.c[k] = *(const float4*)(xr + a.d_inner + 128 + 4 * q);
-    st.z[k] = *(const float4*)(a.zx + r * a.ldzx + (size_t)(2 * hp) * 64 + 4 * q);
+    st.b[k] = *(const float4*)(recB + j * 128 + 4 * q);
+    st.c[k] = *(const float4*)(recC + j * 128 + 4 * q);
+    st.z[k] = *(const float4*)(a.zx + (rowb + min(t0 + j, a.T - 1)) * a.ldzx + (size_t)(2 * hp) * 64 + 4 * q);
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -333,8 +371,14 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
   const int iy = 32 * h2 + col;  // this lane's output position
   const size_t recf = ssd_record_floats(a.H);
 
+  // conv weights and biases of both heads' x channels, for the whole launch
+  if (tid < 128) {
+    const int cch = 2 * hp * 64 + tid;
+    *(float4*)(sm + kSsdOCW + 4 * tid) = *(const float4*)(a.conv_w + (size_t)cch * 4);
+    sm[kSsdOCB + tid] = a.conv_b[cch];
+  }
   SsdStage st;
-  ssd_stage_load(a, hp, tid, rowb, min(kSsdL, a.T), a.gram + (size_t)b * nch * recf, st);
+  ssd_stage_load(a, hp, tid, b, 0, a.gram + (size_t)b * nch * recf, st);
   // gated outputs of the previous chunk, stored once the next chunk's loads
   // have been waited for (a store issued after those loads would hold them up)
   float4 go[4];
@@ -346,16 +390,32 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
     lds_barrier();  // the previous chunk is done with LDS
     // ---- the chunk's operands into LDS: x of both heads, B, C, G, z, parameters
     {
-      const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+      // x: the causal conv of this thread's 4 channels, tokens 4 rg .. 4 rg + 3
+      {
+        const int q = tid & 31, rg = tid >> 5;
+        const float4* cw = (const float4*)(sm + kSsdOCW) + 4 * q;
+        const float4 cw0 = cw[0], cw1 = cw[1], cw2 = cw[2], cw3 = cw[3];
+        const float4 cb = *(const float4*)(sm + kSsdOCB + 4 * q);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 4 * rg + r;
+          const float4 x0 = st.x[r], x1 = st.x[r + 1], x2 = st.x[r + 2], x3 = st.x[r + 3];
+          float4 o;
+          o.x = silu_f(conv4(cb.x, cw0.x, x0.x, cw0.y, x1.x, cw0.z, x2.x, cw0.w, x3.x));
+          o.y = silu_f(conv4(cb.y, cw1.x, x0.y, cw1.y, x1.y, cw1.z, x2.y, cw1.w, x3.y));
+          o.z = silu_f(conv4(cb.z, cw2.x, x0.z, cw2.y, x1.z, cw2.z, x2.z, cw2.w, x3.z));
+          o.w = silu_f(conv4(cb.w, cw3.x, x0.w, cw3.y, x1.w, cw3.z, x2.w, cw3.w, x3.w));
+          if (j >= Lc) o = make_float4(0.f, 0.f, 0.f, 0.f);
+          *(float4*)(sm + kSsdOX + j * kSsdCRow + 4 * q) = o;
+        }
+      }
+      // B and C (conv outputs from the chunk's record, zero past the end), z
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int idx = tid + 512 * k;
         const int j = idx >> 5, q = idx & 31;
-        const bool ok = j < Lc;
-        const float4 xv = ok ? st.x[k] : zero, bv = ok ? st.b[k] : zero, cv = ok ? st.c[k] : zero;
-        *(float4*)(sm + kSsdOX + j * kSsdCRow + 4 * q) = xv;
-        *(float4*)(sm + kSsdOB + j * kSsdCRow + 4 * q) = bv;
-        *(float4*)(sm + kSsdOC + j * kSsdCRow + 4 * q) = cv;
+        *(float4*)(sm + kSsdOB + j * kSsdCRow + 4 * q) = st.b[k];
+        *(float4*)(sm + kSsdOC + j * kSsdCRow + 4 * q) = st.c[k];
         *(float4*)(sm + kSsdOZ + j * kSsdCRow + 4 * q) = st.z[k];
       }
 #pragma unroll
@@ -371,8 +431,7 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
     }
     lds_barrier();
     if (c + 1 < nch)  // loaded while this chunk is computed
-      ssd_stage_load(a, hp, tid, row0 + kSsdL, min(kSsdL, a.T - t0 - kSsdL),
-                     a.gram + ((size_t)b * nch + c + 1) * recf, st);
+      ssd_stage_load(a, hp, tid, b, t0 + kSsdL, a.gram + ((size_t)b * nch + c + 1) * recf, st);
 
     // ---- (a) Y_inter^T[p][i] = exp(A_i) sum_n S_in[p][n] C[i][n], partial over this wave's 64 states, both position blocks
     v16f Y0 = (v16f){}, Y1 = (v16f){};
@@ -478,7 +537,8 @@ hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
     return hipGetLastError();
   }
   if (P == 64 && N == 128) {
-    if (!a.gram || a.H % 2) return hipErrorInvalidValue;
+    if (!a.gram || !a.conv_w || !a.conv_b || !a.conv_state || a.H % 2) return hipErrorInvalidValue;
+    if (a.x_off % 4 || a.ldzx % 4 || a.cdim % 4 || a.conv_bstride % 4) return hipErrorInvalidValue;
     static bool lds_set = false;
     if (!lds_set) {
       const hipError_t e = hipFuncSetAttribute((const void*)ssd_scan_kernel,
@@ -498,6 +558,8 @@ hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
+
+bool scan_takes_conv_inputs(int P, int N) { return P == 64 && N == 128; }
 
 bool scan_supported(int P, int N) {
   return (P == 64 && (N == 128 || N == 64 || N == 16)) || (P == 32 && (N == 16 || N == 128));
