@@ -676,6 +676,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
   const int nc = nok ? n : a.N - 1, mc = mok ? col : a.M - 1;
   const int K = a.K, ks = K / 4;              // k slice of this wave
   const int kbeg = wave * ks, kend = kbeg + ks;
+  // whole groups of scaffold words load 16 bytes at a time where every group start is 16-byte aligned
+  const bool wvec = K % (4 * 32 * 4) == 0;
   const int8_t* qrow = a.q + (size_t)mc * K + 16 * kg;
 
   // Operands of the epilogue (wave 0), loaded before the main loop so that
@@ -726,8 +728,20 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
       af[u] = *(const v4i*)(qrow + k);
       if (KIND == SK_HEAD)
         bf[u] = *(const v4i*)((const int8_t*)a.w + (size_t)nc * K + k + 16 * kg);
-      else
+      else if (!wvec || k0 + 32 * kSkinnyUnroll > kend)  // one word per k-step
         bw[u] = ((const uint32_t*)a.w)[(size_t)nc * (K / 32) + k / 32];
+    }
+    if (KIND != SK_HEAD && wvec && k0 + 32 * kSkinnyUnroll <= kend) {
+      // a whole group: the column's kSkinnyUnroll words are contiguous, four per 16-byte load
+      const uint4* wp = (const uint4*)((const uint32_t*)a.w + (size_t)nc * (K / 32) + k0 / 32);
+#pragma unroll
+      for (int v = 0; v < kSkinnyUnroll / 4; ++v) {
+        const uint4 w4 = wp[v];
+        bw[4 * v] = w4.x;
+        bw[4 * v + 1] = w4.y;
+        bw[4 * v + 2] = w4.z;
+        bw[4 * v + 3] = w4.w;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kSkinnyUnroll; ++u) {
