@@ -34,8 +34,8 @@ PAGES_B512_TOKS = 5081.0  # decode tokens/s at batch 512 (A100), the pages' only
 # (FETCH_SIZE reads 0.5 GiB for it: factor 2.0; WRITE_SIZE reads 1 GiB: 1.0).
 # Valid only for the kernel sources they were taken from (hash below).
 COUNTED_TRAFFIC = {
-    "sources_sha256": "39682a08697673e9fcc4107ec5d4d4abb855e1e51c0ba802b8d2468f35551ea2",
-    "fetch_bytes_per_token": 461174091,
+    "sources_sha256": "b68bd94ac8ac099661d2cbd6b2c0a4d0646b64e458d23916619ab4acd2180158",
+    "fetch_bytes_per_token": 461281474,
     "write_bytes_per_token": 118426844,
 }
 KERNEL_SOURCES = ("bit_quantized_mamba_amd/csrc/persistent.hip", "bit_quantized_mamba_amd/csrc/persistent.h",
