@@ -539,13 +539,10 @@ hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
   if (P == 64 && N == 128) {
     if (!a.gram || !a.conv_w || !a.conv_b || !a.conv_state || a.H % 2) return hipErrorInvalidValue;
     if (a.x_off % 4 || a.ldzx % 4 || a.cdim % 4 || a.conv_bstride % 4) return hipErrorInvalidValue;
-    static bool lds_set = false;
-    if (!lds_set) {
-      const hipError_t e = hipFuncSetAttribute((const void*)ssd_scan_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSsdLds);
-      if (e != hipSuccess) return e;
-      lds_set = true;
-    }
+    // set on every call: the limit is per device, and the call is a host-side table update
+    const hipError_t e = hipFuncSetAttribute((const void*)ssd_scan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kSsdLds);
+    if (e != hipSuccess) return e;
     const int nch = (a.T + kSsdL - 1) / kSsdL;
     hipLaunchKernelGGL(ssd_gram_kernel, dim3(nch, a.B), dim3(256), 0, st, a);
     hipLaunchKernelGGL(ssd_scan_kernel, dim3(a.H / 2, a.B), dim3(512), kSsdLds, st, a);
