@@ -267,6 +267,45 @@ def test_state_round_trip_resume():
     eng2.close()
 
 
+@pytest.mark.parametrize("shape", [synth.TINY, synth.FULL_1P3B])
+def test_degenerate_sizes(shape):
+    # an empty batch or prompt is an error that does no work, zero decode
+    # steps change nothing, and a one-token prefill is one decode step
+    from bit_quantized_mamba_amd import DfssmError
+    eng = engine(shape, max_batch=2)
+    eng.load_synthetic(synth.SEED_BASE)
+    toks = synth.gen_tokens(synth.SEED_BASE, 8, 4, shape.vocab).reshape(2, 2)
+    eng.reset_state(2)
+    eng.prefill(_i32(toks))
+    st0 = [eng.get_state(b) for b in range(2)]
+    empty = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    with pytest.raises(DfssmError):
+        eng.decode_step(empty)
+    with pytest.raises(DfssmError):
+        eng.generate(empty, 3)
+    with pytest.raises(DfssmError):
+        eng.prefill(torch.zeros((0, 4), dtype=torch.int32, device="cuda"))
+    with pytest.raises(DfssmError):
+        eng.prefill(torch.zeros((2, 0), dtype=torch.int32, device="cuda"))
+    t = _i32(toks[:, 1])
+    out = eng.generate(t, 0)
+    assert tuple(out.shape) == (0, 2) and torch.equal(t, _i32(toks[:, 1]))
+    for b in range(2):
+        st = eng.get_state(b)
+        assert np.array_equal(st[0], st0[b][0]) and np.array_equal(st[1], st0[b][1]), b
+    eng.reset_state(2)
+    lg_p, nx_p = eng.prefill(_i32(toks[:, :1]))
+    st_p = [eng.get_state(b) for b in range(2)]
+    eng.reset_state(2)
+    lg_d, nx_d = eng.decode_step(_i32(toks[:, 0]))
+    assert torch.equal(lg_p, lg_d) and torch.equal(nx_p, nx_d)
+    for b in range(2):
+        st = eng.get_state(b)
+        assert np.array_equal(st[0], st_p[b][0]) and np.array_equal(st[1], st_p[b][1]), b
+    eng.check()
+    eng.close()
+
+
 def test_errors_are_reported_without_work():
     from bit_quantized_mamba_amd import DfssmError
     s = synth.TINY
