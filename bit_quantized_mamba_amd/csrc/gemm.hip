@@ -644,6 +644,17 @@ hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st) {
   if (a.K % (2 * kG2KB) == 0) {
     const dim3 grid((a.N + kG2TN - 1) / kG2TN, (a.M + kG2TM - 1) / kG2TM), block(256);
     const size_t lds = 2 * (size_t)G2<kG2TN>::STAGE;
+    if ((size_t)grid.x * grid.y <= 512) {
+      // few tiles (a batch of decode tokens): half-width tiles of 2 x 2 waves
+      // give the launch twice the workgroups
+      const dim3 g64((a.N + 63) / 64, grid.y);
+      const size_t lds64 = 2 * (size_t)G2<64>::STAGE;
+      if (epi == GEMM_EPI_RESIDUAL)
+        hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_RESIDUAL, 64, 2, kG2OCC>), g64, block, lds64, st, a);
+      else
+        hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_STORE, 64, 2, kG2OCC>), g64, block, lds64, st, a);
+      return hipGetLastError();
+    }
     if (epi == GEMM_EPI_RESIDUAL)
       hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_RESIDUAL, kG2TN, kG2WR, kG2OCC>), grid, block, lds, st, a);
     else
