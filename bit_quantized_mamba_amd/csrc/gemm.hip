@@ -230,8 +230,66 @@ __global__ __launch_bounds__(256) void rows_quant_row_kernel(RowsArgs a) {
   }
 }
 
+// LoRA down of many rows on the matrix cores: t[m][r] = float(sum_k A[r][k]
+// q[m][k]) * sA[r] * s[m], the same products as the row quantiser's (the
+// integer sum is exact, so either kernel gives the same t).  Workgroup = 32
+// rows, the four waves take a quarter of K each and sum through LDS; the 16
+// ranks are the first 16 of the 32 MFMA columns (the rest read rank 15 and are
+// zeroed).  Operands go straight from memory into MFMA registers: lane l holds
+// row / rank l % 32 and k-half l / 32 of each 32-wide k-step.
+constexpr int kLoraUnroll = 8;
+
+__global__ __launch_bounds__(256) void lora_down_kernel(RowsArgs a, int K) {
+  __shared__ int red[3][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, kg = lane >> 5;
+  const int m0 = blockIdx.x * 32;
+  const int mc = min(m0 + col, a.M - 1), rc = min(col, 15);
+  const int ks = K / 4, kbeg = wave * ks, kend = kbeg + ks;
+  const int8_t* qrow = a.q + (size_t)mc * K + 16 * kg;
+  const int8_t* arow = a.A + (size_t)rc * K + 16 * kg;
+  v16i acc = (v16i){};
+  for (int k0 = kbeg; k0 < kend; k0 += 32 * kLoraUnroll) {
+    v4i af[kLoraUnroll], bf[kLoraUnroll];
+#pragma unroll
+    for (int u = 0; u < kLoraUnroll; ++u) {
+      af[u] = *(const v4i*)(qrow + k0 + 32 * u);
+      bf[u] = *(const v4i*)(arow + k0 + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < kLoraUnroll; ++u) {
+      if (col >= 16) bf[u] = (v4i){};
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[u], bf[u], acc, 0, 0, 0);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave - 1][r][lane] = acc[r];
+  }
+  __syncthreads();
+  if (wave > 0 || col >= 16) return;
+  const float sa = a.sA[col];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + 8 * (r >> 2) + 4 * kg + (r & 3);
+    const int v = acc[r] + red[0][r][lane] + red[1][r][lane] + red[2][r][lane];
+    if (m < a.M) a.t[(size_t)m * 16 + col] = (float)v * sa * a.s[m];
+  }
+}
+
 hipError_t launch_rows_quant(const RowsArgs& a, int K, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
+  if (a.A && a.M >= 4096 && K % 1024 == 0 && K <= 8192) {
+    // many rows: quantise without the LoRA down, then the LoRA down on the
+    // matrix cores (the quantiser would re-read the 16 rows of A from L2 for
+    // every row)
+    RowsArgs r = a;
+    r.A = nullptr;
+    hipError_t e = launch_rows_quant(r, K, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lora_down_kernel, dim3((a.M + 31) / 32), dim3(256), 0, st, a, K);
+    return hipGetLastError();
+  }
   const dim3 grid((a.M + 3) / 4), block(256);
   switch (K) {
     case 2048: hipLaunchKernelGGL(rows_quant_row_kernel<2048>, dim3(a.M), block, 0, st, a); return hipGetLastError();
