@@ -271,20 +271,36 @@ __global__ __launch_bounds__(256) void ssd_gram_kernel(ScanArgs a) {
   // A_j (running sum of -dt exp(A_log)), dt_j, w_j = exp(A_{L-1} - A_j) dt_j, exp(A_j)
   float* par = rec + kSsdL * kSsdL;
   const size_t rj = row0 + min(lane, Lc - 1);
-  for (int h = wave; h < a.H; h += 4) {
-    const float dt = lane < Lc ? softplus_f(a.zx[rj * a.ldzx + a.dt_off + h] + a.dt_bias[h]) : 0.0f;
-    float cum = -dt * __expf(a.A_log[h]);
+  // the inputs of kHB heads are loaded together (one memory latency per
+  // batch instead of one per head); heads past H read head H - 1, unused
+  constexpr int kHB = 8;
+  for (int h0 = wave; h0 < a.H; h0 += 4 * kHB) {
+    float raw[kHB], bias[kHB], alog[kHB];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float o = __shfl_up(cum, d);
-      if (lane >= d) cum += o;
+    for (int i = 0; i < kHB; ++i) {
+      const int h = min(h0 + 4 * i, a.H - 1);
+      raw[i] = a.zx[rj * a.ldzx + a.dt_off + h];
+      bias[i] = a.dt_bias[h];
+      alog[i] = a.A_log[h];
     }
-    const float end = __shfl(cum, 63);
-    float* ph = par + h * 256;
-    ph[lane] = cum;
-    ph[64 + lane] = dt;
-    ph[128 + lane] = __expf(end - cum) * dt;
-    ph[192 + lane] = __expf(cum);
+#pragma unroll
+    for (int i = 0; i < kHB; ++i) {
+      const int h = h0 + 4 * i;
+      if (h >= a.H) break;
+      const float dt = lane < Lc ? softplus_f(raw[i] + bias[i]) : 0.0f;
+      float cum = -dt * __expf(alog[i]);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_up(cum, d);
+        if (lane >= d) cum += o;
+      }
+      const float end = __shfl(cum, 63);
+      float* ph = par + h * 256;
+      ph[lane] = cum;
+      ph[64 + lane] = dt;
+      ph[128 + lane] = __expf(end - cum) * dt;
+      ph[192 + lane] = __expf(cum);
+    }
   }
 }
 
