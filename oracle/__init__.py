@@ -42,17 +42,20 @@ def lib() -> ctypes.CDLL:
         L.or_scaffold_acc.restype = _i
         L.or_proj.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _p, ctypes.c_float, _p, _p, _p]
         L.or_proj.restype = _i
+        L.or_unpack_signs.argtypes = [_p, _i, _i, _p]
+        L.or_sign_acc.argtypes = [_p, _i, _i, _p, _p]
+        L.or_sign_acc.restype = _i
         L.or_conv_step.argtypes = [_p, _p, _p, _i, _i, _p, _p]
         L.or_ssm_step.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p]
         L.or_gated_rmsnorm.argtypes = [_p, _p, _p, _i, _p]
         L.or_layer_step.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]
         L.or_layer_step.restype = _i
-        L.or_quant_forced.argtypes = [_p, _i, _p, ctypes.c_double, _p, _p]
+        L.or_quant_forced.argtypes = [_p, _i, _p, ctypes.c_double, _p, _p, _p]
         L.or_quant_forced.restype = _i
         L.or_layer_step_forced.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_double,
-                                           _p]
+                                           _p, _p]
         L.or_layer_step_forced.restype = _i
-        L.or_lm_head_forced.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_double, _p]
+        L.or_lm_head_forced.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_double, _p, _p]
         L.or_lm_head_forced.restype = _i
         L.or_lm_head.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p]
         L.or_lm_head.restype = _i
@@ -113,17 +116,19 @@ def quant(u) -> Tuple[np.ndarray, np.float32]:
 TIE_BAND = 1e-3
 
 
-def quant_forced(u, force, delta: float = TIE_BAND) -> Tuple[np.ndarray, np.float32, int]:
+def quant_forced(u, force, delta: float = TIE_BAND) -> Tuple[np.ndarray, np.float32, int, int]:
     """Quantise u (fp64) taking the proposed codes where they are valid roundings.
 
-    Returns (q, s, number of rejected proposals)."""
+    Returns (q, s, number of rejected proposals, number of accepted proposals
+    that differ from the oracle's own code)."""
     u = _c(u, np.float64)
     force = _c(force, np.int8)
     assert force.size == u.size
     q = np.empty(u.size, dtype=np.int8)
     s = np.zeros(1, dtype=np.float32)
-    bad = lib().or_quant_forced(_ptr(u), u.size, _ptr(force), float(delta), _ptr(q), _ptr(s))
-    return q, s[0], bad
+    fl = np.zeros(1, dtype=np.int32)
+    bad = lib().or_quant_forced(_ptr(u), u.size, _ptr(force), float(delta), _ptr(q), _ptr(s), _ptr(fl))
+    return q, s[0], bad, int(fl[0])
 
 
 def rmsnorm(x, w) -> np.ndarray:
@@ -143,6 +148,27 @@ def scaffold_acc(bits, q) -> np.ndarray:
     rc = lib().or_scaffold_acc(_ptr(bits), d_out, q.size, _ptr(q), _ptr(acc))
     if rc != 0:
         raise OverflowError("scaffold accumulator exceeds int32")
+    return acc
+
+
+def unpack_signs(bits, d_in: int) -> np.ndarray:
+    """The scaffold as a dense int8 sign matrix [d_out][d_in] (+1 where the bit is set)."""
+    bits = _c(bits, np.uint32)
+    d_out = bits.shape[0]
+    assert bits.size == d_out * (d_in // 32)
+    out = np.empty((d_out, d_in), dtype=np.int8)
+    lib().or_unpack_signs(_ptr(bits), d_out, d_in, _ptr(out))
+    return out
+
+
+def sign_acc(signs, q) -> np.ndarray:
+    """Scaffold sums from an unpacked sign matrix (the same integers as scaffold_acc)."""
+    signs = _c(signs, np.int8)
+    q = _c(q, np.int8)
+    d_out, d_in = signs.shape
+    acc = np.empty(d_out, dtype=np.int32)
+    if lib().or_sign_acc(_ptr(signs), d_out, d_in, _ptr(q), _ptr(acc)) != 0:
+        raise OverflowError("d_in too large for int32 row sums")
     return acc
 
 
@@ -205,12 +231,34 @@ def gated_rmsnorm(y, z, w) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
-def _layer_ptr_array(layer: Dict[str, np.ndarray], keep: List[np.ndarray]):
-    arr = (ctypes.c_void_p * len(LAYER_KINDS))()
-    for j, k in enumerate(LAYER_KINDS):
+# A layer's pointer array: the 19 tensors in LAYER_KINDS order, then the
+# optional unpacked sign matrices of the two scaffolds (None -> the oracle
+# reads the bits).
+SIGN_KINDS = ["in_signs", "out_signs"]
+LW_STRIDE = len(LAYER_KINDS) + len(SIGN_KINDS)
+
+
+def with_signs(s: Shape, layer: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    """A copy of a layer's weights with its scaffolds also unpacked to sign matrices."""
+    d = dict(layer)
+    d["in_signs"] = unpack_signs(layer["in_bits"], s.d_model)
+    d["out_signs"] = unpack_signs(layer["out_bits"], s.d_inner)
+    return d
+
+
+def _fill_layer_ptrs(arr, base: int, layer: Dict[str, np.ndarray], keep: List[np.ndarray]) -> None:
+    for j, k in enumerate(LAYER_KINDS + SIGN_KINDS):
+        if layer.get(k) is None:
+            arr[base + j] = None
+            continue
         a = np.ascontiguousarray(layer[k])
         keep.append(a)
-        arr[j] = a.ctypes.data
+        arr[base + j] = a.ctypes.data
+
+
+def _layer_ptr_array(layer: Dict[str, np.ndarray], keep: List[np.ndarray]):
+    arr = (ctypes.c_void_p * LW_STRIDE)()
+    _fill_layer_ptrs(arr, 0, layer, keep)
     return arr
 
 
@@ -243,12 +291,21 @@ class ForcedCodeError(AssertionError):
     """A proposed int8 code is not a correct rounding of the oracle's value."""
 
 
+def _count(stats: Optional[Dict[str, int]], flips: int, codes: int) -> None:
+    if stats is not None:
+        stats["flips"] = stats.get("flips", 0) + int(flips)
+        stats["codes"] = stats.get("codes", 0) + int(codes)
+
+
 def layer_step(s: Shape, layer: Dict[str, np.ndarray], h_in, conv_state: np.ndarray, ssm_state: np.ndarray,
-               want_dbg: bool = False, q1_force=None, q2_force=None, delta: float = TIE_BAND):
+               want_dbg: bool = False, q1_force=None, q2_force=None, delta: float = TIE_BAND,
+               stats: Optional[Dict[str, int]] = None):
     """One layer, one token. conv_state [conv_dim][K-1] and ssm_state [H][P][N] (fp64) update in place.
 
     q1_force / q2_force (optional int8 codes) are taken where they are correct
     roundings (see quant_forced); any other proposal raises ForcedCodeError.
+    stats (optional dict) accumulates "flips", the proposed codes taken that
+    differ from the oracle's own, and "codes", the proposed codes seen.
     Returns h_out, or (h_out, dbg dict) with the intermediate vectors and the
     int8 activations (q1, s1, q2, s2) when want_dbg is set.
     """
@@ -274,13 +331,15 @@ def layer_step(s: Shape, layer: Dict[str, np.ndarray], h_in, conv_state: np.ndar
     if f2 is not None:
         assert f2.size == s.d_inner
     rej = np.zeros(1, dtype=np.int32)
+    fl = np.zeros(1, dtype=np.int32)
     rc = lib().or_layer_step_forced(_ptr(sh), lw, _ptr(h_in), _ptr(conv_state), _ptr(ssm_state), _ptr(h_out),
                                     _ptr(dbg), _ptr(q1), _ptr(s1), _ptr(q2), _ptr(s2), _ptr(f1), _ptr(f2),
-                                    float(delta), _ptr(rej))
+                                    float(delta), _ptr(rej), _ptr(fl))
     if rc != 0:
         raise OverflowError("integer accumulator overflow")
     if rej[0]:
         raise ForcedCodeError(f"{int(rej[0])} proposed int8 codes are not correct roundings")
+    _count(stats, fl[0], (0 if f1 is None else f1.size) + (0 if f2 is None else f2.size))
     if not want_dbg:
         return h_out
     d = {k: dbg[a:b].copy() for k, (a, b) in lay.items() if k != "_total"}
@@ -289,21 +348,23 @@ def layer_step(s: Shape, layer: Dict[str, np.ndarray], h_in, conv_state: np.ndar
 
 
 class Model:
-    """A whole stack's weights held for the oracle (canonical layouts)."""
+    """A whole stack's weights held for the oracle (canonical layouts).
 
-    def __init__(self, s: Shape, weights: Dict[str, object]):
+    With signs (the default) each layer's scaffolds are also held unpacked as
+    int8 sign matrices, which the oracle then reads instead of the bits (the
+    same integer sums, several times faster); self.weights["layers"] are those
+    layer dicts, for oracle.layer_step."""
+
+    def __init__(self, s: Shape, weights: Dict[str, object], signs: bool = True):
         self.s = s
         self._keep: List[np.ndarray] = []
-        n = s.n_layer * len(LAYER_KINDS) + len(GLOBAL_KINDS)
+        layers = [with_signs(s, lay) if signs else dict(lay) for lay in weights["layers"]]
+        weights = dict(weights, layers=layers)
+        n = s.n_layer * LW_STRIDE + len(GLOBAL_KINDS)
         self._ptrs = (ctypes.c_void_p * n)()
-        j = 0
         for l in range(s.n_layer):
-            layer = weights["layers"][l]
-            for k in LAYER_KINDS:
-                a = np.ascontiguousarray(layer[k])
-                self._keep.append(a)
-                self._ptrs[j] = a.ctypes.data
-                j += 1
+            _fill_layer_ptrs(self._ptrs, l * LW_STRIDE, layers[l], self._keep)
+        j = s.n_layer * LW_STRIDE
         for k in GLOBAL_KINDS:
             a = np.ascontiguousarray(weights[k])
             self._keep.append(a)
@@ -333,8 +394,10 @@ class Model:
             raise ValueError("token out of range or accumulator overflow")
         return nxt, logits
 
-    def lm_head(self, h, qf_force=None, delta: float = TIE_BAND):
-        """Final norm + tied int8 LM head. Returns (argmax, logits, qf, sf)."""
+    def lm_head(self, h, qf_force=None, delta: float = TIE_BAND, stats: Optional[Dict[str, int]] = None):
+        """Final norm + tied int8 LM head. Returns (argmax, logits, qf, sf).
+
+        qf_force and stats as for layer_step."""
         s = self.s
         h = _c(h, np.float64)
         logits = np.empty(s.vocab, dtype=np.float64)
@@ -345,11 +408,13 @@ class Model:
         fn = self.weights["final_norm"]
         ff = None if qf_force is None else _c(qf_force, np.int8)
         rej = np.zeros(1, dtype=np.int32)
+        fl = np.zeros(1, dtype=np.int32)
         best = lib().or_lm_head_forced(_ptr(self._sh), _ptr(np.ascontiguousarray(E)), _ptr(np.ascontiguousarray(sE)),
                                        _ptr(np.ascontiguousarray(fn)), _ptr(h), _ptr(logits), _ptr(qf), _ptr(sf),
-                                       _ptr(ff), float(delta), _ptr(rej))
+                                       _ptr(ff), float(delta), _ptr(rej), _ptr(fl))
         if rej[0]:
             raise ForcedCodeError(f"{int(rej[0])} proposed int8 codes are not correct roundings")
+        _count(stats, fl[0], 0 if ff is None else ff.size)
         return best, logits, qf, sf[0]
 
     def embed(self, tok: int) -> np.ndarray:

@@ -49,7 +49,13 @@ enum {
   T_OUT_BITS, T_OUT_SW, T_OUT_A, T_OUT_SA, T_OUT_B, T_OUT_SB,
   T_CONV_W, T_CONV_B, T_A_LOG, T_DT_BIAS, T_D, T_NORM_W, T_GNORM_W, T_PER_LAYER
 };
-/* global tensors follow the n_layer * T_PER_LAYER layer pointers */
+/* A layer's pointer array: the T_PER_LAYER tensors above, then two optional
+ * (nullable) pre-unpacked sign matrices of the scaffolds (or_unpack_signs),
+ * int8 [d_in_proj][d_model] and [d_model][d_inner].  When present, the
+ * scaffold sums read the signs from them instead of from the bits; the sums
+ * are the same integers either way.                                         */
+enum { T_IN_SIGNS = T_PER_LAYER, T_OUT_SIGNS, LW_STRIDE };
+/* global tensors follow the n_layer * LW_STRIDE layer pointers */
 enum { G_E = 0, G_SE, G_FNORM };
 
 static double silu(double v) { return v / (1.0 + exp(-v)); }
@@ -96,12 +102,15 @@ void or_quant(const double* u, int n, int8_t* q, float* s_out) {
  * is taken only if it equals the oracle's own code, or differs from it by
  * one with the oracle's scaled value within `delta` of the tie between the
  * two.  Returns the number of proposed codes that were rejected (then q holds
- * the oracle's own codes).                                                   */
-int or_quant_forced(const double* u, int n, const int8_t* force, double delta, int8_t* q, float* s_out) {
+ * the oracle's own codes).  *flipped (nullable) receives the number of
+ * proposed codes that were taken although they differ from the oracle's own
+ * (0 when any proposal was rejected).                                        */
+int or_quant_forced(const double* u, int n, const int8_t* force, double delta, int8_t* q, float* s_out,
+                    int* flipped) {
   float* uf = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
   for (int i = 0; i < n; ++i) uf[i] = (float)u[i];
   or_quant_f32(uf, n, q, s_out);
-  int bad = 0;
+  int bad = 0, flips = 0;
   if (force && *s_out > 0.0f) {
     float amax = 0.0f;
     for (int i = 0; i < n; ++i) if (fabsf(uf[i]) > amax) amax = fabsf(uf[i]);
@@ -111,14 +120,22 @@ int or_quant_forced(const double* u, int n, const int8_t* force, double delta, i
       const int d = (int)force[i] - (int)q[i];
       const double x = (double)(uf[i] * inv);
       const double tie = (double)q[i] + 0.5 * d;
-      if ((d == 1 || d == -1) && fabs(x - tie) <= delta) q[i] = force[i];
-      else ++bad;
+      if ((d == 1 || d == -1) && fabs(x - tie) <= delta) {
+        q[i] = force[i];
+        ++flips;
+      } else {
+        ++bad;
+      }
     }
-    if (bad) or_quant_f32(uf, n, q, s_out);
+    if (bad) {
+      or_quant_f32(uf, n, q, s_out);
+      flips = 0;
+    }
   } else if (force) {
     for (int i = 0; i < n; ++i) bad += force[i] != 0;
   }
   free(uf);
+  if (flipped) *flipped = flips;
   return bad;
 }
 
@@ -153,6 +170,31 @@ int or_scaffold_acc(const uint32_t* bits, int d_out, int d_in, const int8_t* q, 
   return bad ? -1 : 0;
 }
 
+/* The scaffold as a dense sign matrix: signs[o][i] = +1 where bit (i mod 32)
+ * of word bits[o][i/32] is set, -1 otherwise (the layout read above). */
+void or_unpack_signs(const uint32_t* bits, int d_out, int d_in, int8_t* signs) {
+  const int words = d_in / 32;
+#pragma omp parallel for schedule(static)
+  for (int o = 0; o < d_out; ++o)
+    for (int i = 0; i < d_in; ++i)
+      signs[(size_t)o * d_in + i] = ((bits[(size_t)o * words + (i >> 5)] >> (i & 31)) & 1u) ? 1 : -1;
+}
+
+/* acc[o] = sum_i signs[o][i] q_i, the same integer as or_scaffold_acc on the
+ * bits the signs came from.  Row sums fit int32 for d_in <= 131072
+ * (131072 * 127 < 2^31), which is checked.                                   */
+int or_sign_acc(const int8_t* signs, int d_out, int d_in, const int8_t* q, int32_t* acc) {
+  if (d_in > 131072) return -1;
+#pragma omp parallel for schedule(static)
+  for (int o = 0; o < d_out; ++o) {
+    const int8_t* row = signs + (size_t)o * d_in;
+    int32_t a = 0;
+    for (int i = 0; i < d_in; ++i) a += (int32_t)row[i] * (int32_t)q[i];
+    acc[o] = a;
+  }
+  return 0;
+}
+
 /* int8 matrix-vector product: out[r] = sum_c M[r][c] v[c] (exact). */
 static void int8_matvec(const int8_t* M, int rows, int cols, const int8_t* v, int64_t* out) {
 #pragma omp parallel for schedule(static) if (rows >= 4096)
@@ -171,13 +213,24 @@ static void int8_matvec(const int8_t* M, int rows, int cols, const int8_t* v, in
  *   yl[o] = sB[o] * sum_k B[o][k] t[k]                 (B: d_out x r)
  *   y[o]  = ys[o] + yl[o]
  * acc_out / ta_out (nullable) receive the exact integer sums.              */
+int or_proj_signs(const uint32_t* bits, const int8_t* signs, const float* sw, const int8_t* A, const float* sA,
+                  const int8_t* B, const float* sB, int d_in, int d_out, int r,
+                  const int8_t* q, float s, double* y, int32_t* acc_out, int64_t* ta_out);
 int or_proj(const uint32_t* bits, const float* sw, const int8_t* A, const float* sA,
             const int8_t* B, const float* sB, int d_in, int d_out, int r,
             const int8_t* q, float s, double* y, int32_t* acc_out, int64_t* ta_out) {
+  return or_proj_signs(bits, NULL, sw, A, sA, B, sB, d_in, d_out, r, q, s, y, acc_out, ta_out);
+}
+
+/* or_proj with the scaffold optionally given as its unpacked sign matrix
+ * (signs nullable; the bits are used when it is NULL).                      */
+int or_proj_signs(const uint32_t* bits, const int8_t* signs, const float* sw, const int8_t* A, const float* sA,
+                  const int8_t* B, const float* sB, int d_in, int d_out, int r,
+                  const int8_t* q, float s, double* y, int32_t* acc_out, int64_t* ta_out) {
   int32_t* acc = (int32_t*)malloc(sizeof(int32_t) * (size_t)d_out);
   int64_t* ta = (int64_t*)malloc(sizeof(int64_t) * (size_t)r);
   double* t = (double*)malloc(sizeof(double) * (size_t)r);
-  int rc = or_scaffold_acc(bits, d_out, d_in, q, acc);
+  int rc = signs ? or_sign_acc(signs, d_out, d_in, q, acc) : or_scaffold_acc(bits, d_out, d_in, q, acc);
   int8_matvec(A, r, d_in, q, ta);
   for (int k = 0; k < r; ++k) t[k] = (double)ta[k] * (double)sA[k] * (double)s;
 #pragma omp parallel for schedule(static) if (d_out >= 4096)
@@ -257,7 +310,8 @@ void or_gated_rmsnorm(const double* y, const double* z, const float* w, int n, d
 int or_layer_step_forced(const int* sh, const void* const* lw, const double* h_in,
                          double* conv_state, double* ssm_state, double* h_out, double* dbg,
                          int8_t* q1_out, float* s1_out, int8_t* q2_out, float* s2_out,
-                         const int8_t* q1_force, const int8_t* q2_force, double delta, int* rejected) {
+                         const int8_t* q1_force, const int8_t* q2_force, double delta, int* rejected,
+                         int* flipped) {
   const int dm = sh[SH_DM], di = sh[SH_DI], ds = sh[SH_DS], hd = sh[SH_HD], K = sh[SH_K], r = sh[SH_R];
   const int H = di / hd, cdim = di + 2 * ds, dproj = 2 * di + 2 * ds + H;
   double* u = (double*)malloc(sizeof(double) * (size_t)dm);
@@ -272,10 +326,11 @@ int or_layer_step_forced(const int* sh, const void* const* lw, const double* h_i
   float s1, s2;
   int rc = 0;
 
-  int rej = 0;
+  int rej = 0, fl1 = 0, fl2 = 0;
   or_rmsnorm(h_in, (const float*)lw[T_NORM_W], dm, u);
-  rej += or_quant_forced(u, dm, q1_force, delta, q1, &s1);
-  rc |= or_proj((const uint32_t*)lw[T_IN_BITS], (const float*)lw[T_IN_SW], (const int8_t*)lw[T_IN_A],
+  rej += or_quant_forced(u, dm, q1_force, delta, q1, &s1, &fl1);
+  rc |= or_proj_signs((const uint32_t*)lw[T_IN_BITS], (const int8_t*)lw[T_IN_SIGNS], (const float*)lw[T_IN_SW],
+                (const int8_t*)lw[T_IN_A],
                 (const float*)lw[T_IN_SA], (const int8_t*)lw[T_IN_B], (const float*)lw[T_IN_SB],
                 dm, dproj, r, q1, s1, zx, NULL, NULL);
   const double* z = zx;
@@ -285,9 +340,11 @@ int or_layer_step_forced(const int* sh, const void* const* lw, const double* h_i
   or_ssm_step(xc, xc + di, xc + di + ds, dt_raw, (const float*)lw[T_A_LOG], (const float*)lw[T_DT_BIAS],
               (const float*)lw[T_D], H, hd, ds, ssm_state, y, dt);
   or_gated_rmsnorm(y, z, (const float*)lw[T_GNORM_W], di, u2);
-  rej += or_quant_forced(u2, di, q2_force, delta, q2, &s2);
+  rej += or_quant_forced(u2, di, q2_force, delta, q2, &s2, &fl2);
   if (rejected) *rejected = rej;
-  rc |= or_proj((const uint32_t*)lw[T_OUT_BITS], (const float*)lw[T_OUT_SW], (const int8_t*)lw[T_OUT_A],
+  if (flipped) *flipped = fl1 + fl2;
+  rc |= or_proj_signs((const uint32_t*)lw[T_OUT_BITS], (const int8_t*)lw[T_OUT_SIGNS], (const float*)lw[T_OUT_SW],
+                (const int8_t*)lw[T_OUT_A],
                 (const float*)lw[T_OUT_SA], (const int8_t*)lw[T_OUT_B], (const float*)lw[T_OUT_SB],
                 di, dm, r, q2, s2, out, NULL, NULL);
   for (int i = 0; i < dm; ++i) h_out[i] = h_in[i] + out[i];
@@ -313,7 +370,7 @@ int or_layer_step(const int* sh, const void* const* lw, const double* h_in,
                   double* conv_state, double* ssm_state, double* h_out, double* dbg,
                   int8_t* q1_out, float* s1_out, int8_t* q2_out, float* s2_out) {
   return or_layer_step_forced(sh, lw, h_in, conv_state, ssm_state, h_out, dbg, q1_out, s1_out, q2_out, s2_out,
-                              NULL, NULL, 0.0, NULL);
+                              NULL, NULL, 0.0, NULL, NULL);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -323,14 +380,14 @@ int or_layer_step(const int* sh, const void* const* lw, const double* h_in,
  *   index on ties.                                                          */
 int or_lm_head_forced(const int* sh, const int8_t* E, const float* sE, const float* fnorm,
                       const double* h, double* logits, int8_t* qf_out, float* sf_out,
-                      const int8_t* qf_force, double delta, int* rejected) {
+                      const int8_t* qf_force, double delta, int* rejected, int* flipped) {
   const int dm = sh[SH_DM], V = sh[SH_V];
   double* u = (double*)malloc(sizeof(double) * (size_t)dm);
   int8_t* qf = (int8_t*)malloc((size_t)dm);
   int64_t* acc = (int64_t*)malloc(sizeof(int64_t) * (size_t)V);
   float sf;
   or_rmsnorm(h, fnorm, dm, u);
-  int rej = or_quant_forced(u, dm, qf_force, delta, qf, &sf);
+  int rej = or_quant_forced(u, dm, qf_force, delta, qf, &sf, flipped);
   if (rejected) *rejected = rej;
   int8_matvec(E, V, dm, qf, acc);
   int best = 0;
@@ -346,7 +403,7 @@ int or_lm_head_forced(const int* sh, const int8_t* E, const float* sE, const flo
 
 int or_lm_head(const int* sh, const int8_t* E, const float* sE, const float* fnorm,
                const double* h, double* logits, int8_t* qf_out, float* sf_out) {
-  return or_lm_head_forced(sh, E, sE, fnorm, h, logits, qf_out, sf_out, NULL, 0.0, NULL);
+  return or_lm_head_forced(sh, E, sE, fnorm, h, logits, qf_out, sf_out, NULL, 0.0, NULL, NULL);
 }
 
 /* Embedding lookup with the tied table: h[i] = E[tok][i] * sE[tok]. */
@@ -356,7 +413,8 @@ void or_embed(const int* sh, const int8_t* E, const float* sE, int tok, double* 
 }
 
 /* One decode step of one sequence through the whole stack.
- * w: n_layer * 19 layer pointers, then E, sE, final_norm.
+ * w: n_layer * LW_STRIDE layer pointers (19 tensors, 2 optional sign
+ * matrices), then E, sE, final_norm.
  * conv: [n_layer][conv_dim][K-1], ssm: [n_layer][H][P][N] (fp64, updated).
  * logits (nullable): [V]; h_trace (nullable): [(n_layer + 1)][d_model], the
  * residual stream entering each layer and after the last one.
@@ -368,14 +426,14 @@ int or_decode_step(const int* sh, const void* const* w, double* conv, double* ss
   const int K = sh[SH_K], V = sh[SH_V];
   const int H = di / hd, cdim = di + 2 * ds;
   if (tok < 0 || tok >= V) return -2;
-  const void* const* g = w + (size_t)nl * T_PER_LAYER;
+  const void* const* g = w + (size_t)nl * LW_STRIDE;
   double* h = (double*)malloc(sizeof(double) * (size_t)dm);
   double* h2 = (double*)malloc(sizeof(double) * (size_t)dm);
   int rc = 0;
   or_embed(sh, (const int8_t*)g[G_E], (const float*)g[G_SE], tok, h);
   for (int l = 0; l < nl; ++l) {
     if (h_trace) memcpy(h_trace + (size_t)l * dm, h, sizeof(double) * (size_t)dm);
-    rc |= or_layer_step(sh, w + (size_t)l * T_PER_LAYER, h,
+    rc |= or_layer_step(sh, w + (size_t)l * LW_STRIDE, h,
                         conv + (size_t)l * cdim * (K - 1), ssm + (size_t)l * H * hd * ds,
                         h2, NULL, NULL, NULL, NULL, NULL);
     double* t = h; h = h2; h2 = t;

@@ -578,14 +578,17 @@ def test_quant_forced_accepts_only_tie_neighbours():
     q, s = oracle.quant(u)
     assert q.tolist() == [127, 3, 3, -5, 0]
     # proposing the other side of each near-tie is accepted
-    qf, sf, bad = oracle.quant_forced(u, np.array([127, 2, 3, -4, 0], dtype=np.int8))
-    assert bad == 0 and qf.tolist() == [127, 2, 3, -4, 0] and sf == s
+    qf, sf, bad, flips = oracle.quant_forced(u, np.array([127, 2, 3, -4, 0], dtype=np.int8))
+    assert bad == 0 and flips == 2 and qf.tolist() == [127, 2, 3, -4, 0] and sf == s
+    # the oracle's own codes are taken with no flip counted
+    qf, _, bad, flips = oracle.quant_forced(u, q)
+    assert bad == 0 and flips == 0 and np.array_equal(qf, q)
     # a code off by one away from any tie, or off by two, is rejected
     for prop in ([127, 3, 2, -5, 0], [127, 3, 3, -5, 1], [127, 1, 3, -5, 0]):
-        qf, _, bad = oracle.quant_forced(u, np.array(prop, dtype=np.int8))
-        assert bad == 1 and np.array_equal(qf, q)
+        qf, _, bad, flips = oracle.quant_forced(u, np.array(prop, dtype=np.int8))
+        assert bad == 1 and flips == 0 and np.array_equal(qf, q)
     # outside the band the tie neighbour is rejected as well
-    qf, _, bad = oracle.quant_forced(np.array([127.0, 2.5 + 5e-3]), np.array([127, 2], dtype=np.int8))
+    qf, _, bad, _ = oracle.quant_forced(np.array([127.0, 2.5 + 5e-3]), np.array([127, 2], dtype=np.int8))
     assert bad == 1
 
 
@@ -595,9 +598,41 @@ def test_layer_forced_codes_equal_to_own_codes_change_nothing():
     cs1, ss1 = _zero_state(S_T)
     cs2, ss2 = _zero_state(S_T)
     o1, d = oracle.layer_step(S_T, lay, h, cs1, ss1, want_dbg=True)
-    o2 = oracle.layer_step(S_T, lay, h, cs2, ss2, q1_force=d["q1"], q2_force=d["q2"])
+    stats = {}
+    o2 = oracle.layer_step(S_T, lay, h, cs2, ss2, q1_force=d["q1"], q2_force=d["q2"], stats=stats)
     assert np.array_equal(o1, o2) and np.array_equal(ss1, ss2)
+    assert stats == {"flips": 0, "codes": S_T.d_model + S_T.d_inner}
     bad = d["q1"].copy()
     bad[0] = np.clip(int(bad[0]) + 2, -127, 127) if abs(int(bad[0])) < 120 else int(bad[0]) - 2
     with pytest.raises(oracle.ForcedCodeError):
         oracle.layer_step(S_T, lay, h, *_zero_state(S_T), q1_force=bad)
+
+
+# ---------------------------------------------------------------------------
+# the unpacked sign matrix (a faster route to the same scaffold sums)
+# ---------------------------------------------------------------------------
+
+def test_unpacked_signs_match_bit_layout():
+    bits = RNG.integers(0, 2**32, size=(37, 8), dtype=np.uint64).astype(np.uint32)
+    sg = oracle.unpack_signs(bits, 256)
+    want = np.where(np.unpackbits(bits.view(np.uint8), bitorder="little").reshape(37, 256), 1, -1)
+    assert np.array_equal(sg, want)
+    q = RNG.integers(-127, 128, size=256).astype(np.int8)
+    assert np.array_equal(oracle.sign_acc(sg, q), oracle.scaffold_acc(bits, q))
+    # extreme codes: every row at its int32-safe extreme
+    q = np.full(256, -127, np.int8)
+    assert np.array_equal(oracle.sign_acc(sg, q), oracle.scaffold_acc(bits, q))
+
+
+def test_layer_step_with_signs_is_bit_identical():
+    s = synth.TINY
+    lay = synth.gen_layer(s, synth.SEED_BASE + 31, 1)
+    lays = oracle.with_signs(s, lay)
+    h = synth.gen_fp16_normal(synth.SEED_BASE + 31, 2, s.d_model).astype(np.float64)
+    a = [np.zeros((s.conv_dim, s.d_conv - 1)), np.zeros((s.n_heads, s.headdim, s.d_state))]
+    b = [x.copy() for x in a]
+    for _ in range(5):
+        ha, da = oracle.layer_step(s, lay, h, a[0], a[1], want_dbg=True)
+        hb, db = oracle.layer_step(s, lays, h, b[0], b[1], want_dbg=True)
+        assert np.array_equal(ha, hb) and np.array_equal(a[1], b[1]) and np.array_equal(da["q2"], db["q2"])
+        h = ha
