@@ -15,6 +15,10 @@ a bounded sample of the same workload.
 --workload decode-b32, decode-b512 and prefill-8x2048 measure the batched
 path instead (32 or 512 sequences decoding after an 8-token prefill; a
 prefill of 8 x 2048 tokens); their lines carry step-level rooflines.
+--workload tiny-decode (the 2-layer test stack, us/token over 64 tokens),
+layer-1p3b-hot and layer-1p3b-cold (one 1.3B-shaped layer stepped 1000 times
+on fp16 inputs; cold cycles 64 layer copies) measure the two small workloads
+(use --steps 64 / --steps 1000).
 """
 import argparse
 import json
@@ -199,6 +203,172 @@ def bench_batched(args):
     print(json.dumps(out))
 
 
+def layer_step_bytes(s):
+    """Algorithmic HBM bytes of one single-layer decode step at batch 1 (one layer's weights, its conv
+    state read of 3 columns and write of 1, its SSM state read and written, the fp16 input and fp32 output)."""
+    dm, di, N, H, P, r = s.d_model, s.d_inner, s.d_state, s.n_heads, s.headdim, s.rank
+    dp, cd, K = s.d_in_proj, s.conv_dim, s.d_conv
+    f = 4
+    return (dp * dm // 8 + dm * di // 8 + (dp + dm) * f + r * (dm + dp + di + dm) + (2 * r + dp + dm) * f
+            + cd * (K + 1) * f + K * cd * f + 2 * H * P * N * f + (3 * H + dm + di) * f + dm * 2 + dm * f)
+
+
+PHASES = ["residual hop + norm statistics", "quantise", "wait for LoRA down", "in_proj rows", "conv",
+          "B/C hop", "SSM + publish", "gated-output hop + norm statistics", "out_proj rows + publish"]
+
+
+def phase_profile(eng, tok, n_tokens, s):
+    """Per-phase durations of the persistent batch-1 kernel (device timestamps at 10 points of every layer of
+    every workgroup, 100 MHz clock): median, mean, 90th percentile and the mean over layers of the slowest
+    workgroup, for layers 1 .. L-2; plus, per hop, how far the publishers are spread and how long after the
+    last publisher the median receiver has the values."""
+    import numpy as np
+    prof = eng.profile_persistent(tok, n_tokens, n_tokens)
+    p = prof.cpu().numpy().astype(np.int64)  # [T][L+1][G][10]
+    L = s.n_layer
+    ns = 10.0
+    d = np.diff(p[:, 1:L - 1, :, :], axis=-1) * ns
+    out = {"tokens": n_tokens, "phases_ns": {}}
+    for k, nm in enumerate(PHASES):
+        x = d[..., k]
+        out["phases_ns"][nm] = {"median": float(np.median(x)), "mean": round(float(x.mean()), 1),
+                                "p90": float(np.percentile(x, 90)),
+                                "slowest_wg": round(float(x.max(axis=2).mean()), 1)}
+    lp = (p[:, 2:L - 1, :, 0] - p[:, 1:L - 2, :, 0]) * ns
+    out["layer_period_ns"] = {"median": float(np.median(lp)), "mean": round(float(lp.mean()), 1)}
+    e9 = (p[:, 2:L - 1, :, 0] - p[:, 1:L - 2, :, 9]) * ns
+    out["layer_turnaround_ns"] = {"median": float(np.median(e9)), "mean": round(float(e9.mean()), 1)}
+
+    def hop(pl, pe, rl, re):
+        pub, rec = p[:, pl, :, pe], p[:, rl, :, re]
+        last = pub.max(axis=1)
+        return (np.mean(last - pub.min(axis=1)) * ns, np.mean(np.median(rec, axis=1) - last) * ns)
+
+    for name, (pe, rl_off, re) in {"residual": (9, 1, 1), "B/C": (5, 0, 6), "gated output": (7, 0, 8)}.items():
+        v = np.array([hop(l, pe, l + rl_off, re) for l in range(1, L - 2)])
+        out.setdefault("hops_ns", {})[name] = {"publisher_spread": round(float(v[:, 0].mean()), 1),
+                                               "last_publisher_to_median_receiver": round(float(v[:, 1].mean()), 1)}
+    hd = np.diff(p[:, L, :, :5], axis=-1) * ns
+    out["lm_head_ns"] = {nm: float(np.median(hd[..., i]))
+                         for i, nm in enumerate(["residual hop", "quantise", "logits + local argmax", "argmax hop"])}
+    out["token_period_us"] = round(float(np.median((p[1:, 0, :, 0] - p[:-1, 0, :, 0]) * ns)) / 1000, 2)
+    return out
+
+
+def host_facts():
+    """CPU model name (from /proc/cpuinfo), OMP_NUM_THREADS and the usable cores of this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"),
+            "nproc": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()}
+
+
+def bench_small(args):
+    """The tiny 2-layer model's batch-1 decode (64 greedy tokens in one persistent launch) or one
+    1.3B-shaped layer stepped 1000 times on fp16 inputs (hot: one layer; cold: 64 layer copies
+    cycled, more than the 256 MB Infinity Cache)."""
+    import numpy as np
+    import torch
+    import synth
+    from bit_quantized_mamba_amd import Engine
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    common = {"n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "int8/1-bit weights, int32 accumulation, f32 state", "data": "synthetic (seeded weights and tokens)",
+              "cpu_baseline": None}
+    if args.workload == "tiny-decode":
+        s = synth.TINY
+        seed = synth.SEED_BASE
+        n = args.steps
+        eng = Engine.from_shape(s, max_batch=1, device=0)
+        eng.load_synthetic(seed)
+        tok = torch.from_numpy(synth.gen_tokens(seed, 0, 1, s.vocab).astype("int32")).to(dev)
+        out = torch.empty((max(n, args.warmup, 1), 1), dtype=torch.int32, device=dev)
+        if args.warmup:
+            eng.generate(tok, args.warmup, out=out)
+        eng.reset_state(1)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        eng.generate(tok, n, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eng.check()
+        ms = e0.elapsed_time(e1)
+        sb = step_bytes(s)
+        gbs = sb * n / (ms / 1e3) / 1e9
+        res = {"metric": "decode us/token, batch=1, 2-layer test stack (d_model 256)",
+               "value": round(ms * 1e3 / n, 3), "unit": "us/token", "higher_is_better": False, "steps": n,
+               "warmup": args.warmup, "ms_per_step": round(ms / n, 5),
+               "config": {"workload": f"DF-SSM 2-layer test stack (d_model 256, d_inner 512, d_state 16, headdim 32, "
+                                      f"vocab 1024), batch 1, {n} greedy tokens in one persistent launch", "batch": 1},
+               # 0.64 MB per token stays in the caches: the HBM fraction is not a meaningful bound here
+               "roofline": {"bound": "hbm", "scope": "cache-resident (0.64 MB/token): fraction not meaningful",
+                            "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None, "bytes_per_token": sb}}
+    else:
+        cold = args.workload == "layer-1p3b-cold"
+        base = synth.LAYER_1P3B
+        copies = 64 if cold else 1
+        s = synth.Shape(n_layer=copies, d_model=base.d_model, d_inner=base.d_inner, d_state=base.d_state,
+                        headdim=base.headdim, vocab=base.vocab)
+        seed = synth.SEED_BASE + 1
+        n = args.steps
+        eng = Engine.from_shape(s, max_batch=1, device=0)
+        eng.load_synthetic(seed)
+        h16 = synth.gen_fp16_normal(seed, 1, n * s.d_model).reshape(n, 1, s.d_model)
+        hin = torch.from_numpy(h16).to(dev)
+        hout = torch.empty((n, 1, s.d_model), dtype=torch.float32, device=dev)
+        # one HIP graph of all n steps (inputs already in HBM), replayed once per timing
+        g = torch.cuda.CUDAGraph()
+        eng.reset_state(1)
+        torch.cuda.synchronize()
+        cap = torch.cuda.Stream()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(n):
+                    eng.layer_step_f16(i % copies, hin[i], hout[i], stream=cap)
+        for _ in range(max(args.warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        eng.reset_state(1)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eng.check()
+        ms = e0.elapsed_time(e1)
+        sb = layer_step_bytes(s)
+        gbs = sb * n / (ms / 1e3) / 1e9
+        res = {"metric": "single-layer step us/step, batch=1, 1.3B layer shape" + (", cold (64 layer copies)" if cold
+                                                                                  else ", hot"),
+               "value": round(ms * 1e3 / n, 3), "unit": "us/step", "higher_is_better": False, "steps": n,
+               "warmup": args.warmup, "ms_per_step": round(ms / n, 5),
+               "config": {"workload": f"one Mamba-2 1.3B-shaped DF-SSM layer (d_model 2048, d_inner 4096, "
+                                      f"d_state 128), batch 1, {n} steps on seeded fp16 N(0,1) inputs, state "
+                                      f"carried, per-layer kernels replayed as one HIP graph"
+                                      + (f", layer i % {copies} of {copies} copies (working set beyond the "
+                                         f"Infinity Cache)" if cold else ""), "batch": 1},
+               "roofline": {"bound": "hbm", "scope": "whole step", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "bytes_per_step": sb}}
+    eng.close()
+    out = dict(common)
+    out.update(res)
+    print(json.dumps(out))
+
+
 def cpu_baseline(shape, seed, prompt, budget_s):
     """The CPU oracle decoding the same model, timed on a bounded number of steps."""
     import numpy as np
@@ -218,6 +388,7 @@ def cpu_baseline(shape, seed, prompt, budget_s):
         if el >= budget_s or steps >= 1000:
             break
     return {"value": round(steps / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "host": host_facts(),
             "sample": f"{steps} greedy decode steps of the 48-layer model at batch 1 from a zero state "
                       f"({el:.1f} s; weight generation {setup:.1f} s not timed); plain C, fp64, OpenMP over rows"}
 
@@ -232,8 +403,12 @@ def main():
     ap.add_argument("--kernel-breakdown", action="store_true",
                     help="also time each kernel of the per-layer (multi-kernel) path")
     ap.add_argument("--path", choices=["auto", "kernels", "persistent", "gemm"], default="auto")
-    ap.add_argument("--workload", choices=["decode-b1", "decode-b32", "decode-b512", "prefill-8x2048"],
+    ap.add_argument("--workload", choices=["decode-b1", "decode-b32", "decode-b512", "prefill-8x2048",
+                                           "tiny-decode", "layer-1p3b-hot", "layer-1p3b-cold"],
                     default="decode-b1")
+    ap.add_argument("--phase-profile", type=int, default=0, metavar="TOKENS",
+                    help="after the timed region, decode this many tokens with the persistent kernel's phase "
+                         "timestamps and print their summary to stderr (batch 1)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy (read + write) of this many MiB, "
                          "a known-size reference for the HBM byte counters of a profiler run")
@@ -243,6 +418,9 @@ def main():
               f"see the sharding notes); --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload in ("tiny-decode", "layer-1p3b-hot", "layer-1p3b-cold"):
+        bench_small(args)
+        return
     if args.workload != "decode-b1":
         bench_batched(args)
         return
@@ -273,6 +451,8 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     eng.check()
+    if args.phase_profile > 0:
+        print(json.dumps({"phase_profile": phase_profile(eng, tok, args.phase_profile, s)}), file=sys.stderr)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -46,27 +46,48 @@ class Engine:
     `max_batch` sequence slots and the workspace, owned by the library."""
 
     def __init__(self, n_layer: int, d_model: int, d_inner: int, d_state: int, headdim: int, vocab: int,
-                 d_conv: int = 4, rank: int = 16, max_batch: int = 1, device: int = 0, norm_eps: float = 1e-5):
-        self.cfg = DfssmConfig(n_layer, d_model, d_inner, d_state, headdim, vocab, d_conv, rank, max_batch, norm_eps)
+                 d_conv: int = 4, rank: int = 16, max_batch: int = 1, device: int = 0, norm_eps: float = 1e-5,
+                 max_chunk_rows: int = 0, arena=None):
+        """arena: optional uint8 CUDA tensor of at least arena_bytes(...) bytes (256-byte aligned) that
+        holds everything the context needs; the engine keeps a reference to it until close()."""
+        self.cfg = DfssmConfig(n_layer, d_model, d_inner, d_state, headdim, vocab, d_conv, rank, max_batch, norm_eps,
+                               max_chunk_rows)
         self.n_layer, self.d_model, self.d_inner, self.d_state = n_layer, d_model, d_inner, d_state
         self.headdim, self.vocab, self.d_conv, self.rank, self.max_batch = headdim, vocab, d_conv, rank, max_batch
         self.n_heads = d_inner // headdim
         self.conv_dim = d_inner + 2 * d_state
         self.d_in_proj = 2 * d_inner + 2 * d_state + self.n_heads
         self.device = device
+        self._arena = arena
         h = ctypes.c_void_p()
-        call("dfssm_create", ctypes.byref(self.cfg), device, ctypes.byref(h))
+        if arena is None:
+            call("dfssm_create", ctypes.byref(self.cfg), device, None, 0, ctypes.byref(h))
+        else:
+            call("dfssm_create", ctypes.byref(self.cfg), device, arena.data_ptr(),
+                 arena.numel() * arena.element_size(), ctypes.byref(h))
         self._h = h
 
+    @staticmethod
+    def arena_bytes(n_layer: int, d_model: int, d_inner: int, d_state: int, headdim: int, vocab: int,
+                    d_conv: int = 4, rank: int = 16, max_batch: int = 1, norm_eps: float = 1e-5,
+                    max_chunk_rows: int = 0) -> int:
+        """Device bytes an engine of this configuration needs in a caller-provided arena."""
+        cfg = DfssmConfig(n_layer, d_model, d_inner, d_state, headdim, vocab, d_conv, rank, max_batch, norm_eps,
+                          max_chunk_rows)
+        n = ctypes.c_size_t()
+        call("dfssm_arena_bytes", ctypes.byref(cfg), ctypes.byref(n))
+        return n.value
+
     @classmethod
-    def from_shape(cls, s, max_batch: int = 1, device: int = 0) -> "Engine":
+    def from_shape(cls, s, max_batch: int = 1, device: int = 0, max_chunk_rows: int = 0, arena=None) -> "Engine":
         return cls(s.n_layer, s.d_model, s.d_inner, s.d_state, s.headdim, s.vocab, s.d_conv, s.rank,
-                   max_batch=max_batch, device=device)
+                   max_batch=max_batch, device=device, max_chunk_rows=max_chunk_rows, arena=arena)
 
     def close(self) -> None:
         if getattr(self, "_h", None):
             _lib.load().dfssm_destroy(self._h)
             self._h = None
+        self._arena = None
 
     def __del__(self):
         try:
@@ -186,10 +207,25 @@ class Engine:
         call("dfssm_layer_step", self._h, layer, _dp(h_in), _dp(h_out), B, _dp(q1), _dp(q2), _stream(stream))
         return (h_out, q1, q2) if want_codes else h_out
 
-    def trace_step(self, tok, stream=None):
-        """Decode step recording the residual stream per layer and every int8 activation code.
+    def layer_step_f16(self, layer: int, h_in, h_out=None, want_codes: bool = False, stream=None):
+        """layer_step with fp16 input activations h_in ([B][d_model] float16, upcast exactly on the device)."""
+        torch = _torch()
+        if h_in.dtype != torch.float16 or not h_in.is_cuda or not h_in.is_contiguous():
+            raise ValueError("h_in must be a contiguous fp16 CUDA tensor [B][d_model]")
+        B = h_in.shape[0]
+        if h_out is None:
+            h_out = torch.empty((B, self.d_model), dtype=torch.float32, device=h_in.device)
+        q1 = torch.empty((B, self.d_model), dtype=torch.int8, device=h_in.device) if want_codes else None
+        q2 = torch.empty((B, self.d_inner), dtype=torch.int8, device=h_in.device) if want_codes else None
+        call("dfssm_layer_step_f16", self._h, layer, _dp(h_in), _dp(h_out), B, _dp(q1), _dp(q2), _stream(stream))
+        return (h_out, q1, q2) if want_codes else h_out
 
-        Returns dict(h=[L+1][B][d_model], q1=[L][B][d_model], q2=[L][B][d_inner], qf=[B][d_model], logits)."""
+    def trace_step(self, tok, want_acc: bool = True, stream=None):
+        """Decode step recording the residual stream per layer, every int8 activation code and
+        (with want_acc) the exact int32 scaffold sums of every projection row.
+
+        Returns dict(h=[L+1][B][d_model], q1=[L][B][d_model], q2=[L][B][d_inner], qf=[B][d_model], logits,
+        acc1=[L][B][d_in_proj], acc2=[L][B][d_model])."""
         torch = _torch()
         self._check_tok(tok, 1)
         B = tok.shape[0]
@@ -199,16 +235,21 @@ class Engine:
              "q2": torch.empty((self.n_layer, B, self.d_inner), dtype=torch.int8, device=dev),
              "qf": torch.empty((B, self.d_model), dtype=torch.int8, device=dev),
              "logits": torch.empty((B, self.vocab), dtype=torch.float32, device=dev)}
+        if want_acc:
+            t["acc1"] = torch.empty((self.n_layer, B, self.d_in_proj), dtype=torch.int32, device=dev)
+            t["acc2"] = torch.empty((self.n_layer, B, self.d_model), dtype=torch.int32, device=dev)
         call("dfssm_trace_step", self._h, _dp(tok), B, _dp(t["h"]), _dp(t["q1"]), _dp(t["q2"]), _dp(t["qf"]),
-             _dp(t["logits"]), _stream(stream))
+             _dp(t["logits"]), _dp(t.get("acc1")), _dp(t.get("acc2")), _stream(stream))
         return t
 
-    def trace_prefill(self, tok, stream=None):
+    def trace_prefill(self, tok, want_acc: bool = False, stream=None):
         """Prefill of tok ([B][T] int32, one chunk) on the batched path, recording, per token row
-        m = b * T + t, the residual stream per layer and every int8 activation code.
+        m = b * T + t, the residual stream per layer, every int8 activation code and (with
+        want_acc) the exact int32 scaffold sums.
 
         Returns dict(h=[L+1][B*T][d_model], q1=[L][B*T][d_model], q2=[L][B*T][d_inner],
-        qf=[B][d_model], logits=[B][vocab]) (the last two for the last position)."""
+        qf=[B][d_model], logits=[B][vocab]) (the last two for the last position), plus
+        acc1=[L][B*T][d_in_proj] and acc2=[L][B*T][d_model] with want_acc."""
         torch = _torch()
         self._check_tok(tok, 2)
         B, T = tok.shape
@@ -219,8 +260,11 @@ class Engine:
              "q2": torch.empty((self.n_layer, M, self.d_inner), dtype=torch.int8, device=dev),
              "qf": torch.empty((B, self.d_model), dtype=torch.int8, device=dev),
              "logits": torch.empty((B, self.vocab), dtype=torch.float32, device=dev)}
+        if want_acc:
+            t["acc1"] = torch.empty((self.n_layer, M, self.d_in_proj), dtype=torch.int32, device=dev)
+            t["acc2"] = torch.empty((self.n_layer, M, self.d_model), dtype=torch.int32, device=dev)
         call("dfssm_trace_prefill", self._h, _dp(tok), B, T, _dp(t["h"]), _dp(t["q1"]), _dp(t["q2"]),
-             _dp(t["qf"]), _dp(t["logits"]), _stream(stream))
+             _dp(t["qf"]), _dp(t["logits"]), _dp(t.get("acc1")), _dp(t.get("acc2")), _stream(stream))
         return t
 
     PATHS = {"auto": 0, "kernels": 1, "persistent": 2, "gemm": 3}

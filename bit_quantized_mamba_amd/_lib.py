@@ -16,14 +16,15 @@ class DfssmConfig(ctypes.Structure):
     _fields_ = [("n_layer", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_inner", ctypes.c_int32),
                 ("d_state", ctypes.c_int32), ("headdim", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("d_conv", ctypes.c_int32), ("lora_rank", ctypes.c_int32), ("max_batch", ctypes.c_int32),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("max_chunk_rows", ctypes.c_int32)]
 
 
 # (name, argtypes); every function returns int32 status unless listed in _RESTYPE
 EXPORTS = {
     "dfssm_version": [],
     "dfssm_last_error": [_p],
-    "dfssm_create": [ctypes.POINTER(DfssmConfig), _i32, ctypes.POINTER(_p)],
+    "dfssm_arena_bytes": [ctypes.POINTER(DfssmConfig), ctypes.POINTER(_sz)],
+    "dfssm_create": [ctypes.POINTER(DfssmConfig), _i32, _p, _sz, ctypes.POINTER(_p)],
     "dfssm_destroy": [_p],
     "dfssm_device_bytes": [_p, ctypes.POINTER(_sz)],
     "dfssm_set_path": [_p, _i32],
@@ -37,8 +38,9 @@ EXPORTS = {
     "dfssm_generate": [_p, _p, _i32, _i32, _p, _i32, _p],
     "dfssm_prefill": [_p, _p, _i32, _i32, _p, _p, _p],
     "dfssm_layer_step": [_p, _i32, _p, _p, _i32, _p, _p, _p],
-    "dfssm_trace_step": [_p, _p, _i32, _p, _p, _p, _p, _p, _p],
-    "dfssm_trace_prefill": [_p, _p, _i32, _i32, _p, _p, _p, _p, _p, _p],
+    "dfssm_layer_step_f16": [_p, _i32, _p, _p, _i32, _p, _p, _p],
+    "dfssm_trace_step": [_p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p],
+    "dfssm_trace_prefill": [_p, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p],
     "dfssm_check_device": [_p, _p],
     "dfssm_profile_persistent": [_p, _p, _i32, _p, _i32, _p],
     "dfssm_time_kernel": [_p, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_float), _p],

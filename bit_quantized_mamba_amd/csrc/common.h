@@ -141,8 +141,8 @@ struct ProjArgs {
   const float* sB;       // [d_out]
   QPrep in;
   int d_in, d_out, r, B;
+  int32_t* acc;          // [B][d_out] signed scaffold sums (any epilogue), or null
   // EPI_STORE
-  int32_t* acc;
   float* y;
   // EPI_IN_PROJ
   float* zx;             // [B][d_out]
@@ -325,5 +325,6 @@ hipError_t launch_argmax(const float* logits, int V, int B, int32_t* next, int32
 hipError_t launch_quant_rows(const float* u, int rows, int n, int8_t* q, float* s, hipStream_t st);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_f16_to_f32(const void* src, float* dst, size_t n, hipStream_t st);
 
 }  // namespace dfssm

@@ -258,8 +258,8 @@ __global__ __launch_bounds__(256) void proj_gemv_kernel(ProjArgs a) {
       for (int k = 0; k < a.r; ++k) lo += (float)brow[k] * t[k];
       const float y = (float)acc * a.sw[row] * s + a.sB[row] * lo;
       const size_t bo = (size_t)b * a.d_out + row;
+      if (a.acc) a.acc[bo] = acc;
       if (EPI == EPI_STORE) {
-        if (a.acc) a.acc[bo] = acc;
         a.y[bo] = y;
       } else if (EPI == EPI_OUT_PROJ) {
         a.h[bo] += y;
@@ -529,6 +529,19 @@ hipError_t launch_quant_rows(const float* u, int rows, int n, int8_t* q, float* 
 __global__ void zero_kernel(uint32_t* p, size_t nwords) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) p[i] = 0u;
+}
+
+// fp16 -> fp32, exact (every binary16 value is a binary32 value)
+__global__ void f16_to_f32_kernel(const _Float16* __restrict__ src, float* __restrict__ dst, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = (float)src[i];
+}
+
+hipError_t launch_f16_to_f32(const void* src, float* dst, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(f16_to_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const _Float16*)src, dst, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {

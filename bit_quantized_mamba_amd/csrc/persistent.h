@@ -39,6 +39,8 @@ struct PersistArgs {
   int8_t* trace_q1;       // [n_layer][d_model] or null
   int8_t* trace_q2;       // [n_layer][d_inner] or null
   int8_t* trace_qf;       // [d_model] or null
+  int32_t* trace_acc1;    // [n_layer][d_in_proj] in_proj scaffold sums, or null
+  int32_t* trace_acc2;    // [n_layer][d_model] out_proj scaffold sums, or null
   unsigned long long* prof;  // or null: phase timestamps [prof_tokens][n_layer + 1][grid][kProfEvents]
   int prof_tokens;
 };

@@ -28,8 +28,8 @@
 // device-scope atomic loads until the word is fresh.  The small boxes (B/C,
 // argmax) carry {fp32 bits, epoch}, every hop instance with its own epoch.
 // The residual and gated-output boxes carry two values per word with a
-// 2-bit write-count tag in their lowest mantissa bits (pack2), which halves
-// the bytes every workgroup reads at those hops.  Freshness travels in the
+// 2-bit write-count tag in their lowest mantissa bits (pack2; readers clear
+// them), which halves the bytes every workgroup reads at those hops.  Freshness travels in the
 // same single-copy-atomic word as the data, so no fence or flag ordering is
 // involved.  Each box is reused once per layer; a writer can only reach its
 // next use after every reader has passed the hop that follows this one, so
@@ -61,17 +61,25 @@ __device__ __forceinline__ uint64_t pack(float v, unsigned e) { return ((uint64_
 
 // Paired words (the residual and gated-output boxes, whose per-hop volume is
 // large): two fp32 values in one 64-bit word, the lowest mantissa bit of each
-// replaced by one bit of a 2-bit tag, the count of that box's writes mod 4
-// (a 1-ulp perturbation of each value).  Every reader reads every word of its
-// replica at every write, so by per-location coherence it can only see the
-// current write or the one before, whose tag differs.  The host keeps the
-// count across launches and clears the boxes when it cannot vouch for it.
+// carrying one bit of a 2-bit tag, the count of that box's writes mod 4.
+// Every reader reads every word of its replica at every write, so by
+// per-location coherence it can only see the current write or the one before,
+// whose tag differs.  The host keeps the count across launches and clears the
+// boxes when it cannot vouch for it.  Readers clear the tag bits (unpack2):
+// every value crosses a hop with its lowest mantissa bit set to 0 (truncated
+// toward zero by at most 1 ulp), the same whatever the write count, so
+// results do not depend on how many tokens were decoded before, and zeros
+// stay exactly zero.
 constexpr uint64_t kTagMask = 0x0000000100000001ull;
 __device__ __forceinline__ uint64_t tag_bits(unsigned c) {
   return (uint64_t)(c & 1u) | ((uint64_t)((c >> 1) & 1u) << 32);
 }
 __device__ __forceinline__ uint64_t pack2(float v0, float v1, unsigned c) {
   return ((((uint64_t)__float_as_uint(v1) << 32) | __float_as_uint(v0)) & ~kTagMask) | tag_bits(c);
+}
+__device__ __forceinline__ float2 unpack2(uint64_t w) {
+  w &= ~kTagMask;
+  return make_float2(__uint_as_float((unsigned)w), __uint_as_float((unsigned)(w >> 32)));
 }
 
 // The launch's arguments re-read from the kernel-argument segment at the point
@@ -178,7 +186,7 @@ __device__ bool gather_words(const uint64_t* box, int n, unsigned key, float* ds
       const int i = threadIdx.x + m * kPT;
       if (i < n) {
         if (PAIRED)
-          ((float2*)dst)[i] = make_float2(__uint_as_float((unsigned)w[m]), __uint_as_float((unsigned)(w[m] >> 32)));
+          ((float2*)dst)[i] = unpack2(w[m]);
         else
           dst[i] = __uint_as_float((unsigned)w[m]);
       }
@@ -1013,8 +1021,9 @@ __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArg
 #pragma unroll
           for (int m = 0; m < S::GW1; ++m) {
             const int i = threadIdx.x + m * kPT;
-            xa[2 * m] = __uint_as_float((unsigned)wv[m]);
-            xa[2 * m + 1] = __uint_as_float((unsigned)(wv[m] >> 32));
+            const float2 v = unpack2(wv[m]);
+            xa[2 * m] = v.x;
+            xa[2 * m + 1] = v.y;
             if (i < DM / 2) ((float2*)hs)[i] = make_float2(xa[2 * m], xa[2 * m + 1]);
           }
           ++e;
@@ -1066,6 +1075,11 @@ __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArg
         for (int r = 0; r < S::RLI; ++r) tl[r] = ji + S::UI * r < 16 ? tls[ji + S::UI * r] * s1 : 0.0f;
         auto row_out = [&](int m, int part) -> float {
           const int acc = group_sum_i(part, S::UI);
+          if constexpr (TR) {
+            int32_t* ta = kargs()->trace_acc1;
+            const int g = wave + m * kPW, k = g * S::RPPI + subi;
+            if (ta && lead_i && g < S::NGI_T && k < S::NROWS) ta[(size_t)l * S::DPROJ + tm.in_row(k)] = acc;
+          }
           float lo = 0.0f;
 #pragma unroll
           for (int r = 0; r < S::RLI; ++r) lo += (float)ib[m][r] * tl[r];
@@ -1167,8 +1181,9 @@ __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArg
         const bool got = poll_words<S::GW2, true>(gbox, DI / 2, pc, wv, a.abort_flag);
 #pragma unroll
         for (int m = 0; m < S::GW2; ++m) {
-          xg[2 * m] = __uint_as_float((unsigned)wv[m]);
-          xg[2 * m + 1] = __uint_as_float((unsigned)(wv[m] >> 32));
+          const float2 v = unpack2(wv[m]);
+          xg[2 * m] = v.x;
+          xg[2 * m + 1] = v.y;
         }
         pair_stats<S::GW2>(xg, L.gw, DI / 2, pg, red);
         if (!got) *s_stop = 1;
@@ -1217,6 +1232,10 @@ __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArg
           const int k = g * S::RPPO + subo;
           const bool live = g < S::NGO_T && k < S::OUT_PER;
           const int row = w * S::OUT_PER + (live ? k : 0);
+          if constexpr (TR) {
+            int32_t* ta = kargs()->trace_acc2;
+            if (ta && lead_o && live) ta[(size_t)l * DM + row] = acc;
+          }
           const float hv = hs[row] + ((float)acc * osw[m] * s2 + osb[m] * lo);
           // rows k, k + 1 (k even) sit in one group, row k + 1 lead UO lanes up
           const float hn = __int_as_float(__builtin_amdgcn_ds_bpermute(((lane + S::UO) & 63) * 4, __float_as_int(hv)));
@@ -1398,7 +1417,7 @@ bool persistent_layout(int d_model, int d_inner, int d_state, int headdim, size_
 
 hipError_t launch_decode_persistent(const PersistArgs& a, int grid, hipStream_t st) {
   size_t stride = 0;
-  const bool tr = a.prof || a.trace_h || a.trace_q1 || a.trace_q2 || a.trace_qf;
+  const bool tr = a.prof || a.trace_h || a.trace_q1 || a.trace_q2 || a.trace_qf || a.trace_acc1 || a.trace_acc2;
   const void* k = select_kernel(a.d_model, a.d_inner, a.d_state, a.headdim, &stride, tr);
   if (!k) return hipErrorInvalidValue;
   PersistArgs args = a;

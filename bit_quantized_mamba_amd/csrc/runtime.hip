@@ -77,6 +77,18 @@ struct dfssm_ctx {
   // graphs keyed by (B, d_tok, d_out)
   std::map<std::tuple<int, const void*, const void*>, hipGraphExec_t> graphs;
 
+  // memory: one block for weights, state, workspace and mailboxes (the
+  // caller's arena, or a library allocation); the batched-path workspace is
+  // part of the caller's arena, or grows on demand in its own allocation
+  char* arena = nullptr;
+  size_t arena_bytes = 0;
+  bool own_arena = false;
+  size_t chunk_rows = 16384;  // token rows per prefill chunk
+  size_t o_w = 0, o_s = 0, o_ws = 0, o_box = 0, o_abort = 0, o_gw = 0;
+  struct WsOff {
+    size_t h, zx, xc, g, lg, q1, q2, p1, p2, qs1, qs2, s1, s2, t1, t2, nx, ct, er;
+  } wo{};
+
   // batched path (decode with B > 1, prefill): rows of tokens per layer
   struct GemmWs {
     size_t rows = 0;  // capacity in token rows
@@ -86,6 +98,7 @@ struct dfssm_ctx {
     int8_t* q = nullptr;
     int32_t* qsum = nullptr;
     float* gram = nullptr;  // chunked-scan workspace
+    bool fixed = false;     // carved from the caller's arena: never moves or grows
   } gw;
 
   // persistent batch-1 path
@@ -126,6 +139,8 @@ dfssm_status validate(const dfssm_config* c) {
   if (c->lora_rank > 32) return fail(DFSSM_E_UNSUPPORTED, "lora_rank must be <= 32");
   if (c->max_batch > 1024) return fail(DFSSM_E_UNSUPPORTED, "max_batch must be <= 1024");
   if (!(c->norm_eps >= 0.0f)) return fail(DFSSM_E_INVALID, "norm_eps must be >= 0");
+  if (c->max_chunk_rows < 0 || c->max_chunk_rows > (1 << 20))
+    return fail(DFSSM_E_INVALID, "max_chunk_rows must be in [0, 2^20]");
   return DFSSM_OK;
 }
 
@@ -201,8 +216,9 @@ hipError_t norm_quant_in(dfssm_ctx* c, int l, int B, hipStream_t st) {
                            c->lt<float>(l, DFSSM_T_IN_SA), c->r, c->q1, c->pl1, c->qs1, c->s1, c->t1, st);
 }
 
-hipError_t in_proj(dfssm_ctx* c, int l, int B, hipStream_t st) {
+hipError_t in_proj(dfssm_ctx* c, int l, int B, hipStream_t st, int32_t* acc = nullptr) {
   ProjArgs a{};
+  a.acc = acc;
   a.bits = c->lt<uint32_t>(l, DFSSM_T_IN_BITS);
   a.sw = c->lt<float>(l, DFSSM_T_IN_SW);
   a.Bm = c->lt<int8_t>(l, DFSSM_T_IN_B);
@@ -235,8 +251,9 @@ hipError_t norm_quant_out(dfssm_ctx* c, int l, int B, hipStream_t st) {
                            c->lt<float>(l, DFSSM_T_OUT_SA), c->r, c->q2, c->pl2, c->qs2, c->s2, c->t2, st);
 }
 
-hipError_t out_proj(dfssm_ctx* c, int l, int B, hipStream_t st) {
+hipError_t out_proj(dfssm_ctx* c, int l, int B, hipStream_t st, int32_t* acc = nullptr) {
   ProjArgs o{};
+  o.acc = acc;
   o.bits = c->lt<uint32_t>(l, DFSSM_T_OUT_BITS);
   o.sw = c->lt<float>(l, DFSSM_T_OUT_SW);
   o.Bm = c->lt<int8_t>(l, DFSSM_T_OUT_B);
@@ -256,14 +273,14 @@ hipError_t lm_head(dfssm_ctx* c, int B, float* logits, hipStream_t st) {
 }
 
 dfssm_status enqueue_layer(dfssm_ctx* c, int l, int B, hipStream_t st, int8_t* q1_out = nullptr,
-                           int8_t* q2_out = nullptr) {
+                           int8_t* q2_out = nullptr, int32_t* acc1_out = nullptr, int32_t* acc2_out = nullptr) {
   HIP_TRY(norm_quant_in(c, l, B, st));
   if (q1_out) HIP_TRY(hipMemcpyAsync(q1_out, c->q1, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st));
-  HIP_TRY(in_proj(c, l, B, st));
+  HIP_TRY(in_proj(c, l, B, st, acc1_out));
   HIP_TRY(ssm_step(c, l, B, st));
   HIP_TRY(norm_quant_out(c, l, B, st));
   if (q2_out) HIP_TRY(hipMemcpyAsync(q2_out, c->q2, (size_t)B * c->di, hipMemcpyDeviceToDevice, st));
-  HIP_TRY(out_proj(c, l, B, st));
+  HIP_TRY(out_proj(c, l, B, st, acc2_out));
   return DFSSM_OK;
 }
 
@@ -273,6 +290,8 @@ struct Trace {
   int8_t* q1 = nullptr;
   int8_t* q2 = nullptr;
   int8_t* qf = nullptr;
+  int32_t* acc1 = nullptr;  // [L][rows][d_in_proj]
+  int32_t* acc2 = nullptr;  // [L][rows][d_model]
 };
 
 dfssm_status enqueue_step(dfssm_ctx* c, const int32_t* tok, int tok_stride, int B, float* logits, int32_t* next,
@@ -285,7 +304,9 @@ dfssm_status enqueue_step(dfssm_ctx* c, const int32_t* tok, int tok_stride, int 
       HIP_TRY(hipMemcpyAsync(trace + (size_t)l * B * c->dm, c->h, sizeof(float) * B * c->dm,
                              hipMemcpyDeviceToDevice, st));
     dfssm_status r = enqueue_layer(c, l, B, st, tr && tr->q1 ? tr->q1 + (size_t)l * B * c->dm : nullptr,
-                                   tr && tr->q2 ? tr->q2 + (size_t)l * B * c->di : nullptr);
+                                   tr && tr->q2 ? tr->q2 + (size_t)l * B * c->di : nullptr,
+                                   tr && tr->acc1 ? tr->acc1 + (size_t)l * B * c->dproj : nullptr,
+                                   tr && tr->acc2 ? tr->acc2 + (size_t)l * B * c->dm : nullptr);
     if (r != DFSSM_OK) return r;
   }
   if (trace)
@@ -304,22 +325,61 @@ dfssm_status enqueue_step(dfssm_ctx* c, const int32_t* tok, int tok_stride, int 
 // ---------------------------------------------------------------------------
 // batched path: every layer on all B * T token rows at once
 // ---------------------------------------------------------------------------
-constexpr size_t kPrefillChunkRows = 16384;  // token rows per prefill chunk (bounds the workspace)
+constexpr size_t kPrefillChunkRows = 16384;  // default token rows per prefill chunk (bounds the workspace)
 
-// Grow the batched-path workspace to at least `rows` token rows.  Cached
-// graphs hold pointers into it, so they are dropped when it moves.
-dfssm_status ensure_gemm_ws(dfssm_ctx* c, size_t rows) {
-  if (rows <= c->gw.rows) return DFSSM_OK;
-  rows = std::max(rows, (size_t)c->maxB);
+struct GemmLayout {
+  size_t h, s, t, zx, xc, g, q, qs, gram, bytes;
+};
+
+// The batched-path workspace for `rows` token rows.
+GemmLayout gemm_layout(const dfssm_ctx* c, size_t rows) {
+  GemmLayout L{};
   const size_t mx = (size_t)std::max(c->dm, c->di);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
-  const size_t o_h = take(4 * rows * c->dm), o_s = take(4 * rows), o_t = take(4 * rows * 16),
-               o_zx = take(4 * rows * c->dproj), o_xc = take(4 * rows * c->cdim), o_g = take(4 * rows * c->di),
-               o_q = take(rows * mx), o_qs = take(4 * rows),
-               o_gram = take(4 * (rows / kSsdL + (size_t)c->maxB) * ssd_record_floats(c->H));
+  L.h = take(4 * rows * c->dm);
+  L.s = take(4 * rows);
+  L.t = take(4 * rows * 16);
+  L.zx = take(4 * rows * c->dproj);
+  L.xc = take(4 * rows * c->cdim);
+  L.g = take(4 * rows * c->di);
+  L.q = take(rows * mx);
+  L.qs = take(4 * rows);
+  L.gram = take(4 * (rows / kSsdL + (size_t)c->maxB) * ssd_record_floats(c->H));
+  L.bytes = off;
+  return L;
+}
+
+void assign_gemm_ws(dfssm_ctx* c, char* buf, size_t rows, const GemmLayout& L) {
+  c->gw.rows = rows;
+  c->gw.bytes = L.bytes;
+  c->gw.buf = buf;
+  c->gw.h = (float*)(buf + L.h);
+  c->gw.s = (float*)(buf + L.s);
+  c->gw.t = (float*)(buf + L.t);
+  c->gw.zx = (float*)(buf + L.zx);
+  c->gw.xc = (float*)(buf + L.xc);
+  c->gw.g = (float*)(buf + L.g);
+  c->gw.q = (int8_t*)(buf + L.q);
+  c->gw.qsum = (int32_t*)(buf + L.qs);
+  c->gw.gram = (float*)(buf + L.gram);
+}
+
+// Token rows the caller's arena gives the batched path.
+size_t fixed_gemm_rows(const dfssm_ctx* c) { return std::max(c->chunk_rows, (size_t)c->maxB); }
+
+// Grow the batched-path workspace to at least `rows` token rows.  Cached
+// graphs hold pointers into it, so they are dropped when it moves.  In the
+// caller's arena the workspace is fixed: a request beyond it is an error.
+dfssm_status ensure_gemm_ws(dfssm_ctx* c, size_t rows) {
+  if (rows <= c->gw.rows) return DFSSM_OK;
+  if (c->gw.fixed)
+    return fail(DFSSM_E_INVALID, "the arena's batched-path workspace holds " + std::to_string(c->gw.rows) +
+                                     " token rows; " + std::to_string(rows) + " requested");
+  rows = std::max(rows, (size_t)c->maxB);
+  const GemmLayout L = gemm_layout(c, rows);
   char* buf = nullptr;
-  if (hipMalloc(&buf, off) != hipSuccess) {
+  if (hipMalloc(&buf, L.bytes) != hipSuccess) {
     (void)hipGetLastError();
     return fail(DFSSM_E_OOM, "batched-path workspace allocation failed");
   }
@@ -329,18 +389,7 @@ dfssm_status ensure_gemm_ws(dfssm_ctx* c, size_t rows) {
   }
   for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
   c->graphs.clear();
-  c->gw.rows = rows;
-  c->gw.bytes = off;
-  c->gw.buf = buf;
-  c->gw.h = (float*)(buf + o_h);
-  c->gw.s = (float*)(buf + o_s);
-  c->gw.t = (float*)(buf + o_t);
-  c->gw.zx = (float*)(buf + o_zx);
-  c->gw.xc = (float*)(buf + o_xc);
-  c->gw.g = (float*)(buf + o_g);
-  c->gw.q = (int8_t*)(buf + o_q);
-  c->gw.qsum = (int32_t*)(buf + o_qs);
-  c->gw.gram = (float*)(buf + o_gram);
+  assign_gemm_ws(c, buf, rows, L);
   return DFSSM_OK;
 }
 
@@ -357,7 +406,7 @@ hipError_t b_rows_in(dfssm_ctx* c, int l, int M, hipStream_t st) {
   return launch_rows_quant(ra, c->dm, st);
 }
 
-hipError_t b_in_proj(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
+hipError_t b_in_proj(dfssm_ctx* c, int l, int B, int T, hipStream_t st, int32_t* acc = nullptr) {
   auto& w = c->gw;
   const int M = B * T;
   float* conv_l = c->conv + (size_t)l * (c->K - 1) * c->cdim;
@@ -373,11 +422,12 @@ hipError_t b_in_proj(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
     si.xc = w.xc; si.conv_state = conv_l; si.conv_bstride = c->conv_bstride;
     si.conv_w = c->lt<float>(l, DFSSM_T_CONV_W); si.conv_b = c->lt<float>(l, DFSSM_T_CONV_B);
     si.x_off = c->di; si.cdim = c->cdim;
+    si.acc = acc;
     return launch_gemm_skinny(si, SK_IN, st);
   }
   GemmArgs gi{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_IN_BITS), c->lt<float>(l, DFSSM_T_IN_SW),
               c->lt<int8_t>(l, DFSSM_T_IN_B), c->lt<float>(l, DFSSM_T_IN_SB), M, c->dproj, c->dm, w.zx, c->dproj,
-              nullptr};
+              acc};
   if (T == 1) {  // one decode token per sequence: the conv shift register in the GEMM epilogue
     gi.xc = w.xc; gi.conv_state = conv_l; gi.conv_bstride = c->conv_bstride;
     gi.conv_w = c->lt<float>(l, DFSSM_T_CONV_W); gi.conv_b = c->lt<float>(l, DFSSM_T_CONV_B);
@@ -420,7 +470,7 @@ hipError_t b_rows_out(dfssm_ctx* c, int l, int M, hipStream_t st) {
   return launch_rows_quant(rb, c->di, st);
 }
 
-hipError_t b_out_proj(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
+hipError_t b_out_proj(dfssm_ctx* c, int l, int B, int T, hipStream_t st, int32_t* acc = nullptr) {
   auto& w = c->gw;
   const int M = B * T;
   if (skinny_decode(B, T)) {
@@ -432,10 +482,11 @@ hipError_t b_out_proj(dfssm_ctx* c, int l, int B, int T, hipStream_t st) {
     so.sB = c->lt<float>(l, DFSSM_T_OUT_SB);
     so.M = M; so.N = c->dm; so.K = c->di;
     so.y = w.h; so.ldy = c->dm;
+    so.acc = acc;
     return launch_gemm_skinny(so, SK_OUT, st);
   }
   GemmArgs go{w.q, w.s, w.qsum, w.t, c->lt<uint32_t>(l, DFSSM_T_OUT_BITS), c->lt<float>(l, DFSSM_T_OUT_SW),
-              c->lt<int8_t>(l, DFSSM_T_OUT_B), c->lt<float>(l, DFSSM_T_OUT_SB), M, c->dm, c->di, w.h, c->dm, nullptr};
+              c->lt<int8_t>(l, DFSSM_T_OUT_B), c->lt<float>(l, DFSSM_T_OUT_SB), M, c->dm, c->di, w.h, c->dm, acc};
   return launch_bitgemm(go, GEMM_EPI_RESIDUAL, st);
 }
 
@@ -467,15 +518,15 @@ hipError_t b_head(dfssm_ctx* c, int B, int T, float* lg, int8_t* qf_out, hipStre
 }
 
 dfssm_status enqueue_layer_gemm(dfssm_ctx* c, int l, int B, int T, hipStream_t st, int8_t* q1_out,
-                                int8_t* q2_out) {
+                                int8_t* q2_out, int32_t* acc1_out = nullptr, int32_t* acc2_out = nullptr) {
   const int M = B * T;
   HIP_TRY(b_rows_in(c, l, M, st));
   if (q1_out) HIP_TRY(hipMemcpyAsync(q1_out, c->gw.q, (size_t)M * c->dm, hipMemcpyDeviceToDevice, st));
-  HIP_TRY(b_in_proj(c, l, B, T, st));
+  HIP_TRY(b_in_proj(c, l, B, T, st, acc1_out));
   HIP_TRY(b_scan(c, l, B, T, st));
   HIP_TRY(b_rows_out(c, l, M, st));
   if (q2_out) HIP_TRY(hipMemcpyAsync(q2_out, c->gw.q, (size_t)M * c->di, hipMemcpyDeviceToDevice, st));
-  HIP_TRY(b_out_proj(c, l, B, T, st));
+  HIP_TRY(b_out_proj(c, l, B, T, st, acc2_out));
   return DFSSM_OK;
 }
 
@@ -495,7 +546,9 @@ dfssm_status enqueue_step_gemm(dfssm_ctx* c, const int32_t* tok, int tok_stride,
       HIP_TRY(hipMemcpyAsync(tr->h + (size_t)l * M * c->dm, w.h, sizeof(float) * M * c->dm,
                              hipMemcpyDeviceToDevice, st));
     dfssm_status r = enqueue_layer_gemm(c, l, B, T, st, tr && tr->q1 ? tr->q1 + (size_t)l * M * c->dm : nullptr,
-                                        tr && tr->q2 ? tr->q2 + (size_t)l * M * c->di : nullptr);
+                                        tr && tr->q2 ? tr->q2 + (size_t)l * M * c->di : nullptr,
+                                        tr && tr->acc1 ? tr->acc1 + (size_t)l * M * c->dproj : nullptr,
+                                        tr && tr->acc2 ? tr->acc2 + (size_t)l * M * c->dm : nullptr);
     if (r != DFSSM_OK) return r;
   }
   if (tr && tr->h)
@@ -577,6 +630,8 @@ dfssm_status run_persistent(dfssm_ctx* c, const int32_t* tok_in, int32_t* tok_la
     a.trace_q1 = tr->q1;
     a.trace_q2 = tr->q2;
     a.trace_qf = tr->qf;
+    a.trace_acc1 = tr->acc1;
+    a.trace_acc2 = tr->acc2;
   }
   a.prof = prof;
   a.prof_tokens = prof_tokens;
@@ -610,19 +665,15 @@ const char* dfssm_version(void) { return "dfssm-mi355x 0.1 (gfx950)"; }
 
 const char* dfssm_last_error(const dfssm_ctx*) { return g_err.c_str(); }
 
-dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** out) {
-  if (!out) return fail(DFSSM_E_INVALID, "null output pointer");
-  *out = nullptr;
-  dfssm_status v = validate(cfg);
-  if (v != DFSSM_OK) return v;
-  int ndev = 0;
-  HIP_TRY(hipGetDeviceCount(&ndev));
-  if (device < 0 || device >= ndev) return fail(DFSSM_E_INVALID, "device index out of range");
-  HIP_TRY(hipSetDevice(device));
+}  // extern "C"
 
-  dfssm_ctx* c = new dfssm_ctx();
+namespace {
+
+// Dimensions and the memory plan of a context: weights | state | decode
+// workspace | mailboxes | abort flag | batched-path workspace (the last only
+// when the caller provides the arena).  Pure host arithmetic.
+void plan_memory(dfssm_ctx* c, const dfssm_config* cfg) {
   c->cfg = *cfg;
-  c->device = device;
   c->L = cfg->n_layer;
   c->dm = cfg->d_model;
   c->di = cfg->d_inner;
@@ -636,10 +687,11 @@ dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** o
   c->cdim = c->di + 2 * c->N;
   c->dproj = 2 * c->di + 2 * c->N + c->H;
   c->eps = cfg->norm_eps > 0.0f ? cfg->norm_eps : 1e-5f;
+  c->chunk_rows = cfg->max_chunk_rows > 0 ? (size_t)cfg->max_chunk_rows : kPrefillChunkRows;
 
   // weights
   size_t off = 0;
-  c->layer_t.resize((size_t)c->L * DFSSM_T_PER_LAYER);
+  c->layer_t.assign((size_t)c->L * DFSSM_T_PER_LAYER, TensorInfo{});
   for (int l = 0; l < c->L; ++l)
     for (int k = 0; k < DFSSM_T_PER_LAYER; ++k) {
       Spec sp = layer_spec(c, k);
@@ -650,7 +702,7 @@ dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** o
       t.bytes = sp.count * sp.elem;
       off += align_up(t.bytes);
     }
-  c->global_t.resize(3);
+  c->global_t.assign(3, TensorInfo{});
   for (int k = 0; k < 3; ++k) {
     Spec sp = global_spec(c, k);
     TensorInfo& t = c->global_t[k];
@@ -669,55 +721,174 @@ dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** o
   const size_t ssm_bytes = align_up(sizeof(float) * c->ssm_bstride * c->maxB);
   c->sbytes = conv_bytes + ssm_bytes;
 
-  // workspace
+  // decode workspace (all [max_batch][...])
   const size_t B = c->maxB;
   size_t wo = 0;
   auto take = [&](size_t bytes) { size_t o = wo; wo += align_up(bytes); return o; };
-  const size_t o_h = take(sizeof(float) * B * c->dm), o_zx = take(sizeof(float) * B * c->dproj),
-               o_xc = take(sizeof(float) * B * c->cdim), o_g = take(sizeof(float) * B * c->di),
-               o_lg = take(sizeof(float) * B * c->V), o_q1 = take(B * c->dm), o_q2 = take(B * c->di),
-               o_p1 = take(sizeof(uint32_t) * B * (c->dm / 32) * 8),
-               o_p2 = take(sizeof(uint32_t) * B * (c->di / 32) * 8), o_qs1 = take(4 * B), o_qs2 = take(4 * B),
-               o_s1 = take(4 * B), o_s2 = take(4 * B), o_t1 = take(4 * B * c->r), o_t2 = take(4 * B * c->r),
-               o_nx = take(4 * B), o_ct = take(4), o_er = take(4);
+  auto& o = c->wo;
+  o.h = take(sizeof(float) * B * c->dm);
+  o.zx = take(sizeof(float) * B * c->dproj);
+  o.xc = take(sizeof(float) * B * c->cdim);
+  o.g = take(sizeof(float) * B * c->di);
+  o.lg = take(sizeof(float) * B * c->V);
+  o.q1 = take(B * c->dm);
+  o.q2 = take(B * c->di);
+  o.p1 = take(sizeof(uint32_t) * B * (c->dm / 32) * 8);
+  o.p2 = take(sizeof(uint32_t) * B * (c->di / 32) * 8);
+  o.qs1 = take(4 * B);
+  o.qs2 = take(4 * B);
+  o.s1 = take(4 * B);
+  o.s2 = take(4 * B);
+  o.t1 = take(4 * B * c->r);
+  o.t2 = take(4 * B * c->r);
+  o.nx = take(4 * B);
+  o.ct = take(4);
+  o.er = take(4);
   c->wsbytes = wo;
 
-  if (hipMalloc(&c->wbuf, c->wbytes) != hipSuccess || hipMalloc(&c->sbuf, c->sbytes) != hipSuccess ||
-      hipMalloc(&c->ws, c->wsbytes) != hipSuccess) {
-    (void)hipGetLastError();
-    dfssm_destroy(c);
-    return fail(DFSSM_E_OOM, "device allocation failed");
+  // mailboxes of the persistent kernel (sized whenever the shape is one it is
+  // compiled for; unused if the device cannot run it)
+  c->persist_grid = c->H * (c->P / 16);
+  size_t stride = 0, offs[DFSSM_T_PER_LAYER];
+  c->box_words = persistent_layout(c->dm, c->di, c->N, c->P, &stride, offs)
+                     ? persistent_box_words(c->dm, c->di, c->N, c->persist_grid) : 0;
+
+  size_t a = 0;
+  c->o_w = a; a += align_up(c->wbytes);
+  c->o_s = a; a += align_up(c->sbytes);
+  c->o_ws = a; a += align_up(c->wsbytes);
+  c->o_box = a; a += align_up(sizeof(uint64_t) * c->box_words);
+  c->o_abort = a; a += kAlign;
+  c->o_gw = a;
+  c->arena_bytes = a;  // without the batched-path workspace
+}
+
+// ---------------------------------------------------------------------------
+// the stateless matrix-core projection (dfssm_k_gemm and its allocation-free twin)
+// ---------------------------------------------------------------------------
+dfssm_status check_k_gemm(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
+                          const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out, const int8_t* d_q,
+                          const float* d_s, int32_t M, float* d_y) {
+  if (!d_bits || !d_sw || !d_A || !d_sA || !d_B || !d_sB || !d_q || !d_s || !d_y)
+    return fail(DFSSM_E_INVALID, "null pointer");
+  if (d_in < 128 || d_in % 128 || (d_in / 128) > 64 || ((d_in / 128) & (d_in / 128 - 1)))
+    return fail(DFSSM_E_UNSUPPORTED, "d_in must be 128 * 2^k <= 8192");
+  if (d_out < 1 || M < 1 || M > 65535) return fail(DFSSM_E_INVALID, "bad d_out / M");
+  return DFSSM_OK;
+}
+
+// operand scratch of one projection: the activations' bit planes (M d_in
+// bytes), their row sums (4 M) and LoRA-down vectors (64 M)
+size_t k_gemm_scratch_bytes(int d_in, int M) {
+  return align_up((size_t)M * d_in) + align_up(4 * (size_t)M) + align_up(4 * (size_t)M * 16);
+}
+
+hipError_t k_gemm_run(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
+                      const int8_t* d_B, const float* d_sB, int d_in, int d_out, const int8_t* d_q, const float* d_s,
+                      int M, int32_t* d_acc, float* d_y, char* tmp, hipStream_t st) {
+  uint32_t* planes = (uint32_t*)tmp;
+  int32_t* qsum = (int32_t*)(tmp + align_up((size_t)M * d_in));
+  float* t = (float*)(tmp + align_up((size_t)M * d_in) + align_up(4 * (size_t)M));
+  hipError_t e = launch_qprep(d_q, d_s, d_in, M, d_A, d_sA, 16, planes, qsum, t, st);
+  if (e != hipSuccess) return e;
+  if (M <= 32) {  // the decode-sized kernel
+    SkinnyArgs a{};
+    a.q = d_q; a.s = d_s; a.qsum = qsum; a.t = t;
+    a.w = d_bits; a.sw = d_sw; a.Bm = d_B; a.sB = d_sB;
+    a.M = M; a.N = d_out; a.K = d_in;
+    a.y = d_y; a.ldy = d_out; a.acc = d_acc;
+    return launch_gemm_skinny(a, SK_IN, st);
   }
+  GemmArgs a{d_q, d_s, qsum, t, d_bits, d_sw, d_B, d_sB, M, d_out, d_in, d_y, d_out, d_acc};
+  return launch_bitgemm(a, GEMM_EPI_STORE, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+dfssm_status dfssm_arena_bytes(const dfssm_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(DFSSM_E_INVALID, "null output pointer");
+  dfssm_status v = validate(cfg);
+  if (v != DFSSM_OK) return v;
+  dfssm_ctx tmp;
+  plan_memory(&tmp, cfg);
+  *bytes = tmp.o_gw + align_up(gemm_layout(&tmp, fixed_gemm_rows(&tmp)).bytes);
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, void* arena, size_t arena_bytes,
+                          dfssm_ctx** out) {
+  if (!out) return fail(DFSSM_E_INVALID, "null output pointer");
+  *out = nullptr;
+  dfssm_status v = validate(cfg);
+  if (v != DFSSM_OK) return v;
+  if (arena && ((uintptr_t)arena % kAlign))
+    return fail(DFSSM_E_INVALID, "the arena must be 256-byte aligned");
+  int ndev = 0;
+  HIP_TRY(hipGetDeviceCount(&ndev));
+  if (device < 0 || device >= ndev) return fail(DFSSM_E_INVALID, "device index out of range");
+  HIP_TRY(hipSetDevice(device));
+
+  dfssm_ctx* c = new dfssm_ctx();
+  c->device = device;
+  plan_memory(c, cfg);
+  const GemmLayout gl = gemm_layout(c, fixed_gemm_rows(c));
+  const size_t need = c->o_gw + align_up(gl.bytes);
+  if (arena) {
+    if (arena_bytes < need) {
+      delete c;
+      return fail(DFSSM_E_INVALID, "arena too small: " + std::to_string(arena_bytes) + " bytes, need " +
+                                       std::to_string(need) + " (dfssm_arena_bytes)");
+    }
+    c->arena = (char*)arena;
+    c->own_arena = false;
+    assign_gemm_ws(c, c->arena + c->o_gw, fixed_gemm_rows(c), gl);
+    c->gw.fixed = true;
+  } else {
+    if (hipMalloc(&c->arena, c->arena_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      delete c;
+      return fail(DFSSM_E_OOM, "device allocation failed");
+    }
+    c->own_arena = true;
+  }
+  c->wbuf = c->arena + c->o_w;
+  c->sbuf = c->arena + c->o_s;
+  c->ws = c->arena + c->o_ws;
   c->conv = (float*)c->sbuf;
-  c->ssm = (float*)(c->sbuf + conv_bytes);
+  c->ssm = (float*)(c->sbuf + align_up(sizeof(float) * c->conv_bstride * c->maxB));
   char* w = c->ws;
-  c->h = (float*)(w + o_h);
-  c->zx = (float*)(w + o_zx);
-  c->xc = (float*)(w + o_xc);
-  c->g = (float*)(w + o_g);
-  c->logits = (float*)(w + o_lg);
-  c->q1 = (int8_t*)(w + o_q1);
-  c->q2 = (int8_t*)(w + o_q2);
-  c->pl1 = (uint32_t*)(w + o_p1);
-  c->pl2 = (uint32_t*)(w + o_p2);
-  c->qs1 = (int32_t*)(w + o_qs1);
-  c->qs2 = (int32_t*)(w + o_qs2);
-  c->s1 = (float*)(w + o_s1);
-  c->s2 = (float*)(w + o_s2);
-  c->t1 = (float*)(w + o_t1);
-  c->t2 = (float*)(w + o_t2);
-  c->next = (int32_t*)(w + o_nx);
-  c->counter = (int32_t*)(w + o_ct);
-  c->err = (int*)(w + o_er);
-  if (launch_zero(c->sbuf, c->sbytes, nullptr) != hipSuccess || launch_zero(c->ws, c->wsbytes, nullptr) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess) {
+  const auto& o = c->wo;
+  c->h = (float*)(w + o.h);
+  c->zx = (float*)(w + o.zx);
+  c->xc = (float*)(w + o.xc);
+  c->g = (float*)(w + o.g);
+  c->logits = (float*)(w + o.lg);
+  c->q1 = (int8_t*)(w + o.q1);
+  c->q2 = (int8_t*)(w + o.q2);
+  c->pl1 = (uint32_t*)(w + o.p1);
+  c->pl2 = (uint32_t*)(w + o.p2);
+  c->qs1 = (int32_t*)(w + o.qs1);
+  c->qs2 = (int32_t*)(w + o.qs2);
+  c->s1 = (float*)(w + o.s1);
+  c->s2 = (float*)(w + o.s2);
+  c->t1 = (float*)(w + o.t1);
+  c->t2 = (float*)(w + o.t2);
+  c->next = (int32_t*)(w + o.nx);
+  c->counter = (int32_t*)(w + o.ct);
+  c->err = (int*)(w + o.er);
+  c->boxes = c->box_words ? (uint64_t*)(c->arena + c->o_box) : nullptr;
+  c->abort_flag = (int*)(c->arena + c->o_abort);
+  // state, workspace, mailboxes and the abort flag start at zero
+  if (launch_zero(c->arena + c->o_s, c->o_gw - c->o_s, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     dfssm_destroy(c);
     return fail(DFSSM_E_HIP, "initial clear failed");
   }
-  // persistent batch-1 path: layer pointer table, exchange boxes, abort flag
-  c->persist_grid = c->H * (c->P / 16);
+  // persistent batch-1 path: supported on this device, and the weight layout the kernel assumes
   const char* why = "";
-  c->persist_ok = persistent_supported(c->dm, c->di, c->N, c->P, c->H, c->r, c->persist_grid, &why);
+  c->persist_ok = c->box_words > 0 &&
+                  persistent_supported(c->dm, c->di, c->N, c->P, c->H, c->r, c->persist_grid, &why);
   c->persist_why = why;
   if (c->persist_ok && c->L < 2) {
     // the kernel re-reads a layer's conv and SSM state one layer after writing it back
@@ -736,20 +907,6 @@ dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** o
       c->persist_why = "weight layout differs from the persistent kernel's";
     }
   }
-  if (c->persist_ok) {
-    c->box_words = persistent_box_words(c->dm, c->di, c->N, c->persist_grid);
-    if (hipMalloc(&c->boxes, sizeof(uint64_t) * c->box_words) != hipSuccess ||
-        hipMalloc(&c->abort_flag, 256) != hipSuccess) {
-      (void)hipGetLastError();
-      dfssm_destroy(c);
-      return fail(DFSSM_E_OOM, "device allocation failed");
-    }
-    if (launch_zero(c->boxes, sizeof(uint64_t) * c->box_words, nullptr) != hipSuccess ||
-        launch_zero(c->abort_flag, 256, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-      dfssm_destroy(c);
-      return fail(DFSSM_E_HIP, "persistent path setup failed");
-    }
-  }
   *out = c;
   return DFSSM_OK;
 }
@@ -759,18 +916,14 @@ void dfssm_destroy(dfssm_ctx* c) {
   (void)hipSetDevice(c->device);
   (void)hipDeviceSynchronize();
   for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
-  if (c->wbuf) (void)hipFree(c->wbuf);
-  if (c->sbuf) (void)hipFree(c->sbuf);
-  if (c->ws) (void)hipFree(c->ws);
-  if (c->boxes) (void)hipFree(c->boxes);
-  if (c->gw.buf) (void)hipFree(c->gw.buf);
-  if (c->abort_flag) (void)hipFree(c->abort_flag);
+  if (c->gw.buf && !c->gw.fixed) (void)hipFree(c->gw.buf);
+  if (c->arena && c->own_arena) (void)hipFree(c->arena);
   delete c;
 }
 
 dfssm_status dfssm_device_bytes(const dfssm_ctx* c, size_t* bytes) {
   if (!c || !bytes) return fail(DFSSM_E_INVALID, "null argument");
-  *bytes = c->wbytes + c->sbytes + c->wsbytes + c->gw.bytes;
+  *bytes = c->arena_bytes + c->gw.bytes;
   return DFSSM_OK;
 }
 
@@ -979,7 +1132,7 @@ dfssm_status dfssm_prefill(dfssm_ctx* c, const int32_t* d_tok, int32_t B, int32_
   if (T < 1) return fail(DFSSM_E_INVALID, "prompt length must be >= 1");
   if (c->path != DFSSM_PATH_KERNELS) {
     // batched path, in chunks of whole token rows across the B sequences
-    const int tc = (int)std::max<size_t>(1, std::min<size_t>((size_t)T, kPrefillChunkRows / (size_t)B));
+    const int tc = (int)std::max<size_t>(1, std::min<size_t>((size_t)T, c->chunk_rows / (size_t)B));
     if ((v = ensure_gemm_ws(c, (size_t)B * tc)) != DFSSM_OK) return v;
     for (int t0 = 0; t0 < T; t0 += tc) {
       const int n = std::min(tc, T - t0);
@@ -1014,8 +1167,24 @@ dfssm_status dfssm_layer_step(dfssm_ctx* c, int32_t layer, const float* d_h_in, 
   return DFSSM_OK;
 }
 
+dfssm_status dfssm_layer_step_f16(dfssm_ctx* c, int32_t layer, const uint16_t* d_h_f16, float* d_h_out, int32_t B,
+                                  int8_t* d_q1, int8_t* d_q2, void* stream) {
+  dfssm_status v = check_ctx(c);
+  if (v != DFSSM_OK) return v;
+  if ((v = check_B(c, B)) != DFSSM_OK) return v;
+  if (layer < 0 || layer >= c->L) return fail(DFSSM_E_INVALID, "layer out of range");
+  if (!d_h_f16 || !d_h_out) return fail(DFSSM_E_INVALID, "null activation pointer");
+  hipStream_t st = S(stream);
+  HIP_TRY(launch_f16_to_f32(d_h_f16, c->h, (size_t)B * c->dm, st));
+  v = enqueue_layer(c, layer, B, st, d_q1, d_q2);
+  if (v != DFSSM_OK) return v;
+  HIP_TRY(hipMemcpyAsync(d_h_out, c->h, sizeof(float) * B * c->dm, hipMemcpyDeviceToDevice, st));
+  return DFSSM_OK;
+}
+
 dfssm_status dfssm_trace_step(dfssm_ctx* c, const int32_t* d_tok, int32_t B, float* d_h_trace, int8_t* d_q1_trace,
-                              int8_t* d_q2_trace, int8_t* d_qf, float* d_logits, void* stream) {
+                              int8_t* d_q2_trace, int8_t* d_qf, float* d_logits, int32_t* d_acc1_trace,
+                              int32_t* d_acc2_trace, void* stream) {
   dfssm_status v = check_ctx(c);
   if (v != DFSSM_OK) return v;
   if ((v = check_B(c, B)) != DFSSM_OK) return v;
@@ -1025,6 +1194,8 @@ dfssm_status dfssm_trace_step(dfssm_ctx* c, const int32_t* d_tok, int32_t B, flo
   tr.q1 = d_q1_trace;
   tr.q2 = d_q2_trace;
   tr.qf = d_qf;
+  tr.acc1 = d_acc1_trace;
+  tr.acc2 = d_acc2_trace;
   bool pers = false;
   if ((v = use_persistent(c, B, &pers)) != DFSSM_OK) return v;
   if (pers) return run_persistent(c, d_tok, nullptr, nullptr, 1, d_logits, &tr, S(stream));
@@ -1034,19 +1205,21 @@ dfssm_status dfssm_trace_step(dfssm_ctx* c, const int32_t* d_tok, int32_t B, flo
 
 dfssm_status dfssm_trace_prefill(dfssm_ctx* c, const int32_t* d_tok, int32_t B, int32_t T, float* d_h_trace,
                                  int8_t* d_q1_trace, int8_t* d_q2_trace, int8_t* d_qf, float* d_logits,
-                                 void* stream) {
+                                 int32_t* d_acc1_trace, int32_t* d_acc2_trace, void* stream) {
   dfssm_status v = check_ctx(c);
   if (v != DFSSM_OK) return v;
   if ((v = check_B(c, B)) != DFSSM_OK) return v;
   if (!d_tok || !d_h_trace) return fail(DFSSM_E_INVALID, "null pointer");
-  if (T < 1 || (size_t)B * T > kPrefillChunkRows)
-    return fail(DFSSM_E_INVALID, "traced prefill takes 1 <= B * T <= " + std::to_string(kPrefillChunkRows) + " rows");
+  if (T < 1 || (size_t)B * T > c->chunk_rows)
+    return fail(DFSSM_E_INVALID, "traced prefill takes 1 <= B * T <= " + std::to_string(c->chunk_rows) + " rows");
   if ((v = ensure_gemm_ws(c, (size_t)B * T)) != DFSSM_OK) return v;
   Trace tr;
   tr.h = d_h_trace;
   tr.q1 = d_q1_trace;
   tr.q2 = d_q2_trace;
   tr.qf = d_qf;
+  tr.acc1 = d_acc1_trace;
+  tr.acc2 = d_acc2_trace;
   return enqueue_step_gemm(c, d_tok, T, 0, B, T, d_logits, nullptr, nullptr, &tr, true, S(stream));
 }
 
@@ -1194,32 +1367,13 @@ dfssm_status dfssm_k_proj(const uint32_t* d_bits, const float* d_sw, const int8_
 dfssm_status dfssm_k_gemm(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
                           const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out, const int8_t* d_q,
                           const float* d_s, int32_t M, int32_t* d_acc, float* d_y, void* stream) {
-  if (!d_bits || !d_sw || !d_A || !d_sA || !d_B || !d_sB || !d_q || !d_s || !d_y)
-    return fail(DFSSM_E_INVALID, "null pointer");
-  if (d_in < 128 || d_in % 128 || (d_in / 128) > 64 || ((d_in / 128) & (d_in / 128 - 1)))
-    return fail(DFSSM_E_UNSUPPORTED, "d_in must be 128 * 2^k <= 8192");
-  if (d_out < 1 || M < 1 || M > 65535) return fail(DFSSM_E_INVALID, "bad d_out / M");
+  dfssm_status v = check_k_gemm(d_bits, d_sw, d_A, d_sA, d_B, d_sB, d_in, d_out, d_q, d_s, M, d_y);
+  if (v != DFSSM_OK) return v;
   hipStream_t st = S(stream);
-  const size_t pl_bytes = sizeof(uint32_t) * (size_t)M * (d_in / 32) * 8;
   char* tmp = nullptr;
-  const size_t tbytes = align_up(pl_bytes) + align_up(4 * (size_t)M) + align_up(4 * (size_t)M * 16);
-  HIP_TRY(hipMallocAsync((void**)&tmp, tbytes, st));
-  uint32_t* planes = (uint32_t*)tmp;
-  int32_t* qsum = (int32_t*)(tmp + align_up(pl_bytes));
-  float* t = (float*)(tmp + align_up(pl_bytes) + align_up(4 * (size_t)M));
-  hipError_t e = launch_qprep(d_q, d_s, d_in, M, d_A, d_sA, 16, planes, qsum, t, st);
-  if (e == hipSuccess && M <= 32) {  // the decode-sized kernel
-    SkinnyArgs a{};
-    a.q = d_q; a.s = d_s; a.qsum = qsum; a.t = t;
-    a.w = d_bits; a.sw = d_sw; a.Bm = d_B; a.sB = d_sB;
-    a.M = M; a.N = d_out; a.K = d_in;
-    a.y = d_y; a.ldy = d_out; a.acc = d_acc;
-    e = launch_gemm_skinny(a, SK_IN, st);
-  } else if (e == hipSuccess) {
-    GemmArgs a{d_q, d_s, qsum, t, d_bits, d_sw, d_B, d_sB, M, d_out, d_in, d_y, d_out, d_acc};
-    e = launch_bitgemm(a, GEMM_EPI_STORE, st);
-  }
-  hipError_t e2 = hipFreeAsync(tmp, st);
+  HIP_TRY(hipMallocAsync((void**)&tmp, k_gemm_scratch_bytes(d_in, M), st));
+  const hipError_t e = k_gemm_run(d_bits, d_sw, d_A, d_sA, d_B, d_sB, d_in, d_out, d_q, d_s, M, d_acc, d_y, tmp, st);
+  const hipError_t e2 = hipFreeAsync(tmp, st);
   if (e != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_gemm: ") + hipGetErrorString(e));
   if (e2 != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_gemm free: ") + hipGetErrorString(e2));
   return DFSSM_OK;

@@ -294,11 +294,19 @@ __global__ __launch_bounds__(256) void ssd_gram_kernel(ScanArgs a) {
         const float o = __shfl_up(cum, d);
         if (lane >= d) cum += o;
       }
-      const float end = __shfl(cum, 63);
+      // A_{L-1} is the last real token's running sum, and padding lanes (dt
+      // = 0) take exactly that value: the lanes' scan trees round
+      // differently, and when |A| is huge the difference between two trees'
+      // sums of the same terms is far from 0
+      const float end = __shfl(cum, Lc - 1);
+      if (lane >= Lc) cum = end;
       float* ph = par + h * 256;
       ph[lane] = cum;
       ph[64 + lane] = dt;
-      ph[128 + lane] = __expf(end - cum) * dt;
+      // A_{L-1} - A_j <= 0 (the running sums never increase); with huge |A|
+      // the trees' rounding can make it positive, where exp may overflow:
+      // the clamp keeps the exact bound
+      ph[128 + lane] = __expf(fminf(end - cum, 0.0f)) * dt;
       ph[192 + lane] = __expf(cum);
     }
   }
@@ -509,7 +517,7 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
                       dq[4] = {dj.x, dj.y, dj.z, dj.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            Yo = mfma_f32(xq[e], j0 + e <= iy ? gq[e] * __expf(cumi - cq[e]) * dq[e] : 0.0f, Yo);
+            Yo = mfma_f32(xq[e], j0 + e <= iy ? gq[e] * __expf(fminf(cumi - cq[e], 0.0f)) * dq[e] : 0.0f, Yo);
         }
         const float4 wv = *(const float4*)(sPar + 128 + j0);
         const float wq[4] = {wv.x, wv.y, wv.z, wv.w};

@@ -60,11 +60,15 @@ typedef enum {
  * Supported: d_model and d_inner multiples of 128 with d/128 a power of two
  * <= 64; headdim a multiple of 16 and n_heads a multiple of 4; d_state
  * even; d_conv = 4; 1 <= lora_rank <= 32;
- * 1 <= max_batch <= 1024.  norm_eps is the RMSNorm epsilon (1e-5 if 0).   */
+ * 1 <= max_batch <= 1024.  norm_eps is the RMSNorm epsilon (1e-5 if 0).
+ * max_chunk_rows: token rows (summed over the batch) that one prefill chunk
+ * of the batched path holds, 0 for the default 16384; it sizes the
+ * batched-path workspace (0 <= max_chunk_rows <= 2^20).                     */
 typedef struct {
   int32_t n_layer, d_model, d_inner, d_state, headdim, vocab, d_conv, lora_rank;
   int32_t max_batch;
   float norm_eps;
+  int32_t max_chunk_rows;
 } dfssm_config;
 
 /* Per-layer tensor kinds (dfssm_set_tensor / dfssm_get_tensor with layer >= 0). */
@@ -105,10 +109,25 @@ const char* dfssm_version(void);
 /* Message of the last error on this host thread (ctx may be NULL). */
 const char* dfssm_last_error(const dfssm_ctx* ctx);
 
-/* Create a context on `device`: validates cfg, allocates the weights, the
- * recurrent state of max_batch sequences and the activation workspace in
- * device memory (freed by dfssm_destroy).  Synchronous.                      */
-dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, dfssm_ctx** out);
+/* Device bytes a context of this configuration needs when the caller
+ * provides its memory (dfssm_create with an arena): the weights, the
+ * recurrent state of max_batch sequences, the decode workspace, the
+ * persistent kernel's mailboxes and the batched-path workspace of
+ * max(max_chunk_rows, max_batch) token rows.  Host arithmetic only: touches
+ * no device.                                                                */
+dfssm_status dfssm_arena_bytes(const dfssm_config* cfg, size_t* bytes);
+
+/* Create a context on `device`: validates cfg and lays out the weights, the
+ * recurrent state of max_batch sequences, the workspace and the mailboxes in
+ * device memory.  arena: NULL, and the library allocates that memory (freed
+ * by dfssm_destroy; the batched-path workspace then grows on first use), or
+ * a 256-byte-aligned device buffer of at least dfssm_arena_bytes(cfg) bytes
+ * owned by the caller, who must keep it alive until dfssm_destroy returns and
+ * free it afterwards; the context then makes no device allocation of its own
+ * (prefill chunks and traced prefills are bounded by the arena's workspace).
+ * Zeroes the state.  Synchronous.                                          */
+dfssm_status dfssm_create(const dfssm_config* cfg, int32_t device, void* arena, size_t arena_bytes,
+                          dfssm_ctx** out);
 void dfssm_destroy(dfssm_ctx* ctx);
 
 /* Execution path.  DFSSM_PATH_AUTO (default) runs batch-1 decode_step /
@@ -116,17 +135,18 @@ void dfssm_destroy(dfssm_ctx* ctx);
  * across all layers and tokens, hops between workgroups through device
  * memory) when the shape and device allow it, decode of B > 1 sequences and
  * every prefill on the batched path (each layer on all token rows at once:
- * int8 matrix-core GEMMs for the projections, a causal conv over the tokens
- * of each sequence and a sequential SSM scan; prefill in chunks of at most
- * 4096 token rows).  DFSSM_PATH_KERNELS runs everything as per-layer GEMV
- * kernels, one token at a time.  DFSSM_PATH_PERSISTENT is AUTO but fails
- * with DFSSM_E_UNSUPPORTED where batch 1 cannot use the persistent kernel.
- * DFSSM_PATH_GEMM runs every decode (batch 1 included) and prefill on the
- * batched path.                                                             */
+ * int8 matrix-core GEMMs for the projections; the SSM over a prompt as
+ * 64-token chunks of fp32 matrix products with the causal conv inside for
+ * headdim 64 / d_state 128, else a causal conv pass and a sequential scan;
+ * prefill in chunks of at most max_chunk_rows token rows across the batch).
+ * DFSSM_PATH_KERNELS runs everything as per-layer GEMV kernels, one token at
+ * a time.  DFSSM_PATH_PERSISTENT is AUTO but fails with DFSSM_E_UNSUPPORTED
+ * where batch 1 cannot use the persistent kernel.  DFSSM_PATH_GEMM runs
+ * every decode (batch 1 included) and prefill on the batched path.          */
 enum { DFSSM_PATH_AUTO = 0, DFSSM_PATH_KERNELS = 1, DFSSM_PATH_PERSISTENT = 2, DFSSM_PATH_GEMM = 3 };
 dfssm_status dfssm_set_path(dfssm_ctx* ctx, int32_t path);
 
-/* Device bytes the context holds (weights + state + workspace). */
+/* Device bytes the context uses (its arena plus a grown batched-path workspace). */
 dfssm_status dfssm_device_bytes(const dfssm_ctx* ctx, size_t* bytes);
 
 /* Fill every weight with the seeded synthetic generator, on the device, in
@@ -158,15 +178,20 @@ dfssm_status dfssm_reset_state(dfssm_ctx* ctx, int32_t batch, void* stream);
 dfssm_status dfssm_get_state(dfssm_ctx* ctx, int32_t seq, float* host_conv, float* host_ssm);
 dfssm_status dfssm_set_state(dfssm_ctx* ctx, int32_t seq, const float* host_conv, const float* host_ssm);
 
-/* One decode step for sequences [0, B): token d_tok[b] goes through the whole
- * stack, updating the state of slot b.  d_logits: fp32 [B][vocab] or NULL;
+/* One decode step for sequences [0, B) (gist.science summary §2.C: the
+ * decode pipeline of bit-packed scaffold products on int8 operands, the
+ * stateful conv shift register and the SSM recurrence; arxivdaily abstract:
+ * batch-1 decode speed): token d_tok[b] goes through the whole stack,
+ * updating the state of slot b.  d_logits: fp32 [B][vocab] or NULL;
  * d_next: int32 [B] greedy next token (argmax, lowest index on ties) or NULL;
  * d_next may alias d_tok.  A token id outside [0, vocab) is read as 0 and
  * flagged; the flag surfaces as DFSSM_E_DEVICE from dfssm_check_device.     */
 dfssm_status dfssm_decode_step(dfssm_ctx* ctx, const int32_t* d_tok, int32_t B, float* d_logits,
                                int32_t* d_next, void* stream);
 
-/* n_steps greedy decode steps for sequences [0, B).  d_tok [B] holds the
+/* n_steps greedy decode steps for sequences [0, B) (gist.science summary
+ * §2.C: the whole forward replayed as one graph against launch overhead at
+ * batch 1; here one persistent launch at batch 1, a HIP graph otherwise).  d_tok [B] holds the
  * first input tokens and receives the last generated ones; d_out (int32
  * [n_steps][B], may be NULL) receives every generated token.  The argmax is
  * fed back on the device.  With use_graph != 0 one step is captured into a
@@ -175,38 +200,60 @@ dfssm_status dfssm_generate(dfssm_ctx* ctx, int32_t* d_tok, int32_t B, int32_t n
                             int32_t use_graph, void* stream);
 
 /* Prefill sequences [0, B) with the prompt d_tok (int32 [B][T], row-major)
- * starting from their current state; leaves the state after the last token.
+ * starting from their current state (gist.science summary §2.C: the same
+ * stateful conv and SSM recurrence run over the prompt; here the SSM over 64-
+ * token chunks, the pages mentioning chunk boundaries of the state in §2.D);
+ * the result equals T decode steps up to fp32 summation order.  Leaves the
+ * state after the last token.
  * d_last_logits: fp32 [B][vocab] of the last position, or NULL; d_next: int32
  * [B] greedy next token, or NULL.                                           */
 dfssm_status dfssm_prefill(dfssm_ctx* ctx, const int32_t* d_tok, int32_t B, int32_t T, float* d_last_logits,
                            int32_t* d_next, void* stream);
 
-/* One layer for sequences [0, B): d_h_out = d_h_in + mixer(d_h_in), both fp32
- * [B][d_model], using and updating layer `layer` of slots [0, B).  d_q1
- * (int8 [B][d_model]) and d_q2 (int8 [B][d_inner]), when non-NULL, receive
- * the quantised activations fed to in_proj and out_proj.                    */
+/* One layer for sequences [0, B) (gist.science summary §2.B/§2.C: one
+ * Mamba-2 block with its scaffold + LoRA projections, conv shift register and
+ * SSM recurrence): d_h_out = d_h_in + mixer(d_h_in), both fp32 [B][d_model],
+ * using and updating layer `layer` of slots [0, B), on the per-layer GEMV
+ * kernels.  d_q1 (int8 [B][d_model]) and d_q2 (int8 [B][d_inner]), when
+ * non-NULL, receive the quantised activations fed to in_proj and out_proj.  */
 dfssm_status dfssm_layer_step(dfssm_ctx* ctx, int32_t layer, const float* d_h_in, float* d_h_out, int32_t B,
                               int8_t* d_q1, int8_t* d_q2, void* stream);
+
+/* dfssm_layer_step with fp16 input activations: d_h_f16 holds IEEE binary16
+ * values [B][d_model] (upcast exactly to fp32 on the device).              */
+dfssm_status dfssm_layer_step_f16(dfssm_ctx* ctx, int32_t layer, const uint16_t* d_h_f16, float* d_h_out,
+                                  int32_t B, int8_t* d_q1, int8_t* d_q2, void* stream);
 
 /* A decode step that also records its intermediate results: d_h_trace fp32
  * [n_layer + 1][B][d_model] is the residual stream entering every layer and
  * after the last; d_q1_trace int8 [n_layer][B][d_model], d_q2_trace int8
  * [n_layer][B][d_inner] and d_qf int8 [B][d_model] (each may be NULL) are the
- * quantised inputs of every in_proj, out_proj and of the LM head.          */
+ * quantised inputs of every in_proj, out_proj and of the LM head;
+ * d_acc1_trace int32 [n_layer][B][d_in_proj] and d_acc2_trace int32
+ * [n_layer][B][d_model] (each may be NULL) receive the exact scaffold sums
+ * sum_i w(o,i) q_i of every in_proj and out_proj row (gist.science summary
+ * §2.C: the 1-bit scaffold used as int8 operands of an integer product).
+ * Runs on the same path as dfssm_decode_step for this B; at batch 1 on the
+ * persistent path it is the kernel's tracing instantiation, one token per
+ * launch.                                                                   */
 dfssm_status dfssm_trace_step(dfssm_ctx* ctx, const int32_t* d_tok, int32_t B, float* d_h_trace,
                               int8_t* d_q1_trace, int8_t* d_q2_trace, int8_t* d_qf, float* d_logits,
-                              void* stream);
+                              int32_t* d_acc1_trace, int32_t* d_acc2_trace, void* stream);
 
-/* Prefill of sequences [0, B) on the batched path (one chunk: 1 <= B T <=
- * 4096) that also records its intermediate results, row m = b T + t:
- * d_h_trace fp32 [n_layer + 1][B T][d_model], d_q1_trace int8
- * [n_layer][B T][d_model], d_q2_trace int8 [n_layer][B T][d_inner] (each
- * may be NULL but d_h_trace), d_qf int8 [B][d_model] (LM-head input of the
- * last position) and d_logits fp32 [B][vocab] (last position), each may be
- * NULL.  Leaves the state after the last token.  Enqueued.                 */
+/* Prefill of sequences [0, B) on the batched path in one chunk (1 <= B T <=
+ * 16384 token rows, the prefill chunk size) that also records its
+ * intermediate results, row m = b T + t: d_h_trace fp32
+ * [n_layer + 1][B T][d_model], d_q1_trace int8 [n_layer][B T][d_model],
+ * d_q2_trace int8 [n_layer][B T][d_inner] (each may be NULL but d_h_trace),
+ * d_qf int8 [B][d_model] (LM-head input of the last position), d_logits fp32
+ * [B][vocab] (last position), d_acc1_trace int32 [n_layer][B T][d_in_proj]
+ * and d_acc2_trace int32 [n_layer][B T][d_model] (scaffold sums as for
+ * dfssm_trace_step), each may be NULL.  Same kernels and launch shapes as
+ * dfssm_prefill of that chunk.  Leaves the state after the last token.
+ * Enqueued.                                                                */
 dfssm_status dfssm_trace_prefill(dfssm_ctx* ctx, const int32_t* d_tok, int32_t B, int32_t T, float* d_h_trace,
                                  int8_t* d_q1_trace, int8_t* d_q2_trace, int8_t* d_qf, float* d_logits,
-                                 void* stream);
+                                 int32_t* d_acc1_trace, int32_t* d_acc2_trace, void* stream);
 
 /* Kernel timing for roofline reports.  Launches one kernel of the batch-B
  * decode step `iters` times back to back on `stream` (layer i % n_layer on
@@ -252,8 +299,10 @@ dfssm_status dfssm_check_device(dfssm_ctx* ctx, void* stream);
 
 /* ---- stateless kernel entry points (tests) ---------------------------- */
 
-/* Per-row int8 quantiser (see the conventions above): d_u fp32 [rows][n] ->
- * d_q int8 [rows][n], d_s fp32 [rows].  1 <= n <= 65536.                    */
+/* Per-row int8 quantiser (see the conventions above; the pages imply int8
+ * activations by the int8 x int8 product of gist.science summary §2.C):
+ * d_u fp32 [rows][n] -> d_q int8 [rows][n], d_s fp32 [rows].
+ * 1 <= n <= 65536.                                                          */
 dfssm_status dfssm_k_quant(const float* d_u, int32_t rows, int32_t n, int8_t* d_q, float* d_s, void* stream);
 
 /* Scaffold + LoRA projection of B int8 activation rows (gist.science summary
@@ -262,8 +311,9 @@ dfssm_status dfssm_k_quant(const float* d_u, int32_t rows, int32_t n, int8_t* d_
  * y[b][o] = float(acc) * sw[o] * s[b] + sB[o] * sum_k B[o][k] t[b][k].
  * d_bits uint32 [d_out][d_in/32], d_A int8 [r][d_in], d_B int8 [d_out][r],
  * d_q int8 [B][d_in], d_s fp32 [B]; outputs d_acc int32 [B][d_out] (or NULL)
- * and d_y fp32 [B][d_out].  The batch-1 path is the fused bit-unpack GEMV;
- * larger B may use the int8 matrix-core GEMM.                             */
+ * and d_y fp32 [B][d_out].  Runs the per-layer path's bit-plane GEMV for
+ * any B (the int8 matrix-core GEMM is dfssm_k_gemm).  Enqueued; uses
+ * stream-ordered temporary memory.                                          */
 dfssm_status dfssm_k_proj(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
                           const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out, int32_t r,
                           const int8_t* d_q, const float* d_s, int32_t B, int32_t* d_acc, float* d_y,

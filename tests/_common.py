@@ -45,11 +45,49 @@ def trace_to_numpy(tr):
     return {k: v.cpu().numpy() for k, v in tr.items()}
 
 
-def oracle_follow_step(om, st, tok, tr, b=0):
+# Codes the GPU takes on the other side of a rounding tie than the oracle
+# (accepted by the oracle within its tie band) come from the two sides'
+# different fp32 reduction orders: the scaled value x = u * 127 / amax differs
+# by at most ~1e-4 (TIE_BAND's derivation), so a fraction of about 2e-4 of
+# the codes can lie that close to a tie, and far fewer do in practice since
+# most |x| are well below 127.  A systematic off-by-one near ties would take
+# every code of the 2e-3 band (2 x TIE_BAND per unit of x).  The follow tests
+# assert the accepted flips stay below this fraction of all codes.
+MAX_FLIP_FRACTION = 5e-4
+
+# Tie band for long runs (thousands of tokens through all 48 layers).  The
+# GPU carries the recurrence in fp32 (the prefill's chunked scan sums it in
+# another order) and the oracle in fp64, each on its own values.  With the
+# smallest decays of the workload's parameters (A = exp(A_log) near 1, dt
+# near 1e-3) a state remembers ~1000 tokens, so the SSM output can drift by up
+# to ~6e-5 relative between the two (1000 fp32 roundings), which moves the
+# gated norm's scaled value x = u 127 / amax by up to ~7.6e-3; measured: a
+# code 4.7e-3 from its tie after 1336 of 2048 prefill tokens.  A code within
+# 1e-2 of a tie is then still a correct rounding of a value both sides may
+# hold.  The flip-fraction bound above still separates these rare flips
+# (~2e-5 of the codes, measured) from a systematic off-by-one (2e-2 of the
+# codes with this band).
+LONG_RUN_TIE_BAND = 1e-2
+
+
+def new_flip_stats():
+    return {"flips": 0, "codes": 0}
+
+
+def assert_flip_fraction(stats, what=""):
+    codes = max(stats.get("codes", 0), 1)
+    frac = stats.get("flips", 0) / codes
+    assert frac <= MAX_FLIP_FRACTION, (
+        f"{what}: {stats.get('flips', 0)} of {codes} int8 codes taken on the other side of a tie "
+        f"({frac:.2e} > {MAX_FLIP_FRACTION:.0e})")
+
+
+def oracle_follow_step(om, st, tok, tr, b=0, stats=None):
     """One oracle decode step of sequence b that takes the GPU's int8 codes
     (recorded in trace `tr`) wherever they are correct roundings of the
     oracle's own values -- several codes are correct near a rounding tie --
     and otherwise raises.  The oracle runs on its own residual stream.
+    stats (optional) counts the accepted codes that differ from the oracle's.
 
     Returns (h per layer [L+1][d_model], logits, argmax)."""
     import oracle
@@ -58,7 +96,77 @@ def oracle_follow_step(om, st, tok, tr, b=0):
     hs = [h]
     for l in range(s.n_layer):
         h = oracle.layer_step(s, om.weights["layers"][l], h, st.conv[l], st.ssm[l],
-                              q1_force=tr["q1"][l, b], q2_force=tr["q2"][l, b])
+                              q1_force=tr["q1"][l, b], q2_force=tr["q2"][l, b], stats=stats)
         hs.append(h)
-    best, logits, _, _ = om.lm_head(h, qf_force=tr["qf"][b])
+    best, logits, _, _ = om.lm_head(h, qf_force=tr["qf"][b], stats=stats)
     return np.array(hs), logits, best
+
+
+def follow_prefill(om, s, toks, tr, b, T, check_h_at=(), what="", st=None, stats=None):
+    """Oracle run of sequence b over its T prompt tokens (from state st, else
+    from zero), taking the GPU's int8 codes recorded in the prefill trace `tr`
+    (rows m = b T + t) where they are correct roundings.  The residual stream
+    entering every layer is compared at the token positions in check_h_at.
+    Returns (state, logits of the last position)."""
+    import oracle
+    st = oracle.State(s) if st is None else st
+    h = None
+    for t in range(T):
+        m = b * T + t
+        h = om.embed(int(toks[b, t]))
+        for l in range(s.n_layer):
+            if t in check_h_at:
+                assert_close(tr["h"][l, m], h, what=f"{what} h seq {b} token {t} layer {l}")
+            h = oracle.layer_step(s, om.weights["layers"][l], h, st.conv[l], st.ssm[l],
+                                  q1_force=tr["q1"][l, m], q2_force=tr["q2"][l, m], stats=stats)
+        if t in check_h_at:
+            assert_close(tr["h"][s.n_layer, m], h, what=f"{what} h seq {b} token {t} out")
+    _, logits, _, _ = om.lm_head(h, qf_force=tr["qf"][b], stats=stats)
+    return st, logits
+
+
+def check_acc(om, tr, rows, layers, what=""):
+    """The traced int32 scaffold sums of rows `rows` equal the oracle's exact
+    sums on the traced int8 codes, bit for bit, at every layer in `layers`."""
+    import oracle
+    for l in layers:
+        lay = om.weights["layers"][l]
+        for m in rows:
+            a1 = oracle.sign_acc(lay["in_signs"], tr["q1"][l, m]) if "in_signs" in lay else \
+                oracle.scaffold_acc(lay["in_bits"], tr["q1"][l, m])
+            a2 = oracle.sign_acc(lay["out_signs"], tr["q2"][l, m]) if "out_signs" in lay else \
+                oracle.scaffold_acc(lay["out_bits"], tr["q2"][l, m])
+            assert np.array_equal(tr["acc1"][l, m], a1), f"{what} in_proj sums layer {l} row {m}"
+            assert np.array_equal(tr["acc2"][l, m], a2), f"{what} out_proj sums layer {l} row {m}"
+
+
+def explain_rejection(s, layer, h, states, q1g, q2g, h_gpu=None):
+    """Where a GPU int8 code fell outside the oracle's tie band: for the
+    layer's two quantisers, the oracle's scaled value x = u 127 / amax (fp32)
+    at each rejected code, its distance to the tie the GPU's code implies, and
+    the GPU's relative deviation of the residual stream (if given)."""
+    import oracle
+    conv, ssm = states[0].copy(), states[1].copy()
+    out = []
+
+    def scaled(u):
+        uf = np.asarray(u, np.float64).astype(np.float32)
+        amax = np.float32(np.max(np.abs(uf)))
+        return (uf * (np.float32(127.0) / amax)).astype(np.float64) if amax > 0 else uf.astype(np.float64)
+
+    w = layer["norm_w"].astype(np.float64)
+    u1 = h / np.sqrt(np.mean(h * h) + 1e-5) * w
+    x1 = scaled(u1)
+    _, d = oracle.layer_step(s, layer, h, conv, ssm, want_dbg=True, q1_force=q1g)
+    x2 = scaled(d["u2"])
+    for name, x, g in (("q1", x1, q1g), ("q2", x2, q2g)):
+        own = np.clip(np.rint(x), -127, 127)
+        bad = np.nonzero(own != g.astype(np.float64))[0]
+        for i in bad[:4]:
+            tie = own[i] + 0.5 * np.sign(float(g[i]) - own[i])
+            out.append(f"{name}[{i}]: gpu {int(g[i])} oracle {int(own[i])} x {x[i]:.6f} |x - tie| {abs(x[i] - tie):.2e}")
+        out.append(f"{name}: {len(bad)} codes differ")
+    if h_gpu is not None:
+        rms = float(np.sqrt(np.mean(h * h)))
+        out.append(f"residual max |gpu - oracle| / rms {float(np.max(np.abs(h_gpu - h))) / rms:.2e}")
+    return "; ".join(out)

@@ -19,8 +19,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("dfssm_create", "dfssm_load_synthetic", "dfssm_decode_step", "dfssm_prefill", "dfssm_generate",
-              "dfssm_k_proj", "dfssm_k_quant", "dfssm_destroy"):
+    for n in ("dfssm_arena_bytes", "dfssm_create", "dfssm_load_synthetic", "dfssm_decode_step", "dfssm_prefill",
+              "dfssm_generate", "dfssm_layer_step", "dfssm_layer_step_f16", "dfssm_trace_step", "dfssm_k_proj",
+              "dfssm_k_quant", "dfssm_k_gemm", "dfssm_get_state", "dfssm_set_state", "dfssm_destroy"):
         assert n in names
 
 
@@ -42,9 +43,32 @@ def test_version_and_argument_errors_without_gpu():
     L = _lib.load()
     assert b"gfx950" in L.dfssm_version()
     # host-side validation fails before any device work
-    cfg = _lib.DfssmConfig(1, 100, 512, 16, 32, 10, 4, 16, 1, 1e-5)  # d_model not a multiple of 128
+    cfg = _lib.DfssmConfig(1, 100, 512, 16, 32, 10, 4, 16, 1, 1e-5, 0)  # d_model not a multiple of 128
     h = ctypes.c_void_p()
-    rc = L.dfssm_create(ctypes.byref(cfg), 0, ctypes.byref(h))
+    rc = L.dfssm_create(ctypes.byref(cfg), 0, None, 0, ctypes.byref(h))
     assert rc == -5 and not h.value
     assert b"d_model" in L.dfssm_last_error(None)
     assert L.dfssm_k_quant(None, 1, 1, None, None, None) == -1
+    n = ctypes.c_size_t()
+    assert L.dfssm_arena_bytes(ctypes.byref(cfg), ctypes.byref(n)) == -5
+
+
+def test_arena_bytes_host_only():
+    # the arena size is host arithmetic: no device is touched
+    import synth
+    from bit_quantized_mamba_amd import Engine
+    s = synth.FULL_1P3B
+
+    def size(max_batch, rows=0):
+        return Engine.arena_bytes(s.n_layer, s.d_model, s.d_inner, s.d_state, s.headdim, s.vocab,
+                                  max_batch=max_batch, max_chunk_rows=rows)
+
+    one = size(1)
+    weights = sum(synth.model_bytes(s).values())
+    state_per_seq = 4 * s.n_layer * (s.n_heads * s.headdim * s.d_state + (s.d_conv - 1) * s.conv_dim)
+    assert one > weights + state_per_seq
+    # one more sequence slot costs at least its recurrent state
+    assert size(2) - one >= state_per_seq
+    # the batched-path workspace grows with the chunk rows (fp32 h, in_proj output, conv output, g per row)
+    per_row = 4 * (s.d_model + s.d_in_proj + s.conv_dim + s.d_inner)
+    assert size(1, 32768) - size(1, 16384) >= 16384 * per_row

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from tests._common import assert_close, engine, oracle_follow_step, token_ok, trace_to_numpy
+from tests._common import assert_close, engine, follow_prefill, oracle_follow_step, token_ok, trace_to_numpy
 
 pytestmark = pytest.mark.gpu
 
@@ -147,23 +147,7 @@ def test_1p3b_layer_decode_on_gemm_path(B):
 # ---------------------------------------------------------------------------
 
 def _follow_prefill(om, s, toks, tr, b, T, check_h_at=(), h_tol_what="", st=None):
-    """Oracle run of sequence b over its T prompt tokens (from state st, else
-    from zero), taking the GPU's int8 codes where they are correct roundings.
-    Returns (state, logits of the last position)."""
-    st = oracle.State(s) if st is None else st
-    h = None
-    for t in range(T):
-        m = b * T + t
-        h = om.embed(int(toks[b, t]))
-        for l in range(s.n_layer):
-            if t in check_h_at:
-                assert_close(tr["h"][l, m], h, what=f"{h_tol_what} h seq {b} token {t} layer {l}")
-            h = oracle.layer_step(s, om.weights["layers"][l], h, st.conv[l], st.ssm[l],
-                                  q1_force=tr["q1"][l, m], q2_force=tr["q2"][l, m])
-        if t in check_h_at:
-            assert_close(tr["h"][s.n_layer, m], h, what=f"{h_tol_what} h seq {b} token {t} out")
-    _, logits, _, _ = om.lm_head(h, qf_force=tr["qf"][b])
-    return st, logits
+    return follow_prefill(om, s, toks, tr, b, T, check_h_at=check_h_at, what=h_tol_what, st=st)
 
 
 @pytest.mark.parametrize("B,T", [(3, 37), (1, 1), (2, 64)])

@@ -31,9 +31,10 @@ def test_layer_steps_match_oracle(shape, steps):
     ss = np.zeros((shape.n_heads, shape.headdim, shape.d_state))
     worst = 0.0
     for t in range(steps):
+        # fp16 activations on the device, as the single-layer workload feeds them
         h16 = synth.gen_fp16_normal(seed, 1, shape.d_model, start=t * shape.d_model)
         h = h16.astype(np.float32)
-        hg, q1, q2 = eng.layer_step(0, torch.from_numpy(h[None]).cuda(), want_codes=True)
+        hg, q1, q2 = eng.layer_step_f16(0, torch.from_numpy(h16[None]).cuda(), want_codes=True)
         hg = hg.cpu().numpy()[0]
         ho = oracle.layer_step(shape, lay, h.astype(np.float64), cs, ss,
                                q1_force=q1.cpu().numpy()[0], q2_force=q2.cpu().numpy()[0])
@@ -322,3 +323,47 @@ def test_errors_are_reported_without_work():
         eng.check()
     eng.check()  # flag cleared
     eng.close()
+
+
+# ---------------------------------------------------------------------------
+# caller-provided arena
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [synth.TINY, synth.LAYER_1P3B])
+def test_caller_arena_equals_library_memory(shape):
+    # an engine living in a caller's arena (no device allocation of its own)
+    # computes exactly what a library-allocated engine with the same chunk
+    # rows computes (prefill of 2 x 200 tokens in chunks of 64 rows, graph
+    # replay of decode steps); requests beyond the arena's workspace are
+    # refused without work
+    from bit_quantized_mamba_amd import DfssmError, Engine
+    seed = synth.SEED_BASE + 6
+    B, T = 2, 200
+    rows = 64
+    nbytes = Engine.arena_bytes(shape.n_layer, shape.d_model, shape.d_inner, shape.d_state, shape.headdim,
+                                shape.vocab, max_batch=B, max_chunk_rows=rows)
+    arena = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    assert arena.data_ptr() % 256 == 0
+    small = torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(DfssmError):
+        Engine.from_shape(shape, max_batch=B, max_chunk_rows=rows, arena=small)
+    ea = Engine.from_shape(shape, max_batch=B, max_chunk_rows=rows, arena=arena)
+    eb = Engine.from_shape(shape, max_batch=B, max_chunk_rows=rows)
+    toks = synth.gen_tokens(seed, 3, B * T, shape.vocab).reshape(B, T)
+    outs = []
+    for e in (ea, eb):
+        e.load_synthetic(seed)
+        e.reset_state(B)
+        lg, nx = e.prefill(_i32(toks))
+        gen = e.generate(nx, 6, use_graph=True)
+        outs.append((lg.cpu().numpy(), gen.cpu().numpy(), [e.get_state(b) for b in range(B)]))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    for b in range(B):
+        assert np.array_equal(outs[0][2][b][0], outs[1][2][b][0]) and np.array_equal(outs[0][2][b][1], outs[1][2][b][1])
+    with pytest.raises(DfssmError):  # 2 x 200 rows do not fit the arena's 64-row workspace
+        ea.trace_prefill(_i32(toks))
+    assert ea.device_bytes() <= nbytes
+    ea.check()
+    ea.close()
+    eb.close()
+    del arena
