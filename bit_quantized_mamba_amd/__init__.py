@@ -19,7 +19,8 @@ LAYER_KINDS = ["in_bits", "in_sw", "in_A", "in_sA", "in_B", "in_sB", "out_bits",
                "out_B", "out_sB", "conv_w", "conv_b", "A_log", "dt_bias", "D", "norm_w", "gnorm_w"]
 GLOBAL_KINDS = ["E", "sE", "final_norm"]
 
-__all__ = ["Engine", "DfssmError", "k_quant", "k_proj", "k_gemm", "version", "LAYER_KINDS", "GLOBAL_KINDS"]
+__all__ = ["Engine", "DfssmError", "k_quant", "k_proj", "k_gemm", "k_gemm_noalloc", "version", "LAYER_KINDS",
+           "GLOBAL_KINDS"]
 
 
 def version() -> str:
@@ -321,6 +322,22 @@ def k_gemm(bits, sw, A, sA, Bm, sB, q, s, stream=None):
     y = torch.empty((M, d_out), dtype=torch.float32, device=q.device)
     call("dfssm_k_gemm", _dp(bits), _dp(sw), _dp(A), _dp(sA), _dp(Bm), _dp(sB), d_in, d_out, _dp(q), _dp(s), M,
          _dp(acc), _dp(y), _stream(stream))
+    return acc, y
+
+
+def k_gemm_noalloc(bits, sw, A, sA, Bm, sB, q, s, acc=None, y=None, stream=None):
+    """k_gemm without any device allocation by the library (static per-GPU scratch; outputs may be
+    passed in so the call allocates nothing at all)."""
+    torch = _torch()
+    d_out = bits.shape[0]
+    d_in = bits.shape[1] * 32
+    M = q.shape[0]
+    if acc is None:
+        acc = torch.empty((M, d_out), dtype=torch.int32, device=q.device)
+    if y is None:
+        y = torch.empty((M, d_out), dtype=torch.float32, device=q.device)
+    call("dfssm_k_gemm_noalloc", _dp(bits), _dp(sw), _dp(A), _dp(sA), _dp(Bm), _dp(sB), d_in, d_out, _dp(q), _dp(s),
+         M, _dp(acc), _dp(y), _stream(stream))
     return acc, y
 
 

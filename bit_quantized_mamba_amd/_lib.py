@@ -47,6 +47,7 @@ EXPORTS = {
     "dfssm_k_quant": [_p, _i32, _i32, _p, _p, _p],
     "dfssm_k_proj": [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p],
     "dfssm_k_gemm": [_p, _p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _p, _p, _p],
+    "dfssm_k_gemm_noalloc": [_p, _p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _p, _p, _p],
 }
 _RESTYPE = {"dfssm_version": ctypes.c_char_p, "dfssm_last_error": ctypes.c_char_p, "dfssm_destroy": None}
 

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -14,6 +15,13 @@
 #include "persistent.h"
 
 using namespace dfssm;
+
+// Scratch of dfssm_k_gemm_noalloc: a file-scope device array, one copy per
+// GPU for the life of the process.  In host code the array's name stands for
+// no device address (a kernel given it would fault); host code uses only the
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -803,6 +811,29 @@ hipError_t k_gemm_run(const uint32_t* d_bits, const float* d_sw, const int8_t* d
   return launch_bitgemm(a, GEMM_EPI_STORE, st);
 }
 
+// The allocation-free entry point's scratch (declared at file scope above)
+// is reached only through the per-device address that hipGetSymbolAddress
+// returns, taken once per device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dfssm_status noalloc_scratch(char** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DFSSM_E_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DFSSM_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return DFSSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1376,6 +1407,25 @@ dfssm_status dfssm_k_gemm(const uint32_t* d_bits, const float* d_sw, const int8_
   const hipError_t e2 = hipFreeAsync(tmp, st);
   if (e != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_gemm: ") + hipGetErrorString(e));
   if (e2 != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_gemm free: ") + hipGetErrorString(e2));
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_k_gemm_noalloc(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
+                                  const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out,
+                                  const int8_t* d_q, const float* d_s, int32_t M, int32_t* d_acc, float* d_y,
+                                  void* stream) {
+  dfssm_status v = check_k_gemm(d_bits, d_sw, d_A, d_sA, d_B, d_sB, d_in, d_out, d_q, d_s, M, d_y);
+  if (v != DFSSM_OK) return v;
+  const size_t need = k_gemm_scratch_bytes(d_in, M);
+  if (need > kNoAllocScratchBytes)
+    return fail(DFSSM_E_INVALID, "k_gemm_noalloc: M * d_in + 68 M = " + std::to_string(need) +
+                                     " bytes of operand scratch exceed the static " +
+                                     std::to_string(kNoAllocScratchBytes) + "-byte buffer");
+  char* tmp = nullptr;
+  if ((v = noalloc_scratch(&tmp)) != DFSSM_OK) return v;
+  const hipError_t e = k_gemm_run(d_bits, d_sw, d_A, d_sA, d_B, d_sB, d_in, d_out, d_q, d_s, M, d_acc, d_y, tmp,
+                                  S(stream));
+  if (e != hipSuccess) return fail(DFSSM_E_HIP, std::string("k_gemm_noalloc: ") + hipGetErrorString(e));
   return DFSSM_OK;
 }
 

@@ -330,6 +330,20 @@ dfssm_status dfssm_k_gemm(const uint32_t* d_bits, const float* d_sw, const int8_
                           const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out, const int8_t* d_q,
                           const float* d_s, int32_t M, int32_t* d_acc, float* d_y, void* stream);
 
+/* dfssm_k_gemm for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * same arguments, same kernels and results, no hipMalloc / hipFree / stream-
+ * ordered allocation.  The operand scratch (M * d_in + 68 M bytes, each part
+ * rounded up to 256) lives in a static 8 MiB device buffer that each GPU the
+ * library runs on holds until the process ends; larger requests fail with
+ * DFSSM_E_INVALID before any work.  Every call on one GPU shares that buffer:
+ * calls that overlap on one GPU (different streams or threads) race and must
+ * be serialised by the caller.  Enqueued.                                   */
+dfssm_status dfssm_k_gemm_noalloc(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
+                                  const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out,
+                                  const int8_t* d_q, const float* d_s, int32_t M, int32_t* d_acc, float* d_y,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif
