@@ -19,8 +19,8 @@ LAYER_KINDS = ["in_bits", "in_sw", "in_A", "in_sA", "in_B", "in_sB", "out_bits",
                "out_B", "out_sB", "conv_w", "conv_b", "A_log", "dt_bias", "D", "norm_w", "gnorm_w"]
 GLOBAL_KINDS = ["E", "sE", "final_norm"]
 
-__all__ = ["Engine", "DfssmError", "k_quant", "k_proj", "k_gemm", "k_gemm_noalloc", "version", "LAYER_KINDS",
-           "GLOBAL_KINDS"]
+__all__ = ["Engine", "DfssmError", "k_quant", "k_proj", "k_gemm", "k_gemm_noalloc", "k_density_encode",
+           "k_density_decode", "version", "LAYER_KINDS", "GLOBAL_KINDS"]
 
 
 def version() -> str:
@@ -293,6 +293,27 @@ class Engine:
         call("dfssm_profile_persistent", self._h, _dp(tok), n_tokens, _dp(prof), prof_tokens, _stream(stream))
         return prof
 
+    # -- density-field state codec ---------------------------------------------
+    def state_pack(self, seq0: int = 0, nseq: int = 1, stream=None):
+        """Density fields of the SSM state of slots [seq0, seq0 + nseq): (field uint32
+        [nseq][L][H][P][d_state/8], scale fp32 [nseq][L][H][P]) on the device."""
+        torch = _torch()
+        dev = torch.device("cuda", self.device)
+        field = torch.empty((nseq, self.n_layer, self.n_heads, self.headdim, self.d_state // 8), dtype=torch.int32,
+                            device=dev)
+        scale = torch.empty((nseq, self.n_layer, self.n_heads, self.headdim), dtype=torch.float32, device=dev)
+        call("dfssm_state_pack", self._h, seq0, nseq, _dp(field), _dp(scale), _stream(stream))
+        return field, scale
+
+    def state_unpack(self, field, scale, seq0: int = 0, stream=None) -> None:
+        """Replace the SSM state of slots [seq0, seq0 + nseq) by the fields' readout."""
+        nseq = field.shape[0]
+        call("dfssm_state_unpack", self._h, seq0, nseq, _dp(field), _dp(scale), _stream(stream))
+
+    def state_roundtrip(self, seq0: int = 0, nseq: int = 1, stream=None) -> None:
+        """Pass the SSM state of slots [seq0, seq0 + nseq) through the density codec in place."""
+        call("dfssm_state_roundtrip", self._h, seq0, nseq, _stream(stream))
+
     def check(self, stream=None) -> None:
         call("dfssm_check_device", self._h, _stream(stream))
 
@@ -310,6 +331,26 @@ def k_quant(u, stream=None):
     s = torch.empty((rows,), dtype=torch.float32, device=u.device)
     call("dfssm_k_quant", _dp(u), rows, n, _dp(q), _dp(s), _stream(stream))
     return q, s
+
+
+def k_density_encode(x, stream=None):
+    """Density fields of fp32 rows x [rows][n] (n in 16, 32, 64, 128): (field int32 [rows][n/8], scale [rows])."""
+    torch = _torch()
+    rows, n = x.shape
+    field = torch.empty((rows, n // 8), dtype=torch.int32, device=x.device)
+    scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    call("dfssm_k_density_encode", _dp(x), rows, n, _dp(field), _dp(scale), _stream(stream))
+    return field, scale
+
+
+def k_density_decode(field, scale, stream=None):
+    """Popcount readout of density fields: fp32 [rows][n]."""
+    torch = _torch()
+    rows, w = field.shape
+    n = 8 * w
+    x = torch.empty((rows, n), dtype=torch.float32, device=field.device)
+    call("dfssm_k_density_decode", _dp(field), _dp(scale), rows, n, _dp(x), _stream(stream))
+    return x
 
 
 def k_gemm(bits, sw, A, sA, Bm, sB, q, s, stream=None):

@@ -42,6 +42,11 @@ EXPORTS = {
     "dfssm_trace_step": [_p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p],
     "dfssm_trace_prefill": [_p, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p],
     "dfssm_check_device": [_p, _p],
+    "dfssm_state_pack": [_p, _i32, _i32, _p, _p, _p],
+    "dfssm_state_unpack": [_p, _i32, _i32, _p, _p, _p],
+    "dfssm_state_roundtrip": [_p, _i32, _i32, _p],
+    "dfssm_k_density_encode": [_p, _i32, _i32, _p, _p, _p],
+    "dfssm_k_density_decode": [_p, _p, _i32, _i32, _p, _p],
     "dfssm_profile_persistent": [_p, _p, _i32, _p, _i32, _p],
     "dfssm_time_kernel": [_p, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_float), _p],
     "dfssm_k_quant": [_p, _i32, _i32, _p, _p, _p],

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libdfssm.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["gen.hip", "kernels.hip", "persistent.hip", "gemm.hip", "scan.hip", "runtime.hip"]
+SOURCES = ["gen.hip", "kernels.hip", "persistent.hip", "gemm.hip", "scan.hip", "codec.hip", "runtime.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          # packed fp32 instructions stay off in every kernel

@@ -325,6 +325,24 @@ hipError_t launch_argmax(const float* logits, int V, int B, int32_t* next, int32
 hipError_t launch_quant_rows(const float* u, int rows, int n, int8_t* q, float* s, hipStream_t st);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+
+// density-field state codec (codec.hip)
+struct DensityStateArgs {
+  float* ssm;         // sequence s0's state, layout [L][H][P/16][N][16]
+  size_t bstride;     // floats between sequences
+  int rows_per_seq;   // L * H * P
+  int P;
+  int total_rows;     // rows_per_seq * sequences
+  uint32_t* field;    // [total_rows][N / 8] (modes 0, 1)
+  float* scale;       // [total_rows]
+};
+bool density_supported(int n);
+hipError_t launch_density_encode_rows(const float* x, int rows, int n, uint32_t* field, float* scale,
+                                      hipStream_t st);
+hipError_t launch_density_decode_rows(const uint32_t* field, const float* scale, int rows, int n, float* x,
+                                      hipStream_t st);
+// mode 0 pack, 1 unpack, 2 round trip in place
+hipError_t launch_density_state(const DensityStateArgs& a, int n, int mode, hipStream_t st);
 hipError_t launch_f16_to_f32(const void* src, float* dst, size_t n, hipStream_t st);
 
 }  // namespace dfssm

@@ -1395,6 +1395,57 @@ dfssm_status dfssm_k_proj(const uint32_t* d_bits, const float* d_sw, const int8_
   return DFSSM_OK;
 }
 
+dfssm_status dfssm_k_density_encode(const float* d_x, int32_t rows, int32_t n, uint32_t* d_field, float* d_scale,
+                                   void* stream) {
+  if (!d_x || !d_field || !d_scale) return fail(DFSSM_E_INVALID, "null pointer");
+  if (rows < 1) return fail(DFSSM_E_INVALID, "rows must be >= 1");
+  if (!density_supported(n)) return fail(DFSSM_E_UNSUPPORTED, "n must be 16, 32, 64 or 128");
+  HIP_TRY(launch_density_encode_rows(d_x, rows, n, d_field, d_scale, S(stream)));
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_k_density_decode(const uint32_t* d_field, const float* d_scale, int32_t rows, int32_t n, float* d_x,
+                                   void* stream) {
+  if (!d_x || !d_field || !d_scale) return fail(DFSSM_E_INVALID, "null pointer");
+  if (rows < 1) return fail(DFSSM_E_INVALID, "rows must be >= 1");
+  if (!density_supported(n)) return fail(DFSSM_E_UNSUPPORTED, "n must be 16, 32, 64 or 128");
+  HIP_TRY(launch_density_decode_rows(d_field, d_scale, rows, n, d_x, S(stream)));
+  return DFSSM_OK;
+}
+
+static dfssm_status density_state(dfssm_ctx* c, int32_t seq0, int32_t nseq, uint32_t* field, float* scale, int mode,
+                                  void* stream) {
+  dfssm_status v = check_ctx(c, false);
+  if (v != DFSSM_OK) return v;
+  if (seq0 < 0 || nseq < 1 || seq0 + nseq > c->maxB) return fail(DFSSM_E_INVALID, "sequence slots out of range");
+  if (!density_supported(c->N)) return fail(DFSSM_E_UNSUPPORTED, "the density codec needs d_state 16, 32, 64 or 128");
+  if (mode != 2 && (!field || !scale)) return fail(DFSSM_E_INVALID, "null field or scale pointer");
+  DensityStateArgs a{};
+  a.ssm = c->ssm + (size_t)seq0 * c->ssm_bstride;
+  a.bstride = c->ssm_bstride;
+  a.rows_per_seq = c->L * c->H * c->P;
+  a.P = c->P;
+  a.total_rows = a.rows_per_seq * nseq;
+  a.field = field;
+  a.scale = scale;
+  HIP_TRY(launch_density_state(a, c->N, mode, S(stream)));
+  return DFSSM_OK;
+}
+
+dfssm_status dfssm_state_pack(dfssm_ctx* c, int32_t seq0, int32_t nseq, uint32_t* d_field, float* d_scale,
+                              void* stream) {
+  return density_state(c, seq0, nseq, d_field, d_scale, 0, stream);
+}
+
+dfssm_status dfssm_state_unpack(dfssm_ctx* c, int32_t seq0, int32_t nseq, const uint32_t* d_field,
+                                const float* d_scale, void* stream) {
+  return density_state(c, seq0, nseq, (uint32_t*)d_field, (float*)d_scale, 1, stream);
+}
+
+dfssm_status dfssm_state_roundtrip(dfssm_ctx* c, int32_t seq0, int32_t nseq, void* stream) {
+  return density_state(c, seq0, nseq, nullptr, nullptr, 2, stream);
+}
+
 dfssm_status dfssm_k_gemm(const uint32_t* d_bits, const float* d_sw, const int8_t* d_A, const float* d_sA,
                           const int8_t* d_B, const float* d_sB, int32_t d_in, int32_t d_out, const int8_t* d_q,
                           const float* d_s, int32_t M, int32_t* d_acc, float* d_y, void* stream) {

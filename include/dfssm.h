@@ -294,6 +294,31 @@ dfssm_status dfssm_time_kernel(dfssm_ctx* ctx, int32_t kernel, int32_t B, int32_
 dfssm_status dfssm_profile_persistent(dfssm_ctx* ctx, int32_t* d_tok, int32_t n_tokens, uint64_t* d_prof,
                                       int32_t prof_tokens, void* stream);
 
+/* Density-field representation of the SSM state (gist.science summary §2.D:
+ * a binary field with about 4 d_state cells, built by normalisation,
+ * sigma-delta injection with error feedback and binarisation, read back by
+ * popcount, applied at chunk boundaries).  One field per state row (the
+ * d_state values of one head channel), 4 cells per value: scale = max |x|,
+ * density d = (x / scale + 1) / 2, a first-order sigma-delta modulator over
+ * the row's 4 d_state cells in order (a = d + e; cell = (a >= 1/2); e = a -
+ * cell; e starts at 0), readout x' = scale * (popcount of the value's 4 cells
+ * - 2) / 2; every step one fp32 operation.  Cell c of a row is bit c % 32 of
+ * word c / 32: d_state / 8 uint32 words and one fp32 scale per row (7.5 times
+ * smaller than the fp32 row at d_state 128).
+ *
+ * dfssm_state_pack writes the fields of sequence slots [seq0, seq0 + nseq):
+ * d_field uint32 [nseq][n_layer][n_heads][headdim][d_state / 8], d_scale fp32
+ * [nseq][n_layer][n_heads][headdim]; dfssm_state_unpack replaces those slots'
+ * SSM state by the fields' readout; dfssm_state_roundtrip does both in place
+ * (the state passes through the codec, as at a chunk boundary, without
+ * storing the field).  The conv state is untouched.  Requires d_state 16, 32,
+ * 64 or 128.  Enqueued.                                                    */
+dfssm_status dfssm_state_pack(dfssm_ctx* ctx, int32_t seq0, int32_t nseq, uint32_t* d_field, float* d_scale,
+                              void* stream);
+dfssm_status dfssm_state_unpack(dfssm_ctx* ctx, int32_t seq0, int32_t nseq, const uint32_t* d_field,
+                                const float* d_scale, void* stream);
+dfssm_status dfssm_state_roundtrip(dfssm_ctx* ctx, int32_t seq0, int32_t nseq, void* stream);
+
 /* Wait for `stream` and report (then clear) any error flagged by a kernel. */
 dfssm_status dfssm_check_device(dfssm_ctx* ctx, void* stream);
 
@@ -304,6 +329,14 @@ dfssm_status dfssm_check_device(dfssm_ctx* ctx, void* stream);
  * d_u fp32 [rows][n] -> d_q int8 [rows][n], d_s fp32 [rows].
  * 1 <= n <= 65536.                                                          */
 dfssm_status dfssm_k_quant(const float* d_u, int32_t rows, int32_t n, int8_t* d_q, float* d_s, void* stream);
+
+/* The density-field codec on row-major rows (see dfssm_state_pack): d_x
+ * fp32 [rows][n] -> d_field uint32 [rows][n / 8], d_scale fp32 [rows], and
+ * back.  n is 16, 32, 64 or 128.  Enqueued.                               */
+dfssm_status dfssm_k_density_encode(const float* d_x, int32_t rows, int32_t n, uint32_t* d_field, float* d_scale,
+                                   void* stream);
+dfssm_status dfssm_k_density_decode(const uint32_t* d_field, const float* d_scale, int32_t rows, int32_t n, float* d_x,
+                                   void* stream);
 
 /* Scaffold + LoRA projection of B int8 activation rows (gist.science summary
  * §2.B/§2.C):  acc[b][o] = sum_i w(o,i) q[b][i] exactly (int32);

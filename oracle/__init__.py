@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.or_prefill.argtypes = [_p, _p, _p, _p, _p, _i, _p]
         L.or_prefill.restype = _i
         L.or_num_threads.restype = _i
+        L.or_density_encode.argtypes = [_p, _i, _p, _p]
+        L.or_density_decode.argtypes = [_p, ctypes.c_float, _i, _p]
         _lib = L
     return _lib
 
@@ -129,6 +131,36 @@ def quant_forced(u, force, delta: float = TIE_BAND) -> Tuple[np.ndarray, np.floa
     fl = np.zeros(1, dtype=np.int32)
     bad = lib().or_quant_forced(_ptr(u), u.size, _ptr(force), float(delta), _ptr(q), _ptr(s), _ptr(fl))
     return q, s[0], bad, int(fl[0])
+
+
+def density_encode(x) -> Tuple[np.ndarray, np.float32]:
+    """Density field of one state row x (fp32 [n]): (field uint32 [ceil(4n/32)], scale fp32)."""
+    x = _c(x, np.float32)
+    n = x.size
+    field = np.zeros((4 * n + 31) // 32, dtype=np.uint32)
+    sc = np.zeros(1, dtype=np.float32)
+    lib().or_density_encode(_ptr(x), n, _ptr(field), _ptr(sc))
+    return field, sc[0]
+
+
+def density_decode(field, scale, n: int) -> np.ndarray:
+    """Popcount readout of a density field: fp32 [n]."""
+    field = _c(field, np.uint32)
+    assert field.size == (4 * n + 31) // 32
+    x = np.empty(n, dtype=np.float32)
+    lib().or_density_decode(_ptr(field), float(np.float32(scale)), n, _ptr(x))
+    return x
+
+
+def density_roundtrip_state(ssm) -> np.ndarray:
+    """decode(encode(row)) of every d_state row of an SSM state [..., d_state], in fp32 (returned as fp64)."""
+    a = np.asarray(ssm, dtype=np.float64)
+    rows = a.reshape(-1, a.shape[-1]).astype(np.float32)
+    out = np.empty_like(rows)
+    for r in range(rows.shape[0]):
+        f, sc = density_encode(rows[r])
+        out[r] = density_decode(f, sc, rows.shape[1])
+    return out.reshape(a.shape).astype(np.float64)
 
 
 def rmsnorm(x, w) -> np.ndarray:

@@ -459,6 +459,59 @@ int or_prefill(const int* sh, const void* const* w, double* conv, double* ssm, c
   return next;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Density-field representation of the SSM state (gist.science summary §2.D:
+ * a binary field per state element with K^2 about 4 d_state cells, built by
+ * normalisation, sigma-delta injection with error feedback and binarisation,
+ * read back by popcount; applied at chunk boundaries).  Reading taken: one
+ * field per state ROW -- the d_state values S[h][p][:] of one head channel
+ * -- with 4 cells per element (4 d_state cells, K = sqrt(4 d_state)), since a
+ * field of 4 d_state bits per single element would be 16 times larger than
+ * the fp32 value it replaces.  For a row x[0..n):
+ *   normalisation: scale = max |x_i| (0 for an all-zero row);
+ *                  density d_i = (x_i / scale + 1) / 2 in [0, 1];
+ *   sigma-delta:   e = 0; for cell c = 0 .. 4n-1 (element i = c / 4):
+ *                  a = d_i + e; bit_c = (a >= 1/2); e = a - bit_c;
+ *   readout:       p_i = popcount of element i's 4 cells;
+ *                  x_i' = scale * ((p_i - 2) / 2).
+ * The encoder's decisions are taken in fp32 (the precision of the device
+ * kernels; each step one rounded fp32 operation), the readout is exact
+ * (p_i - 2 is a small integer, halving and the product are one rounding).
+ * Field layout: cell c is bit (c % 32) of word c / 32.                     */
+void or_density_encode(const float* x, int n, uint32_t* field, float* scale_out) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    const float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  const int words = (4 * n + 31) / 32;
+  for (int w = 0; w < words; ++w) field[w] = 0u;
+  *scale_out = amax;
+  if (!(amax > 0.0f)) return;
+  float e = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    const float d = (x[i] / amax + 1.0f) * 0.5f;
+    for (int k = 0; k < 4; ++k) {
+      const float a = d + e;
+      const int bit = a >= 0.5f;
+      e = a - (float)bit;
+      const int c = 4 * i + k;
+      if (bit) field[c >> 5] |= 1u << (c & 31);
+    }
+  }
+}
+
+void or_density_decode(const uint32_t* field, float scale, int n, float* x) {
+  for (int i = 0; i < n; ++i) {
+    int p = 0;
+    for (int k = 0; k < 4; ++k) {
+      const int c = 4 * i + k;
+      p += (int)((field[c >> 5] >> (c & 31)) & 1u);
+    }
+    x[i] = scale * ((float)(p - 2) * 0.5f);
+  }
+}
+
 /* Threads the OpenMP loops above use (1 when built without OpenMP). */
 #ifdef _OPENMP
 #include <omp.h>

@@ -636,3 +636,107 @@ def test_layer_step_with_signs_is_bit_identical():
         hb, db = oracle.layer_step(s, lays, h, b[0], b[1], want_dbg=True)
         assert np.array_equal(ha, hb) and np.array_equal(a[1], b[1]) and np.array_equal(da["q2"], db["q2"])
         h = ha
+
+
+# ---------------------------------------------------------------------------
+# density-field state codec (one field of 4 d_state cells per state row)
+# ---------------------------------------------------------------------------
+
+def _bits(field, n):
+    return [(int(field[c >> 5]) >> (c & 31)) & 1 for c in range(4 * n)]
+
+
+def test_density_hand_example():
+    # scale 1, densities 1, .75, .75, 0, .5: the sigma-delta cell sequence
+    # worked by hand (error feedback carried across elements)
+    x = np.array([1.0, 0.5, 0.5, -1.0, 0.0], np.float32)
+    f, sc = oracle.density_encode(x)
+    assert sc == np.float32(1.0) and f.size == 1
+    assert _bits(f, 5) == [1, 1, 1, 1, 1, 1, 0, 1, 1, 1, 0, 1, 0, 0, 0, 0, 1, 0, 1, 0]
+    assert np.array_equal(oracle.density_decode(f, sc, 5), x)
+
+
+def test_density_constant_and_zero_rows():
+    for c in (3.25, -0.75, 1e-20):
+        x = np.full(128, c, np.float32)
+        f, sc = oracle.density_encode(x)
+        assert sc == np.float32(abs(c))
+        assert np.array_equal(oracle.density_decode(f, sc, 128), x)  # exact
+    f, sc = oracle.density_encode(np.zeros(128, np.float32))
+    assert sc == 0 and not f.any() and not oracle.density_decode(f, sc, 128).any()
+
+
+def test_density_error_bounds():
+    # every element within one quantisation step (levels are scale / 2
+    # apart); every prefix sum of the error within scale / 4 (first-order
+    # sigma-delta keeps its carried error in [-1/2, 1/2) cell)
+    for dist in ("normal", "uniform", "sparse", "heavy"):
+        if dist == "normal":
+            x = RNG.standard_normal(128)
+        elif dist == "uniform":
+            x = RNG.uniform(-1, 1, 128)
+        elif dist == "sparse":
+            x = RNG.standard_normal(128) * (RNG.uniform(0, 1, 128) < 0.1)
+        else:
+            x = RNG.standard_cauchy(128)
+        x = x.astype(np.float32)
+        f, sc = oracle.density_encode(x)
+        err = oracle.density_decode(f, sc, 128).astype(np.float64) - x
+        assert np.max(np.abs(err)) <= 0.5 * sc * (1 + 1e-6), dist
+        assert np.max(np.abs(np.cumsum(err))) <= 0.25 * sc * (1 + 1e-5) + 1e-6 * sc * 128, dist
+
+
+def test_density_popcounts_are_rounded_prefix_sums():
+    # With densities on a 1/16 grid every fp32 step is exact, so the cell
+    # counts must follow the closed form of first-order sigma-delta:
+    # sum_{j<=i} p_j = floor(4 sum_{j<=i} d_j + 1/2)
+    d = RNG.integers(0, 17, 64) / 16.0
+    d[0] = 1.0  # fixes scale = 1 (density 1 is the +max element)
+    x = (2 * d - 1).astype(np.float32)
+    f, sc = oracle.density_encode(x)
+    assert sc == 1.0
+    b = np.array(_bits(f, 64)).reshape(64, 4)
+    p = b.sum(axis=1)
+    want = np.floor(4 * np.cumsum(d) + 0.5).astype(int)
+    assert np.array_equal(np.cumsum(p), want)
+
+
+def test_density_readout_is_idempotent():
+    # a read-back row lies on the levels, so encoding it again reads back the
+    # same values (the cell patterns may differ: the carried error restarts)
+    x = RNG.standard_normal(128).astype(np.float32)
+    f, sc = oracle.density_encode(x)
+    y = oracle.density_decode(f, sc, 128)
+    f2, sc2 = oracle.density_encode(y)
+    assert sc2 == sc and np.array_equal(oracle.density_decode(f2, sc2, 128), y)
+
+
+def test_density_field_size_matches_pages():
+    # K^2 about 4 d_state cells per field: 512 bits per row of 128 states,
+    # plus one fp32 scale, against 128 fp32 values
+    s = synth.FULL_1P3B
+    f, _ = oracle.density_encode(np.ones(s.d_state, np.float32))
+    assert f.size * 32 == 4 * s.d_state
+    ratio = (s.d_state * 4) / (f.size * 4 + 4)
+    assert 7.4 < ratio < 7.6
+
+
+def test_density_codec_error_stays_bounded_over_chunks():
+    # the tiny stack decoded with its SSM state passed through the codec at
+    # every 8-token chunk boundary: the state's deviation from the exact run
+    # does not grow with the number of chunks (the recurrence's decay bounds
+    # the accumulated codec noise)
+    s = synth.TINY
+    seed = synth.SEED_BASE + 50
+    om = oracle.Model(s, synth.gen_model(s, seed))
+    a, b = oracle.State(s), oracle.State(s)
+    toks = synth.gen_tokens(seed, 1, 8 * 24, s.vocab)
+    dev = []
+    for c in range(24):
+        for t in toks[8 * c: 8 * c + 8]:
+            om.decode_step(a, int(t), want_logits=False)
+            om.decode_step(b, int(t), want_logits=False)
+        b.ssm[:] = oracle.density_roundtrip_state(b.ssm)
+        dev.append(np.max(np.abs(b.ssm - a.ssm)) / np.max(np.abs(a.ssm)))
+    assert max(dev) < 0.5, dev
+    assert max(dev[12:]) <= 2.0 * max(dev[:12]), dev
