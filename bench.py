@@ -38,9 +38,9 @@ PAGES_B512_TOKS = 5081.0  # decode tokens/s at batch 512 (A100), the pages' only
 # (FETCH_SIZE reads 0.5 GiB for it: factor 2.0; WRITE_SIZE reads 1 GiB: 1.0).
 # Valid only for the kernel sources they were taken from (hash below).
 COUNTED_TRAFFIC = {
-    "sources_sha256": "b68bd94ac8ac099661d2cbd6b2c0a4d0646b64e458d23916619ab4acd2180158",
-    "fetch_bytes_per_token": 461281474,
-    "write_bytes_per_token": 118426844,
+    "sources_sha256": "0364ee11c580422ca866ff1f597c8e860bd6b70c27cc596bb8fdb4dcb9573565",
+    "fetch_bytes_per_token": 460704727,
+    "write_bytes_per_token": 118426848,
 }
 KERNEL_SOURCES = ("bit_quantized_mamba_amd/csrc/persistent.hip", "bit_quantized_mamba_amd/csrc/persistent.h",
                   "bit_quantized_mamba_amd/csrc/common.h")

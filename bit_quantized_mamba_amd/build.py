@@ -1,4 +1,5 @@
-"""Compile the HIP library (gfx950) into bit_quantized_mamba_amd/libdfssm.so."""
+"""Compile the HIP library (gfx950) into bit_quantized_mamba_amd/libdfssm.so,
+and the stand-alone exchange-latency probe into bit_quantized_mamba_amd/hop_probe."""
 import os
 import subprocess
 import sys
@@ -7,6 +8,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libdfssm.so")
+PROBE = os.path.join(HERE, "hop_probe")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["gen.hip", "kernels.hip", "persistent.hip", "gemm.hip", "scan.hip", "codec.hip", "runtime.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -38,6 +40,11 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
     os.replace(OUT + ".tmp", OUT)
+    probe = [HIPCC, *[f for f in FLAGS if f != "-fPIC"], os.path.join(CSRC, "hop_probe.hip"), "-o", PROBE + ".tmp"]
+    r = subprocess.run(probe, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for hop_probe.hip:\n{r.stdout}{r.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
     return OUT
 
 

@@ -900,8 +900,10 @@ __device__ void loader_waves(const PersistArgs& a, const Lds<S>& L) {
   }
 }
 
-// TR: the variant that also writes traces and phase timestamps (tests and
-// profiling); the plain variant has none of that code.
+// MODE 0: the plain kernel.  MODE 1: also writes phase timestamps (profiling;
+// nothing else added, so the phases keep close to the plain kernel's timing).
+// MODE 2: also writes the traces of intermediate values (tests) and the
+// timestamps.
 //
 // Workgroup barriers per token, the same sequence in the compute and loader
 // waves: embedding; per layer residual hop (layers > 0) with the norm
@@ -909,8 +911,9 @@ __device__ void loader_waves(const PersistArgs& a, const Lds<S>& L) {
 // gated-output hop with the gated norm statistics, codes, LoRA-down vector
 // ready, end of layer; then final residual hop, final norm statistics, codes,
 // per-wave argmax candidates, argmax hop, next token chosen.
-template <class S, bool TR>
+template <class S, int MODE>
 __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArgs a) {
+  constexpr bool TR = MODE == 2;
   extern __shared__ unsigned char smem[];
   constexpr int DM = S::DM, DI = S::DI, NS = S::NS, HP = S::HP, G = S::G, CDIM = S::CDIM;
   constexpr int KZ = S::KZ, KX = S::KX, KDT = S::KDT;
@@ -961,7 +964,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_persistent_kernel(PersistArg
 
   // phase timestamps (100 MHz device clock) for performance analysis
   auto prof = [&](int t, int l, int ev) {
-    if constexpr (TR) {
+    if constexpr (MODE >= 1) {
       const KArgs k = kargs();
       if (k->prof && t < k->prof_tokens && threadIdx.x == 0)
         k->prof[(((size_t)t * (k->n_layer + 1) + l) * G + w) * kProfEvents + ev] = wall_clock64();
@@ -1382,8 +1385,10 @@ using ShapeTiny = PShape<256, 512, 16, 32>;
 using Shape1p3b = PShape<2048, 4096, 128, 64>;
 
 template <class S>
-static const void* kernel_of(bool tr) {
-  return tr ? (const void*)decode_persistent_kernel<S, true> : (const void*)decode_persistent_kernel<S, false>;
+static const void* kernel_of(int mode) {
+  return mode == 2 ? (const void*)decode_persistent_kernel<S, 2>
+         : mode == 1 ? (const void*)decode_persistent_kernel<S, 1>
+                     : (const void*)decode_persistent_kernel<S, 0>;
 }
 
 template <class S>
@@ -1397,9 +1402,9 @@ static size_t lds_bytes(int dm, int di, int ns, int hp) {
   return 0;
 }
 
-static const void* select_kernel(int dm, int di, int ns, int hp, size_t* stride, bool tr = false) {
-  if (shape_is<Shape1p3b>(dm, di, ns, hp)) { *stride = Shape1p3b::LSTRIDE; return kernel_of<Shape1p3b>(tr); }
-  if (shape_is<ShapeTiny>(dm, di, ns, hp)) { *stride = ShapeTiny::LSTRIDE; return kernel_of<ShapeTiny>(tr); }
+static const void* select_kernel(int dm, int di, int ns, int hp, size_t* stride, int mode = 0) {
+  if (shape_is<Shape1p3b>(dm, di, ns, hp)) { *stride = Shape1p3b::LSTRIDE; return kernel_of<Shape1p3b>(mode); }
+  if (shape_is<ShapeTiny>(dm, di, ns, hp)) { *stride = ShapeTiny::LSTRIDE; return kernel_of<ShapeTiny>(mode); }
   return nullptr;
 }
 
@@ -1417,8 +1422,9 @@ bool persistent_layout(int d_model, int d_inner, int d_state, int headdim, size_
 
 hipError_t launch_decode_persistent(const PersistArgs& a, int grid, hipStream_t st) {
   size_t stride = 0;
-  const bool tr = a.prof || a.trace_h || a.trace_q1 || a.trace_q2 || a.trace_qf || a.trace_acc1 || a.trace_acc2;
-  const void* k = select_kernel(a.d_model, a.d_inner, a.d_state, a.headdim, &stride, tr);
+  const bool tr = a.trace_h || a.trace_q1 || a.trace_q2 || a.trace_qf || a.trace_acc1 || a.trace_acc2;
+  const int mode = tr ? 2 : a.prof ? 1 : 0;
+  const void* k = select_kernel(a.d_model, a.d_inner, a.d_state, a.headdim, &stride, mode);
   if (!k) return hipErrorInvalidValue;
   PersistArgs args = a;
   void* params[] = {&args};
@@ -1439,8 +1445,8 @@ bool persistent_supported(int d_model, int d_inner, int d_state, int headdim, in
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return no("no device");
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return no("no CU count");
-  for (int tr = 0; tr < 2; ++tr) {  // both variants (plain, tracing) must fit
-    k = select_kernel(d_model, d_inner, d_state, headdim, &stride, tr != 0);
+  for (int mode = 0; mode < 3; ++mode) {  // every variant (plain, timestamps, traces) must fit
+    k = select_kernel(d_model, d_inner, d_state, headdim, &stride, mode);
     const size_t lds = lds_bytes(d_model, d_inner, d_state, headdim);
     if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return no("the kernel's LDS carve-up does not fit a workgroup on this device");
