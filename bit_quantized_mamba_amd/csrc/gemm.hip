@@ -334,9 +334,11 @@ struct GemmTile {
 // Epilogue of a batched scaffold GEMM tile: 2 acc - sum(q) gives the signed
 // scaffold sum, scaled by the column and row scales; the LoRA-up term runs on
 // the f32 matrix cores; store or residual add.  acc[i][j] is the 32 x 32 block
-// at tile rows wm0 + 32 i, columns wn0 + 32 j.  gsm: at least TM * 72 bytes
-// of LDS (reused after the first barrier here).
-template <int TM, int BM, int BN, int EPI>
+// at tile rows wm0 + 32 i, columns wn0 + 32 j.  gsm: at least TM * 88 bytes
+// of LDS (reused after the first barrier here).  CONV: the tile may hold conv
+// channels of decode tokens (a.xc set); without it no register is set aside
+// for the conv windows.
+template <int TM, int BM, int BN, int EPI, bool CONV = true>
 __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i (&acc)[BM][BN], int m0, int n0,
                                                    int wm0, int wn0, unsigned char* gsm) {
   const int lane = threadIdx.x & 63;
@@ -344,7 +346,9 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
   __syncthreads();
   float* s_s = (float*)gsm;              // [TM]
   int* s_qs = (int*)(s_s + TM);          // [TM]
-  float* s_t = (float*)(s_qs + TM);      // [TM][16]
+  // t rows padded to 20 floats: the 16-byte reads of 8 consecutive lanes
+  // (rows 20 floats apart) fall on 8 different groups of 4 banks
+  float* s_t = (float*)(s_qs + TM);      // [TM][20]
   for (int i = threadIdx.x; i < TM; i += 256) {
     const int m = m0 + i;
     s_s[i] = m < a.M ? a.s[m] : 0.0f;
@@ -352,7 +356,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
   }
   for (int i = threadIdx.x; i < TM * 16; i += 256) {
     const int m = m0 + i / 16;
-    s_t[i] = m < a.M ? a.t[(size_t)m * 16 + (i & 15)] : 0.0f;
+    s_t[(i >> 4) * 20 + (i & 15)] = m < a.M ? a.t[(size_t)m * 16 + (i & 15)] : 0.0f;
   }
   __syncthreads();
 #pragma unroll
@@ -378,11 +382,11 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
         prev[i][r] = (EPI == GEMM_EPI_RESIDUAL && m < a.M && nok) ? a.y[(size_t)m * a.ldy + n] : 0.0f;
       }
     // conv shift register of this column (one decode token per row), or none
-    const bool conv_col = EPI == GEMM_EPI_STORE && a.xc && nok && n >= a.x_off && n < a.x_off + a.cdim;
+    const bool conv_col = CONV && EPI == GEMM_EPI_STORE && a.xc && nok && n >= a.x_off && n < a.x_off + a.cdim;
     const int cc = min(max(n - a.x_off, 0), a.cdim - 1);
     float4 cw = make_float4(0.f, 0.f, 0.f, 0.f);
     float cb = 0.0f;
-    if (EPI == GEMM_EPI_STORE && a.xc) {
+    if (CONV && EPI == GEMM_EPI_STORE && a.xc) {
       cw = *(const float4*)(a.conv_w + (size_t)cc * 4);
       cb = a.conv_b[cc];
     }
@@ -392,7 +396,9 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
       // t of row rb + lane % 32, ranks 8 h .. 8 h + 7, split exactly into three
       // bf16 parts (each part is the top 8 significant bits of what is left), so
       // the rank-16 product is three bf16 matrix-core steps with exact products
-      const float* tr = s_t + (rb + (lane & 31)) * 16 + 8 * (lane >> 5);
+      const float4* tr4 = (const float4*)(s_t + (rb + (lane & 31)) * 20 + 8 * (lane >> 5));
+      const float4 ta = tr4[0], tb = tr4[1];
+      const float tr[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
       v8bf t1, t2, t3;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -409,7 +415,7 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
       // the block's conv windows, loaded before any of its stores (rows past
       // the end read the last one)
       float w0[16], w1[16], w2[16];
-      if (EPI == GEMM_EPI_STORE && a.xc) {
+      if (CONV && EPI == GEMM_EPI_STORE && a.xc) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = min(m0 + rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), a.M - 1);
@@ -566,7 +572,7 @@ __device__ __forceinline__ v4i expand16(uint32_t b) {
                (int)spread_nibble(b >> 12)};
 }
 
-template <int EPI, int TN, int WR, int OCC>
+template <int EPI, int TN, int WR, int OCC, bool CONV>
 __global__ __launch_bounds__(256, OCC) void bitgemm2_kernel(GemmArgs a) {
   constexpr int TM = kG2TM, KB = kG2KB, WC = 4 / WR;
   constexpr int BM = TM / WR / 32, BN = TN / WC / 32;
@@ -594,9 +600,11 @@ __global__ __launch_bounds__(256, OCC) void bitgemm2_kernel(GemmArgs a) {
     uint4 a[kG2PT];
     uint32_t b[PB];
   };
-  // branch-free loads: rows and columns past the end read the last one and
-  // are zeroed by a select, so the compiler can count the loads in flight
-  // exactly (a branch around a load makes it wait for all of them)
+  // branch-free loads: rows and columns past the end read the last one, so
+  // the compiler can count the loads in flight exactly (a branch around a
+  // load makes it wait for all of them).  Those copies are stored as they
+  // are: accumulator element (m, n) depends only on A row m and B column n,
+  // and the epilogue stores no row past M and no column past N.
   auto load = [&](int kt, Tile& R) {
 #pragma unroll
     for (int i = 0; i < kG2PT; ++i) {
@@ -617,15 +625,13 @@ __global__ __launch_bounds__(256, OCC) void bitgemm2_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < kG2PT; ++i) {
       const int c = threadIdx.x + 256 * i;
-      const bool mok = m0 + c / kG2AC < a.M;
-      *(uint4*)(As + (c / kG2AC) * kG2ARow + (c % kG2AC) * 16) = mok ? R.a[i] : make_uint4(0, 0, 0, 0);
+      // (stored component by component: a whole-struct copy keeps the
+      // register sets in scratch memory)
+      const uint4 v = R.a[i];
+      *(uint4*)(As + (c / kG2AC) * kG2ARow + (c % kG2AC) * 16) = make_uint4(v.x, v.y, v.z, v.w);
     }
 #pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const bool nok = n0 + c / kG2CW < a.N;
-      Bw[c] = nok ? R.b[i] : 0u;
-    }
+    for (int i = 0; i < PB; ++i) Bw[threadIdx.x + 256 * i] = R.b[i];
   };
   v16i acc[BM][BN];
 #pragma unroll
@@ -675,7 +681,7 @@ __global__ __launch_bounds__(256, OCC) void bitgemm2_kernel(GemmArgs a) {
     __syncthreads();
     load(min(kt + 4, nk - 1), R0);
   }
-  gemm_tile_epilogue<TM, BM, BN, EPI>(a, acc, m0, n0, wm0, wn0, gsm);
+  gemm_tile_epilogue<TM, BM, BN, EPI, CONV>(a, acc, m0, n0, wm0, wn0, gsm);
 }
 
 // tile width, wave rows and workgroups per CU of the many-row scaffold GEMM
@@ -686,7 +692,7 @@ static hipError_t launch_bitgemm_t(const GemmArgs& a, int epi, hipStream_t st) {
   using T = GemmTile<TM, TN>;
   const dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM), block(256);
   size_t lds = 2 * (size_t)T::STAGE;
-  const size_t epi_lds = (size_t)TM * (4 + 4 + 64);
+  const size_t epi_lds = (size_t)TM * (4 + 4 + 80);
   if (epi_lds > lds) lds = epi_lds;
   if (epi == GEMM_EPI_RESIDUAL)
     hipLaunchKernelGGL((bitgemm_kernel<TM, TN, GEMM_EPI_RESIDUAL>), grid, block, lds, st, a);
@@ -708,15 +714,19 @@ hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st) {
       const dim3 g64((a.N + 63) / 64, grid.y);
       const size_t lds64 = 2 * (size_t)G2<64>::STAGE;
       if (epi == GEMM_EPI_RESIDUAL)
-        hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_RESIDUAL, 64, 2, kG2OCC>), g64, block, lds64, st, a);
+        hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_RESIDUAL, 64, 2, kG2OCC, false>), g64, block, lds64, st, a);
+      else if (a.xc)
+        hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_STORE, 64, 2, kG2OCC, true>), g64, block, lds64, st, a);
       else
-        hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_STORE, 64, 2, kG2OCC>), g64, block, lds64, st, a);
+        hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_STORE, 64, 2, kG2OCC, false>), g64, block, lds64, st, a);
       return hipGetLastError();
     }
     if (epi == GEMM_EPI_RESIDUAL)
-      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_RESIDUAL, kG2TN, kG2WR, kG2OCC>), grid, block, lds, st, a);
+      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_RESIDUAL, kG2TN, kG2WR, kG2OCC, false>), grid, block, lds, st, a);
+    else if (a.xc)
+      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_STORE, kG2TN, kG2WR, kG2OCC, true>), grid, block, lds, st, a);
     else
-      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_STORE, kG2TN, kG2WR, kG2OCC>), grid, block, lds, st, a);
+      hipLaunchKernelGGL((bitgemm2_kernel<GEMM_EPI_STORE, kG2TN, kG2WR, kG2OCC, false>), grid, block, lds, st, a);
     return hipGetLastError();
   }
   return launch_bitgemm_t<128, 256>(a, epi, st);

@@ -357,7 +357,10 @@ __device__ __forceinline__ void ssd_stage_load(const ScanArgs& a, int hp, int ti
 
 // Workgroup (head pair, sequence) of 8 waves; wave w serves head 2 hp + (w >> 2),
 // channel block pb = (w >> 1) & 1 (channels 32 pb .. 32 pb + 31) and half
-// h2 = w & 1: it holds the state tiles S^T[n][p] of states 64 h2 .. 64 h2 + 63
+// h2 = (w & 1) ^ (w >> 2) (waves w and w + 4 share a SIMD; with opposite halves
+// each SIMD gets one wave of either half, and the halves differ in work: the
+// first position block's M X needs only j < 32): it holds the state tiles
+// S^T[n][p] of states 64 h2 .. 64 h2 + 63
 // (two 32 x 32 accumulator tiles: lane = channel, register = state) and
 // produces the outputs of chunk positions 32 h2 .. 32 h2 + 31.  Per chunk:
 //  (a) partial C S_in^T over its 64 states for both position blocks (its own
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_kernel(ScanArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   const int hp = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
-  const int hh = wave >> 2, pb = (wave >> 1) & 1, h2 = wave & 1;
+  const int hh = wave >> 2, pb = (wave >> 1) & 1, h2 = (wave & 1) ^ hh;
   const int h = 2 * hp + hh;
   const int p = 32 * pb + col;  // this lane's channel in (b), (c) and the state tiles
   const int nch = (a.T + kSsdL - 1) / kSsdL;
