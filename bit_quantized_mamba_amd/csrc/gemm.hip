@@ -334,7 +334,7 @@ struct GemmTile {
 // Epilogue of a batched scaffold GEMM tile: 2 acc - sum(q) gives the signed
 // scaffold sum, scaled by the column and row scales; the LoRA-up term runs on
 // the f32 matrix cores; store or residual add.  acc[i][j] is the 32 x 32 block
-// at tile rows wm0 + 32 i, columns wn0 + 32 j.  gsm: at least TM * 88 bytes
+// at tile rows wm0 + 32 i, columns wn0 + 32 j.  gsm: at least TM * 120 bytes
 // of LDS (reused after the first barrier here).  CONV: the tile may hold conv
 // channels of decode tokens (a.xc set); without it no register is set aside
 // for the conv windows.
@@ -342,21 +342,54 @@ template <int TM, int BM, int BN, int EPI, bool CONV = true>
 __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i (&acc)[BM][BN], int m0, int n0,
                                                    int wm0, int wn0, unsigned char* gsm) {
   const int lane = threadIdx.x & 63;
-  // row data of the tile into LDS
+  // row data of the tile into LDS: the row scale, the code sum and the
+  // LoRA-down vector t.  The plain store form splits t once per row into its
+  // three bf16 parts (every wave of the tile multiplies the same rows), as
+  // [row][part][16 ranks] with rows 112 bytes apart; the residual and conv
+  // forms keep t as fp32 rows 20 floats apart and split it per lane (measured
+  // faster there).  Either row stride puts the 16-byte reads of 8 consecutive
+  // lanes on 8 different groups of 4 banks.
+  constexpr bool kPreSplit = EPI == GEMM_EPI_STORE && !CONV;
+  constexpr int kTbRow = 112;
   __syncthreads();
   float* s_s = (float*)gsm;              // [TM]
   int* s_qs = (int*)(s_s + TM);          // [TM]
-  // t rows padded to 20 floats: the 16-byte reads of 8 consecutive lanes
-  // (rows 20 floats apart) fall on 8 different groups of 4 banks
-  float* s_t = (float*)(s_qs + TM);      // [TM][20]
+  unsigned char* s_tb = (unsigned char*)(s_qs + TM);  // [TM][kTbRow] (pre-split) or [TM][20] floats
+  float* s_t = (float*)s_tb;
   for (int i = threadIdx.x; i < TM; i += 256) {
     const int m = m0 + i;
     s_s[i] = m < a.M ? a.s[m] : 0.0f;
     s_qs[i] = m < a.M ? a.qsum[m] : 0;
   }
-  for (int i = threadIdx.x; i < TM * 16; i += 256) {
-    const int m = m0 + i / 16;
-    s_t[(i >> 4) * 20 + (i & 15)] = m < a.M ? a.t[(size_t)m * 16 + (i & 15)] : 0.0f;
+  if constexpr (kPreSplit) {
+    for (int i = threadIdx.x; i < TM * 2; i += 256) {  // row i / 2, ranks 8 (i & 1) .. + 7
+      const int m = m0 + i / 2;
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f), w = u;
+      if (m < a.M) {
+        const float4* tp = (const float4*)(a.t + (size_t)m * 16 + 8 * (i & 1));
+        u = tp[0];
+        w = tp[1];
+      }
+      const float tv[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+      v8bf p1, p2, p3;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 b1, b2, b3;
+        bf16_split3(tv[e], b1, b2, b3);
+        p1[e] = b1;
+        p2[e] = b2;
+        p3[e] = b3;
+      }
+      unsigned char* dst = s_tb + (i / 2) * kTbRow + 16 * (i & 1);
+      *(v8bf*)dst = p1;
+      *(v8bf*)(dst + 32) = p2;
+      *(v8bf*)(dst + 64) = p3;
+    }
+  } else {
+    for (int i = threadIdx.x; i < TM * 16; i += 256) {
+      const int m = m0 + i / 16;
+      s_t[(i >> 4) * 20 + (i & 15)] = m < a.M ? a.t[(size_t)m * 16 + (i & 15)] : 0.0f;
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -396,17 +429,24 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
       // t of row rb + lane % 32, ranks 8 h .. 8 h + 7, split exactly into three
       // bf16 parts (each part is the top 8 significant bits of what is left), so
       // the rank-16 product is three bf16 matrix-core steps with exact products
-      const float4* tr4 = (const float4*)(s_t + (rb + (lane & 31)) * 20 + 8 * (lane >> 5));
-      const float4 ta = tr4[0], tb = tr4[1];
-      const float tr[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
       v8bf t1, t2, t3;
+      if constexpr (kPreSplit) {
+        const unsigned char* tb = s_tb + (rb + (lane & 31)) * kTbRow + 16 * (lane >> 5);
+        t1 = *(const v8bf*)tb;
+        t2 = *(const v8bf*)(tb + 32);
+        t3 = *(const v8bf*)(tb + 64);
+      } else {
+        const float4* tr4 = (const float4*)(s_t + (rb + (lane & 31)) * 20 + 8 * (lane >> 5));
+        const float4 ta = tr4[0], tb = tr4[1];
+        const float tr[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 p1, p2, p3;
-        bf16_split3(tr[e], p1, p2, p3);
-        t1[e] = p1;
-        t2[e] = p2;
-        t3[e] = p3;
+        for (int e = 0; e < 8; ++e) {
+          __bf16 p1, p2, p3;
+          bf16_split3(tr[e], p1, p2, p3);
+          t1[e] = p1;
+          t2[e] = p2;
+          t3[e] = p3;
+        }
       }
       v16f lo = (v16f){};
       lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t1, bB, lo, 0, 0, 0);
@@ -425,13 +465,34 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, const v16i
           w2[r] = st[2 * a.cdim];
         }
       }
+      // a block inside the matrix stores without a test per element
+      const bool full = nok && m0 + rb + 32 <= a.M;
+      // row scales and code sums of this lane's rows: four consecutive rows a
+      // read (the residual and conv forms, which hold the block's residual
+      // values or conv windows, read them one at a time and keep fewer
+      // registers live)
+      float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
+      int4 qv = make_int4(0, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ml = rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int m = m0 + ml;
-        if (m < a.M && nok) {
-          const int sacc = 2 * acc[i][j][r] - s_qs[ml];
-          const float y = proj_out(sacc, sw, s_s[ml], sb, lo[r]);
+        float rs;
+        int rq;
+        if constexpr (kPreSplit) {
+          if ((r & 3) == 0) {
+            sv = *(const float4*)(s_s + ml);
+            qv = *(const int4*)(s_qs + ml);
+          }
+          rs = (r & 3) == 0 ? sv.x : (r & 3) == 1 ? sv.y : (r & 3) == 2 ? sv.z : sv.w;
+          rq = (r & 3) == 0 ? qv.x : (r & 3) == 1 ? qv.y : (r & 3) == 2 ? qv.z : qv.w;
+        } else {
+          rs = s_s[ml];
+          rq = s_qs[ml];
+        }
+        if (full || (m < a.M && nok)) {
+          const int sacc = 2 * acc[i][j][r] - rq;
+          const float y = proj_out(sacc, sw, rs, sb, lo[r]);
           a.y[(size_t)m * a.ldy + n] = prev[i][r] + y;
           if (a.acc) a.acc[(size_t)m * a.N + n] = sacc;
           if (conv_col) {  // one decode token: the conv shift register of channel cc
@@ -692,7 +753,7 @@ static hipError_t launch_bitgemm_t(const GemmArgs& a, int epi, hipStream_t st) {
   using T = GemmTile<TM, TN>;
   const dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM), block(256);
   size_t lds = 2 * (size_t)T::STAGE;
-  const size_t epi_lds = (size_t)TM * (4 + 4 + 80);
+  const size_t epi_lds = (size_t)TM * (4 + 4 + 112);
   if (epi_lds > lds) lds = epi_lds;
   if (epi == GEMM_EPI_RESIDUAL)
     hipLaunchKernelGGL((bitgemm_kernel<TM, TN, GEMM_EPI_RESIDUAL>), grid, block, lds, st, a);
