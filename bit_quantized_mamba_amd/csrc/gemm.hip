@@ -794,20 +794,42 @@ hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// skinny GEMM (M <= 32 rows: batched decode, the LM head of a few sequences).
+// skinny GEMM (a few rows: batched decode, the LM head of its sequences).
 // One 32 x 32 output block per workgroup; the four waves take a quarter of K
 // each and sum their accumulators through LDS.  Operands go straight from
 // global memory (the weights streamed once, the codes from L2) into MFMA
 // registers: lane l holds row / column l % 32 and k-half l / 32 of each
 // 32-wide k-step, and 16 scaffold bits become 16 0/1 bytes in registers.
+// More than 32 rows take several 32-row blocks; workgroups are dealt to the
+// 8 XCDs in contiguous runs of tiles with the row block fastest, so the row
+// blocks of a column block read its weights on one XCD (from its L2 after
+// the first).
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyUnroll = 16;  // k-steps whose loads are issued together
 
 template <int KIND>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a0, int nrb) {
   __shared__ int red[3][16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 32;
+  int n0, r0;
+  {
+    const int T = gridDim.x, g = blockIdx.x;  // T = nrb x column blocks
+    const int q = T / 8, r = T % 8, x = g % 8;
+    const int tile = x * q + min(x, r) + g / 8;
+    n0 = (tile / nrb) * 32;
+    r0 = (tile % nrb) * 32;
+  }
+  // this workgroup's row block as a GEMM of its own (at most 32 rows)
+  SkinnyArgs a = a0;
+  a.M = min(32, a0.M - r0);
+  a.q += (size_t)r0 * a0.K;
+  a.s += r0;
+  if (a.qsum) a.qsum += r0;
+  if (a.t) a.t += (size_t)r0 * 16;
+  a.y += (size_t)r0 * a0.ldy;
+  if (a.acc) a.acc += (size_t)r0 * a0.N;
+  if (a.xc) a.xc += (size_t)r0 * a0.cdim;
+  if (a.conv_state) a.conv_state += (size_t)r0 * a0.conv_bstride;
   const int col = lane & 31, kg = lane >> 5;
   const int n = n0 + col;
   const bool nok = n < a.N, mok = col < a.M;  // this lane's B column and A row
@@ -958,12 +980,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
 
 hipError_t launch_gemm_skinny(const SkinnyArgs& a, int kind, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (a.M > 32 || a.K % 128) return hipErrorInvalidValue;
-  const dim3 grid((a.N + 31) / 32), block(256);
+  if (a.K % 128) return hipErrorInvalidValue;
+  const int nrb = (a.M + 31) / 32;
+  const long tiles = (long)nrb * ((a.N + 31) / 32);
+  if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles), block(256);
   switch (kind) {
-    case SK_IN: hipLaunchKernelGGL(gemm_skinny_kernel<SK_IN>, grid, block, 0, st, a); break;
-    case SK_OUT: hipLaunchKernelGGL(gemm_skinny_kernel<SK_OUT>, grid, block, 0, st, a); break;
-    case SK_HEAD: hipLaunchKernelGGL(gemm_skinny_kernel<SK_HEAD>, grid, block, 0, st, a); break;
+    case SK_IN: hipLaunchKernelGGL(gemm_skinny_kernel<SK_IN>, grid, block, 0, st, a, nrb); break;
+    case SK_OUT: hipLaunchKernelGGL(gemm_skinny_kernel<SK_OUT>, grid, block, 0, st, a, nrb); break;
+    case SK_HEAD: hipLaunchKernelGGL(gemm_skinny_kernel<SK_HEAD>, grid, block, 0, st, a, nrb); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -403,9 +403,11 @@ dfssm_status ensure_gemm_ws(dfssm_ctx* c, size_t rows) {
 
 // One layer on rows m = b * T + t of the batched workspace (B sequences in
 // state slots 0..B-1, T tokens each, in order).
-// Decode (one token per sequence) of at most 32 sequences uses the skinny
-// GEMM, with the conv shift register in the in_proj epilogue.
-bool skinny_decode(int B, int T) { return T == 1 && B <= 32; }
+// Decode (one token per sequence) of at most kSkinnyDecodeRows sequences
+// uses the skinny GEMM (32-row blocks), with the conv shift register in the
+// in_proj epilogue; more rows use the tiled GEMM.
+constexpr int kSkinnyDecodeRows = 32;
+bool skinny_decode(int B, int T) { return T == 1 && B <= kSkinnyDecodeRows; }
 
 hipError_t b_rows_in(dfssm_ctx* c, int l, int M, hipStream_t st) {
   auto& w = c->gw;
@@ -507,19 +509,15 @@ hipError_t b_head(dfssm_ctx* c, int B, int T, float* lg, int8_t* qf_out, hipStre
   if (e == hipSuccess && qf_out) e = hipMemcpyAsync(qf_out, w.q, (size_t)B * c->dm, hipMemcpyDeviceToDevice, st);
   if (e != hipSuccess) return e;
   if (c->dm % 128 == 0) {
-    // the int8 LM head on the matrix cores, 32 sequences per launch (the
-    // embedding rows, 103 MB at the 1.3B shape, stream once per launch)
-    for (int b0 = 0; b0 < B; b0 += 32) {
-      SkinnyArgs sh{};
-      sh.q = w.q + (size_t)b0 * c->dm; sh.s = w.s + b0;
-      sh.w = c->lt<int8_t>(-1, DFSSM_G_EMBED);
-      sh.sw = c->lt<float>(-1, DFSSM_G_EMBED_SCALE);
-      sh.M = std::min(32, B - b0); sh.N = c->V; sh.K = c->dm;
-      sh.y = lg + (size_t)b0 * c->V; sh.ldy = c->V;
-      const hipError_t e2 = launch_gemm_skinny(sh, SK_HEAD, st);
-      if (e2 != hipSuccess) return e2;
-    }
-    return hipSuccess;
+    // the int8 LM head on the matrix cores, one launch of 32-row blocks (the
+    // row blocks of a column block share its embedding rows in one XCD's L2)
+    SkinnyArgs sh{};
+    sh.q = w.q; sh.s = w.s;
+    sh.w = c->lt<int8_t>(-1, DFSSM_G_EMBED);
+    sh.sw = c->lt<float>(-1, DFSSM_G_EMBED_SCALE);
+    sh.M = B; sh.N = c->V; sh.K = c->dm;
+    sh.y = lg; sh.ldy = c->V;
+    return launch_gemm_skinny(sh, SK_HEAD, st);
   }
   return launch_lm_head(c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE), w.q, w.s, c->V,
                         c->dm, B, lg, st);
@@ -799,7 +797,7 @@ hipError_t k_gemm_run(const uint32_t* d_bits, const float* d_sw, const int8_t* d
   float* t = (float*)(tmp + align_up((size_t)M * d_in) + align_up(4 * (size_t)M));
   hipError_t e = launch_qprep(d_q, d_s, d_in, M, d_A, d_sA, 16, planes, qsum, t, st);
   if (e != hipSuccess) return e;
-  if (M <= 32) {  // the decode-sized kernel
+  if (M <= kSkinnyDecodeRows) {  // the decode-sized kernel
     SkinnyArgs a{};
     a.q = d_q; a.s = d_s; a.qsum = qsum; a.t = t;
     a.w = d_bits; a.sw = d_sw; a.Bm = d_B; a.sB = d_sB;

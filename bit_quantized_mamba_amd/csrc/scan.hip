@@ -87,24 +87,25 @@ __global__ __launch_bounds__(4 * P) void scan_kernel(ScanArgs a) {
 }
 
 // One decode token per sequence (T = 1), headdim 64, d_state 128.  Workgroup
-// (head pair, sequence) of 512 threads, 256 per head (two heads a workgroup
-// measured 2 % faster per batch-512 step than one); within a head, wave w
+// (four heads, sequence) of 1024 threads, 256 per head (four heads a workgroup
+// measured 3.5 % faster per batch-512 step than one, two 2 %); within a head, wave w
 // takes the channel block pb = w (channels 16 w .. 16 w + 15, one [N][16]
 // slab of the [P/16][N][16] state layout, 8 KB), lane l the channels
 // 16 w + 4 (l & 3) + 0..3 of states n = 16 i + (l >> 2), i = 0..7.  So for
 // each i the 64 lanes of a wave read (and later write) one contiguous 1 KB of
 // state, whole cache lines.  B and C (shared by the heads of a sequence) are
 // staged in LDS once per workgroup; the sum over states crosses the 16 state
-// groups once, through LDS.  With an odd head count the last workgroup's
-// second half has no head and only takes part in the barriers.
-__global__ __launch_bounds__(512) void scan1_kernel(ScanArgs a) {
+// groups once, through LDS.  When the head count is not a multiple of 4,
+// the last workgroup's quarters without a head only take part in the
+// barriers.
+__global__ __launch_bounds__(1024) void scan1_kernel(ScanArgs a) {
   constexpr int P = 64, N = 128, NPT = 8;
-  __shared__ __attribute__((aligned(16))) float red2[2][16][P];
+  __shared__ __attribute__((aligned(16))) float red4[4][16][P];
   __shared__ float sBC[2 * N];
-  const int half = threadIdx.x >> 8, t = threadIdx.x & 255;
-  const int h = 2 * blockIdx.x + half, b = blockIdx.y;
+  const int quarter = threadIdx.x >> 8, t = threadIdx.x & 255;
+  const int h = 4 * blockIdx.x + quarter, b = blockIdx.y;
   const bool live = h < a.H;
-  float (*red)[P] = red2[half];
+  float (*red)[P] = red4[quarter];
   const int lane = t & 63, pb = t >> 6, pq = lane & 3, ns = lane >> 2;
   const int p0 = pb * 16 + pq * 4;
   const int hc = live ? h : a.H - 1;  // a head without work reads valid memory and stores nothing
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(512) void scan1_kernel(ScanArgs a) {
     const v4f v = __builtin_nontemporal_load((const v4f*)(stb + ((size_t)(pb * N + 16 * i + ns) * 16 + pq * 4)));
     S[i] = make_float4(v.x, v.y, v.z, v.w);
   }
-  if (half == 0) sBC[t] = xr[a.d_inner + t];  // B then C (2 N = 256 values)
+  if (quarter == 0) sBC[t] = xr[a.d_inner + t];  // B then C (2 N = 256 values)
   const float4 xv = *(const float4*)(xr + hc * P + p0);
   const float dt = softplus_f(a.zx[(size_t)b * a.ldzx + a.dt_off + hc] + a.dt_bias[hc]);
   const float dA = __expf(-dt * __expf(a.A_log[hc]));
@@ -567,7 +568,7 @@ hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
   const dim3 grid(a.H, a.B);
   if (a.T == 1 && P == 64 && N == 128) {
-    hipLaunchKernelGGL(scan1_kernel, dim3((a.H + 1) / 2, a.B), dim3(512), 0, st, a);
+    hipLaunchKernelGGL(scan1_kernel, dim3((a.H + 3) / 4, a.B), dim3(1024), 0, st, a);
     return hipGetLastError();
   }
   if (P == 64 && N == 128) {
