@@ -453,6 +453,70 @@ def bench_codec(args):
     print(json.dumps(out))
 
 
+def bench_reference(args):
+    """Reference rates of this GPU for the kernels' bounds, printed as one JSON line: the vendor int8 and bf16
+    GEMMs (torch._int_mm, torch.matmul) on the prefill's scaffold shapes, plain device copy / in-place scale /
+    fill bandwidth, and the scaffold GEMM here (dfssm_k_gemm, no acc output) on the in_proj shape over K."""
+    import torch
+    from bit_quantized_mamba_amd import call, _dp, _stream
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+
+    def timed(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3  # us
+
+    out = {"metric": "reference rates of this GPU (vendor GEMMs, device copies) and the scaffold GEMM over K",
+           "n_gpus": 1, "data": "synthetic (seeded)", "gemm": [], "hbm": {}, "k_sweep_in_proj": []}
+    for (M, N, K) in [(16384, 8512, 2048), (16384, 2048, 4096)]:
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+        b = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g).t()
+        us_i8 = timed(lambda: torch._int_mm(a, b))
+        a16 = torch.randn((M, K), dtype=torch.bfloat16, device=dev, generator=g)
+        b16 = torch.randn((K, N), dtype=torch.bfloat16, device=dev, generator=g)
+        us_bf = timed(lambda: a16 @ b16)
+        out["gemm"].append({"M": M, "N": N, "K": K, "int_mm_us": round(us_i8, 1),
+                            "int_mm_TOPs": round(2 * M * N * K / us_i8 / 1e6, 1),
+                            "bf16_matmul_us": round(us_bf, 1)})
+        del a, b, a16, b16
+    x = torch.ones(1 << 27, dtype=torch.float32, device=dev)  # 0.54 GB
+    y = torch.empty_like(x)
+    nb = x.numel() * 4
+    out["hbm"] = {"bytes": nb,
+                  "copy_GBs": round(2 * nb / timed(lambda: y.copy_(x)) / 1e3, 0),
+                  "inplace_scale_GBs": round(2 * nb / timed(lambda: x.mul_(1.0)) / 1e3, 0),
+                  "fill_GBs": round(nb / timed(lambda: y.fill_(0.0)) / 1e3, 0)}
+    del x, y
+    M, N = 16384, 8512
+    for K in (256, 512, 1024, 2048, 4096):
+        bits = torch.randint(-2**31, 2**31 - 1, (N, K // 32), dtype=torch.int32, device=dev, generator=g)
+        sw = torch.rand(N, device=dev, generator=g) * 0.04 + 0.01
+        A = torch.randint(-127, 128, (16, K), dtype=torch.int8, device=dev, generator=g)
+        sA = torch.full((16,), 1e-3, device=dev)
+        Bm = torch.randint(-127, 128, (N, 16), dtype=torch.int8, device=dev, generator=g)
+        sB = torch.full((N,), 1e-3, device=dev)
+        q = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+        s = torch.rand(M, device=dev, generator=g) * 0.01
+        yk = torch.empty((M, N), dtype=torch.float32, device=dev)
+        us = timed(lambda: call("dfssm_k_gemm", _dp(bits), _dp(sw), _dp(A), _dp(sA), _dp(Bm), _dp(sB), K, N,
+                                _dp(q), _dp(s), M, None, _dp(yk), _stream(None)))
+        out["k_sweep_in_proj"].append({"K": K, "us_per_call_incl_operand_prep": round(us, 1)})
+        del bits, A, Bm, q, yk
+    print(json.dumps(out))
+
+
 def cpu_baseline(shape, seed, prompt, budget_s):
     """The CPU oracle decoding the same model, timed on a bounded number of steps."""
     import numpy as np
@@ -488,7 +552,8 @@ def main():
                     help="also time each kernel of the per-layer (multi-kernel) path")
     ap.add_argument("--path", choices=["auto", "kernels", "persistent", "gemm"], default="auto")
     ap.add_argument("--workload", choices=["decode-b1", "decode-b32", "decode-b512", "prefill-8x2048",
-                                           "tiny-decode", "layer-1p3b-hot", "layer-1p3b-cold", "state-codec"],
+                                           "tiny-decode", "layer-1p3b-hot", "layer-1p3b-cold", "state-codec",
+                                           "reference-rates"],
                     default="decode-b1")
     ap.add_argument("--phase-profile", type=int, default=0, metavar="TOKENS",
                     help="after the timed region, decode this many tokens with the persistent kernel's phase "
@@ -504,6 +569,9 @@ def main():
 
     if args.workload == "state-codec":
         bench_codec(args)
+        return
+    if args.workload == "reference-rates":
+        bench_reference(args)
         return
     if args.workload in ("tiny-decode", "layer-1p3b-hot", "layer-1p3b-cold"):
         bench_small(args)
