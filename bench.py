@@ -635,7 +635,14 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "kernel": "decode_persistent_kernel", "bytes_per_launch": sb * args.steps,
-                    "us_per_launch": round(ms * 1e3, 1)}
+                    "us_per_launch": round(ms * 1e3, 1),
+                    # what limits the launch below its HBM bound (measured, not derived from this run)
+                    "limiter": {"what": "all-to-all exchanges between the 256 workgroups: 3 per layer, 1 per token "
+                                        "for the argmax, each one device-coherent store -> load round trip plus the "
+                                        "wait for the slowest publisher",
+                                "us_per_exchange_alone": [1.7, 2.0],
+                                "exchanges_per_token": 3 * s.n_layer + 1,
+                                "us_per_layer": round(ms * 1e3 / args.steps / s.n_layer, 2)}}
     kernels = {}
     if args.kernel_breakdown or not persistent:
         ab = algorithmic_bytes(s)
