@@ -162,6 +162,34 @@ def test_batch_independence():
     one.close()
 
 
+@pytest.mark.parametrize("shape,B", [(synth.TINY, 5),
+                                     (synth.Shape(n_layer=2, d_model=2048, d_inner=4096, d_state=128, headdim=64,
+                                                  vocab=1024), 32)],
+                         ids=["tiny-B5", "1p3b-2layer-B32"])
+def test_split_decode_equals_one_chain(shape, B):
+    # an untraced decode step of 2..32 sequences runs its layers as two
+    # concurrent chains of half the sequences each; the traced step runs one
+    # chain of all of them: logits and every state bit for bit the same
+    seed = synth.SEED_BASE + 7
+    a = engine(shape, max_batch=B)
+    b = engine(shape, max_batch=B)
+    a.load_synthetic(seed)
+    b.load_synthetic(seed)
+    toks = synth.gen_tokens(seed, 1, 4 * B, shape.vocab).reshape(4, B)
+    for t in range(4):
+        lg_a, nx_a = a.decode_step(_i32(toks[t]))
+        tr = trace_to_numpy(b.trace_step(_i32(toks[t])))
+        assert np.array_equal(lg_a.cpu().numpy(), tr["logits"]), t
+    for q in range(B):
+        ca, sa = a.get_state(q)
+        cb, sb = b.get_state(q)
+        assert np.array_equal(ca, cb) and np.array_equal(sa, sb), q
+    a.check()
+    b.check()
+    a.close()
+    b.close()
+
+
 def test_run_to_run_determinism():
     s = synth.TINY
     outs = []
