@@ -87,8 +87,8 @@ struct dfssm_ctx {
 
   // the two halves of a small batched decode step run as concurrent chains
   // on these streams (created on first use): fork and join events
-  hipStream_t split_st[2] = {nullptr, nullptr};
-  hipEvent_t split_ev[3] = {nullptr, nullptr, nullptr};
+  hipStream_t split_st[4] = {};
+  hipEvent_t split_ev[5] = {};
 
   // memory: one block for weights, state, workspace and mailboxes (the
   // caller's arena, or a library allocation); the batched-path workspace is
@@ -609,40 +609,43 @@ struct RowShift {
   }
 };
 
-// Decode steps of 2 .. kSkinnyDecodeRows sequences split the layers into two
-// concurrent chains of half the sequences each: every kernel of the small
-// batch is a chain of memory latency using a fraction of the chip, so two
-// chains overlap (measured 2.79 -> 2.57 ms per batch-32 step).  Sequences are
-// independent and every kernel's result for a row depends on that row alone,
-// so the split changes no value.  The embedding runs before the fork, the
-// final norm, LM head and argmax after the join.
+// Decode steps of 2 .. kSkinnyDecodeRows sequences split the layers into
+// kSplitChains concurrent chains of consecutive sequences: every kernel of
+// the small batch is a chain of memory latency using a fraction of the chip,
+// so the chains overlap (measured 2.79 -> 2.57 ms per batch-32 step with two
+// chains).  Sequences are independent and every kernel's result for a row
+// depends on that row alone, so the split changes no value.  The embedding
+// runs before the fork, the final norm, LM head and argmax after the join.
+constexpr int kSplitChains = 2;
 bool split_decode(int B) { return B >= 2 && B <= kSkinnyDecodeRows; }
 
 dfssm_status enqueue_decode_split(dfssm_ctx* c, const int32_t* tok, int B, float* logits, int32_t* next,
                                   int32_t* out, hipStream_t st) {
-  for (auto& s2 : c->split_st)
-    if (!s2) HIP_TRY(hipStreamCreateWithFlags(&s2, hipStreamNonBlocking));
-  for (auto& e : c->split_ev)
-    if (!e) HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  const int n = std::min(kSplitChains, B);
+  for (int k = 0; k < n; ++k)
+    if (!c->split_st[k]) HIP_TRY(hipStreamCreateWithFlags(&c->split_st[k], hipStreamNonBlocking));
+  for (int k = 0; k <= n; ++k)
+    if (!c->split_ev[k]) HIP_TRY(hipEventCreateWithFlags(&c->split_ev[k], hipEventDisableTiming));
   auto& w = c->gw;
   HIP_TRY(launch_embed_rows(tok, 1, 0, B, 1, c->lt<int8_t>(-1, DFSSM_G_EMBED), c->lt<float>(-1, DFSSM_G_EMBED_SCALE),
                             c->dm, c->V, w.h, c->err, st));
   HIP_TRY(hipEventRecord(c->split_ev[0], st));
-  const int half = B / 2;
-  for (int k = 0; k < 2; ++k) {
+  int r0 = 0;
+  for (int k = 0; k < n; ++k) {
+    const int rows = B / n + (k < B % n ? 1 : 0);
     hipStream_t sk = c->split_st[k];
     HIP_TRY(hipStreamWaitEvent(sk, c->split_ev[0], 0));
     {
-      RowShift shift(c, k ? half : 0);
+      RowShift shift(c, r0);
       for (int l = 0; l < c->L; ++l) {
-        const dfssm_status r = enqueue_layer_gemm(c, l, k ? B - half : half, 1, sk, nullptr, nullptr);
+        const dfssm_status r = enqueue_layer_gemm(c, l, rows, 1, sk, nullptr, nullptr);
         if (r != DFSSM_OK) return r;
       }
     }
     HIP_TRY(hipEventRecord(c->split_ev[1 + k], sk));
+    r0 += rows;
   }
-  HIP_TRY(hipStreamWaitEvent(st, c->split_ev[1], 0));
-  HIP_TRY(hipStreamWaitEvent(st, c->split_ev[2], 0));
+  for (int k = 0; k < n; ++k) HIP_TRY(hipStreamWaitEvent(st, c->split_ev[1 + k], 0));
   float* lg = logits ? logits : c->logits;
   HIP_TRY(b_head(c, B, 1, lg, nullptr, st));
   if (next || out) HIP_TRY(launch_argmax(lg, c->V, B, next ? next : c->next, out, c->counter, st));
