@@ -609,15 +609,17 @@ struct RowShift {
   }
 };
 
-// Decode steps of 2 .. kSkinnyDecodeRows sequences split the layers into
-// kSplitChains concurrent chains of consecutive sequences: every kernel of
-// the small batch is a chain of memory latency using a fraction of the chip,
-// so the chains overlap (measured 2.79 -> 2.57 ms per batch-32 step with two
-// chains).  Sequences are independent and every kernel's result for a row
-// depends on that row alone, so the split changes no value.  The embedding
-// runs before the fork, the final norm, LM head and argmax after the join.
+// Decode steps of two or more sequences split the layers into kSplitChains
+// concurrent chains of consecutive sequences.  At small batches every kernel
+// is a chain of memory latency using a fraction of the chip, so the chains
+// overlap; at large batches one chain's projections overlap the other's
+// state-bound scan (measured per step: batch 32 2.79 -> 2.57 ms, 128 7.69 ->
+// 6.97, 256 12.74 -> 11.64, 512 22.6 -> 20.9; batch 64 unchanged).
+// Sequences are independent and every kernel's result for a row depends on
+// that row alone, so the split changes no value.  The embedding runs before
+// the fork, the final norm, LM head and argmax after the join.
 constexpr int kSplitChains = 2;
-bool split_decode(int B) { return B >= 2 && B <= kSkinnyDecodeRows; }
+bool split_decode(int B) { return B >= 2; }
 
 dfssm_status enqueue_decode_split(dfssm_ctx* c, const int32_t* tok, int B, float* logits, int32_t* next,
                                   int32_t* out, hipStream_t st) {
