@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 import synth
-from tests._common import assert_close, engine, oracle_follow_step, rel_err, token_ok, trace_to_numpy
+from tests._common import (assert_close, assert_flip_fraction, engine, oracle_follow_step, rel_err, token_ok,
+                           trace_to_numpy)
 
 pytestmark = pytest.mark.gpu
 
@@ -140,6 +141,57 @@ def test_prefill_then_decode_equals_decode_loop():
     assert torch.equal(lg_p, lg_d) and torch.equal(nx_p, nx_d)
     for b in range(2):
         assert np.array_equal(st_p[b][0], st_d[b][0]) and np.array_equal(st_p[b][1], st_d[b][1])
+    eng.close()
+
+
+def test_prefill_then_decode_close_to_decode_loop_1p3b():
+    # At the 1.3B shape prefill runs the chunked matrix-core scan and decode
+    # the one-token scan: the same sums in another order, so the invariant
+    # holds within fp32 rounding rather than bit for bit.  Two layers, 2
+    # sequences of 130 tokens (two whole 64-token chunks and a ragged tail),
+    # GPU against GPU, both traced.
+    s = synth.Shape(n_layer=2, d_model=2048, d_inner=4096, d_state=128, headdim=64, vocab=1024)
+    B, T = 2, 130
+    eng = engine(s, max_batch=B)
+    eng.load_synthetic(synth.SEED_BASE + 9)
+    toks = synth.gen_tokens(synth.SEED_BASE + 9, 3, B * T, s.vocab).reshape(B, T)
+    eng.reset_state(B)
+    tp = trace_to_numpy(eng.trace_prefill(_i32(toks)))
+    st_p = [eng.get_state(b) for b in range(B)]
+    eng.reset_state(B)
+    q1 = np.empty_like(tp["q1"])
+    q2 = np.empty_like(tp["q2"])
+    for t in range(T):
+        td = trace_to_numpy(eng.trace_step(_i32(toks[:, t])))
+        q1[:, t::T] = td["q1"]  # rows m = b * T + t
+        q2[:, t::T] = td["q2"]
+    st_d = [eng.get_state(b) for b in range(B)]
+    # Layer 0 sees the same codes on both paths (its input is the embedding),
+    # so its states differ only by the scan's arithmetic: the chunk's running
+    # sums of -dt exp(A_log) reach a few hundred in magnitude, and their fp32
+    # rounding moves the decays exp(A_i - A_j) by up to ~1e-5 relative (the
+    # conv window is the in_proj output itself: bit for bit).
+    assert np.array_equal(q1[0], tp["q1"][0])
+    for b in range(B):
+        assert np.array_equal(st_p[b][0][0], st_d[b][0][0]), b
+        assert_close(st_p[b][1][0], st_d[b][1][0], tol=1e-4, what=f"layer-0 ssm state {b}")
+    # Layer 0's gated-output codes come from those slightly different scan
+    # outputs: a code whose scaled value lies within that rounding of a tie
+    # may land on the other side, one step away; such codes are rare (the
+    # flip-fraction bound of the oracle comparisons).
+    d0 = q2[0].astype(np.int32) - tp["q2"][0].astype(np.int32)
+    assert np.abs(d0).max() <= 1
+    assert_flip_fraction({"flips": int(np.count_nonzero(d0)), "codes": d0.size}, what="layer-0 q2")
+    # Each such flip moves one out_proj input by a quantisation step; layer 1
+    # and the logits carry that (no code is forced here, unlike the oracle
+    # comparisons), so they are held to the long-run bound.
+    diff1 = {k: float(np.count_nonzero(a[1] != b[1])) / a[1].size
+             for k, a, b in (("q1", q1, tp["q1"]), ("q2", q2, tp["q2"]))}
+    for b in range(B):
+        assert_close(st_p[b][0], st_d[b][0], tol=1e-2, what=f"conv state {b} (layer-1 code differences {diff1})")
+        assert_close(st_p[b][1], st_d[b][1], tol=1e-2, what=f"ssm state {b} (layer-1 code differences {diff1})")
+    assert_close(tp["logits"], td["logits"], tol=1e-2, what=f"last logits (layer-1 code differences {diff1})")
+    eng.check()
     eng.close()
 
 
