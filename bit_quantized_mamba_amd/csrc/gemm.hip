@@ -807,7 +807,9 @@ hipError_t launch_bitgemm(const GemmArgs& a, int epi, hipStream_t st) {
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyUnroll = 16;  // k-steps whose loads are issued together
 
-template <int KIND>
+// VEC: K is a multiple of 4 x 32 x kSkinnyUnroll, so every wave's k slice is
+// whole groups of k-steps (the loads need neither clamps nor branches)
+template <int KIND, bool VEC>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a0, int nrb) {
   __shared__ int red[3][16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -884,30 +886,51 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a0, int nrb
   for (int k0 = kbeg; k0 < kend; k0 += 32 * kSkinnyUnroll) {
     v4i af[kSkinnyUnroll], bf[kSkinnyUnroll];
     uint32_t bw[kSkinnyUnroll];
+    if constexpr (VEC) {
+      // every wave's k slice is whole groups: no clamp, no per-step word
+      // loads, and no branch, so no load waits for another one to land
 #pragma unroll
-    for (int u = 0; u < kSkinnyUnroll; ++u) {
-      const int k = min(k0 + 32 * u, kend - 32);  // a partial last group re-reads valid data, zeroed below
-      af[u] = *(const v4i*)(qrow + k);
-      if (KIND == SK_HEAD)
-        bf[u] = *(const v4i*)((const int8_t*)a.w + (size_t)nc * K + k + 16 * kg);
-      else if (!wvec || k0 + 32 * kSkinnyUnroll > kend)  // one word per k-step
-        bw[u] = ((const uint32_t*)a.w)[(size_t)nc * (K / 32) + k / 32];
-    }
-    if (KIND != SK_HEAD && wvec && k0 + 32 * kSkinnyUnroll <= kend) {
-      // a whole group: the column's kSkinnyUnroll words are contiguous, four per 16-byte load
-      const uint4* wp = (const uint4*)((const uint32_t*)a.w + (size_t)nc * (K / 32) + k0 / 32);
+      for (int u = 0; u < kSkinnyUnroll; ++u) {
+        af[u] = *(const v4i*)(qrow + k0 + 32 * u);
+        if (KIND == SK_HEAD) bf[u] = *(const v4i*)((const int8_t*)a.w + (size_t)nc * K + k0 + 32 * u + 16 * kg);
+      }
+      if (KIND != SK_HEAD) {
+        const uint4* wp = (const uint4*)((const uint32_t*)a.w + (size_t)nc * (K / 32) + k0 / 32);
 #pragma unroll
-      for (int v = 0; v < kSkinnyUnroll / 4; ++v) {
-        const uint4 w4 = wp[v];
-        bw[4 * v] = w4.x;
-        bw[4 * v + 1] = w4.y;
-        bw[4 * v + 2] = w4.z;
-        bw[4 * v + 3] = w4.w;
+        for (int v = 0; v < kSkinnyUnroll / 4; ++v) {
+          const uint4 w4 = wp[v];
+          bw[4 * v] = w4.x;
+          bw[4 * v + 1] = w4.y;
+          bw[4 * v + 2] = w4.z;
+          bw[4 * v + 3] = w4.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kSkinnyUnroll; ++u) {
+        const int k = min(k0 + 32 * u, kend - 32);  // a partial last group re-reads valid data, zeroed below
+        af[u] = *(const v4i*)(qrow + k);
+        if (KIND == SK_HEAD)
+          bf[u] = *(const v4i*)((const int8_t*)a.w + (size_t)nc * K + k + 16 * kg);
+        else if (!wvec || k0 + 32 * kSkinnyUnroll > kend)  // one word per k-step
+          bw[u] = ((const uint32_t*)a.w)[(size_t)nc * (K / 32) + k / 32];
+      }
+      if (KIND != SK_HEAD && wvec && k0 + 32 * kSkinnyUnroll <= kend) {
+        // a whole group: the column's kSkinnyUnroll words are contiguous, four per 16-byte load
+        const uint4* wp = (const uint4*)((const uint32_t*)a.w + (size_t)nc * (K / 32) + k0 / 32);
+#pragma unroll
+        for (int v = 0; v < kSkinnyUnroll / 4; ++v) {
+          const uint4 w4 = wp[v];
+          bw[4 * v] = w4.x;
+          bw[4 * v + 1] = w4.y;
+          bw[4 * v + 2] = w4.z;
+          bw[4 * v + 3] = w4.w;
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < kSkinnyUnroll; ++u) {
-      const bool live = mok && k0 + 32 * u < kend;
+      const bool live = mok && (VEC || k0 + 32 * u < kend);
       if (!live) af[u] = (v4i){};
       if (KIND != SK_HEAD) {
         const uint32_t h = nok ? bw[u] >> (16 * kg) : 0u;
@@ -985,10 +1008,14 @@ hipError_t launch_gemm_skinny(const SkinnyArgs& a, int kind, hipStream_t st) {
   const long tiles = (long)nrb * ((a.N + 31) / 32);
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)tiles), block(256);
-  switch (kind) {
-    case SK_IN: hipLaunchKernelGGL(gemm_skinny_kernel<SK_IN>, grid, block, 0, st, a, nrb); break;
-    case SK_OUT: hipLaunchKernelGGL(gemm_skinny_kernel<SK_OUT>, grid, block, 0, st, a, nrb); break;
-    case SK_HEAD: hipLaunchKernelGGL(gemm_skinny_kernel<SK_HEAD>, grid, block, 0, st, a, nrb); break;
+  const bool vec = a.K % (4 * 32 * kSkinnyUnroll) == 0;
+  switch (kind * 2 + (vec ? 1 : 0)) {
+    case SK_IN * 2: hipLaunchKernelGGL((gemm_skinny_kernel<SK_IN, false>), grid, block, 0, st, a, nrb); break;
+    case SK_IN * 2 + 1: hipLaunchKernelGGL((gemm_skinny_kernel<SK_IN, true>), grid, block, 0, st, a, nrb); break;
+    case SK_OUT * 2: hipLaunchKernelGGL((gemm_skinny_kernel<SK_OUT, false>), grid, block, 0, st, a, nrb); break;
+    case SK_OUT * 2 + 1: hipLaunchKernelGGL((gemm_skinny_kernel<SK_OUT, true>), grid, block, 0, st, a, nrb); break;
+    case SK_HEAD * 2: hipLaunchKernelGGL((gemm_skinny_kernel<SK_HEAD, false>), grid, block, 0, st, a, nrb); break;
+    case SK_HEAD * 2 + 1: hipLaunchKernelGGL((gemm_skinny_kernel<SK_HEAD, true>), grid, block, 0, st, a, nrb); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
