@@ -436,7 +436,28 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
   const float* lr = logits + (size_t)b * V;
   float best = -__builtin_huge_valf();
   int idx = 0x7fffffff;
-  for (int v = threadIdx.x; v < V; v += blockDim.x) {
+  // Rows of a multiple of 4 logits from a 16-byte aligned base are read as float4, four
+  // loads in flight per thread (indexes clamped, not branched around, so the
+  // loads issue together); a thread meets its indexes in increasing order, so
+  // the strict compare keeps the lowest index of equal values.
+  const int V4 = V % 4 == 0 && ((uintptr_t)logits & 15) == 0 ? V / 4 : 0;
+  const float4* l4 = (const float4*)lr;
+  for (int base = threadIdx.x; base < V4; base += 4 * (int)blockDim.x) {
+    float4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = l4[min(base + u * (int)blockDim.x, V4 - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * (int)blockDim.x;
+      if (i < V4) {
+        if (x[u].x > best) { best = x[u].x; idx = 4 * i; }
+        if (x[u].y > best) { best = x[u].y; idx = 4 * i + 1; }
+        if (x[u].z > best) { best = x[u].z; idx = 4 * i + 2; }
+        if (x[u].w > best) { best = x[u].w; idx = 4 * i + 3; }
+      }
+    }
+  }
+  for (int v = 4 * V4 + threadIdx.x; v < V; v += blockDim.x) {
     const float x = lr[v];
     if (x > best) { best = x; idx = v; }
   }
