@@ -38,9 +38,9 @@ PAGES_B512_TOKS = 5081.0  # decode tokens/s at batch 512 (A100), the pages' only
 # (FETCH_SIZE reads 0.5 GiB for it: factor 2.0; WRITE_SIZE reads 1 GiB: 1.0).
 # Valid only for the kernel sources they were taken from (hash below).
 COUNTED_TRAFFIC = {
-    "sources_sha256": "0364ee11c580422ca866ff1f597c8e860bd6b70c27cc596bb8fdb4dcb9573565",
-    "fetch_bytes_per_token": 460704727,
-    "write_bytes_per_token": 118426848,
+    "sources_sha256": "7d6f23ed2288ae67b164c6f50683114adfd5a6fbf372422f38c7153b87ae6b7c",
+    "fetch_bytes_per_token": 461728520,
+    "write_bytes_per_token": 118426855,
 }
 KERNEL_SOURCES = ("bit_quantized_mamba_amd/csrc/persistent.hip", "bit_quantized_mamba_amd/csrc/persistent.h",
                   "bit_quantized_mamba_amd/csrc/common.h")
