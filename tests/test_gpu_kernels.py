@@ -129,3 +129,58 @@ def test_k_proj_all_sign_probes():
                         _dev(q), _dev(np.ones(1, np.float32)))
         want = np.where((bits[:, j // 32] >> np.uint32(j % 32)) & 1, 127, -127)
         assert np.array_equal(acc.cpu().numpy()[0], want), j
+
+
+# ---------------------------------------------------------------------------
+# greedy argmax of the batched path: both ways a logits row is read
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("vocab", [1024, 1021], ids=["v1024", "v1021"])
+@pytest.mark.parametrize("aligned", [True, False], ids=["aligned", "offset4"])
+def test_argmax_rows_both_read_forms(vocab, aligned):
+    """Next token = lowest index of each row's maximum logit, whether the row is
+    read four floats at a time (a vocabulary that is a multiple of 4 from a
+    16-byte aligned base) or one float at a time (an odd vocabulary, or a base
+    4 bytes off), including an exact tie with a copy of the winning embedding
+    row near the end of the vocabulary."""
+    import dataclasses
+    shape = dataclasses.replace(synth.TINY, vocab=vocab)
+    seed = synth.SEED_BASE + 77
+    B = 3
+    eng = engine(shape, max_batch=B)
+    eng.set_path("gemm")
+    eng.load_synthetic(seed)
+    toks = synth.gen_tokens(seed, 5, B, vocab)
+
+    def step():
+        eng.reset_state(B)
+        buf = torch.empty(B * vocab + 4, dtype=torch.float32, device="cuda")
+        lg = (buf[:B * vocab] if aligned else buf[1:1 + B * vocab]).view(B, vocab)
+        lg, nx = eng.decode_step(_dev(toks.astype(np.int32)), logits=lg)
+        return lg.cpu().numpy(), nx.cpu().numpy()
+
+    lg, nx = step()
+    assert np.array_equal(nx, np.argmax(lg, axis=1))
+    # row 0's winner copied to the highest index that is neither it nor an
+    # input token (the inputs stay as they were): the same logit bit for bit,
+    # and the lower index wins
+    a = int(nx[0])
+    used = set(int(t) for t in toks)
+    above = sorted(set(range(a + 1, vocab)) - used)
+    if above:
+        dup, winner = above[-1], a
+    else:
+        dup = min(set(range(a)) - used)
+        winner = dup
+    E, sE = eng.get_tensor(-1, "E"), eng.get_tensor(-1, "sE")
+    E[dup], sE[dup] = E[a], sE[a]
+    eng.set_tensor(-1, "E", E)
+    eng.set_tensor(-1, "sE", sE)
+    lg2, nx2 = step()
+    keep = np.arange(vocab) != dup
+    assert np.array_equal(lg2[:, keep], lg[:, keep])
+    assert lg2[0, dup] == lg2[0, a]
+    assert int(nx2[0]) == winner
+    assert np.array_equal(nx2, np.argmax(lg2, axis=1))
+    eng.check()
+    eng.close()
