@@ -517,6 +517,63 @@ def bench_reference(args):
     print(json.dumps(out))
 
 
+def bench_host(args):
+    """Batch-1 greedy decode of the 48-layer model on the host CPU backend (libdfssm_host.so):
+    16-token prompt, untimed warmup steps, then timed steps; the memory roofline is priced against
+    this host's measured copy rate with the same threads, and the CPU oracle is timed beside it."""
+    import numpy as np
+    import synth
+    from bit_quantized_mamba_amd.host import HostEngine
+
+    s = synth.FULL_1P3B
+    seed = synth.SEED_BASE + 2
+    facts = host_facts()
+    threads = min(16, facts["nproc"] or 1)
+    eng = HostEngine.from_shape(s, max_batch=1, threads=threads)
+    eng.load_synthetic(seed)
+    prompt = synth.gen_tokens(seed, 0, 16, s.vocab)
+    steps, warmup = min(args.steps, 128), min(args.warmup, 8)
+    rates = {}
+    isas = ["portable", "auto"]
+    for isa in isas:
+        eng.set_isa(isa)
+        eng.reset_state(1)
+        _, nxt = eng.prefill(prompt[None])
+        tok = nxt.copy()
+        if warmup:
+            eng.generate(tok, warmup)
+        t0 = time.perf_counter()
+        eng.generate(tok, steps if isa == "auto" else max(8, steps // 8))
+        el = time.perf_counter() - t0
+        rates[eng.isa] = (steps if isa == "auto" else max(8, steps // 8)) / el
+        if isa == "auto":
+            ms = el / steps * 1e3
+    value = rates[eng.isa]
+    copy = eng.copy_rate(1 << 30, 5)
+    per_token = step_bytes(s)
+    achieved = per_token * value / 1e9
+    res = {
+        "metric": "decode tokens/s, batch=1, 48-layer 1.3B shape, host CPU backend; % of the host's copy rate",
+        "value": round(value, 2), "unit": "tokens/s", "n_gpus": 0, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8/1-bit weights, int32 accumulation, f32 state", "data": "synthetic (seeded weights and tokens)",
+        "config": {"workload": f"DF-SSM 48-layer 1.3B shape, batch 1, 16-token prefill then greedy decode of "
+                               f"{steps} tokens on the host CPU backend ({eng.isa}, {threads} threads)",
+                   "batch": 1, "prefill": 16, "threads": threads},
+        "roofline": {"bound": "host memory", "achieved": round(achieved, 1), "peak": round(copy, 1), "unit": "GB/s",
+                     "frac": round(achieved / copy, 4), "traffic": None,
+                     "peak_kind": "measured copy rate (read + write) of this host with the same threads",
+                     "bytes_per_token": per_token},
+        "paths_tokens_per_s": {k: round(v, 2) for k, v in rates.items()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(s, seed, prompt, args.cpu_seconds)
+        res["vs_oracle"] = round(value / res["cpu_baseline"]["value"], 2)
+    eng.close()
+    print(json.dumps(res))
+
+
 def cpu_baseline(shape, seed, prompt, budget_s):
     """The CPU oracle decoding the same model, timed on a bounded number of steps."""
     import numpy as np
@@ -553,7 +610,7 @@ def main():
     ap.add_argument("--path", choices=["auto", "kernels", "persistent", "gemm"], default="auto")
     ap.add_argument("--workload", choices=["decode-b1", "decode-b32", "decode-b512", "prefill-8x2048",
                                            "tiny-decode", "layer-1p3b-hot", "layer-1p3b-cold", "state-codec",
-                                           "reference-rates"],
+                                           "reference-rates", "host-decode"],
                     default="decode-b1")
     ap.add_argument("--phase-profile", type=int, default=0, metavar="TOKENS",
                     help="after the timed region, decode this many tokens with the persistent kernel's phase "
@@ -572,6 +629,9 @@ def main():
         return
     if args.workload == "reference-rates":
         bench_reference(args)
+        return
+    if args.workload == "host-decode":
+        bench_host(args)
         return
     if args.workload in ("tiny-decode", "layer-1p3b-hot", "layer-1p3b-cold"):
         bench_small(args)

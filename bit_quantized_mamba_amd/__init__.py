@@ -42,7 +42,29 @@ def _dp(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-class Engine:
+class _Shapes:
+    """Shapes and kind ids of the weight tensors (canonical layouts of include/dfssm.h), from the
+    dimensions an engine holds as attributes."""
+
+    def _tensor_shape(self, layer: int, kind: str):
+        r = self.rank
+        if layer < 0:
+            return {"E": ((self.vocab, self.d_model), np.int8), "sE": ((self.vocab,), np.float32),
+                    "final_norm": ((self.d_model,), np.float32)}[kind]
+        dp, dm, di, cd, H = self.d_in_proj, self.d_model, self.d_inner, self.conv_dim, self.n_heads
+        return {"in_bits": ((dp, dm // 32), np.uint32), "in_sw": ((dp,), np.float32), "in_A": ((r, dm), np.int8),
+                "in_sA": ((r,), np.float32), "in_B": ((dp, r), np.int8), "in_sB": ((dp,), np.float32),
+                "out_bits": ((dm, di // 32), np.uint32), "out_sw": ((dm,), np.float32),
+                "out_A": ((r, di), np.int8), "out_sA": ((r,), np.float32), "out_B": ((dm, r), np.int8),
+                "out_sB": ((dm,), np.float32), "conv_w": ((cd, self.d_conv), np.float32),
+                "conv_b": ((cd,), np.float32), "A_log": ((H,), np.float32), "dt_bias": ((H,), np.float32),
+                "D": ((H,), np.float32), "norm_w": ((dm,), np.float32), "gnorm_w": ((di,), np.float32)}[kind]
+
+    def _kind_id(self, layer: int, kind: str) -> int:
+        return GLOBAL_KINDS.index(kind) if layer < 0 else LAYER_KINDS.index(kind)
+
+
+class Engine(_Shapes):
     """A DF-SSM model held on one GPU: weights, the recurrent state of
     `max_batch` sequence slots and the workspace, owned by the library."""
 
@@ -99,23 +121,6 @@ class Engine:
     # -- weights -----------------------------------------------------------
     def load_synthetic(self, seed: int, stream=None) -> None:
         call("dfssm_load_synthetic", self._h, ctypes.c_uint64(seed), _stream(stream))
-
-    def _tensor_shape(self, layer: int, kind: str):
-        r = self.rank
-        if layer < 0:
-            return {"E": ((self.vocab, self.d_model), np.int8), "sE": ((self.vocab,), np.float32),
-                    "final_norm": ((self.d_model,), np.float32)}[kind]
-        dp, dm, di, cd, H = self.d_in_proj, self.d_model, self.d_inner, self.conv_dim, self.n_heads
-        return {"in_bits": ((dp, dm // 32), np.uint32), "in_sw": ((dp,), np.float32), "in_A": ((r, dm), np.int8),
-                "in_sA": ((r,), np.float32), "in_B": ((dp, r), np.int8), "in_sB": ((dp,), np.float32),
-                "out_bits": ((dm, di // 32), np.uint32), "out_sw": ((dm,), np.float32),
-                "out_A": ((r, di), np.int8), "out_sA": ((r,), np.float32), "out_B": ((dm, r), np.int8),
-                "out_sB": ((dm,), np.float32), "conv_w": ((cd, self.d_conv), np.float32),
-                "conv_b": ((cd,), np.float32), "A_log": ((H,), np.float32), "dt_bias": ((H,), np.float32),
-                "D": ((H,), np.float32), "norm_w": ((dm,), np.float32), "gnorm_w": ((di,), np.float32)}[kind]
-
-    def _kind_id(self, layer: int, kind: str) -> int:
-        return GLOBAL_KINDS.index(kind) if layer < 0 else LAYER_KINDS.index(kind)
 
     def set_tensor(self, layer: int, kind: str, value: np.ndarray) -> None:
         shp, dt = self._tensor_shape(layer, kind)

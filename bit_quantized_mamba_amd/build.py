@@ -1,5 +1,6 @@
 """Compile the HIP library (gfx950) into bit_quantized_mamba_amd/libdfssm.so,
-and the stand-alone exchange-latency probe into bit_quantized_mamba_amd/hop_probe."""
+the stand-alone exchange-latency probe into bit_quantized_mamba_amd/hop_probe,
+and the host CPU backend (g++, OpenMP) into bit_quantized_mamba_amd/libdfssm_host.so."""
 import os
 import subprocess
 import sys
@@ -9,6 +10,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libdfssm.so")
 PROBE = os.path.join(HERE, "hop_probe")
+HOST_SRC = os.path.join(HERE, "host", "dfssm_host.cpp")
+HOST_OUT = os.path.join(HERE, "libdfssm_host.so")
+CXX = os.environ.get("CXX_HOST", "g++")
+# x86-64-v3 baseline (AVX2) for the shared code; the AVX-512 VNNI products are
+# compiled per function and chosen at run time.  No floating-point
+# contraction: the results do not depend on which path or CPU runs them.
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "-fopenmp", "-march=x86-64-v3", "-ffp-contract=off"]
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["gen.hip", "kernels.hip", "persistent.hip", "gemm.hip", "scan.hip", "codec.hip", "runtime.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -45,7 +53,17 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for hop_probe.hip:\n{r.stdout}{r.stderr}")
     os.replace(PROBE + ".tmp", PROBE)
+    build_host()
     return OUT
+
+
+def build_host() -> str:
+    cmd = [CXX, *HOST_FLAGS, HOST_SRC, "-o", HOST_OUT + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"{CXX} failed for dfssm_host.cpp:\n{r.stdout}{r.stderr}")
+    os.replace(HOST_OUT + ".tmp", HOST_OUT)
+    return HOST_OUT
 
 
 if __name__ == "__main__":

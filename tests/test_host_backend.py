@@ -1,0 +1,251 @@
+"""The host CPU backend (libdfssm_host.so, include/dfssm_host.h) against the
+CPU oracle and against its own invariants.  These run on the CPU, here and
+on any machine: the backend is host code.
+
+* its synthetic generator draws the same weights as the seeded input
+  generator, bit for bit;
+* decode steps followed by the oracle (on the backend's int8 codes where
+  they are correct roundings): exact int32 scaffold sums, residual stream,
+  logits and final state within the 1e-3 metric;
+* the AVX-512 VNNI path and the portable path give the same bits (only the
+  integer products differ between them, and those are exact), and so do
+  different thread counts and batch compositions;
+* prefill is the decode loop bit for bit; generate is the step loop;
+* the method's special cases: dt = 0 leaves the state bit for bit, an exact
+  logit tie takes the lower index, an all-zero gate adds exactly nothing;
+* argument errors leave the state untouched."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._common import (assert_close, assert_flip_fraction, check_acc, new_flip_stats,
+                           oracle_follow_step)
+
+H = pytest.importorskip("bit_quantized_mamba_amd.host")
+if not os.path.exists(H.HOST_LIB_PATH):
+    pytest.skip("libdfssm_host.so is not built; run __graft_entry__.build()", allow_module_level=True)
+
+TWO_1P3B = synth.Shape(n_layer=2, d_model=2048, d_inner=4096, d_state=128, headdim=64, vocab=1024)
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _engine(shape, seed, max_batch=1, threads=4, isa="auto"):
+    e = H.HostEngine.from_shape(shape, max_batch=max_batch, threads=threads)
+    e.set_isa(isa)
+    e.load_synthetic(seed)
+    return e
+
+
+def _has_vnni():
+    e = H.HostEngine.from_shape(synth.TINY)
+    try:
+        e.set_isa("avx512vnni")
+        return True
+    except H.DfssmError:
+        return False
+    finally:
+        e.close()
+
+
+def test_host_library_exports_every_declared_function():
+    text = open(os.path.join(ROOT, "include", "dfssm_host.h")).read()
+    names = set(re.findall(r"\b(dfssm_host_\w+)\s*\(", text))
+    assert len(names) >= 15
+    lib = H.load()
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+        assert n in H.EXPORTS, n
+
+
+@pytest.mark.parametrize("shape", [synth.TINY, synth.LAYER_1P3B], ids=["tiny", "layer1p3b"])
+def test_host_generator_matches_seeded_generator(shape):
+    seed = synth.SEED_BASE + 31
+    e = _engine(shape, seed)
+    for l in range(shape.n_layer):
+        for k in synth.LAYER_KINDS:
+            want = synth.gen_layer_tensor(shape, seed, l, k)
+            assert np.array_equal(e.get_tensor(l, k).view(np.uint8), want.view(np.uint8)), (l, k)
+    for k in synth.GLOBAL_KINDS:
+        want = synth.gen_global_tensor(shape, seed, k)
+        assert np.array_equal(e.get_tensor(-1, k).view(np.uint8), want.view(np.uint8)), k
+    e.close()
+
+
+@pytest.mark.parametrize("shape,steps", [(synth.TINY, 24), (TWO_1P3B, 4)], ids=["tiny", "1p3b-2layer"])
+def test_host_decode_followed_by_oracle(shape, steps):
+    seed = synth.SEED_BASE + 32
+    e = _engine(shape, seed)
+    om = oracle.Model(shape, synth.gen_model(shape, seed))
+    st = oracle.State(shape)
+    stats = new_flip_stats()
+    tok = int(synth.gen_tokens(seed, 0, 1, shape.vocab)[0])
+    for i in range(steps):
+        tr = e.trace_step(np.array([tok], np.int32))
+        check_acc(om, tr, [0], range(shape.n_layer), what=f"step {i}")
+        oh, ol, _ = oracle_follow_step(om, st, tok, tr, stats=stats)
+        for l in range(shape.n_layer + 1):
+            assert_close(tr["h"][l, 0], oh[l], what=f"step {i} h layer {l}")
+        assert_close(tr["logits"][0], ol, what=f"step {i} logits")
+        tok = int(np.argmax(tr["logits"][0]))
+    conv, ssm = e.get_state(0)
+    assert_close(conv, st.conv, what="conv state")
+    assert_close(ssm, st.ssm, what="ssm state")
+    assert_flip_fraction(stats, "host decode")
+    e.close()
+
+
+def _run(e, toks, steps, B):
+    """`steps` greedy steps from toks [B]; returns (logits of each step, tokens, state of every slot)."""
+    lgs, outs = [], []
+    t = np.array(toks, np.int32)
+    for _ in range(steps):
+        lg, nx = e.decode_step(t)
+        lgs.append(lg)
+        outs.append(nx)
+        t = nx
+    return np.array(lgs), np.array(outs), [e.get_state(b) for b in range(B)]
+
+
+def _same(a, b):
+    (la, ta, sa), (lb, tb, sb) = a, b
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+    assert np.array_equal(ta, tb)
+    for (ca, xa), (cb, xb) in zip(sa, sb):
+        assert np.array_equal(ca.view(np.uint32), cb.view(np.uint32))
+        assert np.array_equal(xa.view(np.uint32), xb.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape,steps", [(synth.TINY, 6), (TWO_1P3B, 2)], ids=["tiny", "1p3b-2layer"])
+def test_host_instruction_paths_give_the_same_bits(shape, steps):
+    if not _has_vnni():
+        pytest.skip("this CPU has no AVX-512 VNNI")
+    seed = synth.SEED_BASE + 33
+    toks = synth.gen_tokens(seed, 0, 2, shape.vocab)
+    runs = []
+    for isa in ("avx512vnni", "portable"):
+        e = _engine(shape, seed, max_batch=2, isa=isa)
+        assert e.isa == isa
+        runs.append(_run(e, toks, steps, 2))
+        e.close()
+    _same(*runs)
+
+
+def test_host_thread_count_and_batch_do_not_change_results():
+    shape, seed, steps = synth.TINY, synth.SEED_BASE + 34, 5
+    toks = synth.gen_tokens(seed, 0, 3, shape.vocab)
+    runs = []
+    for threads in (1, 3, 8):
+        e = _engine(shape, seed, max_batch=3, threads=threads)
+        runs.append(_run(e, toks, steps, 3))
+        e.close()
+    _same(runs[0], runs[1])
+    _same(runs[0], runs[2])
+    # each sequence alone equals its row of the batch
+    lg3, tk3, st3 = runs[0]
+    for b in range(3):
+        e = _engine(shape, seed, max_batch=1, threads=2)
+        lg1, tk1, st1 = _run(e, toks[b:b + 1], steps, 1)
+        assert np.array_equal(lg1[:, 0].view(np.uint32), lg3[:, b].view(np.uint32))
+        assert np.array_equal(tk1[:, 0], tk3[:, b])
+        for x, y in zip(st1[0], st3[b]):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+        e.close()
+
+
+def test_host_prefill_is_the_decode_loop_and_generate_the_step_loop():
+    shape, seed, T = synth.TINY, synth.SEED_BASE + 35, 9
+    prompt = synth.gen_tokens(seed, 1, 2 * T, shape.vocab).reshape(2, T)
+    a = _engine(shape, seed, max_batch=2)
+    lga, nxa = a.prefill(prompt)
+    b = _engine(shape, seed, max_batch=2)
+    for t in range(T):
+        lgb, nxb = b.decode_step(prompt[:, t])
+    assert np.array_equal(lga.view(np.uint32), lgb.view(np.uint32))
+    assert np.array_equal(nxa, nxb)
+    for s in range(2):
+        for x, y in zip(a.get_state(s), b.get_state(s)):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    tok = nxa.copy()
+    out = a.generate(tok, 6)
+    t = nxb.copy()
+    for i in range(6):
+        _, t = b.decode_step(t)
+        assert np.array_equal(out[i], t)
+    assert np.array_equal(tok, out[-1])
+    a.close()
+    b.close()
+
+
+def test_host_dt_zero_leaves_state_bit_identical():
+    shape, seed = synth.TINY, synth.SEED_BASE + 36
+    e = _engine(shape, seed)
+    for l in range(shape.n_layer):
+        e.set_tensor(l, "dt_bias", np.full(shape.n_heads, -1e4, np.float32))
+    rng = np.random.default_rng(5)
+    ssm = (rng.standard_normal((shape.n_layer, shape.n_heads, shape.headdim, shape.d_state)) * 0.5).astype(np.float32)
+    e.set_state(0, ssm=ssm)
+    e.decode_step(np.array([7], np.int32))
+    assert np.array_equal(e.get_state(0)[1].view(np.uint32), ssm.view(np.uint32))
+    e.close()
+
+
+def test_host_exact_logit_tie_takes_lowest_index():
+    shape, seed = synth.TINY, synth.SEED_BASE + 37
+    e = _engine(shape, seed)
+    tok = np.array([11], np.int32)
+    lg, nx = e.decode_step(tok)
+    a = int(nx[0])
+    assert a == int(np.argmax(lg[0]))
+    E, sE = e.get_tensor(-1, "E"), e.get_tensor(-1, "sE")
+    for other in [v for v in (0, a + 1, shape.vocab - 1) if v not in (a, 11) and v < shape.vocab]:
+        E2, sE2 = E.copy(), sE.copy()
+        E2[other], sE2[other] = E[a], sE[a]
+        e.set_tensor(-1, "E", E2)
+        e.set_tensor(-1, "sE", sE2)
+        e.reset_state(1)
+        lg2, nx2 = e.decode_step(tok)
+        assert lg2[0, other] == lg2[0, a]
+        assert int(nx2[0]) == min(other, a)
+    e.close()
+
+
+def test_host_zero_gate_adds_nothing():
+    shape, seed = synth.TINY, synth.SEED_BASE + 38
+    e = _engine(shape, seed)
+    for l in range(shape.n_layer):
+        sw, sb = e.get_tensor(l, "in_sw"), e.get_tensor(l, "in_sB")
+        sw[:shape.d_inner] = 0.0
+        sb[:shape.d_inner] = 0.0
+        e.set_tensor(l, "in_sw", sw)
+        e.set_tensor(l, "in_sB", sb)
+    tr = e.trace_step(np.array([3], np.int32))
+    assert not tr["q2"].any()
+    for l in range(shape.n_layer):
+        assert np.array_equal(tr["h"][l + 1].view(np.uint32), tr["h"][l].view(np.uint32))
+    e.close()
+
+
+def test_host_argument_errors_leave_state_untouched():
+    shape, seed = synth.TINY, synth.SEED_BASE + 39
+    e = _engine(shape, seed, max_batch=2)
+    e.decode_step(np.array([1, 2], np.int32))
+    before = [e.get_state(b) for b in range(2)]
+    for bad in (np.array([1, shape.vocab], np.int32), np.array([-1, 0], np.int32), np.zeros(3, np.int32),
+                np.zeros(0, np.int32)):
+        with pytest.raises(H.DfssmError):
+            e.decode_step(bad)
+    with pytest.raises(H.DfssmError):
+        e.prefill(np.full((1, 3), shape.vocab, np.int32))
+    short = np.zeros(3, np.float32)  # in_sw of layer 0 has d_in_proj elements
+    with pytest.raises(H.DfssmError):
+        H.call("dfssm_host_set_tensor", e._h, 0, 1, short.ctypes.data, short.nbytes)
+    after = [e.get_state(b) for b in range(2)]
+    for (c0, s0), (c1, s1) in zip(before, after):
+        assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+    with pytest.raises(H.DfssmError):
+        H.HostEngine(2, 100, 512, 16, 32, 1024)  # d_model not a multiple of 64
+    e.close()
