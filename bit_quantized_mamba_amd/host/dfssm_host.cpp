@@ -169,7 +169,6 @@ void gen_fill(void* dst, size_t n, Dist dist, uint64_t key, double a, double b) 
 inline float silu(float v) { return v / (1.0f + std::exp(-v)); }
 inline float softplus(float v) { return v > 20.0f ? v : std::log1p(std::exp(v)); }
 
-constexpr int kBlocks = 16;  // fixed blocks of a row reduction
 
 }  // namespace
 
@@ -198,8 +197,10 @@ struct dfssm_host {
 
   std::vector<float> conv, ssm;  // state
   // workspace
-  std::vector<float> h, zx, xc, g, s, t, stats, lg;
-  std::vector<int32_t> qsum;
+  std::vector<float> h, zx, xc, g, s, stats, lg;
+  std::vector<int32_t> part;                 // [B][chunks][33]: per-chunk LoRA-down dots and code sum
+  std::vector<int32_t> tl_qsum;              // per thread [B]: code sums
+  std::vector<float> tl_t;                   // per thread [B][32]: LoRA-down vectors
   std::vector<int8_t> q;
   std::vector<uint8_t> qu;
   std::vector<float> best_v;
@@ -328,36 +329,43 @@ struct Trace {
   int32_t *acc1 = nullptr, *acc2 = nullptr;
 };
 
-// Inside the parallel region: RMSNorm + int8 quantisation of B rows x[b]
-// (length K, weight w): codes into c->q (row stride K), the unsigned copy
-// q ^ 0x80 into c->qu, scales into c->s, sums of codes into c->qsum.
-// u = rstd (x w) with rstd = 1 / sqrt(mean(x^2) + eps); amax = rstd max |x w|;
-// q = clamp(rint(u (127 / amax)), -127, 127), s = amax / 127 (zero row: 0).
-void quant_rows(dfssm_host* c, const float* x, const float* w, int K, int B) {
-  const int blk = K / kBlocks;
-  float* st = c->stats.data();  // [B][kBlocks][2]
-#pragma omp for schedule(static)
-  for (int i = 0; i < B * kBlocks; ++i) {
-    const int b = i / kBlocks, k0 = (i % kBlocks) * blk;
-    const float* xr = x + (size_t)b * K + k0;
-    const float* wr = w + k0;
-    float ss = 0.0f, pm = 0.0f;
-    for (int k = 0; k < blk; ++k) {
-      ss += xr[k] * xr[k];
-      pm = std::max(pm, std::fabs(xr[k] * wr[k]));
-    }
-    st[2 * i] = ss;
-    st[2 * i + 1] = pm;
+constexpr int kChunk = 256;  // codes per work item of the quantiser
+
+// Sum of squares and max |x w| of one fixed block of a row, written where
+// the row's quantiser finds them (stats [B][nb][2]).  Producers of a row
+// call it for their blocks as they finish them, so the statistics cost no
+// extra pass and no extra barrier.
+inline void block_stats(const float* x, const float* w, int n, float* out) {
+  float ss = 0.0f, pm = 0.0f;
+  for (int k = 0; k < n; ++k) {
+    ss += x[k] * x[k];
+    pm = std::max(pm, std::fabs(x[k] * w[k]));
   }
-  // (implicit barrier)
-  const int nchunk = (K + 255) / 256;
+  out[0] = ss;
+  out[1] = pm;
+}
+
+// Inside the parallel region: RMSNorm + int8 quantisation of B rows x[b]
+// (length K, weight w) whose nb block statistics are in stats [B][nb][2]
+// (summed here in block order): codes into c->q (row stride K), the unsigned
+// copy q + 128 into c->qu, scales into c->s.  u = rstd (x w) with
+// rstd = 1 / sqrt(mean(x^2) + eps); amax = rstd max |x w|;
+// q = clamp(rint(u (127 / amax)), -127, 127), s = amax / 127 (zero row: 0).
+// Each chunk of kChunk codes also leaves its code sum and, with A (the LoRA
+// down matrix, r rows of K), its r integer dot products with the codes (in
+// the unsigned-offset form) in c->part [B][nchunk][33]; row_terms adds the
+// chunks up.  One barrier.
+void quant_rows(dfssm_host* c, const IntOps& ops, const float* x, const float* w, int K, int B, const int8_t* A,
+                const float* stats, int nb) {
+  const int r = c->r;
+  const int nchunk = (K + kChunk - 1) / kChunk;
 #pragma omp for schedule(static)
   for (int i = 0; i < B * nchunk; ++i) {
-    const int b = i / nchunk, k0 = (i % nchunk) * 256, k1 = std::min(K, k0 + 256);
+    const int b = i / nchunk, ci = i % nchunk, k0 = ci * kChunk, k1 = std::min(K, k0 + kChunk);
     float ss = 0.0f, pm = 0.0f;
-    for (int j = 0; j < kBlocks; ++j) {
-      ss += st[2 * (b * kBlocks + j)];
-      pm = std::max(pm, st[2 * (b * kBlocks + j) + 1]);
+    for (int j = 0; j < nb; ++j) {
+      ss += stats[2 * (b * nb + j)];
+      pm = std::max(pm, stats[2 * (b * nb + j) + 1]);
     }
     const float rstd = 1.0f / std::sqrt(ss / (float)K + c->eps);
     const float amax = rstd * pm;
@@ -365,32 +373,38 @@ void quant_rows(dfssm_host* c, const float* x, const float* w, int K, int B) {
     const float* xr = x + (size_t)b * K;
     int8_t* qr = c->q.data() + (size_t)b * K;
     uint8_t* ur = c->qu.data() + (size_t)b * K;
+    int sq = 0;
     for (int k = k0; k < k1; ++k) {
       float v = std::rint(rstd * (xr[k] * w[k]) * inv);
       v = std::min(std::max(v, -127.0f), 127.0f);
       qr[k] = (int8_t)(int)v;
       ur[k] = (uint8_t)((int)qr[k] + 128);
+      sq += qr[k];
     }
-    if (k0 == 0) c->s[b] = amax > 0.0f ? amax / 127.0f : 0.0f;
+    int32_t* part = c->part.data() + ((size_t)b * nchunk + ci) * 33;
+    part[32] = sq;
+    if (A)
+      for (int k = 0; k < r; ++k) part[k] = ops.dotu(ur + k0, A + (size_t)k * K + k0, k1 - k0);
+    if (ci == 0) c->s[b] = amax > 0.0f ? amax / 127.0f : 0.0f;
   }
-#pragma omp for schedule(static)
-  for (int b = 0; b < B; ++b) {
-    int sq = 0;
-    const int8_t* qr = c->q.data() + (size_t)b * K;
-    for (int k = 0; k < K; ++k) sq += qr[k];
-    c->qsum[b] = sq;
-  }
+  // (implicit barrier)
 }
 
-// LoRA down of B code rows: t[b][k] = float(sum_i A[k][i] q_b[i]) sA[k] s_b
-void lora_down(dfssm_host* c, const IntOps& ops, const int8_t* A, const int32_t* asum, const float* sA, int K,
-               int B) {
-  const int r = c->r;
-#pragma omp for schedule(static)
-  for (int i = 0; i < B * r; ++i) {
-    const int b = i / r, k = i % r;
-    const int dot = ops.dotu(c->qu.data() + (size_t)b * K, A + (size_t)k * K, K) - 128 * asum[k];
-    c->t[(size_t)b * 32 + k] = (float)dot * sA[k] * c->s[b];
+// Per thread, after quant_rows: the code sums and the LoRA-down vectors of
+// the B rows, t[b][k] = float(sum_i A[k][i] q_b[i]) sA[k] s_b (the chunks'
+// integers added, the offset's 128 sum_i A[k][i] taken off: exact).
+void row_terms(dfssm_host* c, int K, int B, const int32_t* asum, const float* sA, int32_t* qsum, float* t) {
+  const int nchunk = (K + kChunk - 1) / kChunk, r = c->r;
+  for (int b = 0; b < B; ++b) {
+    int sq = 0;
+    int acc[32] = {};
+    for (int ci = 0; ci < nchunk; ++ci) {
+      const int32_t* part = c->part.data() + ((size_t)b * nchunk + ci) * 33;
+      sq += part[32];
+      for (int k = 0; k < r; ++k) acc[k] += part[k];
+    }
+    qsum[b] = sq;
+    for (int k = 0; k < r; ++k) t[(size_t)b * 32 + k] = (float)(acc[k] - 128 * asum[k]) * sA[k] * c->s[b];
   }
 }
 
@@ -399,19 +413,24 @@ constexpr int kRowBlock = 16;  // scaffold rows per integer call
 // scaffold + LoRA projection of B code rows (length K) to rows [0, n):
 // y = float(2 pos - sum q) sw s + sB sum_k B[o][k] t_k (k in order, from the
 // transposed copy Bt [r][n] so that a block of rows is one vector), then
-// `out(b, o, y, acc)`
-template <class Out>
+// `out(b, o, y, acc)` per row and `done(b, block, o0, count)` per block of
+// kRowBlock rows
+template <class Out, class Done>
 void project(dfssm_host* c, const IntOps& ops, const uint32_t* bits, const float* sw, const int8_t* Bt,
-             const float* sB, int K, int n, int B, Out out) {
+             const float* sB, const int32_t* asum, const float* sA, int K, int n, int B, Out out, Done done) {
   const int r = c->r;
   const int nblk = (n + kRowBlock - 1) / kRowBlock;
+  const size_t me = (size_t)omp_get_thread_num();
+  int32_t* qsum = c->tl_qsum.data() + me * c->maxB;
+  float* tt = c->tl_t.data() + me * c->maxB * 32;
+  row_terms(c, K, B, asum, sA, qsum, tt);
 #pragma omp for schedule(static)
   for (int blk = 0; blk < nblk; ++blk) {
     const int o0 = blk * kRowBlock, cnt = std::min(n, o0 + kRowBlock) - o0;
     for (int b = 0; b < B; ++b) {
       int32_t pos[kRowBlock];
       ops.pos_rows(bits, o0, o0 + cnt, c->q.data() + (size_t)b * K, K, pos);
-      const float* tb = c->t.data() + (size_t)b * 32;
+      const float* tb = tt + (size_t)b * 32;
       float lo[kRowBlock] = {};
       for (int k = 0; k < r; ++k) {
         const int8_t* bk = Bt + (size_t)k * n + o0;
@@ -419,9 +438,10 @@ void project(dfssm_host* c, const IntOps& ops, const uint32_t* bits, const float
         for (int i = 0; i < cnt; ++i) lo[i] += (float)bk[i] * tk;
       }
       for (int i = 0; i < cnt; ++i) {
-        const int o = o0 + i, acc = 2 * pos[i] - c->qsum[b];
+        const int o = o0 + i, acc = 2 * pos[i] - qsum[b];
         out(b, o, (float)acc * sw[o] * c->s[b] + sB[o] * lo[i], acc);
       }
+      done(b, blk, o0, cnt);
     }
   }
 }
@@ -436,12 +456,19 @@ void step(dfssm_host* c, const IntOps& ops, const int32_t* tok, int B, const Tra
   float* hb = c->h.data();
   float* lg = logits ? logits : c->lg.data();
   const int nthr = c->threads;
+  // norm statistics of the residual rows by blocks of kRowBlock, of the gated rows by heads
+  float* st1 = c->stats.data();
+  float* st2 = c->stats.data() + (size_t)B * (dm / kRowBlock) * 2;
+  const int nb1 = dm / kRowBlock, nb2 = H;
 #pragma omp parallel num_threads(nthr)
   {
+    const float* w0 = Lm > 0 ? c->lt[0][DFSSM_T_NORM_W].p<float>() : c->gt[DFSSM_G_FINAL_NORM].p<float>();
 #pragma omp for schedule(static)
-    for (int b = 0; b < B; ++b) {
-      const int tk = tok[b];
-      for (int i = 0; i < dm; ++i) hb[(size_t)b * dm + i] = (float)E[(size_t)tk * dm + i] * sE[tk];
+    for (int i = 0; i < B * nb1; ++i) {
+      const int b = i / nb1, o0 = (i % nb1) * kRowBlock, tk = tok[b];
+      float* hr = hb + (size_t)b * dm + o0;
+      for (int k = 0; k < kRowBlock; ++k) hr[k] = (float)E[(size_t)tk * dm + o0 + k] * sE[tk];
+      block_stats(hr, w0 + o0, kRowBlock, st1 + 2 * (size_t)i);
     }
     for (int l = 0; l < Lm; ++l) {
       auto& T = c->lt[l];
@@ -450,39 +477,40 @@ void step(dfssm_host* c, const IntOps& ops, const int32_t* tok, int B, const Tra
         for (int b = 0; b < B; ++b) std::memcpy(tr->h + ((size_t)l * B + b) * dm, hb + (size_t)b * dm, 4 * dm);
       }
       // ---- pre-norm, quantise, LoRA down, in_proj
-      quant_rows(c, hb, T[DFSSM_T_NORM_W].p<float>(), dm, B);
+      quant_rows(c, ops, hb, T[DFSSM_T_NORM_W].p<float>(), dm, B, T[DFSSM_T_IN_A].p<int8_t>(), st1, nb1);
       if (tr && tr->q1) {
 #pragma omp for schedule(static)
         for (int b = 0; b < B; ++b) std::memcpy(tr->q1 + ((size_t)l * B + b) * dm, c->q.data() + (size_t)b * dm, dm);
       }
-      lora_down(c, ops, T[DFSSM_T_IN_A].p<int8_t>(), c->asum_in[l].data(), T[DFSSM_T_IN_SA].p<float>(), dm, B);
       float* zx = c->zx.data();
-      int32_t* a1 = tr && tr->acc1 ? tr->acc1 + (size_t)l * B * dp : nullptr;
-      project(c, ops, T[DFSSM_T_IN_BITS].p<uint32_t>(), T[DFSSM_T_IN_SW].p<float>(), c->bt_in[l].data(),
-              T[DFSSM_T_IN_SB].p<float>(), dm, dp, B, [&](int b, int o, float y, int acc) {
-                zx[(size_t)b * dp + o] = y;
-                if (a1) a1[(size_t)b * dp + o] = acc;
-              });
-      // ---- conv shift register + SiLU on [x, B, C] (in_proj rows di .. di + cd)
+      float* xc = c->xc.data();
       const float* cw = T[DFSSM_T_CONV_W].p<float>();
       const float* cb = T[DFSSM_T_CONV_B].p<float>();
-      float* xc = c->xc.data();
-#pragma omp for schedule(static)
-      for (int i = 0; i < B * cd; ++i) {
-        const int b = i / cd, ch = i % cd;
-        float* win = c->conv.data() + (size_t)b * c->conv_per_seq() + ((size_t)l * cd + ch) * 3;
-        const float v = zx[(size_t)b * dp + di + ch];
-        const float* wc = cw + (size_t)ch * 4;
-        const float a = cb[ch] + wc[0] * win[0] + wc[1] * win[1] + wc[2] * win[2] + wc[3] * v;
-        win[0] = win[1];
-        win[1] = win[2];
-        win[2] = v;
-        xc[(size_t)b * cd + ch] = silu(a);
-      }
+      int32_t* a1 = tr && tr->acc1 ? tr->acc1 + (size_t)l * B * dp : nullptr;
+      // in_proj rows, and for rows di .. di + cd ([x, B, C]) the conv shift
+      // register + SiLU of that channel, by the thread that made the row
+      project(c, ops, T[DFSSM_T_IN_BITS].p<uint32_t>(), T[DFSSM_T_IN_SW].p<float>(), c->bt_in[l].data(),
+              T[DFSSM_T_IN_SB].p<float>(), c->asum_in[l].data(), T[DFSSM_T_IN_SA].p<float>(), dm, dp, B,
+              [&](int b, int o, float y, int acc) {
+                zx[(size_t)b * dp + o] = y;
+                if (a1) a1[(size_t)b * dp + o] = acc;
+                const int ch = o - di;
+                if (ch >= 0 && ch < cd) {
+                  float* win = c->conv.data() + (size_t)b * c->conv_per_seq() + ((size_t)l * cd + ch) * 3;
+                  const float* wc = cw + (size_t)ch * 4;
+                  const float a = cb[ch] + wc[0] * win[0] + wc[1] * win[1] + wc[2] * win[2] + wc[3] * y;
+                  win[0] = win[1];
+                  win[1] = win[2];
+                  win[2] = y;
+                  xc[(size_t)b * cd + ch] = silu(a);
+                }
+              },
+              [](int, int, int, int) {});
       // ---- SSM recurrence and gate, one (sequence, head) per iteration
       const float* alog = T[DFSSM_T_A_LOG].p<float>();
       const float* dtb = T[DFSSM_T_DT_BIAS].p<float>();
       const float* Dv = T[DFSSM_T_D].p<float>();
+      const float* gw = T[DFSSM_T_GNORM_W].p<float>();
       float* g = c->g.data();
 #pragma omp for schedule(static)
       for (int i = 0; i < B * H; ++i) {
@@ -510,19 +538,24 @@ void step(dfssm_host* c, const IntOps& ops, const int32_t* tok, int B, const Tra
           const float y = part[0] + Dv[hd] * x;
           g[(size_t)b * di + ch] = y * silu(zx[(size_t)b * dp + ch]);
         }
+        block_stats(g + (size_t)b * di + hd * P, gw + hd * P, P, st2 + 2 * (size_t)i);
       }
       // ---- gated RMSNorm, quantise, LoRA down, out_proj + residual
-      quant_rows(c, g, T[DFSSM_T_GNORM_W].p<float>(), di, B);
+      quant_rows(c, ops, g, gw, di, B, T[DFSSM_T_OUT_A].p<int8_t>(), st2, nb2);
       if (tr && tr->q2) {
 #pragma omp for schedule(static)
         for (int b = 0; b < B; ++b) std::memcpy(tr->q2 + ((size_t)l * B + b) * di, c->q.data() + (size_t)b * di, di);
       }
-      lora_down(c, ops, T[DFSSM_T_OUT_A].p<int8_t>(), c->asum_out[l].data(), T[DFSSM_T_OUT_SA].p<float>(), di, B);
       int32_t* a2 = tr && tr->acc2 ? tr->acc2 + (size_t)l * B * dm : nullptr;
+      const float* wn = l + 1 < Lm ? c->lt[l + 1][DFSSM_T_NORM_W].p<float>() : c->gt[DFSSM_G_FINAL_NORM].p<float>();
       project(c, ops, T[DFSSM_T_OUT_BITS].p<uint32_t>(), T[DFSSM_T_OUT_SW].p<float>(), c->bt_out[l].data(),
-              T[DFSSM_T_OUT_SB].p<float>(), di, dm, B, [&](int b, int o, float y, int acc) {
+              T[DFSSM_T_OUT_SB].p<float>(), c->asum_out[l].data(), T[DFSSM_T_OUT_SA].p<float>(), di, dm, B,
+              [&](int b, int o, float y, int acc) {
                 hb[(size_t)b * dm + o] += y;
                 if (a2) a2[(size_t)b * dm + o] = acc;
+              },
+              [&](int b, int blk, int o0, int cnt) {  // statistics for the next norm
+                block_stats(hb + (size_t)b * dm + o0, wn + o0, cnt, st1 + 2 * ((size_t)b * nb1 + blk));
               });
     }
     if (tr && tr->h) {
@@ -531,7 +564,7 @@ void step(dfssm_host* c, const IntOps& ops, const int32_t* tok, int B, const Tra
     }
     if (head) {
       // ---- final norm, quantise, tied int8 LM head, greedy argmax
-      quant_rows(c, hb, c->gt[DFSSM_G_FINAL_NORM].p<float>(), dm, B);
+      quant_rows(c, ops, hb, c->gt[DFSSM_G_FINAL_NORM].p<float>(), dm, B, nullptr, st1, nb1);
       if (tr && tr->qf) {
 #pragma omp for schedule(static)
         for (int b = 0; b < B; ++b) std::memcpy(tr->qf + (size_t)b * dm, c->q.data() + (size_t)b * dm, dm);
@@ -673,9 +706,10 @@ dfssm_status dfssm_host_create(const dfssm_config* cfg, int32_t n_threads, dfssm
     c->xc.assign(B * c->cd, 0.0f);
     c->g.assign(B * c->di, 0.0f);
     c->s.assign(B, 0.0f);
-    c->t.assign(B * 32, 0.0f);
-    c->stats.assign(B * kBlocks * 2, 0.0f);
-    c->qsum.assign(B, 0);
+    c->stats.assign(B * ((size_t)c->dm / kRowBlock + c->H) * 2, 0.0f);
+    c->part.assign(B * ((wide + kChunk - 1) / kChunk) * 33, 0);
+    c->tl_qsum.assign((size_t)c->threads * B, 0);
+    c->tl_t.assign((size_t)c->threads * B * 32, 0.0f);
     c->q.assign(B * wide, 0);
     c->qu.assign(B * wide, 0);
   } catch (const std::bad_alloc&) {
