@@ -103,7 +103,10 @@ __global__ __launch_bounds__(1024) void scan1_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float red4[4][16][P];
   __shared__ float sBC[2 * N];
   const int quarter = threadIdx.x >> 8, t = threadIdx.x & 255;
-  const int h = 4 * blockIdx.x + quarter, b = blockIdx.y;
+  // items (four heads of one sequence) blockIdx.x, blockIdx.x + gridDim.x, ...
+  const int ngrp = (a.H + 3) / 4, nitems = ngrp * a.B;
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+  const int h = 4 * (item % ngrp) + quarter, b = item / ngrp;
   const bool live = h < a.H;
   float (*red)[P] = red4[quarter];
   const int lane = t & 63, pb = t >> 6, pq = lane & 3, ns = lane >> 2;
@@ -155,6 +158,8 @@ __global__ __launch_bounds__(1024) void scan1_kernel(ScanArgs a) {
     const float x = xr[h * P + t];
     const float z = a.zx[(size_t)b * a.ldzx + h * P + t];
     a.g[(size_t)b * a.d_inner + h * P + t] = (yy + a.D[h] * x) * silu_f(z);
+  }
+  __syncthreads();  // sBC and red are the next item's
   }
 }
 
@@ -568,7 +573,14 @@ hipError_t launch_scan(const ScanArgs& a, int P, int N, hipStream_t st) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
   const dim3 grid(a.H, a.B);
   if (a.T == 1 && P == 64 && N == 128) {
-    hipLaunchKernelGGL(scan1_kernel, dim3((a.H + 3) / 4, a.B), dim3(1024), 0, st, a);
+    // Two items per workgroup once there are many more items than the 512
+    // workgroups that fit the chip at once (batch 512 as two chains of 256:
+    // 20.64-20.69 vs 20.88-20.92 ms per step over 32 steps on one box, the
+    // same over 8); with fewer items that would leave CUs idle (batch 32:
+    // 2.69 vs 2.55 ms), and four or more per workgroup measured no better.
+    const int nitems = (a.H + 3) / 4 * a.B;
+    const int per = nitems >= 2048 ? 2 : 1;
+    hipLaunchKernelGGL(scan1_kernel, dim3((nitems + per - 1) / per), dim3(1024), 0, st, a);
     return hipGetLastError();
   }
   if (P == 64 && N == 128) {
