@@ -652,7 +652,9 @@ dfssm_status dfssm_host_create(const dfssm_config* cfg, int32_t n_threads, dfssm
   if (!cfg || !out) return fail(DFSSM_E_INVALID, "null argument");
   *out = nullptr;
   const dfssm_config& k = *cfg;
-  if (k.n_layer < 1 || k.d_model < 64 || k.d_model % 64 || k.d_inner < 64 || k.d_inner % 64 || k.d_state < 16 ||
+  // (d_model, d_inner <= 32768 keeps every offset int8 dot product, 255 * 127 * K, inside int32)
+  if (k.n_layer < 1 || k.d_model < 64 || k.d_model % 64 || k.d_model > 32768 || k.d_inner < 64 || k.d_inner % 64 ||
+      k.d_inner > 32768 || k.d_state < 16 ||
       k.d_state % 16 || k.headdim < 1 || k.d_inner % k.headdim || k.vocab < 1 || k.d_conv != 4 || k.lora_rank < 1 ||
       k.lora_rank > 32 || k.max_batch < 1 || k.max_batch > 1024)
     return fail(DFSSM_E_UNSUPPORTED, "shape outside the host backend's support (see dfssm_host.h)");

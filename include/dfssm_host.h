@@ -13,9 +13,9 @@
  * §3 reports the resulting CPU speed-up (2.9x on an Intel Xeon, baseline
  * unstated).
  *
- * Here a weight row's bits become a 0/1 byte vector (one masked byte
- * broadcast per 64 weights), dpbusd sums the int8 codes where a bit is set
- * (pos), and the scaffold sum is 2 pos - sum(q): an exact int32.  The LM
+ * Here 64 bits of a weight row become a 0/1 byte vector (one mask load and
+ * one masked move of a vector of ones), dpbusd sums the int8 codes where a
+ * bit is set (pos), and the scaffold sum is 2 pos - sum(q): an exact int32.  The LM
  * head and the LoRA down products are int8 x int8 dot products on the same
  * instruction (one operand offset by 128, the offset's exact contribution
  * subtracted).  Every floating-point operation is shared by both integer
@@ -27,8 +27,9 @@
  *    synchronous and returns when its results are written.
  *  - Shapes, tensor kinds, layouts, quantisation and the synthetic generator
  *    are those of dfssm.h (dfssm_config, DFSSM_T_*, DFSSM_G_*).  max_chunk_rows
- *    is ignored.  Supported: d_model and d_inner multiples of 64; d_state a
- *    multiple of 16; d_conv = 4; 1 <= lora_rank <= 32; 1 <= max_batch <= 1024.
+ *    is ignored.  Supported: d_model and d_inner multiples of 64 up to 32768;
+ *    d_state a multiple of 16; d_conv = 4; 1 <= lora_rank <= 32;
+ *    1 <= max_batch <= 1024.
  *  - Every function returns a dfssm_status; on error outputs and state are
  *    untouched and dfssm_host_last_error() describes it.  No C++ exception
  *    crosses this boundary.  A context is not thread-safe; each call runs
