@@ -249,3 +249,29 @@ def test_host_argument_errors_leave_state_untouched():
     with pytest.raises(H.DfssmError):
         H.HostEngine(2, 100, 512, 16, 32, 1024)  # d_model not a multiple of 64
     e.close()
+
+
+def test_host_full_model_prefill_and_greedy_steps_followed_by_oracle():
+    # the 48-layer model at its real vocabulary: a 4-token prompt, then 6
+    # greedy steps, each traced and followed by the oracle on the same codes
+    s, seed = synth.FULL_1P3B, synth.SEED_BASE + 2
+    e = _engine(s, seed, threads=0)
+    om = oracle.Model(s, synth.gen_model(s, seed))
+    st = oracle.State(s)
+    stats = new_flip_stats()
+    prompt = synth.gen_tokens(seed, 0, 4, s.vocab)
+    for t in prompt[:-1]:
+        tr = e.trace_step(np.array([t], np.int32), want_acc=False)
+        oracle_follow_step(om, st, int(t), tr, stats=stats)
+    tok = int(prompt[-1])
+    for i in range(6):
+        tr = e.trace_step(np.array([tok], np.int32), want_acc=False)
+        oh, ol, _ = oracle_follow_step(om, st, tok, tr, stats=stats)
+        assert_close(tr["h"][s.n_layer, 0], oh[s.n_layer], what=f"step {i} final residual")
+        assert_close(tr["logits"][0], ol, what=f"step {i} logits")
+        tok = int(np.argmax(tr["logits"][0]))
+    conv, ssm = e.get_state(0)
+    assert_close(ssm, st.ssm, what="ssm state")
+    assert_close(conv, st.conv, what="conv state")
+    assert_flip_fraction(stats, "host full model")
+    e.close()
