@@ -447,3 +447,40 @@ def test_caller_arena_equals_library_memory(shape):
     ea.close()
     eb.close()
     del arena
+
+
+# ---------------------------------------------------------------------------
+# the device engine and the host engine: two implementations of one step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["persistent", "gemm"])
+def test_device_and_host_engines_agree(path):
+    # the same seeded model and inputs on the device (persistent kernel or the
+    # batched path) and on the host engine, teacher-forced over 12 steps:
+    # logits and final states within the 1e-3 metric of each other, and the
+    # int8 codes equal but for the rare value within rounding of a tie
+    H = pytest.importorskip("bit_quantized_mamba_amd.host")
+    s, seed = synth.TINY, synth.SEED_BASE + 43
+    dev = engine(s)
+    dev.set_path(path)
+    dev.load_synthetic(seed)
+    host = H.HostEngine.from_shape(s, threads=4)
+    host.load_synthetic(seed)
+    toks = synth.gen_tokens(seed, 2, 12, s.vocab)
+    differ = total = 0
+    for i, t in enumerate(toks):
+        trd = trace_to_numpy(dev.trace_step(_i32([t])))
+        trh = host.trace_step(np.array([t], np.int32), want_acc=False)
+        assert_close(trd["logits"][0], trh["logits"][0], what=f"logits step {i}")
+        for k in ("q1", "q2", "qf"):
+            diff = np.abs(trd[k].astype(np.int32) - trh[k].astype(np.int32))
+            assert diff.max() <= 1, (k, i)
+            differ += int(np.count_nonzero(diff))
+            total += diff.size
+    assert differ <= 5e-4 * total, (differ, total)
+    cd, sd = dev.get_state(0)
+    ch, sh = host.get_state(0)
+    assert_close(sd, sh, what="ssm state")
+    assert_close(cd, ch, what="conv state")
+    dev.close()
+    host.close()
