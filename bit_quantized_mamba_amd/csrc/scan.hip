@@ -358,7 +358,10 @@ __device__ __forceinline__ void ssd_stage_load(const ScanArgs& a, int hp, int ti
     const int j = idx >> 5, q = idx & 31;
     st.b[k] = *(const float4*)(recB + j * 128 + 4 * q);
     st.c[k] = *(const float4*)(recC + j * 128 + 4 * q);
-    st.z[k] = *(const float4*)(a.zx + (rowb + min(t0 + j, a.T - 1)) * a.ldzx + (size_t)(2 * hp) * 64 + 4 * q);
+    // z is read once: non-temporal (54.70-54.74 vs 54.90-55.16 ms per 8 x 2048 prefill)
+    const v4f zv = __builtin_nontemporal_load(
+        (const v4f*)(a.zx + (rowb + min(t0 + j, a.T - 1)) * a.ldzx + (size_t)(2 * hp) * 64 + 4 * q));
+    st.z[k] = make_float4(zv.x, zv.y, zv.z, zv.w);
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
